@@ -1,0 +1,178 @@
+/*
+ * hs2.h - C ABI of libhs2.so: the HySparse2 hybrid-block decode path and the
+ * KV-Bridging projection on one MI355X (gfx950).
+ *
+ * The operations (the pages are news reports of arXiv 2609.26368):
+ *  - A hybrid block is one full-attention layer followed by several sparse-
+ *    attention layers; the full layer picks positions from its attention
+ *    scores and the sparse layers reuse its KV cache and its selection
+ *    (toolnavs.com article 2080, section "Ce que fait HySparse2" (fr) /
+ *    "HySparse2가 한 일" (ko); "Luo Fuli Teases Xiaomi MiMo-V3 Architecture"
+ *    (ai.synthepulse.app), paragraphs on KV Reuse and on token selection).
+ *  - The selection is token-level: the 128 most recent positions always, plus
+ *    1024 positions from before that window (readaitime.com news of
+ *    2026-09-24, paragraph on dropping the separate SWA branch; the toolnavs
+ *    sections above).
+ *  - KV Bridging: each bridged full-attention layer builds its own K and V
+ *    from one shared self-decoder hidden state with its own projections
+ *    (toolnavs.com (ko), section "HySparse2가 한 일").
+ *
+ * Readings taken where the pages are silent: softmax scale 1/sqrt(head_dim);
+ * per-token score = sum over query heads of the softmax probability over the
+ * whole context; window = the last 128 positions, current token included;
+ * top-k taken from the positions before the window; ties to the lower
+ * position; a context of at most window + top_k tokens selects every token;
+ * one selection per sequence (MQA: one KV head).
+ *
+ * Conventions for every call:
+ *  - Pointers marked (device) are device memory on the current HIP device;
+ *    pointers marked (host) are host memory read during the call only.
+ *  - The caller owns every buffer.  The library allocates no device memory,
+ *    keeps no pointer after returning, and never synchronises: work is
+ *    enqueued on `stream` (a hipStream_t passed as void*, NULL = the null
+ *    stream) and buffers must stay alive until that stream has run it.
+ *  - Every argument is validated before any HIP call; a failed check returns
+ *    HS2_ERR_INVALID_ARGUMENT, HS2_ERR_UNSUPPORTED or
+ *    HS2_ERR_WORKSPACE_TOO_SMALL and enqueues nothing.  A failed launch
+ *    returns HS2_ERR_HIP.  hs2_last_error_message() (thread-local) explains
+ *    the last non-OK status.  No C++ exception crosses the ABI.
+ *  - Identical inputs give bitwise-identical outputs (fixed reduction order).
+ *  - Calls that share a workspace must not overlap in time.
+ */
+#ifndef HS2_H
+#define HS2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HS2_OK = 0,
+  HS2_ERR_INVALID_ARGUMENT = 1,
+  HS2_ERR_UNSUPPORTED = 2,
+  HS2_ERR_WORKSPACE_TOO_SMALL = 3,
+  HS2_ERR_HIP = 4
+} hs2_status;
+
+typedef enum {
+  HS2_KV_BF16 = 0,     /* bfloat16 rows, 2 bytes per element                     */
+  HS2_KV_FP8_E4M3 = 1  /* OCP E4M3 codes, 1 byte per element, with per-token fp32
+                          scales: value = E4M3(code) * scale[token]             */
+} hs2_kv_dtype;
+
+/* Shape of one decode call (host struct, passed by pointer).
+ * Supported: n_q_heads 16, head_dim 128, window 128, top_k 1024,
+ * n_sparse_layers 0..8, batch >= 0, max_context <= 2^24.                     */
+typedef struct {
+  int32_t batch;            /* B sequences                                       */
+  int32_t n_q_heads;        /* query heads sharing the one KV head (16)          */
+  int32_t head_dim;         /* D (128)                                           */
+  int32_t window;           /* recent positions always selected (128)            */
+  int32_t top_k;            /* positions selected before the window (1024)       */
+  int32_t n_sparse_layers;  /* n_s sparse layers reusing the selection (0..8)    */
+  int32_t kv_dtype;         /* hs2_kv_dtype                                      */
+  float softmax_scale;      /* multiplies q.k; 1/sqrt(head_dim) in the workloads */
+  int64_t total_tokens;     /* N = seq_offsets[B] (host-known; sizes buffers)    */
+  int64_t max_context;      /* >= every L_b (host-known; sizes the grids)        */
+} hs2_decode_desc;
+
+/* Bytes of workspace hs2_decode_block (and every stage call) needs for
+ * `desc`.  Returns 0 when desc is invalid.                                    */
+size_t hs2_decode_workspace_bytes(const hs2_decode_desc* desc);
+
+/* One decode step of one hybrid block for a packed batch.
+ *
+ * seq_offsets (device) int64 [B+1]: sequence b owns cache rows
+ *   [seq_offsets[b], seq_offsets[b+1]); L_b = their difference, 0 <= L_b <=
+ *   max_context; seq_offsets[B] == total_tokens; the current token's K/V is
+ *   already stored at position L_b - 1.
+ * k_cache, v_cache (device): [N][head_dim] rows, bf16 or E4M3 per kv_dtype,
+ *   16-byte aligned.  This is the shared MQA cache of the block's full layer.
+ * k_scale, v_scale (device) fp32 [N]: per-token scales (E4M3 only, else NULL).
+ * q_full (device) fp32 [B][n_q_heads][head_dim]: the full layer's query.
+ * q_sparse (device) fp32 [n_s][B][n_q_heads][head_dim]: each sparse layer's
+ *   query (NULL when n_s == 0).
+ * o_full (device) fp32 [B][n_q_heads][head_dim]: full-attention output.
+ * o_sparse (device) fp32 [n_s][B][n_q_heads][head_dim]: each sparse layer's
+ *   attention over the selected rows of the shared cache.
+ * sel_idx (device) int32 [B][window + top_k]: selected positions within the
+ *   sequence, ascending, padded with -1.
+ * sel_count (device) int32 [B]: min(L_b, window + top_k).
+ * score_out (device) fp32 [N] or NULL: per-token score (sum over heads of the
+ *   softmax probability), for every position of every sequence.
+ * workspace (device), workspace_bytes >= hs2_decode_workspace_bytes(desc),
+ *   256-byte aligned; its contents on entry do not matter.
+ * A sequence with L_b == 0 yields zero outputs, sel_count 0 and all -1.      */
+hs2_status hs2_decode_block(const hs2_decode_desc* desc, const int64_t* seq_offsets,
+                            const void* k_cache, const void* v_cache,
+                            const float* k_scale, const float* v_scale,
+                            const float* q_full, const float* q_sparse,
+                            float* o_full, float* o_sparse,
+                            int32_t* sel_idx, int32_t* sel_count, float* score_out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage call: the full-attention layer alone.  Same arguments as
+ * hs2_decode_block; writes o_full and score_out (required here).            */
+hs2_status hs2_full_decode_score(const hs2_decode_desc* desc, const int64_t* seq_offsets,
+                                 const void* k_cache, const void* v_cache,
+                                 const float* k_scale, const float* v_scale,
+                                 const float* q_full, float* o_full, float* score_out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage call: token selection from given scores.  score (device) fp32 [N]
+ * non-negative; writes sel_idx and sel_count as hs2_decode_block does: the
+ * last `window` positions plus the top_k positions before them by (score
+ * descending, position ascending).                                           */
+hs2_status hs2_topk_select(const hs2_decode_desc* desc, const int64_t* seq_offsets,
+                           const float* score, int32_t* sel_idx, int32_t* sel_count,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage call: the sparse layers over a given selection.  desc->n_sparse_layers
+ * queries in q_sparse; sel_idx/sel_count as written by hs2_topk_select (the
+ * caller may keep them across calls: one selection serves every layer).
+ * With n_sparse_layers == 1 this is one sparse layer at a time.              */
+hs2_status hs2_sparse_decode(const hs2_decode_desc* desc, const int64_t* seq_offsets,
+                             const void* k_cache, const void* v_cache,
+                             const float* k_scale, const float* v_scale,
+                             const float* q_sparse, const int32_t* sel_idx,
+                             const int32_t* sel_count, float* o_sparse,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* KV-Bridging projection: for l in [0, n_bridged):
+ *   k_out[l] = hidden . w_k[l],  v_out[l] = hidden . w_v[l]
+ * hidden (device) bf16 [n_tokens][d_model] row-major;
+ * w_k, w_v (host arrays of n_bridged device pointers) bf16 [d_model][head_dim];
+ * k_out, v_out (host arrays of n_bridged device pointers) bf16
+ *   [n_tokens][head_dim]; fp32 accumulation, round-to-nearest-even output.
+ * Supported: head_dim 128, d_model a positive multiple of 64,
+ * 1 <= n_bridged <= 4, n_tokens >= 0.  All device pointers 16-byte aligned.
+ * workspace (device) >= hs2_bridge_workspace_bytes(...), 256-byte aligned.  */
+size_t hs2_bridge_workspace_bytes(int64_t n_tokens, int32_t d_model, int32_t head_dim,
+                                  int32_t n_bridged);
+hs2_status hs2_bridge_kv(int64_t n_tokens, int32_t d_model, int32_t head_dim, int32_t n_bridged,
+                         const void* hidden, const void* const* w_k, const void* const* w_v,
+                         void* const* k_out, void* const* v_out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Per-stage kernel timing of hs2_decode_block, for benchmarks.  While
+ * enabled, each call records HIP events around its stages on its stream
+ * (HS2_N_STAGES stages: 0 full-attention partial pass, 1 full-attention
+ * merge, 2 score and selection, 3 sparse layers).  hs2_stage_timing_read
+ * waits for the recorded events and returns, per stage, the mean duration in
+ * milliseconds over the calls recorded since the last read (at most 1024),
+ * and the number of calls in *n_calls; it then clears the record.           */
+#define HS2_N_STAGES 4
+hs2_status hs2_stage_timing_enable(int32_t on);
+hs2_status hs2_stage_timing_read(float* mean_ms /* [HS2_N_STAGES] (host) */, int32_t* n_calls);
+
+const char* hs2_status_string(hs2_status status);
+const char* hs2_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HS2_H */

@@ -1,0 +1,173 @@
+// KV-Bridging projection: every bridged full-attention layer builds its own K
+// and V from one shared self-decoder hidden state with its own projections
+// (toolnavs.com article 2080 (ko), section "HySparse2가 한 일"; (fr), section
+// "Ce que fait HySparse2"; "Luo Fuli Teases Xiaomi MiMo-V3 Architecture",
+// paragraph on KV Bridging).  All 2 * n_bridged projections form one GEMM
+//   C[T x (n_out*128)] = H[T x d_model] . [W_k0 | W_v0 | W_k1 | ...]
+// on bf16 MFMA with fp32 accumulation, so H is streamed once for all of them.
+//
+// The weights (a few MB) are first transposed into the workspace so that both
+// operands are contiguous along the reduction dim, the layout the MFMA
+// fragments read.  GEMM tiles: 128 rows x 128 columns (one output matrix) per
+// workgroup, k-step 64, LDS double buffering with the next tile's global loads
+// in flight during the current tile's MFMAs; four waves of 64 x 64 each.
+// Workgroups are ordered so the n_out column tiles of one row block run
+// back to back on the same XCD and share its L2.
+#include "hs2_device.h"
+#include "hs2_internal.h"
+
+namespace hs2 {
+
+namespace {
+constexpr int kBM = 128;
+constexpr int kBN = 128;
+constexpr int kBK = 64;
+constexpr int kPitch = kBK * 2 + 16;  // bytes per LDS row (padded)
+}  // namespace
+
+struct WeightPtrs {
+  const uint16_t* w[8];
+};
+
+// W [d_model][128] (row = reduction index) -> W_t [128][d_model], 64 x 128 tiles.
+__global__ __launch_bounds__(256) void transpose_w_kernel(WeightPtrs src_w, int d_model, uint16_t* w_t) {
+  __shared__ uint16_t tile[64][kDim + 2];
+  const int o = blockIdx.y;
+  const int k0 = blockIdx.x * 64;
+  const uint16_t* src = src_w.w[o];
+  for (int i = threadIdx.x; i < 64 * kDim; i += blockDim.x) {
+    const int r = i / kDim, c = i % kDim;
+    tile[r][c] = src[static_cast<size_t>(k0 + r) * kDim + c];
+  }
+  __syncthreads();
+  uint16_t* dst = w_t + static_cast<size_t>(o) * kDim * d_model;
+  for (int i = threadIdx.x; i < 64 * kDim; i += blockDim.x) {
+    const int c = i / 64, r = i % 64;
+    dst[static_cast<size_t>(c) * d_model + k0 + r] = tile[r][c];
+  }
+}
+
+hipError_t launch_bridge_transpose_w(const uint16_t* const* w, int n_out, int d_model, uint16_t* w_t,
+                                     hipStream_t s) {
+  WeightPtrs p{};
+  for (int i = 0; i < n_out && i < 8; ++i) p.w[i] = w[i];
+  hipLaunchKernelGGL(transpose_w_kernel, dim3(d_model / 64, n_out), dim3(256), 0, s, p, d_model, w_t);
+  return hipGetLastError();
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__global__ __launch_bounds__(256) void bridge_gemm_kernel(BridgeParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][kBM * kPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][kBN * kPitch];
+
+  // XCD-aware order: workgroup id i runs on XCD i % 8; give the n_out column
+  // tiles of one row block consecutive slots on one XCD.
+  const int id = blockIdx.x;
+  const int xcd = id & 7;
+  const int slot = id >> 3;
+  const int m_tiles = static_cast<int>((p.n_tokens + kBM - 1) / kBM);
+  const int mt = (slot / p.n_out) * 8 + xcd;
+  const int nt = slot % p.n_out;
+  if (mt >= m_tiles) return;
+  const int64_t m0 = static_cast<int64_t>(mt) * kBM;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int wm = (wave >> 1) * 64;
+  const int wn = (wave & 1) * 64;
+
+  // Global -> register staging: each thread moves 4 x 16 B of A and of B per k-step.
+  // Chunk c = tid + 256 * j: row c / 8, 16-byte column c % 8.
+  const uint16_t* a_src[4];
+  const uint16_t* b_src[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = tid + 256 * j;
+    const int row = c >> 3, col = (c & 7) * 8;
+    const int64_t arow = min<int64_t>(m0 + row, p.n_tokens - 1);  // clamp the ragged last block
+    a_src[j] = p.hidden + arow * p.d_model + col;
+    b_src[j] = p.w_t + (static_cast<int64_t>(nt) * kBN + row) * p.d_model + col;
+  }
+  u32x4 ra[4], rb[4];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ra[j] = *reinterpret_cast<const u32x4*>(a_src[j] + k0);
+      rb[j] = *reinterpret_cast<const u32x4*>(b_src[j] + k0);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = tid + 256 * j;
+      const int row = c >> 3, colb = (c & 7) * 16;
+      *reinterpret_cast<u32x4*>(&s_a[buf][row * kPitch + colb]) = ra[j];
+      *reinterpret_cast<u32x4*>(&s_b[buf][row * kPitch + colb]) = rb[j];
+    }
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int k_steps = p.d_model / kBK;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int ks = 0; ks < k_steps; ++ks) {
+    const int buf = ks & 1;
+    if (ks + 1 < k_steps) load_tile((ks + 1) * kBK);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&s_a[buf][(wm + 16 * i + n) * kPitch + kk * 64 + 16 * g]));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bfr[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(&s_b[buf][(wn + 16 * j + n) * kPitch + kk * 64 + 16 * g]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16_16x16x32(af[i], bfr[j], acc[i][j]);
+    }
+    if (ks + 1 < k_steps) {
+      store_tile(buf ^ 1);
+    }
+    __syncthreads();
+  }
+
+  // Epilogue: D[row 4g + e][col n] of tile (i, j) -> bf16, round to nearest even.
+  uint16_t* out = p.out[nt];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t row = m0 + wm + 16 * i + 4 * g + e;
+      if (row >= p.n_tokens) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) out[row * kDim + wn + 16 * j + n] = f32_to_bf16_rne(acc[i][j][e]);
+    }
+  }
+}
+
+hipError_t launch_bridge_gemm(const BridgeParams& p, hipStream_t s) {
+  if (p.n_tokens == 0) return hipSuccess;
+  const int64_t m_tiles = (p.n_tokens + kBM - 1) / kBM;
+  const int64_t groups = (m_tiles + 7) / 8;  // row blocks per XCD, rounded up
+  const int64_t blocks = groups * 8 * p.n_out;
+  hipLaunchKernelGGL(bridge_gemm_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace hs2

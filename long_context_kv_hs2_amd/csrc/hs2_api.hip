@@ -1,0 +1,501 @@
+// C ABI of libhs2.so: argument validation (before any HIP call), workspace
+// layout, and the launch sequence of each entry point.  See include/hs2.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/hs2.h"
+#include "hs2_device.h"
+#include "hs2_internal.h"
+
+namespace {
+
+using namespace hs2;
+
+thread_local char g_err[512] = "";
+
+hs2_status fail(hs2_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+hs2_status fail(hs2_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+hs2_status hip_fail(hipError_t e, const char* what) {
+  return fail(HS2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr double kLog2e = 1.4426950408889634;
+constexpr int64_t kMaxContext = int64_t(1) << 24;
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Tokens per full-attention workgroup: enough workgroups to fill 256 CUs
+// several times over, with partial traffic small against the K/V stream.
+int choose_chunk(int64_t total_tokens) {
+  int64_t c = total_tokens / 2048;
+  int64_t p2 = 256;
+  while (p2 * 2 <= c && p2 < 2048) p2 *= 2;
+  return static_cast<int>(p2);
+}
+
+struct DecodeLayout {
+  int chunk = 0;
+  int chunks_per_seq = 0;
+  int splits = 0;
+  size_t partials = 0, stats = 0, spill = 0, score = 0, hist = 0, state = 0, counters = 0, selbuf = 0,
+         sparse = 0, total = 0;
+};
+
+DecodeLayout decode_layout(const hs2_decode_desc& d) {
+  DecodeLayout L;
+  const size_t B = static_cast<size_t>(d.batch);
+  const size_t N = static_cast<size_t>(d.total_tokens);
+  L.chunk = choose_chunk(d.total_tokens);
+  L.chunks_per_seq = static_cast<int>((d.max_context + L.chunk - 1) / L.chunk);
+  if (L.chunks_per_seq < 1) L.chunks_per_seq = 1;
+  L.splits = (kBudget + kSparseRows - 1) / kSparseRows;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.partials = take(B * L.chunks_per_seq * kPartialFloats * sizeof(float));
+  L.stats = take(B * kHeads * 2 * sizeof(float));
+  L.spill = take(N * kHeads * sizeof(float));
+  L.score = take(N * sizeof(float));
+  L.hist = take(B * kRadixPasses * kRadixBins * sizeof(uint32_t));
+  L.state = take(B * sizeof(SelectState));
+  L.counters = take(B * 8 * sizeof(uint32_t));
+  L.selbuf = take(B * kTopK * sizeof(int32_t));
+  L.sparse = take(B * static_cast<size_t>(d.n_sparse_layers > 0 ? d.n_sparse_layers : 1) * L.splits *
+                  kPartialFloats * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+hs2_status check_desc(const hs2_decode_desc* d) {
+  if (!d) return fail(HS2_ERR_INVALID_ARGUMENT, "desc is NULL");
+  if (d->batch < 0) return fail(HS2_ERR_INVALID_ARGUMENT, "batch %d < 0", d->batch);
+  if (d->n_q_heads != kHeads) return fail(HS2_ERR_UNSUPPORTED, "n_q_heads %d (only 16 is supported)", d->n_q_heads);
+  if (d->head_dim != kDim) return fail(HS2_ERR_UNSUPPORTED, "head_dim %d (only 128 is supported)", d->head_dim);
+  if (d->window != kWindow) return fail(HS2_ERR_UNSUPPORTED, "window %d (only 128 is supported)", d->window);
+  if (d->top_k != kTopK) return fail(HS2_ERR_UNSUPPORTED, "top_k %d (only 1024 is supported)", d->top_k);
+  if (d->n_sparse_layers < 0 || d->n_sparse_layers > 8)
+    return fail(HS2_ERR_UNSUPPORTED, "n_sparse_layers %d (0..8 supported)", d->n_sparse_layers);
+  if (d->kv_dtype != HS2_KV_BF16 && d->kv_dtype != HS2_KV_FP8_E4M3)
+    return fail(HS2_ERR_INVALID_ARGUMENT, "kv_dtype %d unknown", d->kv_dtype);
+  if (!(d->softmax_scale > 0.f) || !isfinite(d->softmax_scale))
+    return fail(HS2_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
+  if (d->total_tokens < 0) return fail(HS2_ERR_INVALID_ARGUMENT, "total_tokens < 0");
+  if (d->max_context < 0 || d->max_context > kMaxContext)
+    return fail(HS2_ERR_UNSUPPORTED, "max_context %lld outside [0, 2^24]", static_cast<long long>(d->max_context));
+  if (d->total_tokens > static_cast<int64_t>(d->batch) * d->max_context)
+    return fail(HS2_ERR_INVALID_ARGUMENT, "total_tokens exceeds batch * max_context");
+  return HS2_OK;
+}
+
+hs2_status check_kv(const hs2_decode_desc& d, const int64_t* offs, const void* k, const void* v, const float* ks,
+                    const float* vs) {
+  if (d.batch > 0 && !offs) return fail(HS2_ERR_INVALID_ARGUMENT, "seq_offsets is NULL");
+  if (offs && !aligned(offs, 8)) return fail(HS2_ERR_INVALID_ARGUMENT, "seq_offsets not 8-byte aligned");
+  if (d.total_tokens > 0) {
+    if (!k || !v) return fail(HS2_ERR_INVALID_ARGUMENT, "k_cache/v_cache is NULL");
+    if (!aligned(k, 16) || !aligned(v, 16)) return fail(HS2_ERR_INVALID_ARGUMENT, "k_cache/v_cache not 16-byte aligned");
+    if (d.kv_dtype == HS2_KV_FP8_E4M3) {
+      if (!ks || !vs) return fail(HS2_ERR_INVALID_ARGUMENT, "E4M3 cache needs k_scale and v_scale");
+      if (!aligned(ks, 4) || !aligned(vs, 4)) return fail(HS2_ERR_INVALID_ARGUMENT, "scales not 4-byte aligned");
+    }
+  }
+  if (d.kv_dtype == HS2_KV_BF16 && (ks || vs))
+    return fail(HS2_ERR_INVALID_ARGUMENT, "bf16 cache takes no scales (pass NULL)");
+  return HS2_OK;
+}
+
+hs2_status check_ptr(const void* p, bool needed, size_t align, const char* name) {
+  if (!needed) return HS2_OK;
+  if (!p) return fail(HS2_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(HS2_ERR_INVALID_ARGUMENT, "%s not %zu-byte aligned", name, align);
+  return HS2_OK;
+}
+
+hs2_status check_workspace(const hs2_decode_desc& d, const void* ws, size_t bytes, DecodeLayout& L) {
+  L = decode_layout(d);
+  if (bytes < L.total)
+    return fail(HS2_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", bytes, L.total);
+  if (L.total > 0 && !ws) return fail(HS2_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (ws && !aligned(ws, 256)) return fail(HS2_ERR_INVALID_ARGUMENT, "workspace not 256-byte aligned");
+  return HS2_OK;
+}
+
+#define HS2_TRY(expr)                 \
+  do {                                \
+    const hs2_status _s = (expr);     \
+    if (_s != HS2_OK) return _s;      \
+  } while (0)
+
+#define HS2_HIP(expr, what)                       \
+  do {                                            \
+    const hipError_t _e = (expr);                 \
+    if (_e != hipSuccess) return hip_fail(_e, what); \
+  } while (0)
+
+uint8_t* ws_at(void* ws, size_t off) { return static_cast<uint8_t*>(ws) + off; }
+
+// ---- stage timing -------------------------------------------------------------
+struct TimingRecord {
+  hipEvent_t ev[HS2_N_STAGES + 1];
+};
+std::mutex g_timing_mu;
+bool g_timing_on = false;
+std::vector<TimingRecord> g_records;
+int g_records_used = 0;
+constexpr int kMaxRecords = 1024;
+
+// Returns the record to fill for this call, or nullptr when timing is off.
+hs2_status timing_begin(TimingRecord** out) {
+  *out = nullptr;
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  if (!g_timing_on || g_records_used >= kMaxRecords) return HS2_OK;
+  if (g_records_used == static_cast<int>(g_records.size())) {
+    TimingRecord r;
+    for (int i = 0; i <= HS2_N_STAGES; ++i) HS2_HIP(hipEventCreate(&r.ev[i]), "hipEventCreate");
+    g_records.push_back(r);
+  }
+  *out = &g_records[g_records_used++];
+  return HS2_OK;
+}
+
+hs2_status mark(TimingRecord* rec, int i, hipStream_t s) {
+  if (rec) HS2_HIP(hipEventRecord(rec->ev[i], s), "hipEventRecord");
+  return HS2_OK;
+}
+
+// ---- the decode sequence ----------------------------------------------------------
+struct DecodeArgs {
+  const hs2_decode_desc* d;
+  const int64_t* offs;
+  const void* k;
+  const void* v;
+  const float* ks;
+  const float* vs;
+  const float* q_full;
+  const float* q_sparse;
+  float* o_full;
+  float* o_sparse;
+  int32_t* sel_idx;
+  int32_t* sel_count;
+  float* score_out;
+  void* ws;
+  hipStream_t stream;
+};
+
+FullParams full_params(const DecodeArgs& a, const DecodeLayout& L) {
+  FullParams p;
+  p.seq_offsets = a.offs;
+  p.total_tokens = a.d->total_tokens;
+  p.max_context = a.d->max_context;
+  p.k = static_cast<const uint8_t*>(a.k);
+  p.v = static_cast<const uint8_t*>(a.v);
+  p.k_scale = a.ks;
+  p.v_scale = a.vs;
+  p.q = a.q_full;
+  p.qscale = static_cast<float>(static_cast<double>(a.d->softmax_scale) * kLog2e);
+  p.chunk = L.chunk;
+  p.chunks_per_seq = L.chunks_per_seq;
+  p.partials = reinterpret_cast<float*>(ws_at(a.ws, L.partials));
+  p.spill = reinterpret_cast<float*>(ws_at(a.ws, L.spill));
+  return p;
+}
+
+SelectParams select_params(const DecodeArgs& a, const DecodeLayout& L, float* score) {
+  SelectParams p;
+  p.seq_offsets = a.offs;
+  p.total_tokens = a.d->total_tokens;
+  p.max_context = a.d->max_context;
+  p.window = a.d->window;
+  p.top_k = a.d->top_k;
+  p.budget = a.d->window + a.d->top_k;
+  p.spill = reinterpret_cast<const float*>(ws_at(a.ws, L.spill));
+  p.stats = reinterpret_cast<const float*>(ws_at(a.ws, L.stats));
+  p.score = score;
+  p.hist = reinterpret_cast<uint32_t*>(ws_at(a.ws, L.hist));
+  p.state = reinterpret_cast<SelectState*>(ws_at(a.ws, L.state));
+  p.counters = reinterpret_cast<uint32_t*>(ws_at(a.ws, L.counters));
+  p.selbuf = reinterpret_cast<int32_t*>(ws_at(a.ws, L.selbuf));
+  p.sel_idx = a.sel_idx;
+  p.sel_count = a.sel_count;
+  return p;
+}
+
+hs2_status run_full(const DecodeArgs& a, const DecodeLayout& L, TimingRecord* rec) {
+  const hs2_decode_desc& d = *a.d;
+  const FullParams fp = full_params(a, L);
+  HS2_HIP(launch_full_partial(fp, d.batch, d.kv_dtype == HS2_KV_FP8_E4M3, a.stream), "full-attention partial pass");
+  HS2_TRY(mark(rec, 1, a.stream));
+  MergeParams mp;
+  mp.seq_offsets = a.offs;
+  mp.total_tokens = d.total_tokens;
+  mp.max_context = d.max_context;
+  mp.budget = d.window + d.top_k;
+  mp.partials = fp.partials;
+  mp.chunk = L.chunk;
+  mp.chunks_per_seq = L.chunks_per_seq;
+  mp.stride_seq = L.chunks_per_seq * kPartialFloats;
+  mp.stride_chunk = kPartialFloats;
+  mp.count_from_sel = 0;
+  mp.sel_count = nullptr;
+  mp.out = a.o_full;
+  mp.out_stride_seq = kHeads * kDim;
+  mp.stats = reinterpret_cast<float*>(ws_at(a.ws, L.stats));
+  HS2_HIP(launch_merge(mp, d.batch, a.stream), "full-attention merge");
+  HS2_TRY(mark(rec, 2, a.stream));
+  return HS2_OK;
+}
+
+hs2_status run_sparse(const DecodeArgs& a, const DecodeLayout& L, const int32_t* sel_idx, const int32_t* sel_count) {
+  const hs2_decode_desc& d = *a.d;
+  if (d.n_sparse_layers == 0 || d.batch == 0) return HS2_OK;
+  SparseParams sp;
+  sp.seq_offsets = a.offs;
+  sp.total_tokens = d.total_tokens;
+  sp.max_context = d.max_context;
+  sp.k = static_cast<const uint8_t*>(a.k);
+  sp.v = static_cast<const uint8_t*>(a.v);
+  sp.k_scale = a.ks;
+  sp.v_scale = a.vs;
+  sp.q_sparse = a.q_sparse;
+  sp.qscale = static_cast<float>(static_cast<double>(d.softmax_scale) * kLog2e);
+  sp.batch = d.batch;
+  sp.n_layers = d.n_sparse_layers;
+  sp.budget = d.window + d.top_k;
+  sp.splits = L.splits;
+  sp.sel_idx = sel_idx;
+  sp.sel_count = sel_count;
+  sp.partials = reinterpret_cast<float*>(ws_at(a.ws, L.sparse));
+  HS2_HIP(launch_sparse_partial(sp, d.kv_dtype == HS2_KV_FP8_E4M3, a.stream), "sparse partial pass");
+  MergeParams mp;
+  mp.seq_offsets = a.offs;
+  mp.total_tokens = d.total_tokens;
+  mp.max_context = d.max_context;
+  mp.budget = sp.budget;
+  mp.partials = sp.partials;
+  mp.chunk = kSparseRows;
+  mp.chunks_per_seq = L.splits;
+  mp.stride_seq = d.n_sparse_layers * L.splits * kPartialFloats;
+  mp.stride_chunk = kPartialFloats;
+  mp.count_from_sel = 1;
+  mp.sel_count = sel_count;
+  mp.out = a.o_sparse;
+  mp.out_stride_seq = kHeads * kDim;
+  mp.stats = nullptr;
+  HS2_HIP(launch_merge_layers(mp, d.batch, d.n_sparse_layers, static_cast<int64_t>(L.splits) * kPartialFloats,
+                              static_cast<int64_t>(d.batch) * kHeads * kDim, a.stream),
+          "sparse merge");
+  return HS2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hs2_decode_workspace_bytes(const hs2_decode_desc* desc) {
+  if (check_desc(desc) != HS2_OK) return 0;
+  return decode_layout(*desc).total;
+}
+
+hs2_status hs2_decode_block(const hs2_decode_desc* desc, const int64_t* seq_offsets, const void* k_cache,
+                            const void* v_cache, const float* k_scale, const float* v_scale, const float* q_full,
+                            const float* q_sparse, float* o_full, float* o_sparse, int32_t* sel_idx,
+                            int32_t* sel_count, float* score_out, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  HS2_TRY(check_desc(desc));
+  const hs2_decode_desc& d = *desc;
+  HS2_TRY(check_kv(d, seq_offsets, k_cache, v_cache, k_scale, v_scale));
+  const bool any = d.batch > 0;
+  const bool sparse = any && d.n_sparse_layers > 0;
+  HS2_TRY(check_ptr(q_full, any, 16, "q_full"));
+  HS2_TRY(check_ptr(o_full, any, 16, "o_full"));
+  HS2_TRY(check_ptr(q_sparse, sparse, 16, "q_sparse"));
+  HS2_TRY(check_ptr(o_sparse, sparse, 16, "o_sparse"));
+  HS2_TRY(check_ptr(sel_idx, any, 4, "sel_idx"));
+  HS2_TRY(check_ptr(sel_count, any, 4, "sel_count"));
+  if (score_out && !aligned(score_out, 4)) return fail(HS2_ERR_INVALID_ARGUMENT, "score_out not 4-byte aligned");
+  DecodeLayout L;
+  HS2_TRY(check_workspace(d, workspace, workspace_bytes, L));
+  if (!any) return HS2_OK;
+
+  DecodeArgs a{desc, seq_offsets, k_cache, v_cache, k_scale, v_scale, q_full, q_sparse, o_full, o_sparse,
+               sel_idx, sel_count, score_out, workspace, static_cast<hipStream_t>(stream)};
+  TimingRecord* rec = nullptr;
+  HS2_TRY(timing_begin(&rec));
+  float* score = score_out ? score_out : reinterpret_cast<float*>(ws_at(workspace, L.score));
+  const SelectParams sp = select_params(a, L, score);
+  HS2_HIP(launch_select_init(sp, d.batch, a.stream), "selection init");
+  HS2_TRY(mark(rec, 0, a.stream));
+  HS2_TRY(run_full(a, L, rec));
+  HS2_HIP(launch_score_pass(sp, d.batch, d.max_context, true, a.stream), "score pass");
+  HS2_HIP(launch_radix_passes(sp, d.batch, d.max_context, 1, a.stream), "radix passes");
+  HS2_HIP(launch_emit_finalize(sp, d.batch, d.max_context, a.stream), "selection emit");
+  HS2_TRY(mark(rec, 3, a.stream));
+  HS2_TRY(run_sparse(a, L, sel_idx, sel_count));
+  HS2_TRY(mark(rec, 4, a.stream));
+  return HS2_OK;
+}
+
+hs2_status hs2_full_decode_score(const hs2_decode_desc* desc, const int64_t* seq_offsets, const void* k_cache,
+                                 const void* v_cache, const float* k_scale, const float* v_scale,
+                                 const float* q_full, float* o_full, float* score_out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  HS2_TRY(check_desc(desc));
+  const hs2_decode_desc& d = *desc;
+  HS2_TRY(check_kv(d, seq_offsets, k_cache, v_cache, k_scale, v_scale));
+  const bool any = d.batch > 0;
+  HS2_TRY(check_ptr(q_full, any, 16, "q_full"));
+  HS2_TRY(check_ptr(o_full, any, 16, "o_full"));
+  HS2_TRY(check_ptr(score_out, d.total_tokens > 0, 4, "score_out"));
+  DecodeLayout L;
+  HS2_TRY(check_workspace(d, workspace, workspace_bytes, L));
+  if (!any) return HS2_OK;
+  DecodeArgs a{desc, seq_offsets, k_cache, v_cache, k_scale, v_scale, q_full, nullptr, o_full, nullptr,
+               nullptr, nullptr, score_out, workspace, static_cast<hipStream_t>(stream)};
+  HS2_TRY(run_full(a, L, nullptr));
+  const SelectParams sp = select_params(a, L, score_out);
+  HS2_HIP(launch_score_pass(sp, d.batch, d.max_context, false, a.stream), "score pass");
+  return HS2_OK;
+}
+
+hs2_status hs2_topk_select(const hs2_decode_desc* desc, const int64_t* seq_offsets, const float* score,
+                           int32_t* sel_idx, int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  HS2_TRY(check_desc(desc));
+  const hs2_decode_desc& d = *desc;
+  const bool any = d.batch > 0;
+  if (any && !seq_offsets) return fail(HS2_ERR_INVALID_ARGUMENT, "seq_offsets is NULL");
+  HS2_TRY(check_ptr(score, d.total_tokens > 0, 4, "score"));
+  HS2_TRY(check_ptr(sel_idx, any, 4, "sel_idx"));
+  HS2_TRY(check_ptr(sel_count, any, 4, "sel_count"));
+  DecodeLayout L;
+  HS2_TRY(check_workspace(d, workspace, workspace_bytes, L));
+  if (!any) return HS2_OK;
+  DecodeArgs a{desc, seq_offsets, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+               sel_idx, sel_count, nullptr, workspace, static_cast<hipStream_t>(stream)};
+  const SelectParams sp = select_params(a, L, const_cast<float*>(score));
+  HS2_HIP(launch_select_init(sp, d.batch, a.stream), "selection init");
+  HS2_HIP(launch_radix_passes(sp, d.batch, d.max_context, 0, a.stream), "radix passes");
+  HS2_HIP(launch_emit_finalize(sp, d.batch, d.max_context, a.stream), "selection emit");
+  return HS2_OK;
+}
+
+hs2_status hs2_sparse_decode(const hs2_decode_desc* desc, const int64_t* seq_offsets, const void* k_cache,
+                             const void* v_cache, const float* k_scale, const float* v_scale,
+                             const float* q_sparse, const int32_t* sel_idx, const int32_t* sel_count,
+                             float* o_sparse, void* workspace, size_t workspace_bytes, void* stream) {
+  HS2_TRY(check_desc(desc));
+  const hs2_decode_desc& d = *desc;
+  HS2_TRY(check_kv(d, seq_offsets, k_cache, v_cache, k_scale, v_scale));
+  const bool sparse = d.batch > 0 && d.n_sparse_layers > 0;
+  HS2_TRY(check_ptr(q_sparse, sparse, 16, "q_sparse"));
+  HS2_TRY(check_ptr(o_sparse, sparse, 16, "o_sparse"));
+  HS2_TRY(check_ptr(sel_idx, sparse, 4, "sel_idx"));
+  HS2_TRY(check_ptr(sel_count, sparse, 4, "sel_count"));
+  DecodeLayout L;
+  HS2_TRY(check_workspace(d, workspace, workspace_bytes, L));
+  if (!sparse) return HS2_OK;
+  DecodeArgs a{desc, seq_offsets, k_cache, v_cache, k_scale, v_scale, nullptr, q_sparse, nullptr, o_sparse,
+               nullptr, nullptr, nullptr, workspace, static_cast<hipStream_t>(stream)};
+  return run_sparse(a, L, sel_idx, sel_count);
+}
+
+size_t hs2_bridge_workspace_bytes(int64_t n_tokens, int32_t d_model, int32_t head_dim, int32_t n_bridged) {
+  if (n_tokens < 0 || d_model <= 0 || d_model % 64 || head_dim != kDim || n_bridged < 1 || n_bridged > 4) return 0;
+  return align_up(static_cast<size_t>(2 * n_bridged) * kDim * d_model * sizeof(uint16_t));
+}
+
+hs2_status hs2_bridge_kv(int64_t n_tokens, int32_t d_model, int32_t head_dim, int32_t n_bridged, const void* hidden,
+                         const void* const* w_k, const void* const* w_v, void* const* k_out, void* const* v_out,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_tokens < 0) return fail(HS2_ERR_INVALID_ARGUMENT, "n_tokens < 0");
+  if (head_dim != kDim) return fail(HS2_ERR_UNSUPPORTED, "head_dim %d (only 128 is supported)", head_dim);
+  if (d_model <= 0 || d_model % 64) return fail(HS2_ERR_UNSUPPORTED, "d_model %d must be a positive multiple of 64", d_model);
+  if (n_bridged < 1 || n_bridged > 4) return fail(HS2_ERR_UNSUPPORTED, "n_bridged %d (1..4 supported)", n_bridged);
+  if (n_tokens > (int64_t(1) << 31)) return fail(HS2_ERR_UNSUPPORTED, "n_tokens above 2^31");
+  if (!w_k || !w_v || !k_out || !v_out) return fail(HS2_ERR_INVALID_ARGUMENT, "weight/output pointer array is NULL");
+  const uint16_t* ws[8];
+  uint16_t* outs[8];
+  for (int l = 0; l < n_bridged; ++l) {
+    ws[2 * l] = static_cast<const uint16_t*>(w_k[l]);
+    ws[2 * l + 1] = static_cast<const uint16_t*>(w_v[l]);
+    outs[2 * l] = static_cast<uint16_t*>(k_out[l]);
+    outs[2 * l + 1] = static_cast<uint16_t*>(v_out[l]);
+  }
+  for (int i = 0; i < 2 * n_bridged; ++i) {
+    HS2_TRY(check_ptr(ws[i], true, 16, "w_k/w_v entry"));
+    HS2_TRY(check_ptr(outs[i], n_tokens > 0, 16, "k_out/v_out entry"));
+  }
+  HS2_TRY(check_ptr(hidden, n_tokens > 0, 16, "hidden"));
+  const size_t need = hs2_bridge_workspace_bytes(n_tokens, d_model, head_dim, n_bridged);
+  if (workspace_bytes < need) return fail(HS2_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  HS2_TRY(check_ptr(workspace, true, 256, "workspace"));
+  if (n_tokens == 0) return HS2_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* w_t = static_cast<uint16_t*>(workspace);
+  HS2_HIP(launch_bridge_transpose_w(ws, 2 * n_bridged, d_model, w_t, s), "bridge weight transpose");
+  BridgeParams p;
+  p.n_tokens = n_tokens;
+  p.d_model = d_model;
+  p.n_out = 2 * n_bridged;
+  p.hidden = static_cast<const uint16_t*>(hidden);
+  p.w_t = w_t;
+  for (int i = 0; i < 8; ++i) p.out[i] = i < 2 * n_bridged ? outs[i] : nullptr;
+  HS2_HIP(launch_bridge_gemm(p, s), "bridge GEMM");
+  return HS2_OK;
+}
+
+hs2_status hs2_stage_timing_enable(int32_t on) {
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  g_timing_on = on != 0;
+  return HS2_OK;
+}
+
+hs2_status hs2_stage_timing_read(float* mean_ms, int32_t* n_calls) {
+  if (!mean_ms || !n_calls) return fail(HS2_ERR_INVALID_ARGUMENT, "NULL output");
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  double sum[HS2_N_STAGES] = {0, 0, 0, 0};
+  for (int r = 0; r < g_records_used; ++r) {
+    HS2_HIP(hipEventSynchronize(g_records[r].ev[HS2_N_STAGES]), "hipEventSynchronize");
+    for (int sidx = 0; sidx < HS2_N_STAGES; ++sidx) {
+      float ms = 0.f;
+      HS2_HIP(hipEventElapsedTime(&ms, g_records[r].ev[sidx], g_records[r].ev[sidx + 1]), "hipEventElapsedTime");
+      sum[sidx] += ms;
+    }
+  }
+  for (int sidx = 0; sidx < HS2_N_STAGES; ++sidx)
+    mean_ms[sidx] = g_records_used ? static_cast<float>(sum[sidx] / g_records_used) : 0.f;
+  *n_calls = g_records_used;
+  g_records_used = 0;
+  return HS2_OK;
+}
+
+const char* hs2_status_string(hs2_status status) {
+  switch (status) {
+    case HS2_OK: return "HS2_OK";
+    case HS2_ERR_INVALID_ARGUMENT: return "HS2_ERR_INVALID_ARGUMENT";
+    case HS2_ERR_UNSUPPORTED: return "HS2_ERR_UNSUPPORTED";
+    case HS2_ERR_WORKSPACE_TOO_SMALL: return "HS2_ERR_WORKSPACE_TOO_SMALL";
+    case HS2_ERR_HIP: return "HS2_ERR_HIP";
+  }
+  return "HS2_UNKNOWN_STATUS";
+}
+
+const char* hs2_last_error_message(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,216 @@
+// Device helpers shared by the hybrid-block kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hs2 {
+
+constexpr int kHeads = 16;     // query heads sharing the one KV head (MQA)
+constexpr int kDim = 128;      // head_dim
+constexpr int kWindow = 128;   // recent positions always selected
+constexpr int kTopK = 1024;    // positions selected before the window
+constexpr int kBudget = kWindow + kTopK;
+// One split-K partial: running max m[16] and sum z[16] (log2 domain), then the
+// unnormalised output O[16][128].
+constexpr int kPartialFloats = 2 * kHeads + kHeads * kDim;
+
+// Rows [base, base + len) of sequence b, clamped so that any seq_offsets
+// stays inside the N cache rows and within max_context.
+__device__ __forceinline__ void seq_bounds(const int64_t* offs, int b, int64_t total, int64_t max_ctx,
+                                           int64_t& base, int& len) {
+  int64_t a = offs[b];
+  int64_t e = offs[b + 1];
+  a = a < 0 ? 0 : (a > total ? total : a);
+  e = e < a ? a : (e > total ? total : e);
+  if (e - a > max_ctx) e = a + max_ctx;
+  base = a;
+  len = static_cast<int>(e - a);
+}
+
+// Number of selected rows of a sequence, clamped to what the sequence can hold.
+__device__ __forceinline__ int clamp_count(int count, int len, int budget) {
+  const int cap = len < budget ? len : budget;
+  return count < 0 ? 0 : (count > cap ? cap : count);
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// D[16x16] += A[16x32] B[32x16], bf16 inputs, fp32 accumulate.  Lane l holds
+// row (l % 16) of A and column (l % 16) of B, each with 8 values of the
+// reduction index; D row 4*(l/16)+i, column l%16 is element i.
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// D[16x16] += A[16x4] B[4x16] in fp32.  Lane l holds A[l%16][l/16] and
+// B[l/16][l%16]; D row 4*(l/16)+i, column l%16 is element i.
+__device__ __forceinline__ f32x4 mfma_f32_16x16x4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Split an fp32 value into three bfloat16 parts whose exact sum is the value:
+// each part keeps the top 8 significant bits of what the previous parts left,
+// by truncation, so the subtractions are exact and 3 x 8 bits cover binary32's
+// 24-bit significand.  Products of a part with a bf16 (or E4M3) key are exact
+// in fp32, so three bf16 MFMAs give an fp32-accurate dot product.
+__device__ __forceinline__ void split3(float x, uint32_t& h, uint32_t& m, uint32_t& l) {
+  const uint32_t hu = __float_as_uint(x) & 0xFFFF0000u;
+  const float r1 = x - __uint_as_float(hu);
+  const uint32_t mu = __float_as_uint(r1) & 0xFFFF0000u;
+  const float r2 = r1 - __uint_as_float(mu);
+  const uint32_t lu = __float_as_uint(r2) & 0xFFFF0000u;
+  h = hu >> 16;
+  m = mu >> 16;
+  l = lu >> 16;
+}
+
+// Query operand for S^T = K Q^T with the 16x16x32 MFMA: lane (n = l%16,
+// g = l/16) holds head n, dims 32g + 8s + i for k-step s = 0..3, i = 0..7,
+// as three bf16 parts of (q * qscale).
+struct QFrag {
+  bf16x8 part[3][4];
+};
+
+__device__ __forceinline__ void load_qfrag(const float* __restrict__ q_head, float qscale, int g, QFrag& f) {
+  const float* src = q_head + 32 * g;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const float4 a = *reinterpret_cast<const float4*>(src + 8 * s);
+    const float4 c = *reinterpret_cast<const float4*>(src + 8 * s + 4);
+    const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+    u32x4 ph, pm, pl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t h0, m0, l0, h1, m1, l1;
+      split3(x[2 * i] * qscale, h0, m0, l0);
+      split3(x[2 * i + 1] * qscale, h1, m1, l1);
+      ph[i] = h0 | (h1 << 16);
+      pm[i] = m0 | (m1 << 16);
+      pl[i] = l0 | (l1 << 16);
+    }
+    f.part[0][s] = as_bf16x8(ph);
+    f.part[1][s] = as_bf16x8(pm);
+    f.part[2][s] = as_bf16x8(pl);
+  }
+}
+
+// Two OCP E4M3 codes (bytes 0,1 or 2,3 of w) -> two bf16 packed in a word.
+// The conversion to fp32 is exact and E4M3 has 4 significant bits, so taking
+// the upper half of each fp32 word is exact too.
+template <bool HIGH_PAIR>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HIGH_PAIR);
+  return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
+}
+
+// 16 E4M3 codes -> 16 bf16 (two bf16x8 operands).
+__device__ __forceinline__ void e4m3x16_to_bf16(u32x4 w, bf16x8& lo, bf16x8& hi) {
+  u32x4 a, b;
+  a[0] = e4m3x2_to_bf16x2<false>(w[0]);
+  a[1] = e4m3x2_to_bf16x2<true>(w[0]);
+  a[2] = e4m3x2_to_bf16x2<false>(w[1]);
+  a[3] = e4m3x2_to_bf16x2<true>(w[1]);
+  b[0] = e4m3x2_to_bf16x2<false>(w[2]);
+  b[1] = e4m3x2_to_bf16x2<true>(w[2]);
+  b[2] = e4m3x2_to_bf16x2<false>(w[3]);
+  b[3] = e4m3x2_to_bf16x2<true>(w[3]);
+  lo = as_bf16x8(a);
+  hi = as_bf16x8(b);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// 8 bf16 values (one 16-byte load) -> 8 fp32.
+__device__ __forceinline__ void bf16x8_to_f32(u32x4 w, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = bf16_lo(w[i]);
+    out[2 * i + 1] = bf16_hi(w[i]);
+  }
+}
+
+// 8 E4M3 codes (one 8-byte load) -> 8 fp32.
+__device__ __forceinline__ void e4m3x8_to_f32(u32x2 w, float* out) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
+    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
+    out[4 * i] = a[0];
+    out[4 * i + 1] = a[1];
+    out[4 * i + 2] = b[0];
+    out[4 * i + 3] = b[1];
+  }
+}
+
+// Online-softmax state of one wave for 16 heads: lane (n, g) keeps head n's
+// running max m and its lane-group share of the sum z (log2 domain), and the
+// unnormalised output O^T tile: o[t][i] = O[head n][dim 32g + 8i + t].
+struct SoftmaxState {
+  float m;
+  float z;
+  f32x4 o[8];
+};
+
+__device__ __forceinline__ void softmax_init(SoftmaxState& st) {
+  st.m = -INFINITY;
+  st.z = 0.f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) st.o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// One tile of 16 context tokens for 16 heads.
+//  kf[s]: K operand, lane (n, g): token n, dims 32g + 8s + i (bf16)
+//  vf[r][t]: V operand, lane (n, g): token 4g + r, dim 8n + t (fp32)
+//  kscale[r], vscale[r]: per-token scales of token 4g + r (1 for bf16)
+//  nvalid: tokens of the tile that exist (1..16); others are masked out
+// Returns the log2-domain logits of tokens 4g + r for head n in lg[r]
+// (-inf where masked).
+__device__ __forceinline__ void attend_tile(const QFrag& q, const bf16x8 (&kf)[4], const float (&vf)[4][8],
+                                            const float (&kscale)[4], const float (&vscale)[4], int nvalid,
+                                            int g, SoftmaxState& st, float (&lg)[4]) {
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int part = 0; part < 3; ++part) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s = mfma_bf16_16x16x32(kf[k], q.part[part][k], s);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) lg[r] = (4 * g + r < nvalid) ? s[r] * kscale[r] : -INFINITY;
+  float mx = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float mn = fmaxf(st.m, mx);
+  const float alpha = exp2f(st.m - mn);
+  float p[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) p[r] = exp2f(lg[r] - mn);
+  st.z = st.z * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+  if (__any(alpha != 1.f)) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) st.o[t] *= alpha;
+  }
+  st.m = mn;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float pv = p[r] * vscale[r];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) st.o[t] = mfma_f32_16x16x4(vf[r][t], pv, st.o[t]);
+  }
+}
+
+// Reduce z over the four lane groups (every lane of head n gets the total).
+__device__ __forceinline__ float reduce_z(float z) {
+  z += __shfl_xor(z, 16);
+  z += __shfl_xor(z, 32);
+  return z;
+}
+
+}  // namespace hs2

@@ -1,0 +1,119 @@
+// Internal launch interface between the C ABI (hs2_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hs2 {
+
+// ---- full-attention layer: split-K partial pass and merge -------------------
+struct FullParams {
+  const int64_t* seq_offsets;
+  int64_t total_tokens;
+  int64_t max_context;
+  const uint8_t* k;          // [N][128] bf16 or E4M3
+  const uint8_t* v;
+  const float* k_scale;      // [N] (E4M3) or nullptr
+  const float* v_scale;
+  const float* q;            // [B][16][128]
+  float qscale;              // softmax_scale * log2(e)
+  int chunk;                 // tokens per workgroup, multiple of 64
+  int chunks_per_seq;
+  float* partials;           // [B][chunks_per_seq][kPartialFloats]
+  float* spill;              // [N][16] log2-domain logits
+};
+hipError_t launch_full_partial(const FullParams& p, int batch, bool fp8, hipStream_t s);
+
+struct MergeParams {
+  const int64_t* seq_offsets;
+  int64_t total_tokens;
+  int64_t max_context;
+  int budget;
+  const float* partials;     // [B][chunks_per_seq][kPartialFloats]
+  int chunk;                 // tokens per partial
+  int chunks_per_seq;
+  int stride_seq;            // floats between sequences' partial blocks
+  int stride_chunk;          // floats between partials of one sequence
+  int count_from_sel;        // 0: partial count = ceil(L_b / chunk); 1: ceil(sel_count[b] / chunk)
+  const int32_t* sel_count;
+  float* out;                // [B][16][128] (row b at out + b * out_stride_seq)
+  int64_t out_stride_seq;
+  float* stats;              // [B][16][2] (m, z) or nullptr
+};
+hipError_t launch_merge(const MergeParams& p, int batch, hipStream_t s);
+// Same merge for `layers` stacked problems (sparse layers): partials of layer
+// l start at partials + l * stride_layer, outputs at out + l * out_stride_layer.
+hipError_t launch_merge_layers(const MergeParams& p, int batch, int layers, int64_t stride_layer,
+                               int64_t out_stride_layer, hipStream_t s);
+
+// ---- score and token selection ---------------------------------------------
+struct SelectState {
+  unsigned long long prefix;  // resolved high bits of the threshold key
+  uint32_t rank;              // how many more keys to take among the candidates
+  int32_t shift;              // bit position the prefix applies at
+  int32_t done;               // 1 once the selected set is fixed
+  int32_t pad[3];
+};
+
+struct SelectParams {
+  const int64_t* seq_offsets;
+  int64_t total_tokens;
+  int64_t max_context;
+  int window, top_k, budget;
+  const float* spill;         // [N][16] (score pass only)
+  const float* stats;         // [B][16][2] (score pass only)
+  float* score;               // [N]
+  uint32_t* hist;             // [B][kRadixPasses][2048]
+  SelectState* state;         // [B]
+  uint32_t* counters;         // [B][8]: blocks finished per pass, then emitted count
+  int32_t* selbuf;            // [B][top_k]
+  int32_t* sel_idx;           // [B][budget]
+  int32_t* sel_count;         // [B]
+};
+constexpr int kRadixPasses = 6;
+constexpr int kRadixBins = 2048;
+constexpr int kScoreBlockTokens = 2048;
+hipError_t launch_select_init(const SelectParams& p, int batch, hipStream_t s);
+hipError_t launch_score_pass(const SelectParams& p, int batch, int64_t max_context, bool histogram,
+                             hipStream_t s);
+hipError_t launch_radix_passes(const SelectParams& p, int batch, int64_t max_context, int first_pass,
+                               hipStream_t s);
+hipError_t launch_emit_finalize(const SelectParams& p, int batch, int64_t max_context, hipStream_t s);
+
+// ---- sparse layers -----------------------------------------------------------
+constexpr int kSparseRows = 128;  // selected rows per workgroup
+struct SparseParams {
+  const int64_t* seq_offsets;
+  int64_t total_tokens;
+  int64_t max_context;
+  const uint8_t* k;
+  const uint8_t* v;
+  const float* k_scale;
+  const float* v_scale;
+  const float* q_sparse;      // [n_s][B][16][128]
+  float qscale;
+  int batch;
+  int n_layers;
+  int budget;
+  int splits;                 // ceil(budget / kSparseRows)
+  const int32_t* sel_idx;     // [B][budget]
+  const int32_t* sel_count;   // [B]
+  float* partials;            // [B][n_layers][splits][kPartialFloats]
+};
+hipError_t launch_sparse_partial(const SparseParams& p, bool fp8, hipStream_t s);
+
+// ---- KV bridging ---------------------------------------------------------------
+struct BridgeParams {
+  int64_t n_tokens;
+  int d_model;
+  int n_out;                  // 2 * n_bridged column blocks of 128
+  const uint16_t* hidden;     // [T][d_model]
+  const uint16_t* w_t;        // workspace: [n_out * 128][d_model] (W transposed)
+  uint16_t* out[8];           // [T][128] each
+};
+hipError_t launch_bridge_transpose_w(const uint16_t* const* w, int n_out, int d_model, uint16_t* w_t,
+                                     hipStream_t s);
+hipError_t launch_bridge_gemm(const BridgeParams& p, hipStream_t s);
+
+}  // namespace hs2

@@ -1,0 +1,239 @@
+"""ctypes binding of libhs2.so (include/hs2.h).
+
+Argument marshalling only: torch tensors supply device memory (outputs and
+workspace are allocated with torch) and the current HIP stream; every step of
+the path runs in the library's kernels.  The first call loads the library and
+raises if it is missing; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhs2.so")
+
+HS2_OK = 0
+KV_BF16 = 0
+KV_FP8_E4M3 = 1
+N_STAGES = 4
+STAGE_NAMES = ("full_partial", "full_merge", "score_select", "sparse")
+
+EXPORTED = (
+    "hs2_decode_workspace_bytes", "hs2_decode_block", "hs2_full_decode_score", "hs2_topk_select",
+    "hs2_sparse_decode", "hs2_bridge_workspace_bytes", "hs2_bridge_kv", "hs2_stage_timing_enable",
+    "hs2_stage_timing_read", "hs2_status_string", "hs2_last_error_message",
+)
+
+
+class Hs2Error(RuntimeError):
+    pass
+
+
+class DecodeDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("n_sparse_layers", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("total_tokens", ctypes.c_int64),
+        ("max_context", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libhs2.so and declare its signatures (no HIP call happens here)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise Hs2Error(f"{path} is not built: run `python -m long_context_kv_hs2_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, sz, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+    dp = ctypes.POINTER(DecodeDesc)
+    lib.hs2_decode_workspace_bytes.argtypes = [dp]
+    lib.hs2_decode_workspace_bytes.restype = sz
+    lib.hs2_decode_block.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hs2_decode_block.restype = ctypes.c_int
+    lib.hs2_full_decode_score.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hs2_full_decode_score.restype = ctypes.c_int
+    lib.hs2_topk_select.argtypes = [dp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hs2_topk_select.restype = ctypes.c_int
+    lib.hs2_sparse_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hs2_sparse_decode.restype = ctypes.c_int
+    lib.hs2_bridge_workspace_bytes.argtypes = [i64, i32, i32, i32]
+    lib.hs2_bridge_workspace_bytes.restype = sz
+    lib.hs2_bridge_kv.argtypes = [i64, i32, i32, i32, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                  ctypes.POINTER(vp), ctypes.POINTER(vp), vp, sz, vp]
+    lib.hs2_bridge_kv.restype = ctypes.c_int
+    lib.hs2_stage_timing_enable.argtypes = [i32]
+    lib.hs2_stage_timing_enable.restype = ctypes.c_int
+    lib.hs2_stage_timing_read.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
+    lib.hs2_stage_timing_read.restype = ctypes.c_int
+    lib.hs2_status_string.argtypes = [ctypes.c_int]
+    lib.hs2_status_string.restype = ctypes.c_char_p
+    lib.hs2_last_error_message.argtypes = []
+    lib.hs2_last_error_message.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def check(status: int):
+    if status != HS2_OK:
+        lib = load()
+        raise Hs2Error(f"{lib.hs2_status_string(status).decode()}: {lib.hs2_last_error_message().decode()}")
+
+
+def make_desc(batch, total_tokens, max_context, n_sparse_layers, kv_dtype=KV_BF16, n_q_heads=16, head_dim=128,
+              window=128, top_k=1024, softmax_scale=None) -> DecodeDesc:
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(head_dim)
+    return DecodeDesc(batch, n_q_heads, head_dim, window, top_k, n_sparse_layers, kv_dtype,
+                      softmax_scale, total_tokens, max_context)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def decode_workspace_bytes(desc: DecodeDesc) -> int:
+    return load().hs2_decode_workspace_bytes(ctypes.byref(desc))
+
+
+def _workspace(nbytes, device, workspace=None):
+    if workspace is not None and workspace.numel() >= nbytes:
+        return workspace
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def kv_dtype_of(k: torch.Tensor) -> int:
+    return KV_FP8_E4M3 if k.dtype in (torch.uint8, torch.float8_e4m3fn) else KV_BF16
+
+
+class DecodeBlock:
+    """Reusable decode call: holds the descriptor, outputs and workspace so
+    repeated steps (benchmarks) allocate nothing."""
+
+    def __init__(self, seq_offsets, k, v, q_full, q_sparse, k_scale=None, v_scale=None, max_context=None,
+                 with_score=False, total_tokens=None):
+        dev = k.device
+        self.seq_offsets, self.k, self.v, self.k_scale, self.v_scale = seq_offsets, k, v, k_scale, v_scale
+        self.q_full, self.q_sparse = q_full, q_sparse
+        batch = q_full.shape[0]
+        n_s = 0 if q_sparse is None else q_sparse.shape[0]
+        if max_context is None:
+            max_context = int((seq_offsets[1:] - seq_offsets[:-1]).max().item()) if batch else 0
+        total = k.shape[0] if total_tokens is None else total_tokens
+        self.desc = make_desc(batch, total, max_context, n_s, kv_dtype_of(k))
+        self.o_full = torch.empty((batch, 16, 128), dtype=torch.float32, device=dev)
+        self.o_sparse = torch.empty((n_s, batch, 16, 128), dtype=torch.float32, device=dev) if n_s else None
+        self.sel_idx = torch.empty((batch, 1152), dtype=torch.int32, device=dev)
+        self.sel_count = torch.empty((batch,), dtype=torch.int32, device=dev)
+        self.score = torch.empty((k.shape[0],), dtype=torch.float32, device=dev) if with_score else None
+        self.workspace = _workspace(decode_workspace_bytes(self.desc), dev)
+
+    def __call__(self):
+        check(load().hs2_decode_block(
+            ctypes.byref(self.desc), _ptr(self.seq_offsets), _ptr(self.k), _ptr(self.v), _ptr(self.k_scale),
+            _ptr(self.v_scale), _ptr(self.q_full), _ptr(self.q_sparse), _ptr(self.o_full), _ptr(self.o_sparse),
+            _ptr(self.sel_idx), _ptr(self.sel_count), _ptr(self.score), _ptr(self.workspace),
+            self.workspace.numel(), _stream()))
+        return self
+
+    def outputs(self):
+        return dict(o_full=self.o_full, o_sparse=self.o_sparse, sel_idx=self.sel_idx,
+                    sel_count=self.sel_count, score=self.score)
+
+
+def decode_block(seq_offsets, k, v, q_full, q_sparse, k_scale=None, v_scale=None, max_context=None,
+                 with_score=True):
+    """One hybrid-block decode step; returns a dict of output tensors."""
+    return DecodeBlock(seq_offsets, k, v, q_full, q_sparse, k_scale, v_scale, max_context, with_score)().outputs()
+
+
+def full_decode_score(seq_offsets, k, v, q_full, k_scale=None, v_scale=None, max_context=None):
+    dev = k.device
+    batch = q_full.shape[0]
+    if max_context is None:
+        max_context = int((seq_offsets[1:] - seq_offsets[:-1]).max().item()) if batch else 0
+    desc = make_desc(batch, k.shape[0], max_context, 0, kv_dtype_of(k))
+    o_full = torch.empty((batch, 16, 128), dtype=torch.float32, device=dev)
+    score = torch.empty((k.shape[0],), dtype=torch.float32, device=dev)
+    ws = _workspace(decode_workspace_bytes(desc), dev)
+    check(load().hs2_full_decode_score(ctypes.byref(desc), _ptr(seq_offsets), _ptr(k), _ptr(v), _ptr(k_scale),
+                                       _ptr(v_scale), _ptr(q_full), _ptr(o_full), _ptr(score), _ptr(ws),
+                                       ws.numel(), _stream()))
+    return o_full, score
+
+
+def topk_select(seq_offsets, score, batch, max_context):
+    dev = score.device
+    desc = make_desc(batch, score.shape[0], max_context, 0)
+    sel_idx = torch.empty((batch, 1152), dtype=torch.int32, device=dev)
+    sel_count = torch.empty((batch,), dtype=torch.int32, device=dev)
+    ws = _workspace(decode_workspace_bytes(desc), dev)
+    check(load().hs2_topk_select(ctypes.byref(desc), _ptr(seq_offsets), _ptr(score), _ptr(sel_idx),
+                                 _ptr(sel_count), _ptr(ws), ws.numel(), _stream()))
+    return sel_idx, sel_count
+
+
+def sparse_decode(seq_offsets, k, v, q_sparse, sel_idx, sel_count, k_scale=None, v_scale=None, max_context=None):
+    dev = k.device
+    n_s, batch = q_sparse.shape[0], q_sparse.shape[1]
+    if max_context is None:
+        max_context = int((seq_offsets[1:] - seq_offsets[:-1]).max().item()) if batch else 0
+    desc = make_desc(batch, k.shape[0], max_context, n_s, kv_dtype_of(k))
+    o_sparse = torch.empty((n_s, batch, 16, 128), dtype=torch.float32, device=dev)
+    ws = _workspace(decode_workspace_bytes(desc), dev)
+    check(load().hs2_sparse_decode(ctypes.byref(desc), _ptr(seq_offsets), _ptr(k), _ptr(v), _ptr(k_scale),
+                                   _ptr(v_scale), _ptr(q_sparse), _ptr(sel_idx), _ptr(sel_count), _ptr(o_sparse),
+                                   _ptr(ws), ws.numel(), _stream()))
+    return o_sparse
+
+
+def bridge_workspace_bytes(n_tokens, d_model, n_bridged, head_dim=128) -> int:
+    return load().hs2_bridge_workspace_bytes(n_tokens, d_model, head_dim, n_bridged)
+
+
+def bridge_kv(hidden, w_k, w_v, k_out=None, v_out=None, workspace=None):
+    """K_l = hidden . w_k[l], V_l = hidden . w_v[l] (bf16 in/out, fp32 accumulate)."""
+    dev = hidden.device
+    t, d_model = hidden.shape
+    n = len(w_k)
+    if k_out is None:
+        k_out = [torch.empty((t, 128), dtype=torch.bfloat16, device=dev) for _ in range(n)]
+    if v_out is None:
+        v_out = [torch.empty((t, 128), dtype=torch.bfloat16, device=dev) for _ in range(n)]
+    arr = ctypes.c_void_p * n
+    ws = _workspace(bridge_workspace_bytes(t, d_model, n), dev, workspace)
+    check(load().hs2_bridge_kv(t, d_model, 128, n, _ptr(hidden), arr(*[w.data_ptr() for w in w_k]),
+                               arr(*[w.data_ptr() for w in w_v]), arr(*[o.data_ptr() for o in k_out]),
+                               arr(*[o.data_ptr() for o in v_out]), _ptr(ws), ws.numel(), _stream()))
+    return k_out, v_out
+
+
+def stage_timing(on: bool):
+    check(load().hs2_stage_timing_enable(1 if on else 0))
+
+
+def stage_timing_read():
+    """Mean ms per stage over the calls recorded since the last read."""
+    out = (ctypes.c_float * N_STAGES)()
+    n = ctypes.c_int32(0)
+    check(load().hs2_stage_timing_read(out, ctypes.byref(n)))
+    return dict(zip(STAGE_NAMES, list(out))), n.value

@@ -1,0 +1,133 @@
+"""Parity rules between the HIP path and the fp64 oracle (test infrastructure).
+
+* selection: count min(L, 1152); ascending, unique, in range; the whole
+  window present; equal to the oracle's list except for positions inside the
+  oracle's tie band (|score - s_k| <= 1e-5 * s_k);
+* o_full, o_sparse: max|gpu - ref| / max|ref| per tensor <= 2e-3 (bf16 KV)
+  or 2e-2 (fp8 KV); when the GPU list differs from the oracle's inside the
+  band, the sparse reference is recomputed by the oracle with the GPU's list;
+* score (diagnostic): max_j |gpu - ref| / max(ref_j, s_k), the per-token
+  relative error floored at the k-th score (what decides the selection),
+  at most half the tie band (5e-6).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import hs2_oracle as O
+
+TOL = {"bf16": 2e-3, "fp8_e4m3": 2e-2}
+
+
+def to_device(d, device="cuda"):
+    """Host arrays from long_context_kv_hs2_amd.inputs -> device tensors."""
+    t = {}
+    t["seq_offsets"] = torch.from_numpy(d["seq_offsets"]).to(device)
+    if d["kv"] == "bf16":
+        t["k"] = torch.from_numpy(d["k"].view(np.int16)).view(torch.bfloat16).to(device)
+        t["v"] = torch.from_numpy(d["v"].view(np.int16)).view(torch.bfloat16).to(device)
+        t["k_scale"] = t["v_scale"] = None
+    else:
+        t["k"] = torch.from_numpy(d["k"]).to(device)
+        t["v"] = torch.from_numpy(d["v"]).to(device)
+        t["k_scale"] = torch.from_numpy(d["k_scale"]).to(device)
+        t["v_scale"] = torch.from_numpy(d["v_scale"]).to(device)
+    t["q_full"] = torch.from_numpy(d["q_full"]).to(device)
+    t["q_sparse"] = torch.from_numpy(d["q_sparse"]).to(device) if d["q_sparse"].shape[0] else None
+    lens = np.diff(d["seq_offsets"])
+    t["max_context"] = int(lens.max()) if lens.shape[0] else 0
+    return t
+
+
+def max_abs_rel(got, ref):
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.abs(ref).max()
+    diff = np.abs(np.asarray(got, dtype=np.float64) - ref).max()
+    return float(diff / den) if den > 0 else float(diff)
+
+
+def check_selection(sel_gpu, count, length, ref):
+    """Returns the GPU list (ascending positions); raises on a violation."""
+    want = min(length, 1152)
+    assert count == want, f"count {count} != {want} (L={length})"
+    got = np.asarray(sel_gpu[:count], dtype=np.int64)
+    assert np.all(sel_gpu[count:] == -1), "padding must be -1"
+    if count:
+        assert np.all(np.diff(got) > 0), "not strictly ascending"
+        assert got[0] >= 0 and got[-1] < length, "out of range"
+    window = np.arange(max(0, length - 128), length)
+    assert np.isin(window, got).all(), "window not fully selected"
+    diff = np.setxor1d(got, ref["sel"])
+    outside = np.setdiff1d(diff, ref["band"])
+    assert outside.shape[0] == 0, f"selection differs outside the tie band at {outside[:10]} (L={length})"
+    return got
+
+
+def check_decode(d, out, seqs=None, tol=None, score_tol=5e-6, oracle_cache=None):
+    """Compare GPU outputs (dict of tensors) with the oracle on `seqs`.
+
+    Returns a dict of the worst errors seen.  ``oracle_cache`` may hold
+    per-sequence oracle results already computed (keyed by sequence)."""
+    kv = d["kv"]
+    tol = TOL[kv] if tol is None else tol
+    offs = d["seq_offsets"]
+    b_count = offs.shape[0] - 1
+    seqs = range(b_count) if seqs is None else seqs
+    o_full = out["o_full"].cpu().numpy()
+    o_sparse = out["o_sparse"].cpu().numpy() if out["o_sparse"] is not None else None
+    sel_idx = out["sel_idx"].cpu().numpy()
+    sel_count = out["sel_count"].cpu().numpy()
+    score = out["score"].cpu().numpy() if out.get("score") is not None else None
+    worst = dict(o_full=0.0, o_sparse=0.0, score=0.0, band_diffs=0)
+    for b in seqs:
+        a, e = int(offs[b]), int(offs[b + 1])
+        length = e - a
+        if length == 0:
+            assert sel_count[b] == 0 and np.all(sel_idx[b] == -1)
+            assert np.all(o_full[b] == 0)
+            if o_sparse is not None:
+                assert np.all(o_sparse[:, b] == 0)
+            continue
+        if oracle_cache is not None and b in oracle_cache:
+            ref = oracle_cache[b]
+        else:
+            ks = None if d["k_scale"] is None else d["k_scale"][a:e]
+            vs = None if d["v_scale"] is None else d["v_scale"][a:e]
+            kf = O.decode_kv(d["k"][a:e], kv, ks)
+            vf = O.decode_kv(d["v"][a:e], kv, vs)
+            ref = O.decode_sequence(d["q_full"][b].astype(np.float64), d["q_sparse"][:, b].astype(np.float64), kf, vf)
+            ref["_k"], ref["_v"] = kf, vf
+            if oracle_cache is not None:
+                oracle_cache[b] = ref
+        err = max_abs_rel(o_full[b], ref["o_full"])
+        assert err <= tol, f"o_full seq {b}: {err:.3e} > {tol}"
+        worst["o_full"] = max(worst["o_full"], err)
+        got = check_selection(sel_idx[b], int(sel_count[b]), length, ref)
+        if score is not None:
+            s_k = ref["s_k"] if ref["s_k"] else ref["score"].max()
+            den = np.maximum(ref["score"], s_k)
+            serr = float((np.abs(score[a:e].astype(np.float64) - ref["score"]) / den).max())
+            assert serr <= score_tol, f"score seq {b}: {serr:.3e} (relative, floored at s_k) > {score_tol}"
+            worst["score"] = max(worst["score"], serr)
+        if o_sparse is not None:
+            ref_sparse = ref["o_sparse"]
+            if not np.array_equal(got, ref["sel"]):
+                worst["band_diffs"] += 1
+                redo = O.decode_sequence(d["q_full"][b].astype(np.float64), d["q_sparse"][:, b].astype(np.float64),
+                                         ref["_k"], ref["_v"], sel_override=got)
+                ref_sparse = redo["o_sparse"]
+            for layer in range(ref_sparse.shape[0]):
+                err = max_abs_rel(o_sparse[layer, b], ref_sparse[layer])
+                assert err <= tol, f"o_sparse layer {layer} seq {b}: {err:.3e} > {tol}"
+                worst["o_sparse"] = max(worst["o_sparse"], err)
+    return worst
+
+
+def bf16_ordinal(bits):
+    """bf16 bit patterns -> integers ordered like the values (adjacent values
+    differ by 1), so a difference in ordinals counts ulps."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)

@@ -1,0 +1,144 @@
+"""The C ABI on the host: the library loads, exports every declared symbol,
+and rejects bad arguments with the documented status before any HIP call
+(so these run without a GPU)."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from long_context_kv_hs2_amd import hs2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hs2.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(hs2.LIB_PATH), reason="libhs2.so not built")
+
+INVALID, UNSUPPORTED, SMALL_WS = 1, 2, 3
+FAKE = 0x10000  # a 256-byte aligned non-null address; never dereferenced on the error paths
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hs2_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(hs2.LIB_PATH)
+    names = declared_functions()
+    assert len(names) >= 11
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(hs2.EXPORTED)
+
+
+def desc(**kw):
+    base = dict(batch=2, total_tokens=5000, max_context=4000, n_sparse_layers=2)
+    base.update(kw)
+    return hs2.make_desc(**base)
+
+
+def call_decode(d, ws_bytes=None, **ptrs):
+    lib = hs2.load()
+    p = dict(seq=FAKE, k=FAKE, v=FAKE, ks=None, vs=None, qf=FAKE, qs=FAKE, of=FAKE, os_=FAKE, si=FAKE, sc=FAKE,
+             score=None, ws=FAKE)
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = lib.hs2_decode_workspace_bytes(ctypes.byref(d)) if d is not None else 0
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.hs2_decode_block(None if d is None else ctypes.byref(d), v(p["seq"]), v(p["k"]), v(p["v"]),
+                                v(p["ks"]), v(p["vs"]), v(p["qf"]), v(p["qs"]), v(p["of"]), v(p["os_"]),
+                                v(p["si"]), v(p["sc"]), v(p["score"]), v(p["ws"]), ws_bytes, None)
+
+
+def test_workspace_query():
+    lib = hs2.load()
+    d = desc()
+    n = lib.hs2_decode_workspace_bytes(ctypes.byref(d))
+    # at least the logits spill (64 B per token) and the score buffer
+    assert n >= 5000 * (64 + 4)
+    assert lib.hs2_decode_workspace_bytes(ctypes.byref(desc(head_dim=64))) == 0
+    assert lib.hs2_decode_workspace_bytes(None) == 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("n_q_heads", 8, UNSUPPORTED), ("head_dim", 64, UNSUPPORTED), ("window", 64, UNSUPPORTED),
+    ("top_k", 512, UNSUPPORTED), ("n_sparse_layers", 9, UNSUPPORTED), ("n_sparse_layers", -1, UNSUPPORTED),
+    ("batch", -1, INVALID), ("kv_dtype", 7, INVALID), ("softmax_scale", 0.0, INVALID),
+    ("softmax_scale", math.inf, INVALID), ("total_tokens", -1, INVALID), ("max_context", (1 << 24) + 1, UNSUPPORTED),
+    ("total_tokens", 9000, INVALID),
+])
+def test_bad_descriptor(field, value, status):
+    d = desc()
+    setattr(d, field, value)
+    assert call_decode(d, ws_bytes=1 << 40) == status
+
+
+@pytest.mark.parametrize("name", ["seq", "k", "v", "qf", "qs", "of", "os_", "si", "sc", "ws"])
+def test_null_pointer(name):
+    assert call_decode(desc(), **{name: None}) == INVALID
+    assert hs2.load().hs2_last_error_message().decode()
+
+
+def test_null_descriptor():
+    assert call_decode(None) == INVALID
+
+
+@pytest.mark.parametrize("name,addr", [("k", FAKE + 8), ("qf", FAKE + 4), ("ws", FAKE + 128), ("seq", FAKE + 4)])
+def test_misaligned(name, addr):
+    assert call_decode(desc(), **{name: addr}) == INVALID
+
+
+def test_workspace_too_small():
+    d = desc()
+    n = hs2.load().hs2_decode_workspace_bytes(ctypes.byref(d))
+    assert call_decode(d, ws_bytes=n - 1) == SMALL_WS
+
+
+def test_scales_must_match_dtype():
+    assert call_decode(desc(kv_dtype=1)) == INVALID            # fp8 without scales
+    assert call_decode(desc(kv_dtype=0), ks=FAKE, vs=FAKE) == INVALID  # bf16 with scales
+
+
+def test_sparse_pointers_optional_without_sparse_layers():
+    # n_s = 0: q_sparse and o_sparse may be NULL; the call must still fail on
+    # the NULL workspace, proving it got past the sparse-pointer checks.
+    assert call_decode(desc(n_sparse_layers=0), qs=None, os_=None, ws=None) == INVALID
+    msg = hs2.load().hs2_last_error_message().decode()
+    assert "workspace" in msg
+
+
+def test_bridge_validation():
+    lib = hs2.load()
+    arr = ctypes.c_void_p * 1
+    one = arr(FAKE)
+    assert lib.hs2_bridge_workspace_bytes(1000, 4096, 128, 3) == 6 * 128 * 4096 * 2
+    assert lib.hs2_bridge_workspace_bytes(1000, 100, 128, 3) == 0
+    assert lib.hs2_bridge_kv(10, 4096, 64, 1, FAKE, one, one, one, one, FAKE, 1 << 30, None) == UNSUPPORTED
+    assert lib.hs2_bridge_kv(10, 4000, 128, 1, FAKE, one, one, one, one, FAKE, 1 << 30, None) == UNSUPPORTED
+    assert lib.hs2_bridge_kv(10, 4096, 128, 5, FAKE, one, one, one, one, FAKE, 1 << 30, None) == UNSUPPORTED
+    assert lib.hs2_bridge_kv(-1, 4096, 128, 1, FAKE, one, one, one, one, FAKE, 1 << 30, None) == INVALID
+    assert lib.hs2_bridge_kv(10, 4096, 128, 1, None, one, one, one, one, FAKE, 1 << 30, None) == INVALID
+    assert lib.hs2_bridge_kv(10, 4096, 128, 1, FAKE, one, one, one, one, FAKE, 100, None) == SMALL_WS
+    assert lib.hs2_bridge_kv(10, 4096, 128, 1, FAKE, one, one, None, one, FAKE, 1 << 30, None) == INVALID
+
+
+def test_stage_calls_validate():
+    lib = hs2.load()
+    d = desc()
+    n = lib.hs2_decode_workspace_bytes(ctypes.byref(d))
+    assert lib.hs2_topk_select(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, n, None) == INVALID
+    assert lib.hs2_full_decode_score(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None, FAKE, n,
+                                     None) == INVALID
+    assert lib.hs2_sparse_decode(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, None, FAKE, FAKE, FAKE, n,
+                                 None) == INVALID
+
+
+def test_status_strings():
+    lib = hs2.load()
+    assert lib.hs2_status_string(0) == b"HS2_OK"
+    assert lib.hs2_status_string(3) == b"HS2_ERR_WORKSPACE_TOO_SMALL"
+    assert lib.hs2_status_string(99) == b"HS2_UNKNOWN_STATUS"

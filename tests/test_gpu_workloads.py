@@ -1,0 +1,103 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (one DecodeBlock call, no score output), on sequences the
+oracle computes one by one.  A second call with the score output must give
+bitwise the same results, and its scores are checked as a diagnostic."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_kv_hs2_amd import hs2, inputs
+from oracle import hs2_oracle as O
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_workload(d, seqs):
+    t = parity.to_device(d)
+    blk = hs2.DecodeBlock(t["seq_offsets"], t["k"], t["v"], t["q_full"], t["q_sparse"], t["k_scale"],
+                          t["v_scale"], t["max_context"], with_score=False)
+    blk()
+    torch.cuda.synchronize()
+    bench_out = {k: (v.clone() if v is not None else None) for k, v in blk.outputs().items()}
+    scored = hs2.DecodeBlock(t["seq_offsets"], t["k"], t["v"], t["q_full"], t["q_sparse"], t["k_scale"],
+                             t["v_scale"], t["max_context"], with_score=True)
+    scored()
+    torch.cuda.synchronize()
+    out = scored.outputs()
+    for key in ("o_full", "o_sparse", "sel_idx", "sel_count"):
+        assert torch.equal(bench_out[key], out[key]), f"{key} differs with the score output on"
+    del t, blk
+    w = parity.check_decode(d, out, seqs=seqs)
+    torch.cuda.empty_cache()
+    return w, out
+
+
+def test_workload2_b32_ctx128k_bf16():
+    say("case: workload 2 (B=32, 131072, bf16); oracle on sequences 0, 13, 31")
+    d = inputs.make_decode(2)
+    w, out = run_workload(d, [0, 13, 31])
+    counts = out["sel_count"].cpu().numpy()
+    assert np.all(counts == 1152)
+    say(f"worst {w}")
+
+
+def test_workload3_b4_ctx1m_fp8():
+    say("case: workload 3 (B=4, 1048576, fp8 e4m3); oracle on sequence 2")
+    d = inputs.make_decode(3)
+    w, _ = run_workload(d, [2])
+    say(f"worst {w}")
+
+
+def test_workload4_b64_ragged_agent_mix():
+    d = inputs.make_decode(4)
+    lens = np.diff(d["seq_offsets"])
+    seqs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 7, 40})
+    say(f"case: workload 4 (B=64 ragged, N={lens.sum()}); oracle on {seqs} (L={lens[seqs].tolist()})")
+    w, _ = run_workload(d, seqs)
+    say(f"worst {w}")
+
+
+def test_workload5_bridge_then_decode():
+    say("case: workload 5 bridge (262144 x 4096 -> 3 x (K, V)), sampled rows")
+    br = inputs.make_bridge()
+    dev = "cuda"
+    h = torch.from_numpy(br["h"].view(np.int16)).view(torch.bfloat16).to(dev)
+    wk = [torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).to(dev) for w in br["w_k"]]
+    wv = [torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).to(dev) for w in br["w_v"]]
+    k_out, v_out = hs2.bridge_kv(h, wk, wv)
+    torch.cuda.synchronize()
+    del h
+    rng = np.random.default_rng(0)
+    rows = np.sort(np.concatenate([rng.choice(262144, 1500, replace=False), np.arange(128), 262144 - 1 - np.arange(128)]))
+    rows = np.unique(rows)
+    ks_ref, vs_ref = O.bridge_kv(br["h"], br["w_k"], br["w_v"], rows=rows)
+    worst_ulp = 0
+    for l in range(3):
+        for got_t, ref in ((k_out[l], ks_ref[l]), (v_out[l], vs_ref[l])):
+            got = got_t.view(torch.int16).cpu().numpy().view(np.uint16)[rows]
+            ulps = np.abs(parity.bf16_ordinal(got) - parity.bf16_ordinal(O.f64_to_bf16_bits(ref)))
+            worst_ulp = max(worst_ulp, int(ulps.max()))
+            assert ulps.max() <= 1, f"bridge layer {l}: {ulps.max()} ulp"
+            assert parity.max_abs_rel(O.bf16_bits_to_f64(got), ref) <= 2e-3
+    say(f"bridge worst ulp {worst_ulp}")
+    del br
+    # decode per bridged layer over the GPU-built cache (8 x 32768 packed)
+    queries = inputs.make_bridge_queries()
+    offs = np.arange(9, dtype=np.int64) * 32768
+    for l in range(3):
+        kb = k_out[l].view(torch.int16).cpu().numpy().view(np.uint16)
+        vb = v_out[l].view(torch.int16).cpu().numpy().view(np.uint16)
+        d = dict(seq_offsets=offs, k=kb, v=vb, k_scale=None, v_scale=None, q_full=queries[l][0],
+                 q_sparse=queries[l][1], kv="bf16")
+        say(f"case: workload 5 decode, bridged layer {l}; oracle on sequences 0 and 5")
+        w, _ = run_workload(d, [0, 5])
+        say(f"worst {w}")
