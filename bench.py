@@ -1,0 +1,161 @@
+"""Benchmark: hybrid-block decode tokens/s on one MI355X.
+
+A step is one hs2_decode_block call over one batch: the full-attention layer
+over every context token, the per-token score and the token selection, and
+the sparse layers over the selected rows.  Inputs are resident in HBM before
+the timed region.  Default workload: 32 sequences x 131072 tokens, bf16 MQA
+cache (16 query heads, head_dim 128), window 128 + top-1024, 4 sparse layers.
+
+The roofline object is for the dominant kernel, the full-attention split-K
+pass: algorithmic bytes per launch = N x 512 B (each K and V row read once)
++ B x 8 KiB (the queries), divided by that kernel's mean duration measured
+live with HIP events recorded by the library on the launch stream during
+the timed steps.  ``traffic`` comes from rocprofv3 FETCH_SIZE/WRITE_SIZE runs
+(see profiles/), or is null.
+
+The cpu_baseline leg times the fp64 oracle on a bounded sample of the same
+workload (whole sequences, one after another, until about 15 s have passed).
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 2|3|4]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "hybrid-block decode tokens/s at 128K/1M ctx; achieved HBM GB/s vs peak"
+WORKLOADS = {2: "b32_ctx128k_bf16", 3: "b4_ctx1m_fp8", 4: "b64_ragged_2k_256k_bf16"}
+KV_ROW_BYTES = {"bf16": 2 * 2 * 128, "fp8_e4m3": 2 * 128 + 2 * 4}  # K+V (+ per-token scales)
+
+
+def cpu_baseline(d, budget_s=15.0):
+    """Time the oracle on whole sequences of this workload until `budget_s`."""
+    from oracle import hs2_oracle as O  # the oracle is only ever run here, for the baseline
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    offs = d["seq_offsets"]
+    done, tokens, t0 = 0, 0, time.perf_counter()
+    for b in range(offs.shape[0] - 1):
+        a, e = int(offs[b]), int(offs[b + 1])
+        ks = None if d["k_scale"] is None else d["k_scale"][a:e]
+        vs = None if d["v_scale"] is None else d["v_scale"][a:e]
+        k = O.decode_kv(d["k"][a:e], d["kv"], ks)
+        v = O.decode_kv(d["v"][a:e], d["kv"], vs)
+        O.decode_sequence(d["q_full"][b].astype(np.float64), d["q_sparse"][:, b].astype(np.float64), k, v)
+        done += 1
+        tokens += e - a
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {offs.shape[0] - 1} sequences ({tokens} context tokens), fp64 numpy, "
+                      f"one decode step each, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 1 GiB device copy before the timed region (for HBM counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the decode batch would shard by sequence with no exchange).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from long_context_kv_hs2_amd import hs2, inputs
+
+    hs2.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = inputs.make_decode(args.workload)
+    kv = d["kv"]
+    offs_t = torch.from_numpy(d["seq_offsets"]).to(dev)
+    if kv == "bf16":
+        k = torch.from_numpy(d["k"].view(np.int16)).view(torch.bfloat16).to(dev)
+        v = torch.from_numpy(d["v"].view(np.int16)).view(torch.bfloat16).to(dev)
+        ks = vs = None
+    else:
+        k = torch.from_numpy(d["k"]).to(dev)
+        v = torch.from_numpy(d["v"]).to(dev)
+        ks = torch.from_numpy(d["k_scale"]).to(dev)
+        vs = torch.from_numpy(d["v_scale"]).to(dev)
+    q_full = torch.from_numpy(d["q_full"]).to(dev)
+    q_sparse = torch.from_numpy(d["q_sparse"]).to(dev)
+    lens = np.diff(d["seq_offsets"])
+    batch, n_tokens = int(lens.shape[0]), int(lens.sum())
+    blk = hs2.DecodeBlock(offs_t, k, v, q_full, q_sparse, ks, vs, int(lens.max()), with_score=False)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(args.warmup):
+        blk()
+    torch.cuda.synchronize()
+    hs2.stage_timing(True)
+    hs2.stage_timing_read()  # clear
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        blk()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    hs2.stage_timing(False)
+    stages, n_rec = hs2.stage_timing_read()
+
+    ms_per_step = dt * 1e3 / args.steps
+    value = batch * args.steps / dt
+    k1_ms = stages["full_partial"]
+    alg_bytes = n_tokens * KV_ROW_BYTES[kv] + batch * 16 * 128 * 4
+    achieved = alg_bytes / (k1_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if kv == "bf16" else "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.workload], "batch": batch, "context_tokens": n_tokens,
+                   "max_context": int(lens.max()), "kv_cache": kv, "q_heads": 16, "kv_heads": 1,
+                   "head_dim": 128, "window": 128, "top_k": 1024, "n_sparse_layers": int(q_sparse.shape[0])},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "full_partial_kernel (hs2_full_decode_score split-K pass)",
+                     "alg_bytes_per_launch": alg_bytes, "mean_launch_ms": k1_ms},
+        "stages_ms": {k2: round(v2, 5) for k2, v2 in stages.items()},
+        "stage_calls_timed": n_rec,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(d)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

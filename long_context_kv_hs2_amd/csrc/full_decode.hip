@@ -52,47 +52,70 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
   SoftmaxState st;
   softmax_init(st);
 
-  for (int t0 = w0; t0 < w1; t0 += 16) {
+  // Raw tile registers: K lane (n, g) holds token t0 + n, bytes of dims
+  // 32g .. 32g + 31; V lane (n, g) holds token t0 + 4g + r, dims 8n .. 8n + 7.
+  // Rows past the end are clamped to a valid row and masked out in the tile step.
+  struct Raw {
+    u32x4 k[4];
+    u32x4 v[4];
+    float ks[4], vs[4];
+  };
+  auto load_tile = [&](int t0, Raw& raw) {
     const int nv = min(16, w1 - t0);
-    // K operand: token t0 + n, dims 32g .. 32g + 31 (rows past the end are
-    // clamped to a valid row and masked out below).
-    bf16x8 kf[4];
     const int tk = t0 + min(n, nv - 1);
     if constexpr (FP8) {
       const u32x4* src = reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(tk) * kRowBytes + 32 * g);
-      const u32x4 a = src[0];
-      const u32x4 b2 = src[1];
-      e4m3x16_to_bf16(a, kf[0], kf[1]);
-      e4m3x16_to_bf16(b2, kf[2], kf[3]);
+      raw.k[0] = src[0];
+      raw.k[1] = src[1];
     } else {
       const u32x4* src = reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(tk) * kRowBytes + 64 * g);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) kf[s] = as_bf16x8(src[s]);
+      for (int s = 0; s < 4; ++s) raw.k[s] = src[s];
     }
-    // V operand: token t0 + 4g + r, dims 8n .. 8n + 7.
-    float vf[4][8];
-    float ks[4], vs[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tv = t0 + min(4 * g + r, nv - 1);
       if constexpr (FP8) {
         const u32x2 w = *reinterpret_cast<const u32x2*>(vbase + static_cast<size_t>(tv) * kRowBytes + 8 * n);
-        e4m3x8_to_f32(w, vf[r]);
-        ks[r] = p.k_scale[base + tv];
-        vs[r] = p.v_scale[base + tv];
+        raw.v[r] = u32x4{w[0], w[1], 0u, 0u};
+        raw.ks[r] = p.k_scale[base + tv];
+        raw.vs[r] = p.v_scale[base + tv];
       } else {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(vbase + static_cast<size_t>(tv) * kRowBytes + 16 * n);
-        bf16x8_to_f32(w, vf[r]);
-        ks[r] = 1.f;
-        vs[r] = 1.f;
+        raw.v[r] = *reinterpret_cast<const u32x4*>(vbase + static_cast<size_t>(tv) * kRowBytes + 16 * n);
+        raw.ks[r] = 1.f;
+        raw.vs[r] = 1.f;
       }
     }
+  };
+
+  Raw cur, nxt;
+  if (w0 < w1) load_tile(w0, cur);
+  for (int t0 = w0; t0 < w1; t0 += 16) {
+    const int nv = min(16, w1 - t0);
+    if (t0 + 16 < w1) load_tile(t0 + 16, nxt);  // in flight during this tile's math
+    bf16x8 kf[4];
+    if constexpr (FP8) {
+      e4m3x16_to_bf16(cur.k[0], kf[0], kf[1]);
+      e4m3x16_to_bf16(cur.k[1], kf[2], kf[3]);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) kf[s] = as_bf16x8(cur.k[s]);
+    }
+    float vf[4][8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (FP8)
+        e4m3x8_to_f32(u32x2{cur.v[r][0], cur.v[r][1]}, vf[r]);
+      else
+        bf16x8_to_f32(cur.v[r], vf[r]);
+    }
     float lg[4];
-    attend_tile(q, kf, vf, ks, vs, nv, g, st, lg);
+    attend_tile(q, kf, vf, cur.ks, cur.vs, nv, g, st, lg);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if (4 * g + r < nv) spill[static_cast<size_t>(t0 + 4 * g + r) * kHeads + n] = lg[r];
     }
+    cur = nxt;
   }
 
   // Merge the four waves through LDS.

@@ -50,7 +50,7 @@ struct DecodeLayout {
   int chunk = 0;
   int chunks_per_seq = 0;
   int splits = 0;
-  size_t partials = 0, stats = 0, spill = 0, score = 0, hist = 0, state = 0, counters = 0, selbuf = 0,
+  size_t partials = 0, stats = 0, spill = 0, score = 0, hist0 = 0, counters = 0, selbuf = 0, cand = 0,
          sparse = 0, total = 0;
 };
 
@@ -72,10 +72,10 @@ DecodeLayout decode_layout(const hs2_decode_desc& d) {
   L.stats = take(B * kHeads * 2 * sizeof(float));
   L.spill = take(N * kHeads * sizeof(float));
   L.score = take(N * sizeof(float));
-  L.hist = take(B * kRadixPasses * kRadixBins * sizeof(uint32_t));
-  L.state = take(B * sizeof(SelectState));
-  L.counters = take(B * 8 * sizeof(uint32_t));
+  L.hist0 = take(B * kRadixBins * sizeof(uint32_t));
+  L.counters = take(B * 4 * sizeof(uint32_t));
   L.selbuf = take(B * kTopK * sizeof(int32_t));
+  L.cand = take(B * kCandCap * sizeof(unsigned long long));
   L.sparse = take(B * static_cast<size_t>(d.n_sparse_layers > 0 ? d.n_sparse_layers : 1) * L.splits *
                   kPartialFloats * sizeof(float));
   L.total = off;
@@ -227,10 +227,10 @@ SelectParams select_params(const DecodeArgs& a, const DecodeLayout& L, float* sc
   p.spill = reinterpret_cast<const float*>(ws_at(a.ws, L.spill));
   p.stats = reinterpret_cast<const float*>(ws_at(a.ws, L.stats));
   p.score = score;
-  p.hist = reinterpret_cast<uint32_t*>(ws_at(a.ws, L.hist));
-  p.state = reinterpret_cast<SelectState*>(ws_at(a.ws, L.state));
+  p.hist0 = reinterpret_cast<uint32_t*>(ws_at(a.ws, L.hist0));
   p.counters = reinterpret_cast<uint32_t*>(ws_at(a.ws, L.counters));
   p.selbuf = reinterpret_cast<int32_t*>(ws_at(a.ws, L.selbuf));
+  p.cand = reinterpret_cast<unsigned long long*>(ws_at(a.ws, L.cand));
   p.sel_idx = a.sel_idx;
   p.sel_count = a.sel_count;
   return p;
@@ -342,9 +342,8 @@ hs2_status hs2_decode_block(const hs2_decode_desc* desc, const int64_t* seq_offs
   HS2_HIP(launch_select_init(sp, d.batch, a.stream), "selection init");
   HS2_TRY(mark(rec, 0, a.stream));
   HS2_TRY(run_full(a, L, rec));
-  HS2_HIP(launch_score_pass(sp, d.batch, d.max_context, true, a.stream), "score pass");
-  HS2_HIP(launch_radix_passes(sp, d.batch, d.max_context, 1, a.stream), "radix passes");
-  HS2_HIP(launch_emit_finalize(sp, d.batch, d.max_context, a.stream), "selection emit");
+  HS2_HIP(launch_score_hist(sp, d.batch, d.max_context, true, true, a.stream), "score pass");
+  HS2_HIP(launch_collect_finish(sp, d.batch, d.max_context, a.stream), "selection");
   HS2_TRY(mark(rec, 3, a.stream));
   HS2_TRY(run_sparse(a, L, sel_idx, sel_count));
   HS2_TRY(mark(rec, 4, a.stream));
@@ -369,7 +368,7 @@ hs2_status hs2_full_decode_score(const hs2_decode_desc* desc, const int64_t* seq
                nullptr, nullptr, score_out, workspace, static_cast<hipStream_t>(stream)};
   HS2_TRY(run_full(a, L, nullptr));
   const SelectParams sp = select_params(a, L, score_out);
-  HS2_HIP(launch_score_pass(sp, d.batch, d.max_context, false, a.stream), "score pass");
+  HS2_HIP(launch_score_hist(sp, d.batch, d.max_context, true, false, a.stream), "score pass");
   return HS2_OK;
 }
 
@@ -390,8 +389,8 @@ hs2_status hs2_topk_select(const hs2_decode_desc* desc, const int64_t* seq_offse
                sel_idx, sel_count, nullptr, workspace, static_cast<hipStream_t>(stream)};
   const SelectParams sp = select_params(a, L, const_cast<float*>(score));
   HS2_HIP(launch_select_init(sp, d.batch, a.stream), "selection init");
-  HS2_HIP(launch_radix_passes(sp, d.batch, d.max_context, 0, a.stream), "radix passes");
-  HS2_HIP(launch_emit_finalize(sp, d.batch, d.max_context, a.stream), "selection emit");
+  HS2_HIP(launch_score_hist(sp, d.batch, d.max_context, false, true, a.stream), "score histogram");
+  HS2_HIP(launch_collect_finish(sp, d.batch, d.max_context, a.stream), "selection");
   return HS2_OK;
 }
 

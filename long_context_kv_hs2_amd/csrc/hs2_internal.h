@@ -48,14 +48,6 @@ hipError_t launch_merge_layers(const MergeParams& p, int batch, int layers, int6
                                int64_t out_stride_layer, hipStream_t s);
 
 // ---- score and token selection ---------------------------------------------
-struct SelectState {
-  unsigned long long prefix;  // resolved high bits of the threshold key
-  uint32_t rank;              // how many more keys to take among the candidates
-  int32_t shift;              // bit position the prefix applies at
-  int32_t done;               // 1 once the selected set is fixed
-  int32_t pad[3];
-};
-
 struct SelectParams {
   const int64_t* seq_offsets;
   int64_t total_tokens;
@@ -64,22 +56,23 @@ struct SelectParams {
   const float* spill;         // [N][16] (score pass only)
   const float* stats;         // [B][16][2] (score pass only)
   float* score;               // [N]
-  uint32_t* hist;             // [B][kRadixPasses][2048]
-  SelectState* state;         // [B]
-  uint32_t* counters;         // [B][8]: blocks finished per pass, then emitted count
-  int32_t* selbuf;            // [B][top_k]
+  uint32_t* hist0;            // [B][kRadixBins]: first-digit histogram
+  uint32_t* counters;         // [B][4]: winners emitted, candidates seen
+  int32_t* selbuf;            // [B][top_k]: positions emitted so far
+  unsigned long long* cand;   // [B][kCandCap]: keys of the threshold bin's tokens
   int32_t* sel_idx;           // [B][budget]
   int32_t* sel_count;         // [B]
 };
-constexpr int kRadixPasses = 6;
 constexpr int kRadixBins = 2048;
-constexpr int kScoreBlockTokens = 2048;
+constexpr int kScoreBlockTokens = 2048;   // tokens per score-pass workgroup
+constexpr int kCollectBlockTokens = 8192; // tokens per collect workgroup
+constexpr int kCandCap = 32768;           // candidate keys kept per sequence
 hipError_t launch_select_init(const SelectParams& p, int batch, hipStream_t s);
-hipError_t launch_score_pass(const SelectParams& p, int batch, int64_t max_context, bool histogram,
-                             hipStream_t s);
-hipError_t launch_radix_passes(const SelectParams& p, int batch, int64_t max_context, int first_pass,
-                               hipStream_t s);
-hipError_t launch_emit_finalize(const SelectParams& p, int batch, int64_t max_context, hipStream_t s);
+// score_j from the spilled logits (compute_score) or read from p.score, and
+// the first-digit histogram.
+hipError_t launch_score_hist(const SelectParams& p, int batch, int64_t max_context, bool compute_score,
+                             bool histogram, hipStream_t s);
+hipError_t launch_collect_finish(const SelectParams& p, int batch, int64_t max_context, hipStream_t s);
 
 // ---- sparse layers -----------------------------------------------------------
 constexpr int kSparseRows = 128;  // selected rows per workgroup

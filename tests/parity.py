@@ -131,3 +131,41 @@ def bf16_ordinal(bits):
     b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
     mag = b & 0x7FFF
     return np.where(b & 0x8000, -mag, mag)
+
+
+def check_bridge(h_bits, w_bits, out_bits, rows):
+    """Bridge outputs (bf16 bits [T, 128]) for the given rows against the
+    oracle.  Element-wise bound from the arithmetic: fp32 accumulation of
+    d_model exact bf16 products is within gamma_n * sum|h w| of the exact sum
+    (gamma_n = n u / (1 - n u), u = 2^-24), and the final rounding to bf16
+    adds at most one bf16 ulp.  Also: at least 99.9 % of elements within one
+    ulp of the correctly rounded value (catches a systematic error such as
+    truncation).  No max-abs-relative bar: bf16 output alone is off by up to
+    half an ulp, 2^-9 of the largest element, which a 2e-3 bar would not
+    reliably admit.  Returns (worst ulps, fraction within 1 ulp)."""
+    h = O.bf16_bits_to_f64(h_bits[rows])
+    w = O.bf16_bits_to_f64(w_bits)
+    ref = h @ w
+    abs_sum = np.abs(h) @ np.abs(w)
+    n = h.shape[1]
+    u = 2.0 ** -24
+    gamma = n * u / (1 - n * u)
+    got_bits = out_bits[rows]
+    got = O.bf16_bits_to_f64(got_bits)
+    mag = np.abs(ref) + gamma * abs_sum
+    with np.errstate(divide="ignore"):
+        ulp = np.ldexp(1.0, np.maximum(np.floor(np.log2(np.where(mag > 0, mag, 1.0))).astype(int), -126) - 7)
+    bound = ulp + gamma * abs_sum
+    err = np.abs(got - ref)
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err / bound), err.shape)
+        msg = (f"{int(bad.sum())} of {err.size} elements beyond the bound; worst at {i}: got {got[i]!r} "
+               f"ref {ref[i]!r} bound {bound[i]:.3e} abs_sum {abs_sum[i]:.3e}; "
+               f"max err/abs_sum {float((err / np.maximum(abs_sum, 1e-300)).max()):.3e}")
+        print(msg, flush=True)
+        raise AssertionError(msg)
+    ulps = np.abs(bf16_ordinal(got_bits) - bf16_ordinal(O.f64_to_bf16_bits(ref)))
+    frac1 = float((ulps <= 1).mean())
+    assert frac1 >= 0.999, f"only {frac1:.5f} of elements within 1 ulp"
+    return int(ulps.max()), frac1
