@@ -23,6 +23,7 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
   __shared__ float s_m[4][kHeads];
   __shared__ float s_z[4][kHeads];
   __shared__ float s_o[4][kHeads][kDim];
+  __shared__ u32x4 s_q[kQLdsVecs];
 
   const int b = blockIdx.y;
   const int c = blockIdx.x;
@@ -31,68 +32,65 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
   seq_bounds(p.seq_offsets, b, p.total_tokens, p.max_context, base, len);
   const int c0 = c * p.chunk;
   if (c0 >= len) return;  // uniform over the workgroup
-  const int c1 = min(len, c0 + p.chunk);
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;
   const int g = lane >> 4;
-  const int sub = p.chunk >> 2;
-  const int w0 = c0 + wave * sub;
-  const int w1 = min(c1, w0 + sub);
-
-  QFrag q;
-  load_qfrag(p.q + (static_cast<size_t>(b) * kHeads + n) * kDim, p.qscale, g, q);
+  // Tiles of 16 tokens are dealt round-robin over all waves of the sequence's
+  // workgroups (tile 4c + w + k * 4 * nblk), so at any moment they stream one
+  // compact region of the cache (better DRAM locality than a contiguous range
+  // per wave).  The split-K merge does not depend on which tokens a partial holds.
+  const int nblk = (len + p.chunk - 1) / p.chunk;
+  const int tile_stride = 16 * 4 * nblk;
+  const int w0 = 16 * (4 * c + wave);
+  build_q_lds<FP8>(p.q + static_cast<size_t>(b) * kHeads * kDim, p.qscale, s_q);
+  __syncthreads();
+  const QShared q{s_q, lane};
 
   constexpr int kRowBytes = FP8 ? kDim : 2 * kDim;
-  const uint8_t* kbase = p.k + base * kRowBytes;
-  const uint8_t* vbase = p.v + base * kRowBytes;
-  float* spill = p.spill + base * kHeads;
+  // Uniform per-sequence bases; lanes address rows with 32-bit offsets
+  // (a sequence spans at most 2^24 rows, so its bytes fit in 32 bits).
+  const uint8_t* __restrict__ kbase = p.k + base * kRowBytes;
+  const uint8_t* __restrict__ vbase = p.v + base * kRowBytes;
+  const float* __restrict__ ksb = FP8 ? p.k_scale + base : nullptr;
+  const float* __restrict__ vsb = FP8 ? p.v_scale + base : nullptr;
+  float* __restrict__ spill = p.spill + base * kHeads;
 
   SoftmaxState st;
   softmax_init(st);
 
-  // Raw tile registers: K lane (n, g) holds token t0 + n, bytes of dims
-  // 32g .. 32g + 31; V lane (n, g) holds token t0 + 4g + r, dims 8n .. 8n + 7.
+  // Raw tile registers: K lane (n, g) holds token t0 + n at row bytes
+  // kload_offset(j, g); V lane (n, g) holds token t0 + 4g + r, dims 8n .. 8n + 7.
   // Rows past the end are clamped to a valid row and masked out in the tile step.
   struct Raw {
-    u32x4 k[4];
+    u32x4 k[FP8 ? 2 : 4];
     u32x4 v[4];
     float ks[4], vs[4];
   };
   auto load_tile = [&](int t0, Raw& raw) {
-    const int nv = min(16, w1 - t0);
-    const int tk = t0 + min(n, nv - 1);
-    if constexpr (FP8) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(tk) * kRowBytes + 32 * g);
-      raw.k[0] = src[0];
-      raw.k[1] = src[1];
-    } else {
-      const u32x4* src = reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(tk) * kRowBytes + 64 * g);
+    const int nv = min(16, len - t0);
+    const uint32_t krow = static_cast<uint32_t>(t0 + min(n, nv - 1)) * kRowBytes;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) raw.k[s] = src[s];
-    }
+    for (int j = 0; j < (FP8 ? 2 : 4); ++j)
+      raw.k[j] = *reinterpret_cast<const u32x4*>(kbase + (krow + kload_offset(j, g)));
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int tv = t0 + min(4 * g + r, nv - 1);
+      const uint32_t tv = static_cast<uint32_t>(t0 + min(4 * g + r, nv - 1));
       if constexpr (FP8) {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(vbase + static_cast<size_t>(tv) * kRowBytes + 8 * n);
+        const u32x2 w = *reinterpret_cast<const u32x2*>(vbase + (tv * kRowBytes + 8 * n));
         raw.v[r] = u32x4{w[0], w[1], 0u, 0u};
-        raw.ks[r] = p.k_scale[base + tv];
-        raw.vs[r] = p.v_scale[base + tv];
+        raw.ks[r] = ksb[tv];
+        raw.vs[r] = vsb[tv];
       } else {
-        raw.v[r] = *reinterpret_cast<const u32x4*>(vbase + static_cast<size_t>(tv) * kRowBytes + 16 * n);
+        raw.v[r] = *reinterpret_cast<const u32x4*>(vbase + (tv * kRowBytes + 16 * n));
         raw.ks[r] = 1.f;
         raw.vs[r] = 1.f;
       }
     }
   };
-
-  Raw cur, nxt;
-  if (w0 < w1) load_tile(w0, cur);
-  for (int t0 = w0; t0 < w1; t0 += 16) {
-    const int nv = min(16, w1 - t0);
-    if (t0 + 16 < w1) load_tile(t0 + 16, nxt);  // in flight during this tile's math
+  auto step = [&](int t0, const Raw& cur) {
+    const int nv = min(16, len - t0);
     bf16x8 kf[4];
     if constexpr (FP8) {
       e4m3x16_to_bf16(cur.k[0], kf[0], kf[1]);
@@ -101,21 +99,29 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) kf[s] = as_bf16x8(cur.k[s]);
     }
-    float vf[4][8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if constexpr (FP8)
-        e4m3x8_to_f32(u32x2{cur.v[r][0], cur.v[r][1]}, vf[r]);
-      else
-        bf16x8_to_f32(cur.v[r], vf[r]);
-    }
     float lg[4];
-    attend_tile(q, kf, vf, cur.ks, cur.vs, nv, g, st, lg);
+    attend_tile<FP8>(q, kf, cur.v, cur.ks, cur.vs, nv, g, st, lg);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      if (4 * g + r < nv) spill[static_cast<size_t>(t0 + 4 * g + r) * kHeads + n] = lg[r];
+      if (4 * g + r < nv) spill[static_cast<uint32_t>(t0 + 4 * g + r) * kHeads + n] = lg[r];
     }
-    cur = nxt;
+  };
+
+  // Prefetch ring: the loads of the next kAhead tiles of this wave are in
+  // flight while one tile is computed.
+  constexpr int kAhead = 2;
+  Raw buf[kAhead + 1];
+#pragma unroll
+  for (int a = 0; a < kAhead; ++a)
+    if (w0 + tile_stride * a < len) load_tile(w0 + tile_stride * a, buf[a]);
+  for (int t0 = w0; t0 < len; t0 += tile_stride) {
+    // Compiler-only barrier: keeps the LDS query reads inside the loop rather
+    // than hoisted into 48 registers for the whole loop.
+    asm volatile("" ::: "memory");
+    if (t0 + tile_stride * kAhead < len) load_tile(t0 + tile_stride * kAhead, buf[kAhead]);
+    step(t0, buf[0]);
+#pragma unroll
+    for (int a = 0; a < kAhead; ++a) buf[a] = buf[a + 1];
   }
 
   // Merge the four waves through LDS.
@@ -168,8 +174,27 @@ hipError_t launch_full_partial(const FullParams& p, int batch, bool fp8, hipStre
 }
 
 // Merge split-K partials: per (head, sequence, layer) one workgroup of 128
-// threads (one per output dim) combines the partials in a fixed order.
+// threads (one per output dim).  The max and the sum of the partials are
+// block reductions over a fixed tree; the output accumulates the partials in
+// index order, 128 at a time with their weights staged in LDS, so every
+// reduction order is fixed and loads of successive partials overlap.
+__device__ __forceinline__ float block_reduce_128(float v, float* s_red, bool is_max) {
+  const int d = threadIdx.x;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float o = __shfl_xor(v, off);
+    v = is_max ? fmaxf(v, o) : v + o;
+  }
+  if ((d & 63) == 0) s_red[d >> 6] = v;
+  __syncthreads();
+  const float r = is_max ? fmaxf(s_red[0], s_red[1]) : s_red[0] + s_red[1];
+  __syncthreads();
+  return r;
+}
+
 __global__ __launch_bounds__(128) void merge_kernel(MergeParams p, int64_t stride_layer, int64_t out_stride_layer) {
+  __shared__ float s_red[2];
+  __shared__ float s_f[128];
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int layer = blockIdx.z;
@@ -181,15 +206,28 @@ __global__ __launch_bounds__(128) void merge_kernel(MergeParams p, int64_t strid
   const int count = (items + p.chunk - 1) / p.chunk;
   const float* pb = p.partials + layer * stride_layer + static_cast<int64_t>(b) * p.stride_seq;
   float mx = -INFINITY;
-  for (int c = 0; c < count; ++c) mx = fmaxf(mx, pb[static_cast<int64_t>(c) * p.stride_chunk + h]);
-  float z = 0.f;
+  for (int c = d; c < count; c += 128) mx = fmaxf(mx, pb[static_cast<int64_t>(c) * p.stride_chunk + h]);
+  mx = block_reduce_128(mx, s_red, true);
+  float zpart = 0.f;
   float acc = 0.f;
-  for (int c = 0; c < count; ++c) {
-    const float* pc = pb + static_cast<int64_t>(c) * p.stride_chunk;
-    const float f = exp2f(pc[h] - mx);
-    z += pc[kHeads + h] * f;
-    acc += pc[2 * kHeads + h * kDim + d] * f;
+  for (int c0 = 0; c0 < count; c0 += 128) {
+    const int c = c0 + d;
+    float f = 0.f;
+    if (c < count) {
+      const float* pc = pb + static_cast<int64_t>(c) * p.stride_chunk;
+      const float m = pc[h];
+      f = m == -INFINITY ? 0.f : exp2f(m - mx);
+      zpart += pc[kHeads + h] * f;
+    }
+    s_f[d] = f;
+    __syncthreads();
+    const int nc = min(128, count - c0);
+    const float* po = pb + static_cast<int64_t>(c0) * p.stride_chunk + 2 * kHeads + h * kDim + d;
+#pragma unroll 8
+    for (int j = 0; j < nc; ++j) acc += po[static_cast<int64_t>(j) * p.stride_chunk] * s_f[j];
+    __syncthreads();
   }
+  const float z = block_reduce_128(zpart, s_red, false);
   float* out = p.out + layer * out_stride_layer + b * p.out_stride_seq + h * kDim;
   out[d] = count ? acc / z : 0.f;
   if (p.stats && layer == 0 && d == 0) {

@@ -8,7 +8,7 @@
 #include <mutex>
 #include <vector>
 
-#include "../../include/hs2.h"
+#include "hs2.h"
 #include "hs2_device.h"
 #include "hs2_internal.h"
 

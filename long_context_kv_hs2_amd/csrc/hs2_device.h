@@ -71,35 +71,77 @@ __device__ __forceinline__ void split3(float x, uint32_t& h, uint32_t& m, uint32
   l = lu >> 16;
 }
 
-// Query operand for S^T = K Q^T with the 16x16x32 MFMA: lane (n = l%16,
-// g = l/16) holds head n, dims 32g + 8s + i for k-step s = 0..3, i = 0..7,
-// as three bf16 parts of (q * qscale).
-struct QFrag {
+// Reduction-dim layout of S^T = K Q^T on the 16x16x32 MFMA.  Lane (n = l%16,
+// g = l/16) holds, for k-step s = 0..3, eight consecutive dims starting at
+// kdim0(s, g) of token n (K operand) and of head n (Q operand).  The layout is
+// chosen so each 16-byte K load instruction of a wave reads 64 contiguous
+// bytes of every row: bf16 step s, group g -> dims 32s + 8g; E4M3 (one 16-byte
+// load per two steps) -> dims 64(s/2) + 16g + 8(s%2).
+template <bool FP8>
+__device__ __forceinline__ int kdim0(int s, int g) {
+  return FP8 ? 64 * (s >> 1) + 16 * g + 8 * (s & 1) : 32 * s + 8 * g;
+}
+
+// Three bf16 parts of (q * qscale) for the 8 dims of (k-step s, group g).
+template <bool FP8>
+__device__ __forceinline__ void split_q8(const float* __restrict__ q_head, int s, int g, float qscale, u32x4& ph,
+                                         u32x4& pm, u32x4& pl) {
+  const float* src = q_head + kdim0<FP8>(s, g);
+  const float4 a = *reinterpret_cast<const float4*>(src);
+  const float4 c = *reinterpret_cast<const float4*>(src + 4);
+  const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t h0, m0, l0, h1, m1, l1;
+    split3(x[2 * i] * qscale, h0, m0, l0);
+    split3(x[2 * i + 1] * qscale, h1, m1, l1);
+    ph[i] = h0 | (h1 << 16);
+    pm[i] = m0 | (m1 << 16);
+    pl[i] = l0 | (l1 << 16);
+  }
+}
+
+// Query operand held in registers (one wave's own query).
+struct QRegs {
   bf16x8 part[3][4];
+  __device__ __forceinline__ bf16x8 get(int p, int s) const { return part[p][s]; }
 };
 
-__device__ __forceinline__ void load_qfrag(const float* __restrict__ q_head, float qscale, int g, QFrag& f) {
-  const float* src = q_head + 32 * g;
+template <bool FP8>
+__device__ __forceinline__ void load_qregs(const float* __restrict__ q_head, float qscale, int g, QRegs& f) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    const float4 a = *reinterpret_cast<const float4*>(src + 8 * s);
-    const float4 c = *reinterpret_cast<const float4*>(src + 8 * s + 4);
-    const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
     u32x4 ph, pm, pl;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t h0, m0, l0, h1, m1, l1;
-      split3(x[2 * i] * qscale, h0, m0, l0);
-      split3(x[2 * i + 1] * qscale, h1, m1, l1);
-      ph[i] = h0 | (h1 << 16);
-      pm[i] = m0 | (m1 << 16);
-      pl[i] = l0 | (l1 << 16);
-    }
+    split_q8<FP8>(q_head, s, g, qscale, ph, pm, pl);
     f.part[0][s] = as_bf16x8(ph);
     f.part[1][s] = as_bf16x8(pm);
     f.part[2][s] = as_bf16x8(pl);
   }
 }
+
+// Query operand shared by a workgroup's waves through LDS: s_q[(p*4 + s)*64 + lane].
+constexpr int kQLdsVecs = 3 * 4 * 64;
+struct QShared {
+  const u32x4* s_q;
+  int lane;
+  __device__ __forceinline__ bf16x8 get(int p, int s) const { return as_bf16x8(s_q[(p * 4 + s) * 64 + lane]); }
+};
+
+// Build the LDS query operand of heads [16][128] with 256 threads.
+template <bool FP8>
+__device__ __forceinline__ void build_q_lds(const float* __restrict__ q_heads, float qscale, u32x4* s_q) {
+  const int s = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  u32x4 ph, pm, pl;
+  split_q8<FP8>(q_heads + (lane & 15) * kDim, s, lane >> 4, qscale, ph, pm, pl);
+  s_q[(0 * 4 + s) * 64 + lane] = ph;
+  s_q[(1 * 4 + s) * 64 + lane] = pm;
+  s_q[(2 * 4 + s) * 64 + lane] = pl;
+}
+
+// Row byte offset of the j-th 16-byte K load of lane group g (bf16: j = s,
+// four loads; E4M3: j = s/2, two loads), matching kdim0.
+__device__ __forceinline__ int kload_offset(int j, int g) { return 64 * j + 16 * g; }
 
 // Two OCP E4M3 codes (bytes 0,1 or 2,3 of w) -> two bf16 packed in a word.
 // The conversion to fp32 is exact and E4M3 has 4 significant bits, so taking
@@ -167,20 +209,23 @@ __device__ __forceinline__ void softmax_init(SoftmaxState& st) {
 }
 
 // One tile of 16 context tokens for 16 heads.
-//  kf[s]: K operand, lane (n, g): token n, dims 32g + 8s + i (bf16)
-//  vf[r][t]: V operand, lane (n, g): token 4g + r, dim 8n + t (fp32)
+//  kf[s]: K operand, lane (n, g): token n, dims kdim0(s, g) + i (bf16)
+//  vraw[r]: V values of token 4g + r, dims 8n .. 8n + 7, lane (n, g): eight
+//           bf16 (16 bytes) or eight E4M3 codes (first 8 bytes); converted to
+//           fp32 just before their MFMAs
 //  kscale[r], vscale[r]: per-token scales of token 4g + r (1 for bf16)
 //  nvalid: tokens of the tile that exist (1..16); others are masked out
 // Returns the log2-domain logits of tokens 4g + r for head n in lg[r]
 // (-inf where masked).
-__device__ __forceinline__ void attend_tile(const QFrag& q, const bf16x8 (&kf)[4], const float (&vf)[4][8],
+template <bool FP8, class QSrc>
+__device__ __forceinline__ void attend_tile(const QSrc& q, const bf16x8 (&kf)[4], const u32x4 (&vraw)[4],
                                             const float (&kscale)[4], const float (&vscale)[4], int nvalid,
                                             int g, SoftmaxState& st, float (&lg)[4]) {
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int part = 0; part < 3; ++part) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) s = mfma_bf16_16x16x32(kf[k], q.part[part][k], s);
+    for (int k = 0; k < 4; ++k) s = mfma_bf16_16x16x32(kf[k], q.get(part, k), s);
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) lg[r] = (4 * g + r < nvalid) ? s[r] * kscale[r] : -INFINITY;
@@ -201,8 +246,13 @@ __device__ __forceinline__ void attend_tile(const QFrag& q, const bf16x8 (&kf)[4
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float pv = p[r] * vscale[r];
+    float vf[8];
+    if constexpr (FP8)
+      e4m3x8_to_f32(u32x2{vraw[r][0], vraw[r][1]}, vf);
+    else
+      bf16x8_to_f32(vraw[r], vf);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) st.o[t] = mfma_f32_16x16x4(vf[r][t], pv, st.o[t]);
+    for (int t = 0; t < 8; ++t) st.o[t] = mfma_f32_16x16x4(vf[t], pv, st.o[t]);
   }
 }
 

@@ -35,22 +35,40 @@ __global__ __launch_bounds__(256) void sparse_partial_kernel(SparseParams p) {
   const int rows = min(kSparseRows, count - r0);
   const int32_t* sel = p.sel_idx + static_cast<size_t>(b) * p.budget + r0;
 
-  // Gather: rows past `rows` copy the last valid row (masked out later).
+  // Gather: rows past `rows` copy the last valid row (masked out later).  All
+  // of a thread's loads are issued before any is stored to LDS.
   constexpr int kChunks = kRowBytes / 16;
-  for (int c = threadIdx.x; c < kSparseRows * kChunks; c += blockDim.x) {
+  constexpr int kPer = kSparseRows * kChunks / 256;
+  u32x4 kv[kPer], vv[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int c = threadIdx.x + 256 * i;
     const int row = c / kChunks;
     const int part = c % kChunks;
     const int64_t pos = base + min(max(sel[min(row, rows - 1)], 0), len - 1);
-    const u32x4 kv = *reinterpret_cast<const u32x4*>(p.k + pos * kRowBytes + 16 * part);
-    const u32x4 vv = *reinterpret_cast<const u32x4*>(p.v + pos * kRowBytes + 16 * part);
-    *reinterpret_cast<u32x4*>(s_k + row * kPitch + 16 * part) = kv;
-    *reinterpret_cast<u32x4*>(s_v + row * kPitch + 16 * part) = vv;
+    kv[i] = *reinterpret_cast<const u32x4*>(p.k + pos * kRowBytes + 16 * part);
+    vv[i] = *reinterpret_cast<const u32x4*>(p.v + pos * kRowBytes + 16 * part);
+  }
+  float ksc = 1.f, vsc = 1.f;
+  if constexpr (FP8) {
+    if (threadIdx.x < kSparseRows) {
+      const int64_t pos = base + min(max(sel[min(static_cast<int>(threadIdx.x), rows - 1)], 0), len - 1);
+      ksc = p.k_scale[pos];
+      vsc = p.v_scale[pos];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    const int row = c / kChunks;
+    const int part = c % kChunks;
+    *reinterpret_cast<u32x4*>(s_k + row * kPitch + 16 * part) = kv[i];
+    *reinterpret_cast<u32x4*>(s_v + row * kPitch + 16 * part) = vv[i];
   }
   if constexpr (FP8) {
-    for (int row = threadIdx.x; row < kSparseRows; row += blockDim.x) {
-      const int64_t pos = base + min(max(sel[min(row, rows - 1)], 0), len - 1);
-      s_ks[row] = p.k_scale[pos];
-      s_vs[row] = p.v_scale[pos];
+    if (threadIdx.x < kSparseRows) {
+      s_ks[threadIdx.x] = ksc;
+      s_vs[threadIdx.x] = vsc;
     }
   }
   __syncthreads();
@@ -60,39 +78,39 @@ __global__ __launch_bounds__(256) void sparse_partial_kernel(SparseParams p) {
   const int n = lane & 15;
   const int g = lane >> 4;
   for (int layer = wave; layer < p.n_layers; layer += 4) {
-    QFrag q;
-    load_qfrag(p.q_sparse + ((static_cast<size_t>(layer) * p.batch + b) * kHeads + n) * kDim, p.qscale, g, q);
+    QRegs q;
+    load_qregs<FP8>(p.q_sparse + ((static_cast<size_t>(layer) * p.batch + b) * kHeads + n) * kDim, p.qscale, g, q);
     SoftmaxState st;
     softmax_init(st);
     for (int t0 = 0; t0 < rows; t0 += 16) {
       const int nv = min(16, rows - t0);
       bf16x8 kf[4];
+      const uint8_t* krow = s_k + (t0 + n) * kPitch;
       if constexpr (FP8) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(s_k + (t0 + n) * kPitch + 32 * g);
-        e4m3x16_to_bf16(src[0], kf[0], kf[1]);
-        e4m3x16_to_bf16(src[1], kf[2], kf[3]);
+        e4m3x16_to_bf16(*reinterpret_cast<const u32x4*>(krow + kload_offset(0, g)), kf[0], kf[1]);
+        e4m3x16_to_bf16(*reinterpret_cast<const u32x4*>(krow + kload_offset(1, g)), kf[2], kf[3]);
       } else {
-        const u32x4* src = reinterpret_cast<const u32x4*>(s_k + (t0 + n) * kPitch + 64 * g);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) kf[s] = as_bf16x8(src[s]);
+        for (int s = 0; s < 4; ++s) kf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + kload_offset(s, g)));
       }
-      float vf[4][8];
+      u32x4 vraw[4];
       float ks[4], vs[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = t0 + 4 * g + r;
         if constexpr (FP8) {
-          e4m3x8_to_f32(*reinterpret_cast<const u32x2*>(s_v + row * kPitch + 8 * n), vf[r]);
+          const u32x2 w = *reinterpret_cast<const u32x2*>(s_v + row * kPitch + 8 * n);
+          vraw[r] = u32x4{w[0], w[1], 0u, 0u};
           ks[r] = s_ks[row];
           vs[r] = s_vs[row];
         } else {
-          bf16x8_to_f32(*reinterpret_cast<const u32x4*>(s_v + row * kPitch + 16 * n), vf[r]);
+          vraw[r] = *reinterpret_cast<const u32x4*>(s_v + row * kPitch + 16 * n);
           ks[r] = 1.f;
           vs[r] = 1.f;
         }
       }
       float lg[4];
-      attend_tile(q, kf, vf, ks, vs, nv, g, st, lg);
+      attend_tile<FP8>(q, kf, vraw, ks, vs, nv, g, st, lg);
     }
     const float z = reduce_z(st.z);
     float* out = p.partials + ((static_cast<size_t>(b) * p.n_layers + layer) * p.splits + split) * kPartialFloats;
