@@ -18,7 +18,13 @@
 
 namespace hs2 {
 
-template <bool FP8>
+// BOUND: instead of spilling the 16 logits of each token, keep per token
+// shat_j = sum_h exp2(l_hj - m_h^t) / z_h^t with the wave's running max m^t and
+// running sum z^t after the token's tile, and per tile those (m^t, z^t).  Then
+// score_j = sum_h a_hj F_h^t with F_h^t = z_h^t exp2(m_h^t - M_h) / Z_h, so
+// score_j lies in shat_j * [min_h F_h^t, max_h F_h^t]; the selection prunes with
+// these bounds and rescores the survivors exactly.
+template <bool FP8, bool BOUND>
 __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
   __shared__ float s_m[4][kHeads];
   __shared__ float s_z[4][kHeads];
@@ -55,7 +61,8 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
   const uint8_t* __restrict__ vbase = p.v + base * kRowBytes;
   const float* __restrict__ ksb = FP8 ? p.k_scale + base : nullptr;
   const float* __restrict__ vsb = FP8 ? p.v_scale + base : nullptr;
-  float* __restrict__ spill = p.spill + base * kHeads;
+  float* __restrict__ spill = BOUND ? nullptr : p.spill + base * kHeads;
+  float* __restrict__ shat = BOUND ? p.shat + base : nullptr;
 
   SoftmaxState st;
   softmax_init(st);
@@ -99,11 +106,27 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) kf[s] = as_bf16x8(cur.k[s]);
     }
-    float lg[4];
-    attend_tile<FP8>(q, kf, cur.v, cur.ks, cur.vs, nv, g, st, lg);
+    float lg[4], pr[4];
+    attend_tile<FP8>(q, kf, cur.v, cur.ks, cur.vs, nv, g, st, lg, pr);
+    if constexpr (BOUND) {
+      const float zt = reduce_z(st.z);  // head n's running sum over the wave's tiles so far
+      const float inv = 1.f / zt;
+      float sh[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (4 * g + r < nv) spill[static_cast<uint32_t>(t0 + 4 * g + r) * kHeads + n] = lg[r];
+      for (int r = 0; r < 4; ++r) sh[r] = row_sum16(pr[r] * inv);
+      // lane n < 4 of row g writes token t0 + 4g + n: 16 consecutive floats per tile
+      const float mine = n == 0 ? sh[0] : n == 1 ? sh[1] : n == 2 ? sh[2] : sh[3];
+      if (n < 4 && 4 * g + n < nv) shat[static_cast<uint32_t>(t0 + 4 * g + n)] = mine;
+      if (g == 0) {
+        float* ts = p.tile_stats + tile_slot(base, b, t0 >> 4) * (2 * kHeads);
+        ts[n] = st.m;
+        ts[kHeads + n] = zt;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (4 * g + r < nv) spill[static_cast<uint32_t>(t0 + 4 * g + r) * kHeads + n] = lg[r];
+      }
     }
   };
 
@@ -163,13 +186,17 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
   o4[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
-hipError_t launch_full_partial(const FullParams& p, int batch, bool fp8, hipStream_t s) {
+hipError_t launch_full_partial(const FullParams& p, int batch, bool fp8, bool bound_mode, hipStream_t s) {
   if (batch == 0) return hipSuccess;
   const dim3 grid(p.chunks_per_seq, batch);
-  if (fp8)
-    hipLaunchKernelGGL(full_partial_kernel<true>, grid, dim3(256), 0, s, p);
+  if (fp8 && bound_mode)
+    hipLaunchKernelGGL((full_partial_kernel<true, true>), grid, dim3(256), 0, s, p);
+  else if (fp8)
+    hipLaunchKernelGGL((full_partial_kernel<true, false>), grid, dim3(256), 0, s, p);
+  else if (bound_mode)
+    hipLaunchKernelGGL((full_partial_kernel<false, true>), grid, dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL(full_partial_kernel<false>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((full_partial_kernel<false, false>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -51,7 +51,7 @@ struct DecodeLayout {
   int chunks_per_seq = 0;
   int splits = 0;
   size_t partials = 0, stats = 0, spill = 0, score = 0, hist0 = 0, counters = 0, selbuf = 0, cand = 0,
-         sparse = 0, total = 0;
+         shat = 0, tile_stats = 0, cand_idx = 0, sparse = 0, total = 0;
 };
 
 DecodeLayout decode_layout(const hs2_decode_desc& d) {
@@ -76,6 +76,9 @@ DecodeLayout decode_layout(const hs2_decode_desc& d) {
   L.counters = take(B * 4 * sizeof(uint32_t));
   L.selbuf = take(B * kTopK * sizeof(int32_t));
   L.cand = take(B * kCandCap * sizeof(unsigned long long));
+  L.shat = take(N * sizeof(float));
+  L.tile_stats = take(((N >> 4) + B + 1) * 2 * kHeads * sizeof(float));
+  L.cand_idx = take(B * kCandCap * sizeof(int32_t));
   L.sparse = take(B * static_cast<size_t>(d.n_sparse_layers > 0 ? d.n_sparse_layers : 1) * L.splits *
                   kPartialFloats * sizeof(float));
   L.total = off;
@@ -213,6 +216,8 @@ FullParams full_params(const DecodeArgs& a, const DecodeLayout& L) {
   p.chunks_per_seq = L.chunks_per_seq;
   p.partials = reinterpret_cast<float*>(ws_at(a.ws, L.partials));
   p.spill = reinterpret_cast<float*>(ws_at(a.ws, L.spill));
+  p.shat = reinterpret_cast<float*>(ws_at(a.ws, L.shat));
+  p.tile_stats = reinterpret_cast<float*>(ws_at(a.ws, L.tile_stats));
   return p;
 }
 
@@ -231,15 +236,23 @@ SelectParams select_params(const DecodeArgs& a, const DecodeLayout& L, float* sc
   p.counters = reinterpret_cast<uint32_t*>(ws_at(a.ws, L.counters));
   p.selbuf = reinterpret_cast<int32_t*>(ws_at(a.ws, L.selbuf));
   p.cand = reinterpret_cast<unsigned long long*>(ws_at(a.ws, L.cand));
+  p.shat = reinterpret_cast<const float*>(ws_at(a.ws, L.shat));
+  p.tile_stats = reinterpret_cast<const float*>(ws_at(a.ws, L.tile_stats));
+  p.cand_idx = reinterpret_cast<int32_t*>(ws_at(a.ws, L.cand_idx));
+  p.k = static_cast<const uint8_t*>(a.k);
+  p.k_scale = a.ks;
+  p.q = a.q_full;
+  p.qscale = static_cast<float>(static_cast<double>(a.d->softmax_scale) * kLog2e);
   p.sel_idx = a.sel_idx;
   p.sel_count = a.sel_count;
   return p;
 }
 
-hs2_status run_full(const DecodeArgs& a, const DecodeLayout& L, TimingRecord* rec) {
+hs2_status run_full(const DecodeArgs& a, const DecodeLayout& L, bool bound_mode, TimingRecord* rec) {
   const hs2_decode_desc& d = *a.d;
   const FullParams fp = full_params(a, L);
-  HS2_HIP(launch_full_partial(fp, d.batch, d.kv_dtype == HS2_KV_FP8_E4M3, a.stream), "full-attention partial pass");
+  HS2_HIP(launch_full_partial(fp, d.batch, d.kv_dtype == HS2_KV_FP8_E4M3, bound_mode, a.stream),
+          "full-attention partial pass");
   HS2_TRY(mark(rec, 1, a.stream));
   MergeParams mp;
   mp.seq_offsets = a.offs;
@@ -337,13 +350,23 @@ hs2_status hs2_decode_block(const hs2_decode_desc* desc, const int64_t* seq_offs
                sel_idx, sel_count, score_out, workspace, static_cast<hipStream_t>(stream)};
   TimingRecord* rec = nullptr;
   HS2_TRY(timing_begin(&rec));
+  // Without a score output the full pass keeps only score bounds (4 + 8 bytes
+  // per token instead of 64 bytes of logits) and the selection rescores the
+  // few positions the bounds cannot rule out; with it, every logit is kept and
+  // every score computed.  Both give the same scores for the positions that
+  // matter, hence the same selection.
+  const bool bound_mode = score_out == nullptr;
   float* score = score_out ? score_out : reinterpret_cast<float*>(ws_at(workspace, L.score));
   const SelectParams sp = select_params(a, L, score);
   HS2_HIP(launch_select_init(sp, d.batch, a.stream), "selection init");
   HS2_TRY(mark(rec, 0, a.stream));
-  HS2_TRY(run_full(a, L, rec));
-  HS2_HIP(launch_score_hist(sp, d.batch, d.max_context, true, true, a.stream), "score pass");
-  HS2_HIP(launch_collect_finish(sp, d.batch, d.max_context, a.stream), "selection");
+  HS2_TRY(run_full(a, L, bound_mode, rec));
+  if (bound_mode) {
+    HS2_HIP(launch_bound_select(sp, d.batch, d.max_context, d.kv_dtype == HS2_KV_FP8_E4M3, a.stream), "selection");
+  } else {
+    HS2_HIP(launch_score_hist(sp, d.batch, d.max_context, true, true, a.stream), "score pass");
+    HS2_HIP(launch_collect_finish(sp, d.batch, d.max_context, a.stream), "selection");
+  }
   HS2_TRY(mark(rec, 3, a.stream));
   HS2_TRY(run_sparse(a, L, sel_idx, sel_count));
   HS2_TRY(mark(rec, 4, a.stream));
@@ -366,7 +389,7 @@ hs2_status hs2_full_decode_score(const hs2_decode_desc* desc, const int64_t* seq
   if (!any) return HS2_OK;
   DecodeArgs a{desc, seq_offsets, k_cache, v_cache, k_scale, v_scale, q_full, nullptr, o_full, nullptr,
                nullptr, nullptr, score_out, workspace, static_cast<hipStream_t>(stream)};
-  HS2_TRY(run_full(a, L, nullptr));
+  HS2_TRY(run_full(a, L, false, nullptr));
   const SelectParams sp = select_params(a, L, score_out);
   HS2_HIP(launch_score_hist(sp, d.batch, d.max_context, true, false, a.stream), "score pass");
   return HS2_OK;

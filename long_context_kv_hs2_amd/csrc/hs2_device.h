@@ -216,11 +216,11 @@ __device__ __forceinline__ void softmax_init(SoftmaxState& st) {
 //  kscale[r], vscale[r]: per-token scales of token 4g + r (1 for bf16)
 //  nvalid: tokens of the tile that exist (1..16); others are masked out
 // Returns the log2-domain logits of tokens 4g + r for head n in lg[r]
-// (-inf where masked).
+// (-inf where masked) and p[r] = exp2(lg[r] - running max after this tile).
 template <bool FP8, class QSrc>
 __device__ __forceinline__ void attend_tile(const QSrc& q, const bf16x8 (&kf)[4], const u32x4 (&vraw)[4],
                                             const float (&kscale)[4], const float (&vscale)[4], int nvalid,
-                                            int g, SoftmaxState& st, float (&lg)[4]) {
+                                            int g, SoftmaxState& st, float (&lg)[4], float (&p)[4]) {
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int part = 0; part < 3; ++part) {
@@ -234,7 +234,6 @@ __device__ __forceinline__ void attend_tile(const QSrc& q, const bf16x8 (&kf)[4]
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   const float mn = fmaxf(st.m, mx);
   const float alpha = exp2f(st.m - mn);
-  float p[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) p[r] = exp2f(lg[r] - mn);
   st.z = st.z * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
@@ -254,6 +253,16 @@ __device__ __forceinline__ void attend_tile(const QSrc& q, const bf16x8 (&kf)[4]
 #pragma unroll
     for (int t = 0; t < 8; ++t) st.o[t] = mfma_f32_16x16x4(vf[t], pv, st.o[t]);
   }
+}
+
+// Sum over the 16 lanes of a row (the 16 heads of one lane group); every
+// lane of the row gets the total.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 8);
+  return v;
 }
 
 // Reduce z over the four lane groups (every lane of head n gets the total).

@@ -21,9 +21,14 @@ struct FullParams {
   int chunk;                 // tokens per workgroup, multiple of 64
   int chunks_per_seq;
   float* partials;           // [B][chunks_per_seq][kPartialFloats]
-  float* spill;              // [N][16] log2-domain logits
+  float* spill;              // spill mode: [N][16] log2-domain logits
+  float* shat;               // bound mode: [N] per-token sum over heads of the running-normalised weights
+  float* tile_stats;         // bound mode: [tile_slots][32] running (max, sum) per head after each tile
 };
-hipError_t launch_full_partial(const FullParams& p, int batch, bool fp8, hipStream_t s);
+// Slot of tile t (tokens [16t, 16t + 16)) of the sequence starting at row `base`:
+// unique over all sequences, at most N/16 + B.
+__host__ __device__ inline int64_t tile_slot(int64_t base, int b, int t) { return (base >> 4) + b + t; }
+hipError_t launch_full_partial(const FullParams& p, int batch, bool fp8, bool bound_mode, hipStream_t s);
 
 struct MergeParams {
   const int64_t* seq_offsets;
@@ -53,26 +58,39 @@ struct SelectParams {
   int64_t total_tokens;
   int64_t max_context;
   int window, top_k, budget;
-  const float* spill;         // [N][16] (score pass only)
-  const float* stats;         // [B][16][2] (score pass only)
+  const float* spill;         // [N][16] (spill mode)
+  const float* stats;         // [B][16][2] global (max, sum) per head
+  const float* shat;          // [N] (bound mode)
+  const float* tile_stats;    // [tile_slots][32] (bound mode)
   float* score;               // [N]
   uint32_t* hist0;            // [B][kRadixBins]: first-digit histogram
   uint32_t* counters;         // [B][4]: winners emitted, candidates seen
   int32_t* selbuf;            // [B][top_k]: positions emitted so far
-  unsigned long long* cand;   // [B][kCandCap]: keys of the threshold bin's tokens
+  unsigned long long* cand;   // [B][kCandCap]: candidate keys
+  int32_t* cand_idx;          // [B][kCandCap]: candidate positions (bound mode)
   int32_t* sel_idx;           // [B][budget]
   int32_t* sel_count;         // [B]
+  // exact rescoring of candidates (bound mode)
+  const uint8_t* k;
+  const float* k_scale;
+  const float* q;             // [B][16][128]
+  float qscale;
 };
 constexpr int kRadixBins = 2048;
 constexpr int kScoreBlockTokens = 2048;   // tokens per score-pass workgroup
 constexpr int kCollectBlockTokens = 8192; // tokens per collect workgroup
-constexpr int kCandCap = 32768;           // candidate keys kept per sequence
+constexpr int kBoundBlockTokens = 4096;   // tokens per bound-pass workgroup (one 16-token tile per thread)
+constexpr int kRefineBlocks = 64;         // rescoring workgroups per sequence
+constexpr int kCandCap = 32768;           // candidates kept per sequence
 hipError_t launch_select_init(const SelectParams& p, int batch, hipStream_t s);
-// score_j from the spilled logits (compute_score) or read from p.score, and
-// the first-digit histogram.
+// Spill mode: score_j from the spilled logits (compute_score) or read from
+// p.score, and the first-digit histogram.
 hipError_t launch_score_hist(const SelectParams& p, int batch, int64_t max_context, bool compute_score,
                              bool histogram, hipStream_t s);
 hipError_t launch_collect_finish(const SelectParams& p, int batch, int64_t max_context, hipStream_t s);
+// Bound mode: histogram of the lower bounds, candidates by upper bound, exact
+// rescoring of the candidates, exact top-k among them.
+hipError_t launch_bound_select(const SelectParams& p, int batch, int64_t max_context, bool fp8, hipStream_t s);
 
 // ---- sparse layers -----------------------------------------------------------
 constexpr int kSparseRows = 128;  // selected rows per workgroup

@@ -109,8 +109,8 @@ __global__ __launch_bounds__(256) void sparse_partial_kernel(SparseParams p) {
           vs[r] = 1.f;
         }
       }
-      float lg[4];
-      attend_tile<FP8>(q, kf, vraw, ks, vs, nv, g, st, lg);
+      float lg[4], pr[4];
+      attend_tile<FP8>(q, kf, vraw, ks, vs, nv, g, st, lg, pr);
     }
     const float z = reduce_z(st.z);
     float* out = p.partials + ((static_cast<size_t>(b) * p.n_layers + layer) * p.splits + split) * kPartialFloats;

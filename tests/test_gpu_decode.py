@@ -25,12 +25,22 @@ def say(msg):
 
 
 def run(d, with_score=True):
+    """Run the decode step with the score output (every logit kept) and
+    without it (score bounds, rescoring the survivors): both must agree
+    bitwise.  Returns the outputs of the run with scores."""
     t = parity.to_device(d)
     blk = hs2.DecodeBlock(t["seq_offsets"], t["k"], t["v"], t["q_full"], t["q_sparse"], t["k_scale"],
                           t["v_scale"], t["max_context"], with_score)
     blk()
+    other = hs2.DecodeBlock(t["seq_offsets"], t["k"], t["v"], t["q_full"], t["q_sparse"], t["k_scale"],
+                            t["v_scale"], t["max_context"], not with_score)
+    other()
     torch.cuda.synchronize()
-    return blk.outputs(), t, blk
+    a, b = blk.outputs(), other.outputs()
+    for key in ("o_full", "o_sparse", "sel_idx", "sel_count"):
+        if a[key] is not None:
+            assert torch.equal(a[key], b[key]), f"{key} differs between the two score paths"
+    return a, t, blk
 
 
 def test_workload1_b1_ctx4k():
