@@ -19,17 +19,25 @@
 namespace hs2 {
 
 // BOUND: instead of spilling the 16 logits of each token, keep per token
-// shat_j = sum_h exp2(l_hj - m_h^t) / z_h^t with the wave's running max m^t and
-// running sum z^t after the token's tile, and per tile those (m^t, z^t).  Then
-// score_j = sum_h a_hj F_h^t with F_h^t = z_h^t exp2(m_h^t - M_h) / Z_h, so
-// score_j lies in shat_j * [min_h F_h^t, max_h F_h^t]; the selection prunes with
-// these bounds and rescores the survivors exactly.
+// shat_j = sum_h exp2(l_hj - m_h^t) c_h^t with the wave's running max m^t after
+// the token's tile and c^t ~ 1 / (running sum z^t), and per tile (m^t, c^t).
+// Then score_j = sum_h a_hj F_h^t with F_h^t = exp2(m_h^t - M_h) / (c_h^t Z_h),
+// so score_j lies in shat_j * [min_h F_h^t, max_h F_h^t]; the selection prunes
+// with these bounds and rescores the survivors exactly.
+// Bound-mode outputs of one wave's tiles wait in LDS until the loop ends: on
+// CDNA loads and stores share one in-order completion counter, so stores in
+// the streaming loop would put their write latency into every load wait.
+constexpr int kMaxWaveTiles = kMaxChunk / 64;
+constexpr int kTileOut = 3 * kHeads;  // shat[16], m[16], c[16]
+
 template <bool FP8, bool BOUND>
 __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
   __shared__ float s_m[4][kHeads];
   __shared__ float s_z[4][kHeads];
-  __shared__ float s_o[4][kHeads][kDim];
+  // the merge buffer O[4][16][128] and, before it, the bound-mode tile outputs
+  __shared__ __attribute__((aligned(16))) float s_raw[BOUND ? 4 * kMaxWaveTiles * kTileOut : 4 * kHeads * kDim];
   __shared__ u32x4 s_q[kQLdsVecs];
+  float(*s_o)[kHeads][kDim] = reinterpret_cast<float(*)[kHeads][kDim]>(s_raw);
 
   const int b = blockIdx.y;
   const int c = blockIdx.x;
@@ -50,9 +58,8 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
   const int nblk = (len + p.chunk - 1) / p.chunk;
   const int tile_stride = 16 * 4 * nblk;
   const int w0 = 16 * (4 * c + wave);
-  build_q_lds<FP8>(p.q + static_cast<size_t>(b) * kHeads * kDim, p.qscale, s_q);
-  __syncthreads();
-  const QShared q{s_q, lane};
+
+  const QShared q{s_q, lane};  // filled below, after the first tile's loads are issued
 
   constexpr int kRowBytes = FP8 ? kDim : 2 * kDim;
   // Uniform per-sequence bases; lanes address rows with 32-bit offsets
@@ -75,15 +82,17 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
     u32x4 v[4];
     float ks[4], vs[4];
   };
+  // Loads are issued unconditionally (rows clamped to the sequence's last
+  // row), so the compiler can count exactly which loads are still in flight
+  // when a tile is consumed; a prefetch past the end re-reads one cached row.
   auto load_tile = [&](int t0, Raw& raw) {
-    const int nv = min(16, len - t0);
-    const uint32_t krow = static_cast<uint32_t>(t0 + min(n, nv - 1)) * kRowBytes;
+    const uint32_t krow = static_cast<uint32_t>(min(t0 + n, len - 1)) * kRowBytes;
 #pragma unroll
     for (int j = 0; j < (FP8 ? 2 : 4); ++j)
       raw.k[j] = *reinterpret_cast<const u32x4*>(kbase + (krow + kload_offset(j, g)));
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const uint32_t tv = static_cast<uint32_t>(t0 + min(4 * g + r, nv - 1));
+      const uint32_t tv = static_cast<uint32_t>(min(t0 + 4 * g + r, len - 1));
       if constexpr (FP8) {
         const u32x2 w = *reinterpret_cast<const u32x2*>(vbase + (tv * kRowBytes + 8 * n));
         raw.v[r] = u32x4{w[0], w[1], 0u, 0u};
@@ -96,7 +105,7 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
       }
     }
   };
-  auto step = [&](int t0, const Raw& cur) {
+  auto step = [&](int t0, int ti, const Raw& cur) {
     const int nv = min(16, len - t0);
     bf16x8 kf[4];
     if constexpr (FP8) {
@@ -109,18 +118,20 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
     float lg[4], pr[4];
     attend_tile<FP8>(q, kf, cur.v, cur.ks, cur.vs, nv, g, st, lg, pr);
     if constexpr (BOUND) {
-      const float zt = reduce_z(st.z);  // head n's running sum over the wave's tiles so far
-      const float inv = 1.f / zt;
+      // a_hj = p_hj * c_h with c_h the reciprocal of head h's running sum;
+      // the stored c_h (not 1/z) is what the bounds divide by, so the
+      // approximate reciprocal costs no validity.
+      const float c = __builtin_amdgcn_rcpf(reduce_z(st.z));
       float sh[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sh[r] = row_sum16(pr[r] * inv);
-      // lane n < 4 of row g writes token t0 + 4g + n: 16 consecutive floats per tile
+      for (int r = 0; r < 4; ++r) sh[r] = row_sum16(pr[r] * c);
+      // lane n < 4 of row g holds token 4g + n; lanes of row 0 hold head n's (m, c)
+      float* out = s_raw + (wave * kMaxWaveTiles + ti) * kTileOut;
       const float mine = n == 0 ? sh[0] : n == 1 ? sh[1] : n == 2 ? sh[2] : sh[3];
-      if (n < 4 && 4 * g + n < nv) shat[static_cast<uint32_t>(t0 + 4 * g + n)] = mine;
+      if (n < 4) out[4 * g + n] = mine;
       if (g == 0) {
-        float* ts = p.tile_stats + tile_slot(base, b, t0 >> 4) * (2 * kHeads);
-        ts[n] = st.m;
-        ts[kHeads + n] = zt;
+        out[kHeads + n] = st.m;
+        out[2 * kHeads + n] = c;
       }
     } else {
 #pragma unroll
@@ -130,21 +141,46 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
     }
   };
 
-  // Prefetch ring: the loads of the next kAhead tiles of this wave are in
-  // flight while one tile is computed.
-  constexpr int kAhead = 2;
-  Raw buf[kAhead + 1];
-#pragma unroll
-  for (int a = 0; a < kAhead; ++a)
-    if (w0 + tile_stride * a < len) load_tile(w0 + tile_stride * a, buf[a]);
-  for (int t0 = w0; t0 < len; t0 += tile_stride) {
-    // Compiler-only barrier: keeps the LDS query reads inside the loop rather
-    // than hoisted into 48 registers for the whole loop.
-    asm volatile("" ::: "memory");
-    if (t0 + tile_stride * kAhead < len) load_tile(t0 + tile_stride * kAhead, buf[kAhead]);
-    step(t0, buf[0]);
-#pragma unroll
-    for (int a = 0; a < kAhead; ++a) buf[a] = buf[a + 1];
+  // Two-slot ring, unrolled so each slot keeps its own registers: while one
+  // tile is computed the next tile's loads are in flight.  (Rotating slots by
+  // copying would wait for the in-flight loads at every copy.)  The scheduling
+  // barriers pin each batch of loads ahead of the math of the tile before it;
+  // left free, the scheduler sinks them past that math and the prefetch is lost.
+  Raw ra, rb;
+  int t0 = w0;
+  int ti = 0;  // ordinal of the tile within this wave
+  load_tile(t0, ra);  // in flight while the query operand is built
+  build_q_lds<FP8>(p.q + static_cast<size_t>(b) * kHeads * kDim, p.qscale, s_q);
+  __syncthreads();
+  while (t0 < len) {
+    load_tile(t0 + tile_stride, rb);
+    __builtin_amdgcn_sched_barrier(0);
+    step(t0, ti++, ra);
+    __builtin_amdgcn_sched_barrier(0);
+    t0 += tile_stride;
+    if (t0 >= len) break;
+    load_tile(t0 + tile_stride, ra);
+    __builtin_amdgcn_sched_barrier(0);
+    step(t0, ti++, rb);
+    __builtin_amdgcn_sched_barrier(0);
+    t0 += tile_stride;
+  }
+
+  if constexpr (BOUND) {
+    // Write this wave's tile outputs: shat of the tokens that exist, and the
+    // per-tile (m, c) of every tile.
+    const int ntiles = w0 < len ? (len - 1 - w0) / tile_stride + 1 : 0;
+    for (int i = lane; i < ntiles * 16; i += 64) {
+      const int ti = i >> 4, e = i & 15;
+      const int tok = w0 + ti * tile_stride + e;
+      if (tok < len) shat[static_cast<uint32_t>(tok)] = s_raw[(wave * kMaxWaveTiles + ti) * kTileOut + e];
+    }
+    for (int i = lane; i < ntiles * 2 * kHeads; i += 64) {
+      const int ti = i >> 5, e = i & 31;
+      const int tile = (w0 + ti * tile_stride) >> 4;
+      p.tile_stats[tile_slot(base, b, tile) * (2 * kHeads) + e] = s_raw[(wave * kMaxWaveTiles + ti) * kTileOut + kHeads + e];
+    }
+    __syncthreads();  // the merge below reuses this LDS
   }
 
   // Merge the four waves through LDS.

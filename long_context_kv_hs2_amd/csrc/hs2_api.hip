@@ -37,12 +37,13 @@ constexpr int64_t kMaxContext = int64_t(1) << 24;
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// Tokens per full-attention workgroup: enough workgroups to fill 256 CUs
-// several times over, with partial traffic small against the K/V stream.
+// Tokens per full-attention workgroup: about 1024 workgroups (two rounds on
+// 256 CUs at two workgroups each), so the per-workgroup start-up latency and
+// partial write are paid few times, with at most 4096 tokens each.
 int choose_chunk(int64_t total_tokens) {
-  int64_t c = total_tokens / 2048;
+  int64_t c = total_tokens / 1024;
   int64_t p2 = 256;
-  while (p2 * 2 <= c && p2 < 2048) p2 *= 2;
+  while (p2 * 2 <= c && p2 < kMaxChunk) p2 *= 2;
   return static_cast<int>(p2);
 }
 

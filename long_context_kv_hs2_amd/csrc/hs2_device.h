@@ -193,8 +193,9 @@ __device__ __forceinline__ void e4m3x8_to_f32(u32x2 w, float* out) {
 }
 
 // Online-softmax state of one wave for 16 heads: lane (n, g) keeps head n's
-// running max m and its lane-group share of the sum z (log2 domain), and the
-// unnormalised output O^T tile: o[t][i] = O[head n][dim 32g + 8i + t].
+// reference max m (log2 domain; at most kRescaleSlack below the running max),
+// its lane-group share of the sum z of exp2(l - m), and the unnormalised
+// output O^T tile: o[t][i] = O[head n][dim 32g + 8i + t], all relative to m.
 struct SoftmaxState {
   float m;
   float z;
@@ -216,7 +217,8 @@ __device__ __forceinline__ void softmax_init(SoftmaxState& st) {
 //  kscale[r], vscale[r]: per-token scales of token 4g + r (1 for bf16)
 //  nvalid: tokens of the tile that exist (1..16); others are masked out
 // Returns the log2-domain logits of tokens 4g + r for head n in lg[r]
-// (-inf where masked) and p[r] = exp2(lg[r] - running max after this tile).
+// (-inf where masked) and p[r] = exp2(lg[r] - st.m), st.m being the head's
+// reference max after this tile (within kRescaleSlack of the true running max).
 template <bool FP8, class QSrc>
 __device__ __forceinline__ void attend_tile(const QSrc& q, const bf16x8 (&kf)[4], const u32x4 (&vraw)[4],
                                             const float (&kscale)[4], const float (&vscale)[4], int nvalid,
@@ -232,16 +234,24 @@ __device__ __forceinline__ void attend_tile(const QSrc& q, const bf16x8 (&kf)[4]
   float mx = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float mn = fmaxf(st.m, mx);
-  const float alpha = exp2f(st.m - mn);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) p[r] = exp2f(lg[r] - mn);
-  st.z = st.z * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-  if (__any(alpha != 1.f)) {
+  // Lazy rescaling: a head keeps its reference max until a tile exceeds it by
+  // more than kRescaleSlack (log2 units), so weights stay <= 2^kRescaleSlack and
+  // the accumulators are rescaled only a few times per wave instead of at
+  // nearly every tile.  Every partial carries its reference, so the math is
+  // unchanged.
+  constexpr float kRescaleSlack = 8.f;
+  const bool raise = mx > st.m + kRescaleSlack;  // true on a head's first tile (m = -inf)
+  if (__any(raise)) {
+    const float mn = raise ? mx : st.m;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - mn);  // 0 on the first tile, 1 if unchanged
+    st.z *= alpha;
 #pragma unroll
     for (int t = 0; t < 8; ++t) st.o[t] *= alpha;
+    st.m = mn;
   }
-  st.m = mn;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(lg[r] - st.m);
+  st.z += (p[0] + p[1]) + (p[2] + p[3]);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float pv = p[r] * vscale[r];
@@ -257,11 +267,19 @@ __device__ __forceinline__ void attend_tile(const QSrc& q, const bf16x8 (&kf)[4]
 
 // Sum over the 16 lanes of a row (the 16 heads of one lane group); every
 // lane of the row gets the total.
+// DPP lane moves within a row of 16 (plain VALU, no LDS crossbar): swap
+// neighbours, swap pairs, reverse each half-row, reverse the row.  After the
+// first two adds every lane of a quad holds the quad's sum; mirroring the
+// half-row pairs quad 0 with quad 1, mirroring the row pairs the two halves.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float row_sum16(float v) {
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
+  v += dpp_move<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_move<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_move<0x141>(v);  // row_half_mirror
+  v += dpp_move<0x140>(v);  // row_mirror
   return v;
 }
 

@@ -8,6 +8,7 @@
 namespace hs2 {
 
 // ---- full-attention layer: split-K partial pass and merge -------------------
+constexpr int kMaxChunk = 4096;  // most tokens one full-attention workgroup takes
 struct FullParams {
   const int64_t* seq_offsets;
   int64_t total_tokens;
@@ -23,7 +24,7 @@ struct FullParams {
   float* partials;           // [B][chunks_per_seq][kPartialFloats]
   float* spill;              // spill mode: [N][16] log2-domain logits
   float* shat;               // bound mode: [N] per-token sum over heads of the running-normalised weights
-  float* tile_stats;         // bound mode: [tile_slots][32] running (max, sum) per head after each tile
+  float* tile_stats;         // bound mode: [tile_slots][32] per head after each tile: running max, ~1/running sum
 };
 // Slot of tile t (tokens [16t, 16t + 16)) of the sequence starting at row `base`:
 // unique over all sequences, at most N/16 + B.

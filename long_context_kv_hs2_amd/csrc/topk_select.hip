@@ -34,8 +34,9 @@
 //     and append the window.
 //
 // Bound mode (no score output): the full pass kept per token
-// shat_j = sum_h a_hj and per 16-token tile the wave's running (max, sum) per
-// head, which bound score_j within shat_j * [min_h F_h, max_h F_h].
+// shat_j = sum_h a_hj and per 16-token tile the wave's running max and
+// (approximately) reciprocal running sum per head, which bound score_j within
+// shat_j * [min_h F_h, max_h F_h].
 //  1. histogram of the lower bounds' first digit;
 //  2. collect the positions whose upper bound reaches the lower edge of the bin
 //     holding the k-th largest lower bound: at least k positions have a score
@@ -403,14 +404,14 @@ hipError_t launch_collect_finish(const SelectParams& p, int batch, int64_t max_c
 
 // ---- bound mode ------------------------------------------------------------
 
-// Per-tile bound factors F_h = z_h^t exp2(m_h^t - M_h) / Z_h: their min and max.
+// Per-tile bound factors F_h = exp2(m_h^t - M_h) / (c_h^t Z_h): their min and max.
 __device__ __forceinline__ void tile_factors(const float* __restrict__ ts, const float (&mx)[kHeads],
                                              const float (&iz)[kHeads], float& fmin, float& fmax) {
   fmin = INFINITY;
   fmax = 0.f;
 #pragma unroll
   for (int h = 0; h < kHeads; ++h) {
-    const float f = ts[kHeads + h] * exp2f(ts[h] - mx[h]) * iz[h];
+    const float f = exp2f(ts[h] - mx[h]) * iz[h] / ts[kHeads + h];
     fmin = fminf(fmin, f);
     fmax = fmaxf(fmax, f);
   }
