@@ -10,8 +10,9 @@ The roofline object is for the dominant kernel, the full-attention split-K
 pass: algorithmic bytes per launch = N x 512 B (each K and V row read once)
 + B x 8 KiB (the queries), divided by that kernel's mean duration measured
 live with HIP events recorded by the library on the launch stream during
-the timed steps.  ``traffic`` comes from rocprofv3 FETCH_SIZE/WRITE_SIZE runs
-(see profiles/), or is null.
+the timed steps.  ``traffic`` is the kernel's HBM bytes per launch from the
+rocprofv3 FETCH_SIZE/WRITE_SIZE runs summarised under profiles/ (scaled by a
+1 GiB copy), or null when the kernel source changed since they were taken.
 
 The cpu_baseline leg times the fp64 oracle on a bounded sample of the same
 workload (whole sequences, one after another, until about 15 s have passed).
@@ -30,9 +31,30 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_PROFILE = {2: "profiles/full_partial_b32_ctx128k_bf16_hbm_traffic.md"}
+KERNEL_SOURCES = ("long_context_kv_hs2_amd/csrc/full_decode.hip", "long_context_kv_hs2_amd/csrc/hs2_device.h")
 METRIC = "hybrid-block decode tokens/s at 128K/1M ctx; achieved HBM GB/s vs peak"
 WORKLOADS = {2: "b32_ctx128k_bf16", 3: "b4_ctx1m_fp8", 4: "b64_ragged_2k_256k_bf16"}
 KV_ROW_BYTES = {"bf16": 2 * 2 * 128, "fp8_e4m3": 2 * 128 + 2 * 4}  # K+V (+ per-token scales)
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the full-attention pass from the committed
+    rocprofv3 counter summary, or None when there is none for this workload or
+    the kernel source changed since the counters were taken."""
+    import hashlib
+
+    path = TRAFFIC_PROFILE.get(workload)
+    if not path or not os.path.exists(os.path.join(ROOT, path)):
+        return None
+    text = open(os.path.join(ROOT, path), encoding="utf-8").read()
+    fields = dict(line.split(": ", 1) for line in text.splitlines()
+                  if line.startswith(("traffic_bytes_per_launch: ", "source_sha256: ")))
+    sha = hashlib.sha256(b"".join(open(os.path.join(ROOT, f), "rb").read() for f in KERNEL_SOURCES)).hexdigest()
+    if fields.get("source_sha256", "").strip() != sha:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(d, budget_s=15.0):
@@ -146,7 +168,7 @@ def main():
                    "max_context": int(lens.max()), "kv_cache": kv, "q_heads": 16, "kv_heads": 1,
                    "head_dim": 128, "window": 128, "top_k": 1024, "n_sparse_layers": int(q_sparse.shape[0])},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload),
                      "kernel": "full_partial_kernel (hs2_full_decode_score split-K pass)",
                      "alg_bytes_per_launch": alg_bytes, "mean_launch_ms": k1_ms},
         "stages_ms": {k2: round(v2, 5) for k2, v2 in stages.items()},
