@@ -17,7 +17,13 @@ rocprofv3 FETCH_SIZE/WRITE_SIZE runs summarised under profiles/ (scaled by a
 The cpu_baseline leg times the fp64 oracle on a bounded sample of the same
 workload (whole sequences, one after another, until about 15 s have passed).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 2|3|4]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 2|3|4|5]
+
+Workload 5 times the KV-Bridging projection (262144 x 4096 hidden states into
+3 layers' K and V, one bf16 MFMA GEMM) and then each bridged layer's decode
+step (8 sequences x 32768 tokens over the bridged cache); its roofline is the
+GEMM's against the dense bf16 MFMA peak, and its value the decode tokens/s
+through the 3 bridged hybrid blocks.
 """
 
 from __future__ import annotations
@@ -35,7 +41,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_PROFILE = {2: "profiles/full_partial_b32_ctx128k_bf16_hbm_traffic.md"}
 KERNEL_SOURCES = ("long_context_kv_hs2_amd/csrc/full_decode.hip", "long_context_kv_hs2_amd/csrc/hs2_device.h")
 METRIC = "hybrid-block decode tokens/s at 128K/1M ctx; achieved HBM GB/s vs peak"
-WORKLOADS = {2: "b32_ctx128k_bf16", 3: "b4_ctx1m_fp8", 4: "b64_ragged_2k_256k_bf16"}
+WORKLOADS = {2: "b32_ctx128k_bf16", 3: "b4_ctx1m_fp8", 4: "b64_ragged_2k_256k_bf16",
+             5: "bridge_262144x4096_3layers_then_b8x32k_decode"}
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 KV_ROW_BYTES = {"bf16": 2 * 2 * 128, "fp8_e4m3": 2 * 128 + 2 * 4}  # K+V (+ per-token scales)
 
 
@@ -85,6 +93,67 @@ def cpu_baseline(d, budget_s=15.0):
                       f"one decode step each, {dt:.1f} s"}
 
 
+def bench_bridge(args, torch, hs2, inputs, dev):
+    br = inputs.make_bridge()
+    t_rows, d_model = br["h"].shape
+    bits = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    h = bits(br["h"])
+    wk = [bits(w) for w in br["w_k"]]
+    wv = [bits(w) for w in br["w_v"]]
+    n_l = len(wk)
+    k_out = [torch.empty((t_rows, 128), dtype=torch.bfloat16, device=dev) for _ in range(n_l)]
+    v_out = [torch.empty((t_rows, 128), dtype=torch.bfloat16, device=dev) for _ in range(n_l)]
+    ws = torch.empty(hs2.bridge_workspace_bytes(t_rows, d_model, n_l), dtype=torch.uint8, device=dev)
+    queries = inputs.make_bridge_queries()
+    batch = queries[0][0].shape[0]
+    offs = torch.arange(batch + 1, dtype=torch.int64, device=dev) * (t_rows // batch)
+    blocks = [hs2.DecodeBlock(offs, k_out[l], v_out[l], torch.from_numpy(queries[l][0]).to(dev),
+                              torch.from_numpy(queries[l][1]).to(dev), None, None, t_rows // batch)
+              for l in range(n_l)]
+
+    def bridge():
+        hs2.bridge_kv(h, wk, wv, k_out, v_out, ws)
+
+    for _ in range(args.warmup):
+        bridge()
+        for blk in blocks:
+            blk()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        bridge()
+    e1.record()
+    torch.cuda.synchronize()
+    bridge_ms = e0.elapsed_time(e1) / args.steps
+    hs2.stage_timing(True)
+    hs2.stage_timing_read()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for blk in blocks:
+            blk()
+    torch.cuda.synchronize()
+    decode_s = (time.perf_counter() - t0) / args.steps
+    hs2.stage_timing(False)
+    stages, _ = hs2.stage_timing_read()
+    flops = 2.0 * t_rows * d_model * 2 * n_l * 128
+    tflops = flops / (bridge_ms * 1e-3) / 1e12
+    return {
+        "metric": METRIC, "value": batch / decode_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": decode_s * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": WORKLOADS[5], "tokens": t_rows, "d_model": d_model, "bridged_layers": n_l,
+                   "decode_batch": batch, "context_per_sequence": t_rows // batch, "n_sparse_layers": 4},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "bridge_gemm_kernel (hs2_bridge_kv)", "alg_flops_per_launch": flops,
+                     "mean_launch_ms": bridge_ms},
+        "bridge_ms": bridge_ms,
+        "decode_stages_ms_per_layer": {k: round(v, 5) for k, v in stages.items()},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -107,6 +176,9 @@ def main():
     hs2.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == 5:
+        print(json.dumps(bench_bridge(args, torch, hs2, inputs, dev)), flush=True)
+        return
     d = inputs.make_decode(args.workload)
     kv = d["kv"]
     offs_t = torch.from_numpy(d["seq_offsets"]).to(dev)
