@@ -13,6 +13,8 @@
 // three exact bf16 parts (fp32-accurate logits), an online softmax per head in
 // registers, and O^T += V^T P^T on fp32 MFMA (fp32 probabilities).  The four
 // waves' (m, z, O) are merged through LDS into one partial per workgroup.
+#include <algorithm>
+
 #include "hs2_device.h"
 #include "hs2_internal.h"
 
@@ -20,15 +22,50 @@ namespace hs2 {
 
 // BOUND: instead of spilling the 16 logits of each token, keep per token
 // shat_j = sum_h exp2(l_hj - m_h^t) c_h^t with the wave's running max m^t after
-// the token's tile and c^t ~ 1 / (running sum z^t), and per tile (m^t, c^t).
-// Then score_j = sum_h a_hj F_h^t with F_h^t = exp2(m_h^t - M_h) / (c_h^t Z_h),
-// so score_j lies in shat_j * [min_h F_h^t, max_h F_h^t]; the selection prunes
-// with these bounds and rescores the survivors exactly.
+// the token's tile and c^t ~ 1 / (running sum z^t), and per tile and head
+// u_h^t = m_h^t - log2 c_h^t.  Then score_j = sum_h a_hj F_h^t with
+// F_h^t = exp2(m_h^t - M_h) / (c_h^t Z_h) = exp2(u_h^t - M_h) / Z_h, so score_j
+// lies in shat_j * [min_h F_h^t, max_h F_h^t]; the selection prunes with these
+// bounds and rescores the survivors exactly.
 // Bound-mode outputs of one wave's tiles wait in LDS until the loop ends: on
 // CDNA loads and stores share one in-order completion counter, so stores in
 // the streaming loop would put their write latency into every load wait.
 constexpr int kMaxWaveTiles = kMaxChunk / 64;
-constexpr int kTileOut = 3 * kHeads;  // shat[16], m[16], c[16]
+constexpr int kTileOut = 2 * kHeads;  // shat[16], u[16]
+
+// Work item wg of the 1-D grid: the non-empty (sequence, chunk) pairs of the
+// batch, numbered in order.  A 1-D grid of just these deals the workgroups
+// evenly over the XCDs; a 2-D grid over the longest sequence has holes, and
+// an XCD that is dealt more non-empty workgroups than it holds at once runs
+// a second round while the others idle.  Every lane of the wave computes the
+// same answer; false past the last item.
+__device__ bool find_work(const FullParams& p, int wg, int& b, int& c) {
+  const int lane = threadIdx.x & 63;
+  int carry = 0;  // items of the sequences before this pass
+  for (int s0 = 0; s0 < p.batch; s0 += 64) {
+    const int sb = s0 + lane;
+    int64_t sbase = 0;
+    int slen = 0;
+    if (sb < p.batch) seq_bounds(p.seq_offsets, sb, p.total_tokens, p.max_context, sbase, slen);
+    const int nb = (slen + p.chunk - 1) / p.chunk;
+    int incl = nb;  // inclusive prefix sum over the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    const int total = __shfl(incl, 63);
+    if (wg < carry + total) {
+      const uint64_t hit = __ballot(carry + incl > wg);
+      const int src = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+      b = s0 + src;
+      c = wg - carry - __shfl(incl - nb, src);
+      return true;
+    }
+    carry += total;
+  }
+  return false;
+}
 
 template <bool FP8, bool BOUND>
 __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
@@ -39,15 +76,15 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
   __shared__ u32x4 s_q[kQLdsVecs];
   float(*s_o)[kHeads][kDim] = reinterpret_cast<float(*)[kHeads][kDim]>(s_raw);
 
-  const int b = blockIdx.y;
-  const int c = blockIdx.x;
+  int b, c;
+  if (!find_work(p, blockIdx.x, b, c)) return;  // uniform over the workgroup
+  b = __builtin_amdgcn_readfirstlane(b);
+  c = __builtin_amdgcn_readfirstlane(c);
   int64_t base;
   int len;
   seq_bounds(p.seq_offsets, b, p.total_tokens, p.max_context, base, len);
-  const int c0 = c * p.chunk;
-  if (c0 >= len) return;  // uniform over the workgroup
 
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar loop control
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;
   const int g = lane >> 4;
@@ -106,7 +143,7 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
     }
   };
   auto step = [&](int t0, int ti, const Raw& cur) {
-    const int nv = min(16, len - t0);
+    const int nv = min(16, len - t0);  // <= 0: a masked tile past the end
     bf16x8 kf[4];
     if constexpr (FP8) {
       e4m3x16_to_bf16(cur.k[0], kf[0], kf[1]);
@@ -128,10 +165,11 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
       // lane n < 4 of row g holds token 4g + n; lanes of row 0 hold head n's (m, c)
       float* out = s_raw + (wave * kMaxWaveTiles + ti) * kTileOut;
       const float mine = n == 0 ? sh[0] : n == 1 ? sh[1] : n == 2 ? sh[2] : sh[3];
+      if (nv <= 0) return;  // the masked tile past the end has no slot
       if (n < 4) out[4 * g + n] = mine;
       if (g == 0) {
-        out[kHeads + n] = st.m;
-        out[2 * kHeads + n] = c;
+        // log2 error ~1e-7: far inside the selection's 2^-10 slack
+        out[kHeads + n] = st.m - __builtin_amdgcn_logf(c);
       }
     } else {
 #pragma unroll
@@ -146,39 +184,64 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
   // copying would wait for the in-flight loads at every copy.)  The scheduling
   // barriers pin each batch of loads ahead of the math of the tile before it;
   // left free, the scheduler sinks them past that math and the prefetch is lost.
+  // The loop leaves only at its bottom: an exit between the two halves gives
+  // the compiler a path on which the second slot's loads reach the loop top
+  // still in flight, and it then waits for them before the next loads are
+  // issued, every iteration.  So the second half always runs; when a wave has
+  // an odd number of tiles its last step sees a tile past the end, fully
+  // masked (zero weights, no outputs).
   Raw ra, rb;
-  int t0 = w0;
-  int ti = 0;  // ordinal of the tile within this wave
+  int t0 = w0;  // < len: the workgroup has a token, and so has each wave's first tile
+  int ti = 0;   // ordinal of the tile within this wave
   load_tile(t0, ra);  // in flight while the query operand is built
   build_q_lds<FP8>(p.q + static_cast<size_t>(b) * kHeads * kDim, p.qscale, s_q);
   __syncthreads();
-  while (t0 < len) {
-    load_tile(t0 + tile_stride, rb);
-    __builtin_amdgcn_sched_barrier(0);
-    step(t0, ti++, ra);
-    __builtin_amdgcn_sched_barrier(0);
-    t0 += tile_stride;
-    if (t0 >= len) break;
-    load_tile(t0 + tile_stride, ra);
-    __builtin_amdgcn_sched_barrier(0);
-    step(t0, ti++, rb);
-    __builtin_amdgcn_sched_barrier(0);
-    t0 += tile_stride;
+  if (t0 < len) {
+    for (;;) {
+      load_tile(t0 + tile_stride, rb);
+      __builtin_amdgcn_sched_barrier(0);
+      step(t0, ti++, ra);
+      __builtin_amdgcn_sched_barrier(0);
+      load_tile(t0 + 2 * tile_stride, ra);
+      __builtin_amdgcn_sched_barrier(0);
+      step(t0 + tile_stride, ti++, rb);
+      __builtin_amdgcn_sched_barrier(0);
+      t0 += 2 * tile_stride;
+      if (t0 >= len) break;
+    }
   }
 
   if constexpr (BOUND) {
     // Write this wave's tile outputs: shat of the tokens that exist, and the
-    // per-tile (m, c) of every tile.
+    // per-tile u of every tile.
+    // 16-byte stores, all issued before any completes: the flush is on the
+    // critical path of the workgroup's end.
     const int ntiles = w0 < len ? (len - 1 - w0) / tile_stride + 1 : 0;
-    for (int i = lane; i < ntiles * 16; i += 64) {
-      const int ti = i >> 4, e = i & 15;
-      const int tok = w0 + ti * tile_stride + e;
-      if (tok < len) shat[static_cast<uint32_t>(tok)] = s_raw[(wave * kMaxWaveTiles + ti) * kTileOut + e];
+    const float* wraw = s_raw + wave * kMaxWaveTiles * kTileOut;
+#pragma unroll
+    for (int it = 0; it < kMaxWaveTiles * 4 / 64; ++it) {
+      const int i = lane + 64 * it;  // float4 i: tile i / 4, tokens 4 (i % 4) ..
+      const int ti = i >> 2, e = 4 * (i & 3);
+      if (ti < ntiles) {
+        const float4 v = *reinterpret_cast<const float4*>(wraw + ti * kTileOut + e);
+        const int tok = w0 + ti * tile_stride + e;
+        if (tok + 3 < len && (base & 3) == 0) {  // 16-byte aligned: tok is a multiple of 4
+          *reinterpret_cast<float4*>(shat + tok) = v;
+        } else {
+          const float vv[4] = {v.x, v.y, v.z, v.w};
+          for (int u = 0; u < 4 && tok + u < len; ++u) shat[tok + u] = vv[u];
+        }
+      }
     }
-    for (int i = lane; i < ntiles * 2 * kHeads; i += 64) {
-      const int ti = i >> 5, e = i & 31;
-      const int tile = (w0 + ti * tile_stride) >> 4;
-      p.tile_stats[tile_slot(base, b, tile) * (2 * kHeads) + e] = s_raw[(wave * kMaxWaveTiles + ti) * kTileOut + kHeads + e];
+#pragma unroll
+    for (int it = 0; it < kMaxWaveTiles * 4 / 64; ++it) {
+      const int i = lane + 64 * it;  // float4 i: tile i / 4, heads 4 (i % 4) ..
+      const int ti = i >> 2, e = 4 * (i & 3);
+      if (ti < ntiles) {
+        const int tile = (w0 + ti * tile_stride) >> 4;
+        *reinterpret_cast<float4*>(p.tile_stats + tile_slot(base, b, tile) * kHeads + e) =
+            *reinterpret_cast<const float4*>(wraw + ti * kTileOut + kHeads + e);
+      }
     }
     __syncthreads();  // the merge below reuses this LDS
   }
@@ -224,7 +287,10 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
 
 hipError_t launch_full_partial(const FullParams& p, int batch, bool fp8, bool bound_mode, hipStream_t s) {
   if (batch == 0) return hipSuccess;
-  const dim3 grid(p.chunks_per_seq, batch);
+  // at most sum_b ceil(L_b / chunk) < N / chunk + B work items
+  const int64_t items = std::min<int64_t>(static_cast<int64_t>(batch) * p.chunks_per_seq,
+                                          (p.total_tokens + p.chunk - 1) / p.chunk + batch);
+  const dim3 grid(static_cast<unsigned>(items));
   if (fp8 && bound_mode)
     hipLaunchKernelGGL((full_partial_kernel<true, true>), grid, dim3(256), 0, s, p);
   else if (fp8)

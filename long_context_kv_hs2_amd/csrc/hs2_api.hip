@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -37,14 +38,20 @@ constexpr int64_t kMaxContext = int64_t(1) << 24;
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// Tokens per full-attention workgroup: about 1024 workgroups (two rounds on
-// 256 CUs at two workgroups each), so the per-workgroup start-up latency and
-// partial write are paid few times, with at most 4096 tokens each.
-int choose_chunk(int64_t total_tokens) {
-  int64_t c = total_tokens / 1024;
-  int64_t p2 = 256;
-  while (p2 * 2 <= c && p2 < kMaxChunk) p2 *= 2;
-  return static_cast<int>(p2);
+// Tokens per full-attention workgroup.  The pass runs best as one round of
+// workgroups, two per CU of a 256-CU part: a workgroup's end (writing its
+// per-tile outputs, merging its waves) overlaps no streaming, so it should
+// happen once, and a partly filled second round would leave CUs idle.  A
+// batch takes sum_b ceil(L_b / chunk) < N / chunk + B workgroups, so
+// chunk >= N / (512 - B) keeps them within 512.  Chunks are multiples of 64
+// tokens (four waves of 16-token tiles) in [256, kMaxChunk].  The choice
+// affects speed only, never results.
+int choose_chunk(int64_t total_tokens, int batch) {
+  constexpr int64_t kSlots = 512;
+  const int64_t denom = std::max<int64_t>(kSlots - batch, kSlots / 4);
+  int64_t c = (total_tokens + denom - 1) / denom;
+  c = (c + 63) / 64 * 64;
+  return static_cast<int>(std::min<int64_t>(std::max<int64_t>(c, 256), kMaxChunk));
 }
 
 struct DecodeLayout {
@@ -59,7 +66,7 @@ DecodeLayout decode_layout(const hs2_decode_desc& d) {
   DecodeLayout L;
   const size_t B = static_cast<size_t>(d.batch);
   const size_t N = static_cast<size_t>(d.total_tokens);
-  L.chunk = choose_chunk(d.total_tokens);
+  L.chunk = choose_chunk(d.total_tokens, d.batch);
   L.chunks_per_seq = static_cast<int>((d.max_context + L.chunk - 1) / L.chunk);
   if (L.chunks_per_seq < 1) L.chunks_per_seq = 1;
   L.splits = (kBudget + kSparseRows - 1) / kSparseRows;
@@ -78,7 +85,7 @@ DecodeLayout decode_layout(const hs2_decode_desc& d) {
   L.selbuf = take(B * kTopK * sizeof(int32_t));
   L.cand = take(B * kCandCap * sizeof(unsigned long long));
   L.shat = take(N * sizeof(float));
-  L.tile_stats = take(((N >> 4) + B + 1) * 2 * kHeads * sizeof(float));
+  L.tile_stats = take(((N >> 4) + B + 1) * kHeads * sizeof(float));
   L.cand_idx = take(B * kCandCap * sizeof(int32_t));
   L.sparse = take(B * static_cast<size_t>(d.n_sparse_layers > 0 ? d.n_sparse_layers : 1) * L.splits *
                   kPartialFloats * sizeof(float));
@@ -213,6 +220,7 @@ FullParams full_params(const DecodeArgs& a, const DecodeLayout& L) {
   p.v_scale = a.vs;
   p.q = a.q_full;
   p.qscale = static_cast<float>(static_cast<double>(a.d->softmax_scale) * kLog2e);
+  p.batch = a.d->batch;
   p.chunk = L.chunk;
   p.chunks_per_seq = L.chunks_per_seq;
   p.partials = reinterpret_cast<float*>(ws_at(a.ws, L.partials));

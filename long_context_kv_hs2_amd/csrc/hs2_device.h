@@ -53,7 +53,24 @@ __device__ __forceinline__ f32x4 mfma_f32_16x16x4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// D[16x16] += A[16x16] B[16x16], bf16 inputs, fp32 accumulate.  Lane l holds
+// row (l % 16) of A and column (l % 16) of B, each with the 4 values of the
+// reduction index 4*(l/16) .. 4*(l/16)+3; D as above.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
+                                                  0, 0, 0);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Byte permute of the pair {hi_word, lo_word}: selector byte i picks byte
+// sel_i of the 8-byte value lo_word | hi_word << 32.
+__device__ __forceinline__ uint32_t perm(uint32_t hi_word, uint32_t lo_word, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi_word, lo_word, sel);
+}
+constexpr uint32_t kLoHalves = 0x05040100u;  // (lo_word.lo16, hi_word.lo16)
+constexpr uint32_t kHiHalves = 0x07060302u;  // (lo_word.hi16, hi_word.hi16)
 
 // Split an fp32 value into three bfloat16 parts whose exact sum is the value:
 // each part keeps the top 8 significant bits of what the previous parts left,
@@ -149,7 +166,7 @@ __device__ __forceinline__ int kload_offset(int j, int g) { return 64 * j + 16 *
 template <bool HIGH_PAIR>
 __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
   const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HIGH_PAIR);
-  return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
+  return perm(__float_as_uint(f[1]), __float_as_uint(f[0]), kHiHalves);
 }
 
 // 16 E4M3 codes -> 16 bf16 (two bf16x8 operands).
@@ -165,31 +182,6 @@ __device__ __forceinline__ void e4m3x16_to_bf16(u32x4 w, bf16x8& lo, bf16x8& hi)
   b[3] = e4m3x2_to_bf16x2<true>(w[3]);
   lo = as_bf16x8(a);
   hi = as_bf16x8(b);
-}
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// 8 bf16 values (one 16-byte load) -> 8 fp32.
-__device__ __forceinline__ void bf16x8_to_f32(u32x4 w, float* out) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    out[2 * i] = bf16_lo(w[i]);
-    out[2 * i + 1] = bf16_hi(w[i]);
-  }
-}
-
-// 8 E4M3 codes (one 8-byte load) -> 8 fp32.
-__device__ __forceinline__ void e4m3x8_to_f32(u32x2 w, float* out) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
-    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
-    out[4 * i] = a[0];
-    out[4 * i + 1] = a[1];
-    out[4 * i + 2] = b[0];
-    out[4 * i + 3] = b[1];
-  }
 }
 
 // Online-softmax state of one wave for 16 heads: lane (n, g) keeps head n's
@@ -209,11 +201,66 @@ __device__ __forceinline__ void softmax_init(SoftmaxState& st) {
   for (int t = 0; t < 8; ++t) st.o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
+// O^T += V^T P^T for one tile of 16 tokens on bf16 MFMA (16x16x16).
+// Reduction index = the tile's tokens.  MFMA j serves dims 8m + j (A row m),
+// so lane (m, g) needs V[4g + r][8m + j] for r = 0..3: its own four V loads,
+// regrouped by byte permutes (no data crosses lanes).  The B operand is the
+// lane's own four probabilities.  P (times the per-token V scale) is split
+// into a bf16 head and a bf16 tail, so the product keeps 16 significant bits
+// of each weight (V itself is exact in bf16); MFMA j leaves
+// O[head n][dim 32g + 8i + j] in element i of st.o[j] on lane (n, g).
+template <bool FP8>
+__device__ __forceinline__ void pv_tile(const u32x4 (&vraw)[4], const float (&p)[4], const float (&vscale)[4],
+                                        SoftmaxState& st) {
+  float w[4], tail[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    w[r] = FP8 ? p[r] * vscale[r] : p[r];
+    tail[r] = w[r] - __uint_as_float(__float_as_uint(w[r]) & 0xFFFF0000u);  // exact
+  }
+  const u32x2 ph = {perm(__float_as_uint(w[1]), __float_as_uint(w[0]), kHiHalves),
+                    perm(__float_as_uint(w[3]), __float_as_uint(w[2]), kHiHalves)};
+  const u32x2 pl = {perm(__float_as_uint(tail[1]), __float_as_uint(tail[0]), kHiHalves),
+                    perm(__float_as_uint(tail[3]), __float_as_uint(tail[2]), kHiHalves)};
+  u32x2 a[8];
+  if constexpr (FP8) {
+    // codes of dims 4h .. 4h + 3 sit in word h of each token's load
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        const uint32_t t0 = vraw[2 * pr][h], t1 = vraw[2 * pr + 1][h];
+        // interleave the two tokens' codes: (t0.d, t1.d, t0.d+1, t1.d+1)
+        const uint32_t x01 = perm(t1, t0, 0x05010400u);
+        const uint32_t x23 = perm(t1, t0, 0x07030602u);
+        a[4 * h + 0][pr] = e4m3x2_to_bf16x2<false>(x01);
+        a[4 * h + 1][pr] = e4m3x2_to_bf16x2<true>(x01);
+        a[4 * h + 2][pr] = e4m3x2_to_bf16x2<false>(x23);
+        a[4 * h + 3][pr] = e4m3x2_to_bf16x2<true>(x23);
+      }
+    }
+  } else {
+    // word i of a token's load holds dims 2i (low half) and 2i + 1 (high half)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        const uint32_t t0 = vraw[2 * pr][i], t1 = vraw[2 * pr + 1][i];
+        a[2 * i][pr] = perm(t1, t0, kLoHalves);
+        a[2 * i + 1][pr] = perm(t1, t0, kHiHalves);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) st.o[j] = mfma_bf16_16x16x16(a[j], ph, st.o[j]);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) st.o[j] = mfma_bf16_16x16x16(a[j], pl, st.o[j]);
+}
+
 // One tile of 16 context tokens for 16 heads.
 //  kf[s]: K operand, lane (n, g): token n, dims kdim0(s, g) + i (bf16)
 //  vraw[r]: V values of token 4g + r, dims 8n .. 8n + 7, lane (n, g): eight
-//           bf16 (16 bytes) or eight E4M3 codes (first 8 bytes); converted to
-//           fp32 just before their MFMAs
+//           bf16 (16 bytes) or eight E4M3 codes (first 8 bytes)
 //  kscale[r], vscale[r]: per-token scales of token 4g + r (1 for bf16)
 //  nvalid: tokens of the tile that exist (1..16); others are masked out
 // Returns the log2-domain logits of tokens 4g + r for head n in lg[r]
@@ -252,17 +299,7 @@ __device__ __forceinline__ void attend_tile(const QSrc& q, const bf16x8 (&kf)[4]
 #pragma unroll
   for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(lg[r] - st.m);
   st.z += (p[0] + p[1]) + (p[2] + p[3]);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float pv = p[r] * vscale[r];
-    float vf[8];
-    if constexpr (FP8)
-      e4m3x8_to_f32(u32x2{vraw[r][0], vraw[r][1]}, vf);
-    else
-      bf16x8_to_f32(vraw[r], vf);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) st.o[t] = mfma_f32_16x16x4(vf[t], pv, st.o[t]);
-  }
+  pv_tile<FP8>(vraw, p, vscale, st);
 }
 
 // Sum over the 16 lanes of a row (the 16 heads of one lane group); every

@@ -8,7 +8,7 @@
 namespace hs2 {
 
 // ---- full-attention layer: split-K partial pass and merge -------------------
-constexpr int kMaxChunk = 4096;  // most tokens one full-attention workgroup takes
+constexpr int kMaxChunk = 8192;  // most tokens one full-attention workgroup takes
 struct FullParams {
   const int64_t* seq_offsets;
   int64_t total_tokens;
@@ -19,12 +19,13 @@ struct FullParams {
   const float* v_scale;
   const float* q;            // [B][16][128]
   float qscale;              // softmax_scale * log2(e)
+  int batch;
   int chunk;                 // tokens per workgroup, multiple of 64
   int chunks_per_seq;
   float* partials;           // [B][chunks_per_seq][kPartialFloats]
   float* spill;              // spill mode: [N][16] log2-domain logits
   float* shat;               // bound mode: [N] per-token sum over heads of the running-normalised weights
-  float* tile_stats;         // bound mode: [tile_slots][32] per head after each tile: running max, ~1/running sum
+  float* tile_stats;         // bound mode: [tile_slots][16] per head after each tile: running max - log2(~1/running sum)
 };
 // Slot of tile t (tokens [16t, 16t + 16)) of the sequence starting at row `base`:
 // unique over all sequences, at most N/16 + B.
@@ -62,7 +63,7 @@ struct SelectParams {
   const float* spill;         // [N][16] (spill mode)
   const float* stats;         // [B][16][2] global (max, sum) per head
   const float* shat;          // [N] (bound mode)
-  const float* tile_stats;    // [tile_slots][32] (bound mode)
+  const float* tile_stats;    // [tile_slots][16] (bound mode)
   float* score;               // [N]
   uint32_t* hist0;            // [B][kRadixBins]: first-digit histogram
   uint32_t* counters;         // [B][4]: winners emitted, candidates seen

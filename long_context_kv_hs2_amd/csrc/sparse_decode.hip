@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void sparse_partial_kernel(SparseParams p) {
   }
   __syncthreads();
 
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar loop control
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;
   const int g = lane >> 4;

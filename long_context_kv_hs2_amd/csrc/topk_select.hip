@@ -404,14 +404,14 @@ hipError_t launch_collect_finish(const SelectParams& p, int batch, int64_t max_c
 
 // ---- bound mode ------------------------------------------------------------
 
-// Per-tile bound factors F_h = exp2(m_h^t - M_h) / (c_h^t Z_h): their min and max.
+// Per-tile bound factors F_h = exp2(u_h^t - M_h) / Z_h: their min and max.
 __device__ __forceinline__ void tile_factors(const float* __restrict__ ts, const float (&mx)[kHeads],
                                              const float (&iz)[kHeads], float& fmin, float& fmax) {
   fmin = INFINITY;
   fmax = 0.f;
 #pragma unroll
   for (int h = 0; h < kHeads; ++h) {
-    const float f = exp2f(ts[h] - mx[h]) * iz[h] / ts[kHeads + h];
+    const float f = exp2f(ts[h] - mx[h]) * iz[h];
     fmin = fminf(fmin, f);
     fmax = fmaxf(fmax, f);
   }
@@ -449,7 +449,7 @@ __global__ __launch_bounds__(256) void bound_hist_kernel(SelectParams p) {
   const int tile = (j0 >> 4) + threadIdx.x;
   if (16 * tile < dom) {
     float fmin, fmax;
-    tile_factors(p.tile_stats + tile_slot(base, b, tile) * (2 * kHeads), mx, iz, fmin, fmax);
+    tile_factors(p.tile_stats + tile_slot(base, b, tile) * kHeads, mx, iz, fmin, fmax);
     const float4* sh = reinterpret_cast<const float4*>(p.shat + base + 16 * tile);
     const int nv = min(16, dom - 16 * tile);
     // shat rows are 64-byte aligned only when base is a multiple of 16: load scalars otherwise
@@ -505,7 +505,7 @@ __global__ __launch_bounds__(256) void collect_bound_kernel(SelectParams p) {
   const int tile = (j0 >> 4) + threadIdx.x;
   if (16 * tile < dom) {
     float fmin, fmax;
-    tile_factors(p.tile_stats + tile_slot(base, b, tile) * (2 * kHeads), mx, iz, fmin, fmax);
+    tile_factors(p.tile_stats + tile_slot(base, b, tile) * kHeads, mx, iz, fmin, fmax);
     const int nv = min(16, dom - 16 * tile);
     for (int i = 0; i < nv; ++i) {
       const int j = 16 * tile + i;
@@ -549,7 +549,7 @@ __global__ __launch_bounds__(256) void refine_kernel(SelectParams p) {
     s_iz[threadIdx.x] = 1.f / p.stats[(static_cast<int64_t>(b) * kHeads + threadIdx.x) * 2 + 1];
   }
   __syncthreads();
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar loop control
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;
   const int g = lane >> 4;
