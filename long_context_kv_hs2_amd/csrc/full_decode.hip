@@ -11,8 +11,11 @@
 // straight from HBM into registers (16-byte loads), so every K/V byte is read
 // exactly once.  Per tile: S^T = K Q^T on bf16 MFMA with the query split into
 // three exact bf16 parts (fp32-accurate logits), an online softmax per head in
-// registers, and O^T += V^T P^T on fp32 MFMA (fp32 probabilities).  The four
-// waves' (m, z, O) are merged through LDS into one partial per workgroup.
+// registers, and O^T += V^T P^T on bf16 MFMA with each weight split into a
+// bf16 head and tail (16 significant bits).  The four waves' (m, z, O) are
+// merged through LDS into one partial per workgroup.  The first workgroup of
+// each sequence also clears the sequence's selection histogram and counters
+// for the kernels that follow.
 #include <algorithm>
 
 #include "hs2_device.h"
@@ -95,6 +98,8 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
   const int nblk = (len + p.chunk - 1) / p.chunk;
   const int tile_stride = 16 * 4 * nblk;
   const int w0 = 16 * (4 * c + wave);
+  const int nt = w0 < len ? (len - 1 - w0) / tile_stride + 1 : 0;  // this wave's tiles
+  auto tok0 = [&](int k) { return k < nt ? w0 + k * tile_stride : len; };  // len: past the end
 
   const QShared q{s_q, lane};  // filled below, after the first tile's loads are issued
 
@@ -142,7 +147,11 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
       }
     }
   };
-  auto step = [&](int t0, int ti, const Raw& cur) {
+  // Bound mode: c_h ~ 1 / (head h's running sum), refreshed every other tile,
+  // and its log2.  Any c_h > 0 gives valid bounds as long as the stored u
+  // uses the same c_h: the bounds divide by exactly what shat multiplied by.
+  float cfac = 1.f, lcf = 0.f;
+  auto step = [&](int t0, int ti, bool refresh, const Raw& cur) {
     const int nv = min(16, len - t0);  // <= 0: a masked tile past the end
     bf16x8 kf[4];
     if constexpr (FP8) {
@@ -155,22 +164,20 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
     float lg[4], pr[4];
     attend_tile<FP8>(q, kf, cur.v, cur.ks, cur.vs, nv, g, st, lg, pr);
     if constexpr (BOUND) {
-      // a_hj = p_hj * c_h with c_h the reciprocal of head h's running sum;
-      // the stored c_h (not 1/z) is what the bounds divide by, so the
-      // approximate reciprocal costs no validity.
-      const float c = __builtin_amdgcn_rcpf(reduce_z(st.z));
-      float sh[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sh[r] = row_sum16(pr[r] * c);
-      // lane n < 4 of row g holds token 4g + n; lanes of row 0 hold head n's (m, c)
-      float* out = s_raw + (wave * kMaxWaveTiles + ti) * kTileOut;
-      const float mine = n == 0 ? sh[0] : n == 1 ? sh[1] : n == 2 ? sh[2] : sh[3];
-      if (nv <= 0) return;  // the masked tile past the end has no slot
-      if (n < 4) out[4 * g + n] = mine;
-      if (g == 0) {
-        // log2 error ~1e-7: far inside the selection's 2^-10 slack
-        out[kHeads + n] = st.m - __builtin_amdgcn_logf(c);
+      if (refresh) {
+        cfac = __builtin_amdgcn_rcpf(reduce_z(st.z));
+        lcf = __builtin_amdgcn_logf(cfac);  // error ~1e-7: far inside the selection's 2^-10 slack
       }
+      // a_hj = p_hj * c_h summed over the heads: lane n of row g ends with
+      // token 4g + (n >> 2)
+      float x[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = pr[r] * cfac;
+      const float sh = row_sums4(x, n);
+      if (nv <= 0) return;  // the masked tile past the end has no slot
+      float* out = s_raw + (wave * kMaxWaveTiles + ti) * kTileOut;
+      if ((n & 3) == 0) out[4 * g + (n >> 2)] = sh;
+      if (g == 0) out[kHeads + n] = st.m - lcf;  // u_h = m_h - log2 c_h
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -191,23 +198,20 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
   // an odd number of tiles its last step sees a tile past the end, fully
   // masked (zero weights, no outputs).
   Raw ra, rb;
-  int t0 = w0;  // < len: the workgroup has a token, and so has each wave's first tile
-  int ti = 0;   // ordinal of the tile within this wave
-  load_tile(t0, ra);  // in flight while the query operand is built
+  load_tile(tok0(0), ra);  // in flight while the query operand is built
   build_q_lds<FP8>(p.q + static_cast<size_t>(b) * kHeads * kDim, p.qscale, s_q);
   __syncthreads();
-  if (t0 < len) {
-    for (;;) {
-      load_tile(t0 + tile_stride, rb);
+  if (nt > 0) {
+    for (int k = 0;; k += 2) {
+      load_tile(tok0(k + 1), rb);
       __builtin_amdgcn_sched_barrier(0);
-      step(t0, ti++, ra);
+      step(tok0(k), k, true, ra);
       __builtin_amdgcn_sched_barrier(0);
-      load_tile(t0 + 2 * tile_stride, ra);
+      load_tile(tok0(k + 2), ra);
       __builtin_amdgcn_sched_barrier(0);
-      step(t0 + tile_stride, ti++, rb);
+      step(tok0(k + 1), k + 1, false, rb);
       __builtin_amdgcn_sched_barrier(0);
-      t0 += 2 * tile_stride;
-      if (t0 >= len) break;
+      if (k + 2 >= nt) break;
     }
   }
 
@@ -216,7 +220,7 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
     // per-tile u of every tile.
     // 16-byte stores, all issued before any completes: the flush is on the
     // critical path of the workgroup's end.
-    const int ntiles = w0 < len ? (len - 1 - w0) / tile_stride + 1 : 0;
+    const int ntiles = nt;
     const float* wraw = s_raw + wave * kMaxWaveTiles * kTileOut;
 #pragma unroll
     for (int it = 0; it < kMaxWaveTiles * 4 / 64; ++it) {
@@ -283,6 +287,11 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
   float4* o4 = reinterpret_cast<float4*>(out + 2 * kHeads + h * kDim + d0);
   o4[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
   o4[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  if (c == 0) {
+    uint4* hz = reinterpret_cast<uint4*>(p.hist0 + static_cast<size_t>(b) * kRadixBins);
+    for (int i = threadIdx.x; i < kRadixBins / 4; i += 256) hz[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (threadIdx.x < 4) p.counters[b * 4 + threadIdx.x] = 0u;
+  }
 }
 
 hipError_t launch_full_partial(const FullParams& p, int batch, bool fp8, bool bound_mode, hipStream_t s) {
@@ -299,83 +308,6 @@ hipError_t launch_full_partial(const FullParams& p, int batch, bool fp8, bool bo
     hipLaunchKernelGGL((full_partial_kernel<false, true>), grid, dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL((full_partial_kernel<false, false>), grid, dim3(256), 0, s, p);
-  return hipGetLastError();
-}
-
-// Merge split-K partials: per (head, sequence, layer) one workgroup of 128
-// threads (one per output dim).  The max and the sum of the partials are
-// block reductions over a fixed tree; the output accumulates the partials in
-// index order, 128 at a time with their weights staged in LDS, so every
-// reduction order is fixed and loads of successive partials overlap.
-__device__ __forceinline__ float block_reduce_128(float v, float* s_red, bool is_max) {
-  const int d = threadIdx.x;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const float o = __shfl_xor(v, off);
-    v = is_max ? fmaxf(v, o) : v + o;
-  }
-  if ((d & 63) == 0) s_red[d >> 6] = v;
-  __syncthreads();
-  const float r = is_max ? fmaxf(s_red[0], s_red[1]) : s_red[0] + s_red[1];
-  __syncthreads();
-  return r;
-}
-
-__global__ __launch_bounds__(128) void merge_kernel(MergeParams p, int64_t stride_layer, int64_t out_stride_layer) {
-  __shared__ float s_red[2];
-  __shared__ float s_f[128];
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
-  const int layer = blockIdx.z;
-  const int d = threadIdx.x;
-  int64_t base;
-  int len;
-  seq_bounds(p.seq_offsets, b, p.total_tokens, p.max_context, base, len);
-  const int items = p.count_from_sel ? clamp_count(p.sel_count[b], len, p.budget) : len;
-  const int count = (items + p.chunk - 1) / p.chunk;
-  const float* pb = p.partials + layer * stride_layer + static_cast<int64_t>(b) * p.stride_seq;
-  float mx = -INFINITY;
-  for (int c = d; c < count; c += 128) mx = fmaxf(mx, pb[static_cast<int64_t>(c) * p.stride_chunk + h]);
-  mx = block_reduce_128(mx, s_red, true);
-  float zpart = 0.f;
-  float acc = 0.f;
-  for (int c0 = 0; c0 < count; c0 += 128) {
-    const int c = c0 + d;
-    float f = 0.f;
-    if (c < count) {
-      const float* pc = pb + static_cast<int64_t>(c) * p.stride_chunk;
-      const float m = pc[h];
-      f = m == -INFINITY ? 0.f : exp2f(m - mx);
-      zpart += pc[kHeads + h] * f;
-    }
-    s_f[d] = f;
-    __syncthreads();
-    const int nc = min(128, count - c0);
-    const float* po = pb + static_cast<int64_t>(c0) * p.stride_chunk + 2 * kHeads + h * kDim + d;
-#pragma unroll 8
-    for (int j = 0; j < nc; ++j) acc += po[static_cast<int64_t>(j) * p.stride_chunk] * s_f[j];
-    __syncthreads();
-  }
-  const float z = block_reduce_128(zpart, s_red, false);
-  float* out = p.out + layer * out_stride_layer + b * p.out_stride_seq + h * kDim;
-  out[d] = count ? acc / z : 0.f;
-  if (p.stats && layer == 0 && d == 0) {
-    p.stats[(static_cast<int64_t>(b) * kHeads + h) * 2] = mx;
-    p.stats[(static_cast<int64_t>(b) * kHeads + h) * 2 + 1] = z;
-  }
-}
-
-hipError_t launch_merge(const MergeParams& p, int batch, hipStream_t s) {
-  if (batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(merge_kernel, dim3(kHeads, batch, 1), dim3(kDim), 0, s, p, int64_t(0), int64_t(0));
-  return hipGetLastError();
-}
-
-hipError_t launch_merge_layers(const MergeParams& p, int batch, int layers, int64_t stride_layer,
-                               int64_t out_stride_layer, hipStream_t s) {
-  if (batch == 0 || layers == 0) return hipSuccess;
-  hipLaunchKernelGGL(merge_kernel, dim3(kHeads, batch, layers), dim3(kDim), 0, s, p, stride_layer,
-                     out_stride_layer);
   return hipGetLastError();
 }
 

@@ -83,10 +83,12 @@ DecodeLayout decode_layout(const hs2_decode_desc& d) {
   L.hist0 = take(B * kRadixBins * sizeof(uint32_t));
   L.counters = take(B * 4 * sizeof(uint32_t));
   L.selbuf = take(B * kTopK * sizeof(int32_t));
-  L.cand = take(B * kCandCap * sizeof(unsigned long long));
+  // spill mode: [B][kCandCap] keys of the threshold bin; bound mode: one slot
+  // per position (every candidate's exact key, sequence b's from row base_b)
+  L.cand = take(std::max(B * kCandCap, N) * sizeof(unsigned long long));
+  L.cand_idx = take(N * sizeof(int32_t));
   L.shat = take(N * sizeof(float));
   L.tile_stats = take(((N >> 4) + B + 1) * kHeads * sizeof(float));
-  L.cand_idx = take(B * kCandCap * sizeof(int32_t));
   L.sparse = take(B * static_cast<size_t>(d.n_sparse_layers > 0 ? d.n_sparse_layers : 1) * L.splits *
                   kPartialFloats * sizeof(float));
   L.total = off;
@@ -227,6 +229,8 @@ FullParams full_params(const DecodeArgs& a, const DecodeLayout& L) {
   p.spill = reinterpret_cast<float*>(ws_at(a.ws, L.spill));
   p.shat = reinterpret_cast<float*>(ws_at(a.ws, L.shat));
   p.tile_stats = reinterpret_cast<float*>(ws_at(a.ws, L.tile_stats));
+  p.hist0 = reinterpret_cast<uint32_t*>(ws_at(a.ws, L.hist0));
+  p.counters = reinterpret_cast<uint32_t*>(ws_at(a.ws, L.counters));
   return p;
 }
 
@@ -257,7 +261,10 @@ SelectParams select_params(const DecodeArgs& a, const DecodeLayout& L, float* sc
   return p;
 }
 
-hs2_status run_full(const DecodeArgs& a, const DecodeLayout& L, bool bound_mode, TimingRecord* rec) {
+// Full-attention pass and merge.  With `bound_sel` (bound mode) the merge
+// launch also runs the selection's first pass.
+hs2_status run_full(const DecodeArgs& a, const DecodeLayout& L, const SelectParams* bound_sel, TimingRecord* rec) {
+  const bool bound_mode = bound_sel != nullptr;
   const hs2_decode_desc& d = *a.d;
   const FullParams fp = full_params(a, L);
   HS2_HIP(launch_full_partial(fp, d.batch, d.kv_dtype == HS2_KV_FP8_E4M3, bound_mode, a.stream),
@@ -278,7 +285,11 @@ hs2_status run_full(const DecodeArgs& a, const DecodeLayout& L, bool bound_mode,
   mp.out = a.o_full;
   mp.out_stride_seq = kHeads * kDim;
   mp.stats = reinterpret_cast<float*>(ws_at(a.ws, L.stats));
-  HS2_HIP(launch_merge(mp, d.batch, a.stream), "full-attention merge");
+  if (bound_mode) {
+    HS2_HIP(launch_merge_bound_hist(mp, *bound_sel, d.batch, d.max_context, a.stream), "merge and bound histogram");
+  } else {
+    HS2_HIP(launch_merge(mp, d.batch, a.stream), "full-attention merge");
+  }
   HS2_TRY(mark(rec, 2, a.stream));
   return HS2_OK;
 }
@@ -367,9 +378,10 @@ hs2_status hs2_decode_block(const hs2_decode_desc* desc, const int64_t* seq_offs
   const bool bound_mode = score_out == nullptr;
   float* score = score_out ? score_out : reinterpret_cast<float*>(ws_at(workspace, L.score));
   const SelectParams sp = select_params(a, L, score);
-  HS2_HIP(launch_select_init(sp, d.batch, a.stream), "selection init");
+  // (bound mode: the full pass itself clears the selection's histogram and counters)
+  if (!bound_mode) HS2_HIP(launch_select_init(sp, d.batch, a.stream), "selection init");
   HS2_TRY(mark(rec, 0, a.stream));
-  HS2_TRY(run_full(a, L, bound_mode, rec));
+  HS2_TRY(run_full(a, L, bound_mode ? &sp : nullptr, rec));
   if (bound_mode) {
     HS2_HIP(launch_bound_select(sp, d.batch, d.max_context, d.kv_dtype == HS2_KV_FP8_E4M3, a.stream), "selection");
   } else {
@@ -398,7 +410,7 @@ hs2_status hs2_full_decode_score(const hs2_decode_desc* desc, const int64_t* seq
   if (!any) return HS2_OK;
   DecodeArgs a{desc, seq_offsets, k_cache, v_cache, k_scale, v_scale, q_full, nullptr, o_full, nullptr,
                nullptr, nullptr, score_out, workspace, static_cast<hipStream_t>(stream)};
-  HS2_TRY(run_full(a, L, false, nullptr));
+  HS2_TRY(run_full(a, L, nullptr, nullptr));
   const SelectParams sp = select_params(a, L, score_out);
   HS2_HIP(launch_score_hist(sp, d.batch, d.max_context, true, false, a.stream), "score pass");
   return HS2_OK;

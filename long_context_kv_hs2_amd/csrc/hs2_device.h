@@ -302,21 +302,26 @@ __device__ __forceinline__ void attend_tile(const QSrc& q, const bf16x8 (&kf)[4]
   pv_tile<FP8>(vraw, p, vscale, st);
 }
 
-// Sum over the 16 lanes of a row (the 16 heads of one lane group); every
-// lane of the row gets the total.
-// DPP lane moves within a row of 16 (plain VALU, no LDS crossbar): swap
-// neighbours, swap pairs, reverse each half-row, reverse the row.  After the
-// first two adds every lane of a quad holds the quad's sum; mirroring the
-// half-row pairs quad 0 with quad 1, mirroring the row pairs the two halves.
+// DPP lane moves within a row of 16 lanes (plain VALU, no LDS crossbar).
 template <int CTRL>
 __device__ __forceinline__ float dpp_move(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float row_sum16(float v) {
-  v += dpp_move<0xB1>(v);   // quad_perm [1, 0, 3, 2]
-  v += dpp_move<0x4E>(v);   // quad_perm [2, 3, 0, 1]
-  v += dpp_move<0x141>(v);  // row_half_mirror
-  v += dpp_move<0x140>(v);  // row_mirror
+// Four sums over the 16 lanes of a row at once (reduce-scatter): lane n ends
+// with the row's total of x[n >> 2].  Mirroring the row pairs lane n with a
+// lane of the other half: each keeps two of the four values and sends the
+// other two.  Mirroring the half-row pairs the two quads of a half: each keeps
+// one.  Two swaps inside the quad finish the sum.
+__device__ __forceinline__ float row_sums4(const float (&x)[4], int n) {
+  const bool hi8 = (n & 8) != 0;
+  float k0 = hi8 ? x[2] : x[0], k1 = hi8 ? x[3] : x[1];
+  k0 += dpp_move<0x140>(hi8 ? x[0] : x[2]);  // row_mirror
+  k1 += dpp_move<0x140>(hi8 ? x[1] : x[3]);
+  const bool hi4 = (n & 4) != 0;
+  float v = hi4 ? k1 : k0;
+  v += dpp_move<0x141>(hi4 ? k0 : k1);  // row_half_mirror
+  v += dpp_move<0x4E>(v);               // quad_perm [2, 3, 0, 1]
+  v += dpp_move<0xB1>(v);               // quad_perm [1, 0, 3, 2]
   return v;
 }
 

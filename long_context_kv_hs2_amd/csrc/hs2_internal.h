@@ -26,6 +26,8 @@ struct FullParams {
   float* spill;              // spill mode: [N][16] log2-domain logits
   float* shat;               // bound mode: [N] per-token sum over heads of the running-normalised weights
   float* tile_stats;         // bound mode: [tile_slots][16] per head after each tile: running max - log2(~1/running sum)
+  uint32_t* hist0;           // [B][kRadixBins] selection histogram, cleared here
+  uint32_t* counters;        // [B][4] selection counters, cleared here
 };
 // Slot of tile t (tokens [16t, 16t + 16)) of the sequence starting at row `base`:
 // unique over all sequences, at most N/16 + B.
@@ -68,8 +70,8 @@ struct SelectParams {
   uint32_t* hist0;            // [B][kRadixBins]: first-digit histogram
   uint32_t* counters;         // [B][4]: winners emitted, candidates seen
   int32_t* selbuf;            // [B][top_k]: positions emitted so far
-  unsigned long long* cand;   // [B][kCandCap]: candidate keys
-  int32_t* cand_idx;          // [B][kCandCap]: candidate positions (bound mode)
+  unsigned long long* cand;   // spill mode: [B][kCandCap] threshold-bin keys; bound mode: [N] exact candidate keys
+  int32_t* cand_idx;          // bound mode: [N] candidate positions
   int32_t* sel_idx;           // [B][budget]
   int32_t* sel_count;         // [B]
   // exact rescoring of candidates (bound mode)
@@ -83,15 +85,18 @@ constexpr int kScoreBlockTokens = 2048;   // tokens per score-pass workgroup
 constexpr int kCollectBlockTokens = 8192; // tokens per collect workgroup
 constexpr int kBoundBlockTokens = 4096;   // tokens per bound-pass workgroup (one 16-token tile per thread)
 constexpr int kRefineBlocks = 64;         // rescoring workgroups per sequence
-constexpr int kCandCap = 32768;           // candidates kept per sequence
+constexpr int kCandCap = 32768;           // threshold-bin keys kept per sequence (spill mode)
 hipError_t launch_select_init(const SelectParams& p, int batch, hipStream_t s);
 // Spill mode: score_j from the spilled logits (compute_score) or read from
 // p.score, and the first-digit histogram.
 hipError_t launch_score_hist(const SelectParams& p, int batch, int64_t max_context, bool compute_score,
                              bool histogram, hipStream_t s);
 hipError_t launch_collect_finish(const SelectParams& p, int batch, int64_t max_context, hipStream_t s);
-// Bound mode: histogram of the lower bounds, candidates by upper bound, exact
-// rescoring of the candidates, exact top-k among them.
+// Bound mode: the full layer's merge fused with the histogram of the lower
+// bounds; then the candidates by upper bound with their exact keys, and the
+// exact top-k among them.
+hipError_t launch_merge_bound_hist(const MergeParams& mp, const SelectParams& p, int batch, int64_t max_context,
+                                   hipStream_t s);
 hipError_t launch_bound_select(const SelectParams& p, int batch, int64_t max_context, bool fp8, hipStream_t s);
 
 // ---- sparse layers -----------------------------------------------------------

@@ -47,6 +47,7 @@
 //  4. finish as above over the exact candidate keys.
 #include "hs2_device.h"
 #include "hs2_internal.h"
+#include "merge.h"
 
 namespace hs2 {
 
@@ -72,23 +73,30 @@ struct Resolved {
 };
 
 // Block-wide: find the bin where the count from the top reaches `rank`.
+// Thread t owns bins [t * per, (t + 1) * per); suffix sums run within each
+// wave by lane shuffles, and across the waves through NT / 64 totals in
+// s_scan, so the whole search takes three barriers.
 template <int NT>
 __device__ Resolved block_resolve(const uint32_t* hist, int nbins, uint32_t rank, uint32_t* s_scan, Resolved* s_out) {
+  constexpr int kWaves = NT / 64;
   const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = t >> 6;
   const int per = nbins >= NT ? nbins / NT : 1;
   const int lo = t * per;
   uint32_t sum = 0;
   for (int i = 0; i < per; ++i)
     if (lo + i < nbins) sum += hist[lo + i];
-  s_scan[t] = sum;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
-    const uint32_t add = t + off < NT ? s_scan[t + off] : 0u;
-    __syncthreads();
-    s_scan[t] += add;
-    __syncthreads();
+  uint32_t suf = sum;  // keys in this lane's bins and in those of the lanes above it
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t o = __shfl_down(suf, d);
+    if (lane + d < 64) suf += o;
   }
-  const uint32_t above = s_scan[t] - sum;  // keys in bins above this thread's range
+  if (lane == 0) s_scan[w] = suf;  // the wave's total
+  __syncthreads();
+  uint32_t above = suf - sum;  // keys in bins above this thread's range
+  for (int w2 = w + 1; w2 < kWaves; ++w2) above += s_scan[w2];
   if (above < rank && rank <= above + sum) {
     uint32_t acc = above;
     for (int i = lo + per - 1; i >= lo; --i) {
@@ -285,6 +293,9 @@ __global__ __launch_bounds__(256) void collect_kernel(SelectParams p) {
 // inside the D0 bin (winners above it are already in selbuf).  Bound mode: the
 // candidate list holds exact keys of every position that can be selected;
 // resolve the threshold over all of them.  Emit, sort ascending, add the window.
+// The radix passes read the candidates from LDS when they fit there.
+constexpr int kFinishLdsKeys = 16384;
+
 template <bool BOUND>
 __global__ __launch_bounds__(1024) void finish_kernel(SelectParams p) {
   __shared__ uint32_t s_hist[kRadixBins];
@@ -292,6 +303,7 @@ __global__ __launch_bounds__(1024) void finish_kernel(SelectParams p) {
   __shared__ Resolved s_res;
   __shared__ int32_t s_sel[kTopK];
   __shared__ uint32_t s_n;
+  __shared__ unsigned long long s_keys[kFinishLdsKeys];
   const int b = blockIdx.x;
   const int t = threadIdx.x;
   int64_t base;
@@ -304,10 +316,31 @@ __global__ __launch_bounds__(1024) void finish_kernel(SelectParams p) {
     return;
   }
   const int dom = len - p.window;
-  const uint32_t ncand = p.counters[b * 4 + 1];
-  const bool overflow = ncand > static_cast<uint32_t>(kCandCap);
-  const unsigned long long* cand = p.cand + static_cast<size_t>(b) * kCandCap;
+  // Bound mode: the keys fill the sequence's region cand[base, base + ncand),
+  // which has room for every position.  Spill mode: cand[b][0, kCandCap),
+  // and a scan of the D0 bin's scores when that overflowed.
+  uint32_t ncand = p.counters[b * 4 + 1];
+  if (BOUND) ncand = min(ncand, static_cast<uint32_t>(dom));
+  const bool overflow = !BOUND && ncand > static_cast<uint32_t>(kCandCap);
+  const unsigned long long* cand = BOUND ? p.cand + base : p.cand + static_cast<size_t>(b) * kCandCap;
   const float* score = p.score + base;
+  const bool staged = !overflow && ncand <= static_cast<uint32_t>(kFinishLdsKeys);
+  if (staged) {
+    constexpr int kBatch = 8;  // loads in flight per thread
+    for (uint32_t i0 = 0; i0 < ncand; i0 += kBatch * 1024) {
+      unsigned long long k8[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const uint32_t i = i0 + u * 1024 + t;
+        k8[u] = i < ncand ? cand[i] : 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const uint32_t i = i0 + u * 1024 + t;
+        if (i < ncand) s_keys[i] = k8[u];
+      }
+    }
+  }
   uint32_t d0 = 0;
   uint32_t nwin = 0;
   uint32_t rank = static_cast<uint32_t>(p.top_k);
@@ -332,8 +365,21 @@ __global__ __launch_bounds__(1024) void finish_kernel(SelectParams p) {
   // Visit every key that can still be selected: the candidate list, or a scan
   // of the sequence's scores (spill mode: the D0 bin only) when it overflowed.
   auto for_each_key = [&](auto&& fn) {
-    if (!overflow) {
-      for (uint32_t i = t; i < ncand; i += blockDim.x) fn(cand[i]);
+    if (staged) {
+      for (uint32_t i = t; i < ncand; i += blockDim.x) fn(s_keys[i]);
+    } else if (!overflow) {
+      constexpr int kBatch = 8;  // loads in flight per thread
+      for (uint32_t i0 = 0; i0 < ncand; i0 += kBatch * 1024) {
+        unsigned long long k8[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const uint32_t i = i0 + u * 1024 + t;
+          k8[u] = i < ncand ? cand[i] : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+          if (i0 + u * 1024 + t < ncand) fn(k8[u]);
+      }
     } else {
       for (int j = t; j < dom; j += blockDim.x) {
         const float sc = score[j];
@@ -371,21 +417,30 @@ __global__ __launch_bounds__(1024) void finish_kernel(SelectParams p) {
     }
   });
   __syncthreads();
+  // Bitonic sort, one position per thread: partners within a wave trade by
+  // lane shuffle, partners in other waves through LDS (the histogram's room,
+  // free by now, as two buffers taken in turn: one barrier per such stage).
+  int32_t x = s_sel[t];
+  int32_t* xbuf = reinterpret_cast<int32_t*>(s_hist);  // [2][kTopK]
+  static_assert(kRadixBins >= 2 * kTopK, "two sort buffers fit in the histogram");
+  int nb = 0;
   for (int size = 2; size <= kTopK; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const int partner = t ^ stride;
-      if (partner > t) {
-        const bool up = (t & size) == 0;
-        const int32_t a = s_sel[t], c = s_sel[partner];
-        if ((a > c) == up) {
-          s_sel[t] = c;
-          s_sel[partner] = a;
-        }
+      int32_t y;
+      if (stride >= 64) {
+        xbuf[nb * kTopK + t] = x;
+        __syncthreads();
+        y = xbuf[nb * kTopK + (t ^ stride)];
+        nb ^= 1;
+      } else {
+        y = __shfl_xor(x, stride);
       }
-      __syncthreads();
+      const bool up = (t & size) == 0;
+      const bool lower = (t & stride) == 0;
+      x = (lower == up) ? min(x, y) : max(x, y);
     }
   }
-  out[t] = s_sel[t];
+  out[t] = x;
   if (t < p.window) out[p.top_k + t] = dom + t;
   if (t == 0) p.sel_count[b] = p.budget;
 }
@@ -404,128 +459,186 @@ hipError_t launch_collect_finish(const SelectParams& p, int batch, int64_t max_c
 
 // ---- bound mode ------------------------------------------------------------
 
-// Per-tile bound factors F_h = exp2(u_h^t - M_h) / Z_h: their min and max.
-__device__ __forceinline__ void tile_factors(const float* __restrict__ ts, const float (&mx)[kHeads],
-                                             const float (&iz)[kHeads], float& fmin, float& fmax) {
+// Slack on the pruning threshold and on the upper bounds: far above fp32
+// rounding, the approximate exp2 / log2, and the rounding-order difference
+// between the first pass's own copy of (M_h, Z_h) and the merge's.
+constexpr float kLowSlack = 1.f - 1.f / 1024.f;
+constexpr float kHighSlack = 1.f + 1.f / 1024.f;
+
+// Min and max over heads of a tile's bound factors F_h = exp2(u_h - M_h) / Z_h.
+__device__ __forceinline__ void tile_factors(const float (&u)[kHeads], const float* s_mx, const float* s_iz,
+                                             float& fmin, float& fmax) {
   fmin = INFINITY;
   fmax = 0.f;
 #pragma unroll
   for (int h = 0; h < kHeads; ++h) {
-    const float f = exp2f(ts[h] - mx[h]) * iz[h];
+    const float f = exp2f(u[h] - s_mx[h]) * s_iz[h];
     fmin = fminf(fmin, f);
     fmax = fmaxf(fmax, f);
   }
 }
 
-__device__ __forceinline__ void load_global_stats(const SelectParams& p, int b, float (&mx)[kHeads], float (&iz)[kHeads]) {
-  const float* st = p.stats + static_cast<int64_t>(b) * kHeads * 2;
+// A tile's 16 shat values (nv of them real) and its 16 per-head u values.
+__device__ __forceinline__ void load_tile_bounds(const SelectParams& p, int64_t base, int b, int tile, int nv,
+                                                 float (&v)[16], float (&u)[kHeads]) {
+  const float4* us = reinterpret_cast<const float4*>(p.tile_stats + tile_slot(base, b, tile) * kHeads);
 #pragma unroll
-  for (int h = 0; h < kHeads; ++h) {
-    mx[h] = st[2 * h];
-    iz[h] = 1.f / st[2 * h + 1];
+  for (int q = 0; q < 4; ++q) {
+    const float4 x = us[q];
+    u[4 * q] = x.x; u[4 * q + 1] = x.y; u[4 * q + 2] = x.z; u[4 * q + 3] = x.w;
+  }
+  if ((base & 3) == 0) {  // 16-byte aligned rows
+    const float4* sh = reinterpret_cast<const float4*>(p.shat + base + 16 * tile);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 x = sh[q];
+      v[4 * q] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = p.shat[base + 16 * tile + min(i, nv - 1)];
   }
 }
 
-// Slack on the pruning threshold and upper bounds: far above fp32 rounding.
-constexpr float kLowSlack = 1.f - 1.f / 1024.f;
-constexpr float kHighSlack = 1.f + 1.f / 1024.f;
-
-// Histogram of the lower bounds lb_j = shat_j * min_h F_h (first 11-bit digit).
-// One thread per 16-token tile.
-__global__ __launch_bounds__(256) void bound_hist_kernel(SelectParams p) {
+// The full layer's merge and the bound selection's first pass in one launch.
+// Workgroups x < 16 merge head x of sequence y and write its (M, Z).  The
+// others histogram the first digit of the lower bounds lb_j = shat_j min_h F_h
+// over a block of kBoundBlockTokens out-of-window positions (one 16-token tile
+// per thread), with (M_h, Z_h) recomputed from the partials' (m, z): the
+// merge's copy is not written yet, and the copies differ by rounding order
+// only, which the slack covers.
+__global__ __launch_bounds__(256) void merge_bound_hist_kernel(MergeParams mp, SelectParams p) {
+  __shared__ MergeShared msh;
   __shared__ uint32_t s_hist[kRadixBins];
+  __shared__ float s_mx[kHeads], s_iz[kHeads];
   const int b = blockIdx.y;
+  if (blockIdx.x < kHeads) {
+    merge_one(mp, blockIdx.x, b, 0, 0, 0, msh);
+    return;
+  }
   int64_t base;
   int len;
   seq_bounds(p.seq_offsets, b, p.total_tokens, p.max_context, base, len);
   if (len <= p.budget) return;
   const int dom = len - p.window;
-  const int j0 = blockIdx.x * kBoundBlockTokens;
+  const int j0 = (blockIdx.x - kHeads) * kBoundBlockTokens;
   if (j0 >= dom) return;
-  float mx[kHeads], iz[kHeads];
-  load_global_stats(p, b, mx, iz);
-  for (int i = threadIdx.x; i < kRadixBins; i += blockDim.x) s_hist[i] = 0;
-  __syncthreads();
-  const int tile = (j0 >> 4) + threadIdx.x;
-  if (16 * tile < dom) {
-    float fmin, fmax;
-    tile_factors(p.tile_stats + tile_slot(base, b, tile) * kHeads, mx, iz, fmin, fmax);
-    const float4* sh = reinterpret_cast<const float4*>(p.shat + base + 16 * tile);
-    const int nv = min(16, dom - 16 * tile);
-    // shat rows are 64-byte aligned only when base is a multiple of 16: load scalars otherwise
-    float v[16];
-    if ((base & 3) == 0) {
+  const int t = threadIdx.x;
+  const int tile = (j0 >> 4) + t;
+  const bool valid = 16 * tile < dom;
+  const int nv = min(16, dom - 16 * tile);
+  float v[16], u[kHeads];
+  if (valid) load_tile_bounds(p, base, b, tile, nv, v, u);
+  for (int i = t; i < kRadixBins; i += 256) s_hist[i] = 0;
+  {
+    // (M_h, Z_h): 16 lanes per head, partials c = l, l + 16, ...
+    const int h = t >> 4, l = t & 15;
+    const int count = (len + mp.chunk - 1) / mp.chunk;
+    const float* pb = mp.partials + static_cast<int64_t>(b) * mp.stride_seq;
+    float m = -INFINITY;
+    for (int c = l; c < count; c += 16) m = fmaxf(m, pb[static_cast<int64_t>(c) * mp.stride_chunk + h]);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 x = sh[q];
-        v[4 * q] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = p.shat[base + 16 * tile + min(i, nv - 1)];
+    for (int off = 8; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    float z = 0.f;
+    for (int c = l; c < count; c += 16) {
+      const float* pc = pb + static_cast<int64_t>(c) * mp.stride_chunk;
+      const float mc = pc[h];
+      if (mc != -INFINITY) z += pc[kHeads + h] * exp2f(mc - m);
     }
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) z += __shfl_xor(z, off);
+    if (l == 0) {
+      s_mx[h] = m;
+      s_iz[h] = 1.f / z;
+    }
+  }
+  __syncthreads();
+  if (valid) {
+    float fmin, fmax;
+    tile_factors(u, s_mx, s_iz, fmin, fmax);
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       if (i < nv) atomicAdd(&s_hist[digit0(v[i] * fmin)], 1u);
   }
   __syncthreads();
   uint32_t* gh = p.hist0 + static_cast<size_t>(b) * kRadixBins;
-  for (int i = threadIdx.x; i < kRadixBins; i += blockDim.x) {
+  for (int i = t; i < kRadixBins; i += 256) {
     const uint32_t c = s_hist[i];
     if (c) atomicAdd(gh + i, c);
   }
 }
 
-// Candidates: every out-of-window position whose upper bound reaches the lower
-// edge of the bin holding the k-th largest lower bound.  The workgroup builds
-// its list in LDS and reserves room in the sequence's list with one atomic.
+hipError_t launch_merge_bound_hist(const MergeParams& mp, const SelectParams& p, int batch, int64_t max_context,
+                                   hipStream_t s) {
+  if (batch == 0) return hipSuccess;
+  const unsigned blocks = static_cast<unsigned>((max_context + kBoundBlockTokens - 1) / kBoundBlockTokens);
+  hipLaunchKernelGGL(merge_bound_hist_kernel, dim3(kHeads + blocks, batch), dim3(256), 0, s, mp, p);
+  return hipGetLastError();
+}
+
+// Candidates: workgroup j of a sequence takes the 16-token tiles j, j + nb,
+// j + 2 nb, ... of its out-of-window positions (nb workgroups, one tile per
+// thread).  The tiles each wave of the full pass visited first have the
+// loosest bounds and sit together at the start of the sequence; striding
+// spreads them.  Each workgroup resolves the pruning threshold from the
+// finished lower-bound histogram (every workgroup of the sequence finds the
+// same one): the lower edge of the bin holding the k-th largest lower bound,
+// so at least k positions score at or above it.  It keeps the positions whose
+// upper bound reaches it, so every position of the exact top-k (ties
+// included) is kept; it gathers them in LDS and places them in the sequence's
+// list (room for every position) with one atomic.
 __global__ __launch_bounds__(256) void collect_bound_kernel(SelectParams p) {
   __shared__ uint32_t s_hist[kRadixBins];
   __shared__ uint32_t s_scan[256];
   __shared__ Resolved s_res;
   __shared__ int32_t s_list[kBoundBlockTokens];
-  __shared__ uint32_t s_cnt;
-  __shared__ uint32_t s_base;
+  __shared__ float s_mx[kHeads], s_iz[kHeads];
+  __shared__ uint32_t s_cnt, s_base;
   const int b = blockIdx.y;
   int64_t base;
   int len;
   seq_bounds(p.seq_offsets, b, p.total_tokens, p.max_context, base, len);
   if (len <= p.budget) return;
   const int dom = len - p.window;
-  const int j0 = blockIdx.x * kBoundBlockTokens;
-  if (j0 >= dom) return;
-  float mx[kHeads], iz[kHeads];
-  load_global_stats(p, b, mx, iz);
+  const int nb = (dom + kBoundBlockTokens - 1) / kBoundBlockTokens;
+  if (static_cast<int>(blockIdx.x) >= nb) return;
+  const int t = threadIdx.x;
+  const int tile = blockIdx.x + t * nb;
+  const bool valid = 16 * tile < dom;
+  const int nv = min(16, dom - 16 * tile);
+  float v[16], u[kHeads];
+  if (valid) load_tile_bounds(p, base, b, tile, nv, v, u);
   const uint32_t* gh = p.hist0 + static_cast<size_t>(b) * kRadixBins;
-  for (int i = threadIdx.x; i < kRadixBins; i += blockDim.x) s_hist[i] = gh[i];
-  if (threadIdx.x == 0) s_cnt = 0;
+  for (int i = t; i < kRadixBins; i += 256) s_hist[i] = gh[i];
+  if (t < kHeads) {
+    s_mx[t] = p.stats[(static_cast<int64_t>(b) * kHeads + t) * 2];
+    s_iz[t] = 1.f / p.stats[(static_cast<int64_t>(b) * kHeads + t) * 2 + 1];
+  }
+  if (t == 0) s_cnt = 0;
   __syncthreads();
   const Resolved r0 = block_resolve<256>(s_hist, kRadixBins, static_cast<uint32_t>(p.top_k), s_scan, &s_res);
   const float thr = __uint_as_float(static_cast<uint32_t>(r0.digit) << 20) * kLowSlack;
-  const int tile = (j0 >> 4) + threadIdx.x;
-  if (16 * tile < dom) {
+  if (valid) {
     float fmin, fmax;
-    tile_factors(p.tile_stats + tile_slot(base, b, tile) * kHeads, mx, iz, fmin, fmax);
-    const int nv = min(16, dom - 16 * tile);
-    for (int i = 0; i < nv; ++i) {
-      const int j = 16 * tile + i;
-      if (p.shat[base + j] * fmax * kHighSlack >= thr) s_list[atomicAdd(&s_cnt, 1u)] = j;
-    }
+    tile_factors(u, s_mx, s_iz, fmin, fmax);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (i < nv && v[i] * fmax * kHighSlack >= thr) s_list[atomicAdd(&s_cnt, 1u)] = 16 * tile + i;
   }
   __syncthreads();
-  if (threadIdx.x == 0) s_base = s_cnt ? atomicAdd(p.counters + b * 4 + 1, s_cnt) : 0u;
+  const uint32_t ncand = s_cnt;
+  if (t == 0) s_base = ncand ? atomicAdd(p.counters + b * 4 + 1, ncand) : 0u;
   __syncthreads();
-  int32_t* cidx = p.cand_idx + static_cast<size_t>(b) * kCandCap;
-  for (uint32_t i = threadIdx.x; i < s_cnt; i += blockDim.x) {
-    const uint32_t slot = s_base + i;
-    if (slot < static_cast<uint32_t>(kCandCap)) cidx[slot] = s_list[i];
-  }
+  int32_t* ci = p.cand_idx + base;  // the sequence's region: one slot per position
+  for (uint32_t i = t; i < ncand; i += 256) ci[s_base + i] = s_list[i];
 }
 
-// Exact scores of the candidates (every out-of-window position when the list
-// overflowed): the same split-query MFMA sequence as the full pass gives the
-// same logits, and the same head-ordered sum gives the same score as the
-// spill path.  Keys go to the candidate key list (or scores to p.score).
+// Exact keys of the candidates, 16 per MFMA tile: the split query from LDS
+// and the same MFMA sequence as the full pass give the same logits, and the
+// same head-ordered sum as the score pass gives the same score, so the keys
+// are bitwise those of the spill path.  kRefineBlocks workgroups per
+// sequence deal the candidate tiles round-robin over their waves; each wave
+// has its next tile's loads in flight while it scores the current one.
 template <bool FP8>
 __global__ __launch_bounds__(256) void refine_kernel(SelectParams p) {
   __shared__ u32x4 s_q[kQLdsVecs];
@@ -538,37 +651,55 @@ __global__ __launch_bounds__(256) void refine_kernel(SelectParams p) {
   seq_bounds(p.seq_offsets, b, p.total_tokens, p.max_context, base, len);
   if (len <= p.budget) return;
   const int dom = len - p.window;
-  const uint32_t ncand = p.counters[b * 4 + 1];
-  const bool overflow = ncand > static_cast<uint32_t>(kCandCap);
-  const int items = overflow ? dom : static_cast<int>(ncand);
-  const int ntiles = (items + 15) >> 4;
+  const int ncand = static_cast<int>(min(p.counters[b * 4 + 1], static_cast<uint32_t>(dom)));
+  const int ntiles = (ncand + 15) >> 4;
   if (static_cast<int>(blockIdx.x) * 4 >= ntiles) return;  // uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar loop control
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  constexpr int kRowBytes = FP8 ? kDim : 2 * kDim;
+  const uint8_t* __restrict__ kbase = p.k + base * kRowBytes;
+  const int32_t* ci = p.cand_idx + base;
+  const int stride = gridDim.x * 4;
+
+  struct Raw {
+    u32x4 k[FP8 ? 2 : 4];
+    float ks[4];
+    int pos;
+  };
+  // lane (n, g): candidate n of the tile (clamped to the last one), row bytes
+  // kload_offset(j, g); ks[r]: the K scale of candidate 4g + r
+  auto load = [&](int tile, Raw& r) {
+    const int i0 = min(tile, ntiles - 1) * 16;
+    r.pos = min(max(ci[i0 + min(n, ncand - 1 - i0)], 0), dom - 1);
+    const uint32_t krow = static_cast<uint32_t>(r.pos) * kRowBytes;
+#pragma unroll
+    for (int j = 0; j < (FP8 ? 2 : 4); ++j) r.k[j] = *reinterpret_cast<const u32x4*>(kbase + (krow + kload_offset(j, g)));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r.ks[q] = FP8 ? p.k_scale[base + __shfl(r.pos, 4 * g + q)] : 1.f;
+  };
+  Raw ra, rb;
+  int tile = blockIdx.x * 4 + wave;
+  load(tile, ra);
   build_q_lds<FP8>(p.q + static_cast<size_t>(b) * kHeads * kDim, p.qscale, s_q);
   if (threadIdx.x < kHeads) {
     s_mx[threadIdx.x] = p.stats[(static_cast<int64_t>(b) * kHeads + threadIdx.x) * 2];
     s_iz[threadIdx.x] = 1.f / p.stats[(static_cast<int64_t>(b) * kHeads + threadIdx.x) * 2 + 1];
   }
   __syncthreads();
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar loop control
-  const int lane = threadIdx.x & 63;
-  const int n = lane & 15;
-  const int g = lane >> 4;
   const QShared q{s_q, lane};
-  constexpr int kRowBytes = FP8 ? kDim : 2 * kDim;
-  const uint8_t* __restrict__ kbase = p.k + base * kRowBytes;
-  const int32_t* cidx = p.cand_idx + static_cast<size_t>(b) * kCandCap;
-  for (int tile = blockIdx.x * 4 + wave; tile < ntiles; tile += gridDim.x * 4) {
+  unsigned long long* ck = p.cand + base;  // the sequence's region: one slot per position
+  auto score = [&](int tile, const Raw& r) {
     const int i0 = tile * 16;
-    const int nv = min(16, items - i0);
-    const int pos = overflow ? i0 + min(n, nv - 1) : cidx[i0 + min(n, nv - 1)];
-    const uint32_t krow = static_cast<uint32_t>(pos) * kRowBytes;
+    const int nvc = min(16, ncand - i0);
     bf16x8 kf[4];
     if constexpr (FP8) {
-      e4m3x16_to_bf16(*reinterpret_cast<const u32x4*>(kbase + (krow + kload_offset(0, g))), kf[0], kf[1]);
-      e4m3x16_to_bf16(*reinterpret_cast<const u32x4*>(kbase + (krow + kload_offset(1, g))), kf[2], kf[3]);
+      e4m3x16_to_bf16(r.k[0], kf[0], kf[1]);
+      e4m3x16_to_bf16(r.k[1], kf[2], kf[3]);
     } else {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) kf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(kbase + (krow + kload_offset(s, g))));
+      for (int s2 = 0; s2 < 4; ++s2) kf[s2] = as_bf16x8(r.k[s2]);
     }
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -577,25 +708,30 @@ __global__ __launch_bounds__(256) void refine_kernel(SelectParams p) {
       for (int k = 0; k < 4; ++k) sacc = mfma_bf16_16x16x32(kf[k], q.get(part, k), sacc);
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int slot = 4 * g + r;
-      const int spos = __shfl(pos, slot);  // lane `slot` (group 0) holds that token's position
-      const float ks = FP8 ? p.k_scale[base + spos] : 1.f;
-      s_lg[wave][slot][n] = sacc[r] * ks;
-    }
+    for (int q4 = 0; q4 < 4; ++q4) s_lg[wave][4 * g + q4][n] = sacc[q4] * r.ks[q4];
     asm volatile("" ::: "memory");  // the reads below must follow the writes above
     if (lane < 16) {
       float acc = 0.f;
 #pragma unroll
       for (int h = 0; h < kHeads; ++h) acc = __builtin_fmaf(exp2f(s_lg[wave][lane][h] - s_mx[h]), s_iz[h], acc);
-      if (lane < nv) {
-        if (overflow)
-          p.score[base + pos] = acc;
-        else
-          p.cand[static_cast<size_t>(b) * kCandCap + i0 + lane] = select_key(acc, pos);
-      }
+      if (lane < nvc) ck[i0 + lane] = select_key(acc, r.pos);
     }
     asm volatile("" ::: "memory");  // the next tile's writes must follow these reads
+  };
+  // two-slot ring; a load past the last tile re-reads the last one (unused)
+  for (;;) {
+    load(tile + stride, rb);
+    __builtin_amdgcn_sched_barrier(0);
+    score(tile, ra);
+    __builtin_amdgcn_sched_barrier(0);
+    tile += stride;
+    if (tile >= ntiles) break;
+    load(tile + stride, ra);
+    __builtin_amdgcn_sched_barrier(0);
+    score(tile, rb);
+    __builtin_amdgcn_sched_barrier(0);
+    tile += stride;
+    if (tile >= ntiles) break;
   }
 }
 
@@ -603,11 +739,8 @@ hipError_t launch_bound_select(const SelectParams& p, int batch, int64_t max_con
   if (batch == 0) return hipSuccess;
   if (max_context > 0) {
     const dim3 grid(static_cast<unsigned>((max_context + kBoundBlockTokens - 1) / kBoundBlockTokens), batch);
-    hipLaunchKernelGGL(bound_hist_kernel, grid, dim3(256), 0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(collect_bound_kernel, grid, dim3(256), 0, s, p);
-    e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 rgrid(kRefineBlocks, batch);
     if (fp8)
