@@ -38,7 +38,8 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_PROFILE = {2: "profiles/full_partial_b32_ctx128k_bf16_hbm_traffic.md"}
+TRAFFIC_PROFILE = {2: "profiles/full_partial_b32_ctx128k_bf16_hbm_traffic.md",
+                   3: "profiles/full_partial_b4_ctx1m_fp8_hbm_traffic.md"}
 KERNEL_SOURCES = ("long_context_kv_hs2_amd/csrc/full_decode.hip", "long_context_kv_hs2_amd/csrc/hs2_device.h")
 METRIC = "hybrid-block decode tokens/s at 128K/1M ctx; achieved HBM GB/s vs peak"
 WORKLOADS = {2: "b32_ctx128k_bf16", 3: "b4_ctx1m_fp8", 4: "b64_ragged_2k_256k_bf16",
