@@ -279,10 +279,13 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] += s_o[w][h][d0 + j] * f;
   }
-  float* out = p.partials + (static_cast<size_t>(b) * p.chunks_per_seq + c) * kPartialFloats;
+  const size_t item = static_cast<size_t>(b) * p.chunks_per_seq + c;
+  float* out = p.partials + item * kPartialFloats;
   if ((threadIdx.x & 15) == 0) {
     out[h] = mx;
     out[kHeads + h] = zz;
+    p.pstats[item * 2 * kHeads + h] = mx;  // compact copy for the selection's first pass
+    p.pstats[item * 2 * kHeads + kHeads + h] = zz;
   }
   float4* o4 = reinterpret_cast<float4*>(out + 2 * kHeads + h * kDim + d0);
   o4[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);

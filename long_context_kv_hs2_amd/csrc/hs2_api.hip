@@ -58,7 +58,7 @@ struct DecodeLayout {
   int chunk = 0;
   int chunks_per_seq = 0;
   int splits = 0;
-  size_t partials = 0, stats = 0, spill = 0, score = 0, hist0 = 0, counters = 0, selbuf = 0, cand = 0,
+  size_t partials = 0, stats = 0, pstats = 0, spill = 0, score = 0, hist0 = 0, counters = 0, selbuf = 0, cand = 0,
          shat = 0, tile_stats = 0, cand_idx = 0, sparse = 0, total = 0;
 };
 
@@ -78,6 +78,7 @@ DecodeLayout decode_layout(const hs2_decode_desc& d) {
   };
   L.partials = take(B * L.chunks_per_seq * kPartialFloats * sizeof(float));
   L.stats = take(B * kHeads * 2 * sizeof(float));
+  L.pstats = take(B * L.chunks_per_seq * 2 * kHeads * sizeof(float));
   L.spill = take(N * kHeads * sizeof(float));
   L.score = take(N * sizeof(float));
   L.hist0 = take(B * kRadixBins * sizeof(uint32_t));
@@ -226,6 +227,7 @@ FullParams full_params(const DecodeArgs& a, const DecodeLayout& L) {
   p.chunk = L.chunk;
   p.chunks_per_seq = L.chunks_per_seq;
   p.partials = reinterpret_cast<float*>(ws_at(a.ws, L.partials));
+  p.pstats = reinterpret_cast<float*>(ws_at(a.ws, L.pstats));
   p.spill = reinterpret_cast<float*>(ws_at(a.ws, L.spill));
   p.shat = reinterpret_cast<float*>(ws_at(a.ws, L.shat));
   p.tile_stats = reinterpret_cast<float*>(ws_at(a.ws, L.tile_stats));
@@ -244,6 +246,8 @@ SelectParams select_params(const DecodeArgs& a, const DecodeLayout& L, float* sc
   p.budget = a.d->window + a.d->top_k;
   p.spill = reinterpret_cast<const float*>(ws_at(a.ws, L.spill));
   p.stats = reinterpret_cast<const float*>(ws_at(a.ws, L.stats));
+  p.pstats = reinterpret_cast<const float*>(ws_at(a.ws, L.pstats));
+  p.chunks_per_seq = L.chunks_per_seq;
   p.score = score;
   p.hist0 = reinterpret_cast<uint32_t*>(ws_at(a.ws, L.hist0));
   p.counters = reinterpret_cast<uint32_t*>(ws_at(a.ws, L.counters));

@@ -23,6 +23,7 @@ struct FullParams {
   int chunk;                 // tokens per workgroup, multiple of 64
   int chunks_per_seq;
   float* partials;           // [B][chunks_per_seq][kPartialFloats]
+  float* pstats;             // [B][chunks_per_seq][32]: each partial's (m[16], z[16]) again, packed
   float* spill;              // spill mode: [N][16] log2-domain logits
   float* shat;               // bound mode: [N] per-token sum over heads of the running-normalised weights
   float* tile_stats;         // bound mode: [tile_slots][16] per head after each tile: running max - log2(~1/running sum)
@@ -64,6 +65,8 @@ struct SelectParams {
   int window, top_k, budget;
   const float* spill;         // [N][16] (spill mode)
   const float* stats;         // [B][16][2] global (max, sum) per head
+  const float* pstats;        // [B][chunks_per_seq][32] the full pass's partial (m, z)
+  int chunks_per_seq;
   const float* shat;          // [N] (bound mode)
   const float* tile_stats;    // [tile_slots][16] (bound mode)
   float* score;               // [N]

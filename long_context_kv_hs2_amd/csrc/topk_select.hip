@@ -504,9 +504,9 @@ __device__ __forceinline__ void load_tile_bounds(const SelectParams& p, int64_t 
 // Workgroups x < 16 merge head x of sequence y and write its (M, Z).  The
 // others histogram the first digit of the lower bounds lb_j = shat_j min_h F_h
 // over a block of kBoundBlockTokens out-of-window positions (one 16-token tile
-// per thread), with (M_h, Z_h) recomputed from the partials' (m, z): the
-// merge's copy is not written yet, and the copies differ by rounding order
-// only, which the slack covers.
+// per thread), with (M_h, Z_h) recomputed from the partials' (m, z), read
+// from the full pass's packed copy: the merge's result is not written yet,
+// and the two differ by rounding order only, which the slack covers.
 __global__ __launch_bounds__(256) void merge_bound_hist_kernel(MergeParams mp, SelectParams p) {
   __shared__ MergeShared msh;
   __shared__ uint32_t s_hist[kRadixBins];
@@ -531,22 +531,39 @@ __global__ __launch_bounds__(256) void merge_bound_hist_kernel(MergeParams mp, S
   if (valid) load_tile_bounds(p, base, b, tile, nv, v, u);
   for (int i = t; i < kRadixBins; i += 256) s_hist[i] = 0;
   {
-    // (M_h, Z_h): 16 lanes per head, partials c = l, l + 16, ...
+    // (M_h, Z_h): 16 lanes per head, partials c = l, l + 16, ..., eight
+    // loads in flight per lane, merged online; then across the 16 lanes.
     const int h = t >> 4, l = t & 15;
     const int count = (len + mp.chunk - 1) / mp.chunk;
-    const float* pb = mp.partials + static_cast<int64_t>(b) * mp.stride_seq;
-    float m = -INFINITY;
-    for (int c = l; c < count; c += 16) m = fmaxf(m, pb[static_cast<int64_t>(c) * mp.stride_chunk + h]);
+    const float* pb = p.pstats + static_cast<int64_t>(b) * p.chunks_per_seq * (2 * kHeads);
+    float m = -INFINITY, z = 0.f;
+    auto fold = [](float& m, float& z, float mc, float zc) {  // (m, z) += (mc, zc)
+      if (mc == -INFINITY) return;
+      if (mc > m) {
+        z = z * exp2f(m - mc) + zc;
+        m = mc;
+      } else {
+        z += zc * exp2f(mc - m);
+      }
+    };
+    constexpr int kBatch = 8;
+    for (int c0 = l; c0 < count; c0 += 16 * kBatch) {
+      float mv[kBatch], zv[kBatch];
 #pragma unroll
-    for (int off = 8; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    float z = 0.f;
-    for (int c = l; c < count; c += 16) {
-      const float* pc = pb + static_cast<int64_t>(c) * mp.stride_chunk;
-      const float mc = pc[h];
-      if (mc != -INFINITY) z += pc[kHeads + h] * exp2f(mc - m);
+      for (int u = 0; u < kBatch; ++u) {
+        const int c = c0 + 16 * u;
+        const float* pc = pb + static_cast<int64_t>(min(c, count - 1)) * (2 * kHeads);
+        mv[u] = c < count ? pc[h] : -INFINITY;
+        zv[u] = pc[kHeads + h];
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) fold(m, z, mv[u], zv[u]);
     }
 #pragma unroll
-    for (int off = 8; off > 0; off >>= 1) z += __shfl_xor(z, off);
+    for (int off = 8; off > 0; off >>= 1) {
+      const float mo = __shfl_xor(m, off), zo = __shfl_xor(z, off);
+      fold(m, z, mo, zo);
+    }
     if (l == 0) {
       s_mx[h] = m;
       s_iz[h] = 1.f / z;
