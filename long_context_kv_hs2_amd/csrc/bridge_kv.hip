@@ -8,21 +8,25 @@
 //
 // The weights (a few MB) are first transposed into the workspace so that both
 // operands are contiguous along the reduction dim, the layout the MFMA
-// fragments read.  GEMM tiles: 128 rows x 128 columns (one output matrix) per
-// workgroup, k-step 64, LDS double buffering with the next tile's global loads
-// in flight during the current tile's MFMAs; four waves of 64 x 64 each.
-// Workgroups are ordered so the n_out column tiles of one row block run
-// back to back on the same XCD and share its L2.
+// fragments read.  GEMM tiles: 256 rows x 256 columns (two output matrices)
+// per workgroup of eight waves, each wave 128 x 64; k-step 64; LDS double
+// buffering, with the next two k-steps' global loads in flight in registers.
+// A tile this large keeps each CU's operand traffic (about 30 bytes per clock
+// at the MFMA peak) within what its load path delivers; 128 x 128 tiles need
+// twice that.  Workgroups are ordered so the column tiles of one row block
+// run back to back on the same XCD and share its L2.
 #include "hs2_device.h"
 #include "hs2_internal.h"
 
 namespace hs2 {
 
 namespace {
-constexpr int kBM = 128;
-constexpr int kBN = 128;
-constexpr int kBK = 64;
-constexpr int kPitch = kBK * 2 + 16;  // bytes per LDS row (padded)
+constexpr int kBM = 256;  // workgroup tile: 256 rows x 256 output columns
+constexpr int kBN = 256;
+constexpr int kBK = 64;   // k-step: two 16x16x32 MFMAs deep
+constexpr int kWM = 128;  // wave tile (8 waves, 2 x 4)
+constexpr int kWN = 64;
+constexpr int kPitch = kBK * 2 + 16;  // bytes per LDS row (padded: 8 rows of a fragment read hit all banks)
 }  // namespace
 
 struct WeightPtrs {
@@ -61,18 +65,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-__global__ __launch_bounds__(256) void bridge_gemm_kernel(BridgeParams p) {
+__global__ __launch_bounds__(512) void bridge_gemm_kernel(BridgeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t s_a[2][kBM * kPitch];
   __shared__ __attribute__((aligned(16))) uint8_t s_b[2][kBN * kPitch];
 
-  // XCD-aware order: workgroup id i runs on XCD i % 8; give the n_out column
-  // tiles of one row block consecutive slots on one XCD.
+  // XCD-aware order: workgroup id i runs on XCD i % 8; give the column tiles
+  // of one row block consecutive slots on one XCD, so they share its L2.
+  const int n_ct = p.n_out * kDim / kBN;
   const int id = blockIdx.x;
   const int xcd = id & 7;
   const int slot = id >> 3;
   const int m_tiles = static_cast<int>((p.n_tokens + kBM - 1) / kBM);
-  const int mt = (slot / p.n_out) * 8 + xcd;
-  const int nt = slot % p.n_out;
+  const int mt = (slot / n_ct) * 8 + xcd;
+  const int ct = slot % n_ct;
   if (mt >= m_tiles) return;
   const int64_t m0 = static_cast<int64_t>(mt) * kBM;
 
@@ -81,82 +86,108 @@ __global__ __launch_bounds__(256) void bridge_gemm_kernel(BridgeParams p) {
   const int lane = tid & 63;
   const int n = lane & 15;
   const int g = lane >> 4;
-  const int wm = (wave >> 1) * 64;
-  const int wn = (wave & 1) * 64;
+  const int wm = (wave & 1) * kWM;
+  const int wn = (wave >> 1) * kWN;
 
-  // Global -> register staging: each thread moves 4 x 16 B of A and of B per k-step.
-  // Chunk c = tid + 256 * j: row c / 8, 16-byte column c % 8.
+  // Global -> register staging: each thread moves 4 x 16 B of A and of B per
+  // k-step.  Chunk c = tid + 512 * j: row c / 8, 16-byte column c % 8.
   const uint16_t* a_src[4];
   const uint16_t* b_src[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int c = tid + 256 * j;
+    const int c = tid + 512 * j;
     const int row = c >> 3, col = (c & 7) * 8;
     const int64_t arow = min<int64_t>(m0 + row, p.n_tokens - 1);  // clamp the ragged last block
     a_src[j] = p.hidden + arow * p.d_model + col;
-    b_src[j] = p.w_t + (static_cast<int64_t>(nt) * kBN + row) * p.d_model + col;
+    b_src[j] = p.w_t + (static_cast<int64_t>(ct) * kBN + row) * p.d_model + col;
   }
-  u32x4 ra[4], rb[4];
-  auto load_tile = [&](int k0) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ra[j] = *reinterpret_cast<const u32x4*>(a_src[j] + k0);
-      rb[j] = *reinterpret_cast<const u32x4*>(b_src[j] + k0);
-    }
+  // Register slots for the k-steps in flight.  (k-steps past the end re-read
+  // the last one: unconditional loads keep the compiler's count of loads in
+  // flight exact.)
+  struct Slot {
+    u32x4 a[4], b[4];
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = tid + 256 * j;
-      const int row = c >> 3, colb = (c & 7) * 16;
-      *reinterpret_cast<u32x4*>(&s_a[buf][row * kPitch + colb]) = ra[j];
-      *reinterpret_cast<u32x4*>(&s_b[buf][row * kPitch + colb]) = rb[j];
-    }
-  };
-
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   const int k_steps = p.d_model / kBK;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int ks = 0; ks < k_steps; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < k_steps) load_tile((ks + 1) * kBK);
+  auto load_tile = [&](int ks, Slot& r) {
+    const int k0 = min(ks, k_steps - 1) * kBK;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r.a[j] = *reinterpret_cast<const u32x4*>(a_src[j] + k0);
+      r.b[j] = *reinterpret_cast<const u32x4*>(b_src[j] + k0);
+    }
+  };
+  auto store_tile = [&](int buf, const Slot& r) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = tid + 512 * j;
+      const int row = c >> 3, colb = (c & 7) * 16;
+      *reinterpret_cast<u32x4*>(&s_a[buf][row * kPitch + colb]) = r.a[j];
+      *reinterpret_cast<u32x4*>(&s_b[buf][row * kPitch + colb]) = r.b[j];
+    }
+  };
+
+  constexpr int kFM = kWM / 16, kFN = kWN / 16;  // 16 x 16 fragments per wave
+  f32x4 acc[kFM][kFN];
+#pragma unroll
+  for (int i = 0; i < kFM; ++i)
+#pragma unroll
+    for (int j = 0; j < kFN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // One k-step of 64, as two MFMA steps of 32: lane (n, g) of fragment i holds
+  // row 16i + n, k = 32 kk + 8g .. + 7.
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 af[4], bfr[4];
+      bf16x8 af[kFM], bfr[kFN];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kFM; ++i)
         af[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&s_a[buf][(wm + 16 * i + n) * kPitch + kk * 64 + 16 * g]));
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < kFN; ++j)
         bfr[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(&s_b[buf][(wn + 16 * j + n) * kPitch + kk * 64 + 16 * g]));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kFM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16_16x16x32(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < kFN; ++j) acc[i][j] = mfma_bf16_16x16x32(af[i], bfr[j], acc[i][j]);
     }
-    if (ks + 1 < k_steps) {
-      store_tile(buf ^ 1);
-    }
+  };
+  // At the top of k-step ks: LDS buffer ks & 1 holds tile ks and the two
+  // register slots hold tiles ks + 1 and ks + 2 in flight.  After computing
+  // tile ks, tile ks + 1 goes to the other buffer (whose readers finished at
+  // the last barrier) and its slot takes tile ks + 3.  Unrolled by two so
+  // each slot keeps its registers.
+  Slot sa, sb;
+  load_tile(0, sa);
+  load_tile(1, sb);
+  store_tile(0, sa);
+  load_tile(2, sa);
+  __syncthreads();
+  for (int ks = 0;; ks += 2) {
+    compute(0);
+    store_tile(1, sb);
     __syncthreads();
+    if (ks + 1 >= k_steps) break;
+    load_tile(ks + 3, sb);
+    compute(1);
+    store_tile(0, sa);
+    __syncthreads();
+    if (ks + 2 >= k_steps) break;
+    load_tile(ks + 4, sa);
   }
 
-  // Epilogue: D[row 4g + e][col n] of tile (i, j) -> bf16, round to nearest even.
-  uint16_t* out = p.out[nt];
+  // Epilogue: D[row 4g + e][col n] of fragment (i, j) -> bf16, round to
+  // nearest even; column c of the tile belongs to output matrix c / 128.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int j = 0; j < kFN; ++j) {
+    const int col = ct * kBN + wn + 16 * j + n;
+    uint16_t* out = p.out[col >> 7] + (col & (kDim - 1));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t row = m0 + wm + 16 * i + 4 * g + e;
-      if (row >= p.n_tokens) continue;
+    for (int i = 0; i < kFM; ++i) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) out[row * kDim + wn + 16 * j + n] = f32_to_bf16_rne(acc[i][j][e]);
+      for (int e = 0; e < 4; ++e) {
+        const int64_t row = m0 + wm + 16 * i + 4 * g + e;
+        if (row < p.n_tokens) out[row * kDim] = f32_to_bf16_rne(acc[i][j][e]);
+      }
     }
   }
 }
@@ -165,8 +196,8 @@ hipError_t launch_bridge_gemm(const BridgeParams& p, hipStream_t s) {
   if (p.n_tokens == 0) return hipSuccess;
   const int64_t m_tiles = (p.n_tokens + kBM - 1) / kBM;
   const int64_t groups = (m_tiles + 7) / 8;  // row blocks per XCD, rounded up
-  const int64_t blocks = groups * 8 * p.n_out;
-  hipLaunchKernelGGL(bridge_gemm_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p);
+  const int64_t blocks = groups * 8 * (p.n_out * kDim / kBN);
+  hipLaunchKernelGGL(bridge_gemm_kernel, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, p);
   return hipGetLastError();
 }
 
