@@ -117,6 +117,27 @@ __device__ Resolved block_resolve(const uint32_t* hist, int nbins, uint32_t rank
   return r;
 }
 
+// Block-wide exclusive prefix sum of one value per thread (NT threads):
+// lane shuffles within each wave, NT / 64 wave totals through s_scan.
+template <int NT>
+__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_scan) {
+  constexpr int kWaves = NT / 64;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = t >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) s_scan[w] = incl;
+  __syncthreads();
+  uint32_t before = incl - v;
+  for (int w2 = 0; w2 < w; ++w2) before += s_scan[w2];
+  return before;  // s_scan[0 .. NT/64) keeps the wave totals: sync before reusing it
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(256) void select_init_kernel(SelectParams p) {
@@ -417,9 +438,41 @@ __global__ __launch_bounds__(1024) void finish_kernel(SelectParams p) {
     }
   });
   __syncthreads();
-  // Bitonic sort, one position per thread: partners within a wave trade by
-  // lane shuffle, partners in other waves through LDS (the histogram's room,
-  // free by now, as two buffers taken in turn: one barrier per such stage).
+  // Ascending order.  For out-of-window ranges up to 4096 bitmap words (131072
+  // positions), mark the selected positions in a bitmap (in the candidate
+  // room, free by now) and read them back in order: each thread counts the
+  // bits of its run of at most four words, a block scan gives its first
+  // output slot, and it emits its positions.  (Longer runs per thread cost
+  // more in LDS bank conflicts than the sort below.)
+  const uint32_t nwords = (static_cast<uint32_t>(dom) + 31) >> 5;
+  if (nwords <= 4u * 1024u) {
+    uint32_t* bm = reinterpret_cast<uint32_t*>(s_keys);
+    for (uint32_t i = t; i < nwords; i += blockDim.x) bm[i] = 0u;
+    __syncthreads();
+    const int32_t pos = s_sel[t];
+    atomicOr(&bm[pos >> 5], 1u << (pos & 31));
+    __syncthreads();
+    const uint32_t per = (nwords + 1023) >> 10;
+    const uint32_t w0 = t * per, w1 = min(w0 + per, nwords);
+    uint32_t cnt = 0;
+    for (uint32_t w = w0; w < w1; ++w) cnt += __popc(bm[w]);
+    uint32_t slot = block_exclusive_scan<1024>(cnt, s_scan);
+    for (uint32_t w = w0; w < w1; ++w) {
+      uint32_t bits = bm[w];
+      while (bits) {
+        const int bit = __ffs(bits) - 1;
+        bits &= bits - 1;
+        out[slot++] = static_cast<int32_t>(w * 32 + bit);
+      }
+    }
+    if (t < p.window) out[p.top_k + t] = dom + t;
+    if (t == 0) p.sel_count[b] = p.budget;
+    return;
+  }
+  // Otherwise a bitonic sort, one position per thread: partners within a wave
+  // trade by lane shuffle, partners in other waves through LDS (the
+  // histogram's room, free by now, as two buffers taken in turn: one barrier
+  // per such stage).
   int32_t x = s_sel[t];
   int32_t* xbuf = reinterpret_cast<int32_t*>(s_hist);  // [2][kTopK]
   static_assert(kRadixBins >= 2 * kTopK, "two sort buffers fit in the histogram");
