@@ -59,7 +59,7 @@ struct DecodeLayout {
   int chunks_per_seq = 0;
   int splits = 0;
   size_t partials = 0, stats = 0, pstats = 0, spill = 0, score = 0, hist0 = 0, counters = 0, selbuf = 0, cand = 0,
-         shat = 0, tile_stats = 0, cand_idx = 0, sparse = 0, total = 0;
+         shat = 0, tile_stats = 0, tile_ub = 0, cand_idx = 0, sparse = 0, total = 0;
 };
 
 DecodeLayout decode_layout(const hs2_decode_desc& d) {
@@ -90,6 +90,7 @@ DecodeLayout decode_layout(const hs2_decode_desc& d) {
   L.cand_idx = take(N * sizeof(int32_t));
   L.shat = take(N * sizeof(float));
   L.tile_stats = take(((N >> 4) + B + 1) * kHeads * sizeof(float));
+  L.tile_ub = take(((N >> 4) + B + 1) * 2 * sizeof(float));
   L.sparse = take(B * static_cast<size_t>(d.n_sparse_layers > 0 ? d.n_sparse_layers : 1) * L.splits *
                   kPartialFloats * sizeof(float));
   L.total = off;
@@ -255,6 +256,7 @@ SelectParams select_params(const DecodeArgs& a, const DecodeLayout& L, float* sc
   p.cand = reinterpret_cast<unsigned long long*>(ws_at(a.ws, L.cand));
   p.shat = reinterpret_cast<const float*>(ws_at(a.ws, L.shat));
   p.tile_stats = reinterpret_cast<const float*>(ws_at(a.ws, L.tile_stats));
+  p.tile_ub = reinterpret_cast<float*>(ws_at(a.ws, L.tile_ub));
   p.cand_idx = reinterpret_cast<int32_t*>(ws_at(a.ws, L.cand_idx));
   p.k = static_cast<const uint8_t*>(a.k);
   p.k_scale = a.ks;

@@ -69,6 +69,7 @@ struct SelectParams {
   int chunks_per_seq;
   const float* shat;          // [N] (bound mode)
   const float* tile_stats;    // [tile_slots][16] (bound mode)
+  float* tile_ub;             // [tile_slots][2] (bound mode): max over the tile of shat * max_h F_h, and max_h F_h
   float* score;               // [N]
   uint32_t* hist0;            // [B][kRadixBins]: first-digit histogram
   uint32_t* counters;         // [B][4]: winners emitted, candidates seen

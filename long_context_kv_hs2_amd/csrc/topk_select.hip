@@ -531,15 +531,8 @@ __device__ __forceinline__ void tile_factors(const float (&u)[kHeads], const flo
   }
 }
 
-// A tile's 16 shat values (nv of them real) and its 16 per-head u values.
-__device__ __forceinline__ void load_tile_bounds(const SelectParams& p, int64_t base, int b, int tile, int nv,
-                                                 float (&v)[16], float (&u)[kHeads]) {
-  const float4* us = reinterpret_cast<const float4*>(p.tile_stats + tile_slot(base, b, tile) * kHeads);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float4 x = us[q];
-    u[4 * q] = x.x; u[4 * q + 1] = x.y; u[4 * q + 2] = x.z; u[4 * q + 3] = x.w;
-  }
+// A tile's 16 shat values (nv of them real).
+__device__ __forceinline__ void load_tile_shat(const SelectParams& p, int64_t base, int tile, int nv, float (&v)[16]) {
   if ((base & 3) == 0) {  // 16-byte aligned rows
     const float4* sh = reinterpret_cast<const float4*>(p.shat + base + 16 * tile);
 #pragma unroll
@@ -551,6 +544,18 @@ __device__ __forceinline__ void load_tile_bounds(const SelectParams& p, int64_t 
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = p.shat[base + 16 * tile + min(i, nv - 1)];
   }
+}
+
+// ... and its 16 per-head u values.
+__device__ __forceinline__ void load_tile_bounds(const SelectParams& p, int64_t base, int b, int tile, int nv,
+                                                 float (&v)[16], float (&u)[kHeads]) {
+  const float4* us = reinterpret_cast<const float4*>(p.tile_stats + tile_slot(base, b, tile) * kHeads);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 x = us[q];
+    u[4 * q] = x.x; u[4 * q + 1] = x.y; u[4 * q + 2] = x.z; u[4 * q + 3] = x.w;
+  }
+  load_tile_shat(p, base, tile, nv, v);
 }
 
 // The full layer's merge and the bound selection's first pass in one launch.
@@ -626,9 +631,16 @@ __global__ __launch_bounds__(256) void merge_bound_hist_kernel(MergeParams mp, S
   if (valid) {
     float fmin, fmax;
     tile_factors(u, s_mx, s_iz, fmin, fmax);
+    float tmax = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (i < nv) atomicAdd(&s_hist[digit0(v[i] * fmin)], 1u);
+    for (int i = 0; i < 16; ++i) {
+      if (i < nv) {
+        atomicAdd(&s_hist[digit0(v[i] * fmin)], 1u);
+        tmax = fmaxf(tmax, v[i] * fmax);
+      }
+    }
+    // the tile's largest upper bound, so the collection can skip whole tiles
+    *reinterpret_cast<float2*>(p.tile_ub + tile_slot(base, b, tile) * 2) = make_float2(tmax, fmax);
   }
   __syncthreads();
   uint32_t* gh = p.hist0 + static_cast<size_t>(b) * kRadixBins;
@@ -655,14 +667,15 @@ hipError_t launch_merge_bound_hist(const MergeParams& mp, const SelectParams& p,
 // same one): the lower edge of the bin holding the k-th largest lower bound,
 // so at least k positions score at or above it.  It keeps the positions whose
 // upper bound reaches it, so every position of the exact top-k (ties
-// included) is kept; it gathers them in LDS and places them in the sequence's
-// list (room for every position) with one atomic.
+// included) is kept; a tile whose largest upper bound (from the first pass)
+// misses the threshold is skipped without reading its tokens.  The kept
+// positions are gathered in LDS and placed in the sequence's list (room for
+// every position) with one atomic.
 __global__ __launch_bounds__(256) void collect_bound_kernel(SelectParams p) {
   __shared__ uint32_t s_hist[kRadixBins];
   __shared__ uint32_t s_scan[256];
   __shared__ Resolved s_res;
   __shared__ int32_t s_list[kBoundBlockTokens];
-  __shared__ float s_mx[kHeads], s_iz[kHeads];
   __shared__ uint32_t s_cnt, s_base;
   const int b = blockIdx.y;
   int64_t base;
@@ -676,24 +689,41 @@ __global__ __launch_bounds__(256) void collect_bound_kernel(SelectParams p) {
   const int tile = blockIdx.x + t * nb;
   const bool valid = 16 * tile < dom;
   const int nv = min(16, dom - 16 * tile);
-  float v[16], u[kHeads];
-  if (valid) load_tile_bounds(p, base, b, tile, nv, v, u);
+  float2 ubf = make_float2(0.f, 0.f);  // (tile's largest upper bound, its max_h F_h)
+  if (valid) ubf = *reinterpret_cast<const float2*>(p.tile_ub + tile_slot(base, b, tile) * 2);
   const uint32_t* gh = p.hist0 + static_cast<size_t>(b) * kRadixBins;
   for (int i = t; i < kRadixBins; i += 256) s_hist[i] = gh[i];
-  if (t < kHeads) {
-    s_mx[t] = p.stats[(static_cast<int64_t>(b) * kHeads + t) * 2];
-    s_iz[t] = 1.f / p.stats[(static_cast<int64_t>(b) * kHeads + t) * 2 + 1];
-  }
   if (t == 0) s_cnt = 0;
   __syncthreads();
   const Resolved r0 = block_resolve<256>(s_hist, kRadixBins, static_cast<uint32_t>(p.top_k), s_scan, &s_res);
   const float thr = __uint_as_float(static_cast<uint32_t>(r0.digit) << 20) * kLowSlack;
-  if (valid) {
-    float fmin, fmax;
-    tile_factors(u, s_mx, s_iz, fmin, fmax);
+  uint32_t mine = 0;  // bit i: token 16 tile + i is a candidate
+  if (valid && ubf.x * kHighSlack >= thr) {
+    float v[16];
+    load_tile_shat(p, base, tile, nv, v);
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      if (i < nv && v[i] * fmax * kHighSlack >= thr) s_list[atomicAdd(&s_cnt, 1u)] = 16 * tile + i;
+      if (i < nv && v[i] * ubf.y * kHighSlack >= thr) mine |= 1u << i;
+  }
+  // Room in the LDS list: one atomic per wave, lane offsets by a wave prefix
+  // sum (per-candidate atomics on one counter serialise).
+  {
+    const int lane = t & 63;
+    const uint32_t cnt = __popc(mine);
+    uint32_t incl = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    uint32_t wbase = 0;
+    if (lane == 63 && incl) wbase = atomicAdd(&s_cnt, incl);
+    uint32_t slot = __shfl(wbase, 63) + incl - cnt;
+    while (mine) {
+      const int i = __ffs(mine) - 1;
+      mine &= mine - 1;
+      s_list[slot++] = 16 * tile + i;
+    }
   }
   __syncthreads();
   const uint32_t ncand = s_cnt;
