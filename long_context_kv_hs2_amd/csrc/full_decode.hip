@@ -24,7 +24,7 @@
 namespace hs2 {
 
 // BOUND: instead of spilling the 16 logits of each token, keep per token
-// shat_j = sum_h exp2(l_hj - m_h^t) c_h^t with the wave's running max m^t after
+// shat_j = sum_h exp2(l_hj - m_h^t) c_h^t (written as bf16) with the wave's running max m^t after
 // the token's tile and c^t ~ 1 / (running sum z^t), and per tile and head
 // u_h^t = m_h^t - log2 c_h^t.  Then score_j = sum_h a_hj F_h^t with
 // F_h^t = exp2(m_h^t - M_h) / (c_h^t Z_h) = exp2(u_h^t - M_h) / Z_h, so score_j
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
   const float* __restrict__ ksb = FP8 ? p.k_scale + base : nullptr;
   const float* __restrict__ vsb = FP8 ? p.v_scale + base : nullptr;
   float* __restrict__ spill = BOUND ? nullptr : p.spill + base * kHeads;
-  float* __restrict__ shat = BOUND ? p.shat + base : nullptr;
+  uint16_t* __restrict__ shat = BOUND ? p.shat + base : nullptr;
 
   SoftmaxState st;
   softmax_init(st);
@@ -229,10 +229,14 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
       if (ti < ntiles) {
         const float4 v = *reinterpret_cast<const float4*>(wraw + ti * kTileOut + e);
         const int tok = w0 + ti * tile_stride + e;
-        if (tok + 3 < len && (base & 3) == 0) {  // 16-byte aligned: tok is a multiple of 4
-          *reinterpret_cast<float4*>(shat + tok) = v;
+        // bf16, round to nearest even: the selection's slack covers the 2^-9
+        // relative rounding
+        const uint32_t b01 = bf16_rne(v.x) | (bf16_rne(v.y) << 16), b23 = bf16_rne(v.z) | (bf16_rne(v.w) << 16);
+        if (tok + 3 < len && (base & 3) == 0) {  // 8-byte aligned: tok is a multiple of 4
+          *reinterpret_cast<uint2*>(shat + tok) = make_uint2(b01, b23);
         } else {
-          const float vv[4] = {v.x, v.y, v.z, v.w};
+          const uint16_t vv[4] = {static_cast<uint16_t>(b01), static_cast<uint16_t>(b01 >> 16),
+                                  static_cast<uint16_t>(b23), static_cast<uint16_t>(b23 >> 16)};
           for (int u = 0; u < 4 && tok + u < len; ++u) shat[tok + u] = vv[u];
         }
       }

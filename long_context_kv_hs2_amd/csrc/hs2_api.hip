@@ -88,7 +88,7 @@ DecodeLayout decode_layout(const hs2_decode_desc& d) {
   // per position (every candidate's exact key, sequence b's from row base_b)
   L.cand = take(std::max(B * kCandCap, N) * sizeof(unsigned long long));
   L.cand_idx = take(N * sizeof(int32_t));
-  L.shat = take(N * sizeof(float));
+  L.shat = take(N * sizeof(uint16_t));
   L.tile_stats = take(((N >> 4) + B + 1) * kHeads * sizeof(float));
   L.tile_ub = take(((N >> 4) + B + 1) * 2 * sizeof(float));
   L.sparse = take(B * static_cast<size_t>(d.n_sparse_layers > 0 ? d.n_sparse_layers : 1) * L.splits *
@@ -230,7 +230,7 @@ FullParams full_params(const DecodeArgs& a, const DecodeLayout& L) {
   p.partials = reinterpret_cast<float*>(ws_at(a.ws, L.partials));
   p.pstats = reinterpret_cast<float*>(ws_at(a.ws, L.pstats));
   p.spill = reinterpret_cast<float*>(ws_at(a.ws, L.spill));
-  p.shat = reinterpret_cast<float*>(ws_at(a.ws, L.shat));
+  p.shat = reinterpret_cast<uint16_t*>(ws_at(a.ws, L.shat));
   p.tile_stats = reinterpret_cast<float*>(ws_at(a.ws, L.tile_stats));
   p.hist0 = reinterpret_cast<uint32_t*>(ws_at(a.ws, L.hist0));
   p.counters = reinterpret_cast<uint32_t*>(ws_at(a.ws, L.counters));
@@ -254,7 +254,7 @@ SelectParams select_params(const DecodeArgs& a, const DecodeLayout& L, float* sc
   p.counters = reinterpret_cast<uint32_t*>(ws_at(a.ws, L.counters));
   p.selbuf = reinterpret_cast<int32_t*>(ws_at(a.ws, L.selbuf));
   p.cand = reinterpret_cast<unsigned long long*>(ws_at(a.ws, L.cand));
-  p.shat = reinterpret_cast<const float*>(ws_at(a.ws, L.shat));
+  p.shat = reinterpret_cast<const uint16_t*>(ws_at(a.ws, L.shat));
   p.tile_stats = reinterpret_cast<const float*>(ws_at(a.ws, L.tile_stats));
   p.tile_ub = reinterpret_cast<float*>(ws_at(a.ws, L.tile_ub));
   p.cand_idx = reinterpret_cast<int32_t*>(ws_at(a.ws, L.cand_idx));
@@ -376,7 +376,7 @@ hs2_status hs2_decode_block(const hs2_decode_desc* desc, const int64_t* seq_offs
                sel_idx, sel_count, score_out, workspace, static_cast<hipStream_t>(stream)};
   TimingRecord* rec = nullptr;
   HS2_TRY(timing_begin(&rec));
-  // Without a score output the full pass keeps only score bounds (4 + 8 bytes
+  // Without a score output the full pass keeps only score bounds (2 + 4 bytes
   // per token instead of 64 bytes of logits) and the selection rescores the
   // few positions the bounds cannot rule out; with it, every logit is kept and
   // every score computed.  Both give the same scores for the positions that

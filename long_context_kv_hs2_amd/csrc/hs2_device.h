@@ -64,6 +64,12 @@ __device__ __forceinline__ f32x4 mfma_bf16_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 // Byte permute of the pair {hi_word, lo_word}: selector byte i picks byte
 // sel_i of the 8-byte value lo_word | hi_word << 32.
 __device__ __forceinline__ uint32_t perm(uint32_t hi_word, uint32_t lo_word, uint32_t sel) {

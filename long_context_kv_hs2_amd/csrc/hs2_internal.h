@@ -25,7 +25,7 @@ struct FullParams {
   float* partials;           // [B][chunks_per_seq][kPartialFloats]
   float* pstats;             // [B][chunks_per_seq][32]: each partial's (m[16], z[16]) again, packed
   float* spill;              // spill mode: [N][16] log2-domain logits
-  float* shat;               // bound mode: [N] per-token sum over heads of the running-normalised weights
+  uint16_t* shat;            // bound mode: [N] per-token sum over heads of the running-normalised weights, bf16 (RNE)
   float* tile_stats;         // bound mode: [tile_slots][16] per head after each tile: running max - log2(~1/running sum)
   uint32_t* hist0;           // [B][kRadixBins] selection histogram, cleared here
   uint32_t* counters;        // [B][4] selection counters, cleared here
@@ -67,7 +67,7 @@ struct SelectParams {
   const float* stats;         // [B][16][2] global (max, sum) per head
   const float* pstats;        // [B][chunks_per_seq][32] the full pass's partial (m, z)
   int chunks_per_seq;
-  const float* shat;          // [N] (bound mode)
+  const uint16_t* shat;       // [N] bf16 (bound mode)
   const float* tile_stats;    // [tile_slots][16] (bound mode)
   float* tile_ub;             // [tile_slots][2] (bound mode): max over the tile of shat * max_h F_h, and max_h F_h
   float* score;               // [N]

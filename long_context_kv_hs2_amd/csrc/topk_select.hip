@@ -34,16 +34,16 @@
 //     and append the window.
 //
 // Bound mode (no score output): the full pass kept per token
-// shat_j = sum_h a_hj and per 16-token tile the wave's running max and
-// (approximately) reciprocal running sum per head, which bound score_j within
-// shat_j * [min_h F_h, max_h F_h].
-//  1. histogram of the lower bounds' first digit;
+// shat_j = sum_h a_hj (bf16) and per 16-token tile and head
+// u_h = m_h - log2 c_h (its running max and approximate reciprocal running
+// sum), which bound score_j within shat_j * [min_h F_h, max_h F_h].
+//  1. histogram of the lower bounds' first digit (fused with the merge);
 //  2. collect the positions whose upper bound reaches the lower edge of the bin
-//     holding the k-th largest lower bound: at least k positions have a score
-//     at or above that edge, so every position of the exact top-k (ties
-//     included) is collected;
+//     holding the k-th largest lower bound, less the slack: at least k
+//     positions have a score at or above that edge, so every position of the
+//     exact top-k (ties included) is collected;
 //  3. rescore the candidates exactly, with the same arithmetic as the spill
-//     path (every position if the list overflowed);
+//     path;
 //  4. finish as above over the exact candidate keys.
 #include "hs2_device.h"
 #include "hs2_internal.h"
@@ -512,11 +512,12 @@ hipError_t launch_collect_finish(const SelectParams& p, int batch, int64_t max_c
 
 // ---- bound mode ------------------------------------------------------------
 
-// Slack on the pruning threshold and on the upper bounds: far above fp32
-// rounding, the approximate exp2 / log2, and the rounding-order difference
-// between the first pass's own copy of (M_h, Z_h) and the merge's.
-constexpr float kLowSlack = 1.f - 1.f / 1024.f;
-constexpr float kHighSlack = 1.f + 1.f / 1024.f;
+// Slack on the pruning threshold and on the upper bounds: 2^-7, four times
+// the 2^-9 relative rounding of shat to bf16, and far above fp32 rounding, the
+// approximate exp2 / log2, and the rounding-order difference between the
+// first pass's own copy of (M_h, Z_h) and the merge's.
+constexpr float kLowSlack = 1.f - 1.f / 128.f;
+constexpr float kHighSlack = 1.f + 1.f / 128.f;
 
 // Min and max over heads of a tile's bound factors F_h = exp2(u_h - M_h) / Z_h.
 __device__ __forceinline__ void tile_factors(const float (&u)[kHeads], const float* s_mx, const float* s_iz,
@@ -531,18 +532,23 @@ __device__ __forceinline__ void tile_factors(const float (&u)[kHeads], const flo
   }
 }
 
-// A tile's 16 shat values (nv of them real).
+// A tile's 16 shat values (nv of them real), stored as bf16.
 __device__ __forceinline__ void load_tile_shat(const SelectParams& p, int64_t base, int tile, int nv, float (&v)[16]) {
-  if ((base & 3) == 0) {  // 16-byte aligned rows
-    const float4* sh = reinterpret_cast<const float4*>(p.shat + base + 16 * tile);
+  if ((base & 7) == 0) {  // 16-byte aligned rows
+    const uint4* sh = reinterpret_cast<const uint4*>(p.shat + base + 16 * tile);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 x = sh[q];
-      v[4 * q] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
+    for (int q = 0; q < 2; ++q) {
+      const uint4 x = sh[q];
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[8 * q + 2 * k] = __uint_as_float(w[k] << 16);
+        v[8 * q + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+      }
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = p.shat[base + 16 * tile + min(i, nv - 1)];
+    for (int i = 0; i < 16; ++i) v[i] = __uint_as_float(static_cast<uint32_t>(p.shat[base + 16 * tile + min(i, nv - 1)]) << 16);
   }
 }
 
