@@ -57,7 +57,6 @@ int choose_chunk(int64_t total_tokens, int batch) {
 struct DecodeLayout {
   int chunk = 0;
   int chunks_per_seq = 0;
-  int splits = 0;
   size_t partials = 0, stats = 0, pstats = 0, spill = 0, score = 0, hist0 = 0, counters = 0, selbuf = 0, cand = 0,
          shat = 0, tile_stats = 0, tile_ub = 0, cand_idx = 0, sparse = 0, total = 0;
 };
@@ -69,7 +68,6 @@ DecodeLayout decode_layout(const hs2_decode_desc& d) {
   L.chunk = choose_chunk(d.total_tokens, d.batch);
   L.chunks_per_seq = static_cast<int>((d.max_context + L.chunk - 1) / L.chunk);
   if (L.chunks_per_seq < 1) L.chunks_per_seq = 1;
-  L.splits = (kBudget + kSparseRows - 1) / kSparseRows;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -91,8 +89,9 @@ DecodeLayout decode_layout(const hs2_decode_desc& d) {
   L.shat = take(N * sizeof(uint16_t));
   L.tile_stats = take(((N >> 4) + B + 1) * kHeads * sizeof(float));
   L.tile_ub = take(((N >> 4) + B + 1) * 2 * sizeof(float));
-  L.sparse = take(B * static_cast<size_t>(d.n_sparse_layers > 0 ? d.n_sparse_layers : 1) * L.splits *
-                  kPartialFloats * sizeof(float));
+  const int n_sparse = d.n_sparse_layers > 0 ? d.n_sparse_layers : 1;
+  const int slices = sparse_slices(d.batch, n_sparse);
+  L.sparse = take(slices > 1 ? B * n_sparse * static_cast<size_t>(slices) * kPartialFloats * sizeof(float) : 0);
   L.total = off;
   return L;
 }
@@ -316,29 +315,11 @@ hs2_status run_sparse(const DecodeArgs& a, const DecodeLayout& L, const int32_t*
   sp.batch = d.batch;
   sp.n_layers = d.n_sparse_layers;
   sp.budget = d.window + d.top_k;
-  sp.splits = L.splits;
   sp.sel_idx = sel_idx;
   sp.sel_count = sel_count;
+  sp.out = a.o_sparse;
   sp.partials = reinterpret_cast<float*>(ws_at(a.ws, L.sparse));
-  HS2_HIP(launch_sparse_partial(sp, d.kv_dtype == HS2_KV_FP8_E4M3, a.stream), "sparse partial pass");
-  MergeParams mp;
-  mp.seq_offsets = a.offs;
-  mp.total_tokens = d.total_tokens;
-  mp.max_context = d.max_context;
-  mp.budget = sp.budget;
-  mp.partials = sp.partials;
-  mp.chunk = kSparseRows;
-  mp.chunks_per_seq = L.splits;
-  mp.stride_seq = d.n_sparse_layers * L.splits * kPartialFloats;
-  mp.stride_chunk = kPartialFloats;
-  mp.count_from_sel = 1;
-  mp.sel_count = sel_count;
-  mp.out = a.o_sparse;
-  mp.out_stride_seq = kHeads * kDim;
-  mp.stats = nullptr;
-  HS2_HIP(launch_merge_layers(mp, d.batch, d.n_sparse_layers, static_cast<int64_t>(L.splits) * kPartialFloats,
-                              static_cast<int64_t>(d.batch) * kHeads * kDim, a.stream),
-          "sparse merge");
+  HS2_HIP(launch_sparse_attend(sp, d.kv_dtype == HS2_KV_FP8_E4M3, a.stream), "sparse layers");
   return HS2_OK;
 }
 

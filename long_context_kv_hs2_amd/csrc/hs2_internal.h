@@ -52,10 +52,6 @@ struct MergeParams {
   float* stats;              // [B][16][2] (m, z) or nullptr
 };
 hipError_t launch_merge(const MergeParams& p, int batch, hipStream_t s);
-// Same merge for `layers` stacked problems (sparse layers): partials of layer
-// l start at partials + l * stride_layer, outputs at out + l * out_stride_layer.
-hipError_t launch_merge_layers(const MergeParams& p, int batch, int layers, int64_t stride_layer,
-                               int64_t out_stride_layer, hipStream_t s);
 
 // ---- score and token selection ---------------------------------------------
 struct SelectParams {
@@ -104,7 +100,6 @@ hipError_t launch_merge_bound_hist(const MergeParams& mp, const SelectParams& p,
 hipError_t launch_bound_select(const SelectParams& p, int batch, int64_t max_context, bool fp8, hipStream_t s);
 
 // ---- sparse layers -----------------------------------------------------------
-constexpr int kSparseRows = 128;  // selected rows per workgroup
 struct SparseParams {
   const int64_t* seq_offsets;
   int64_t total_tokens;
@@ -118,12 +113,16 @@ struct SparseParams {
   int batch;
   int n_layers;
   int budget;
-  int splits;                 // ceil(budget / kSparseRows)
   const int32_t* sel_idx;     // [B][budget]
   const int32_t* sel_count;   // [B]
-  float* partials;            // [B][n_layers][splits][kPartialFloats]
+  float* out;                 // [n_layers][B][16][128]
+  float* partials;            // [n_layers][B][slices][kPartialFloats] when the selection is sliced
 };
-hipError_t launch_sparse_partial(const SparseParams& p, bool fp8, hipStream_t s);
+constexpr int kSparseFillWorkgroups = 128;  // slice the selection while the grid has fewer workgroups
+// Slices of each (layer, sequence) selection the sparse pass uses (1: no partials, no merge).
+int sparse_slices(int batch, int n_layers);
+// Attention over the selected rows: one launch, plus a merge when sliced.
+hipError_t launch_sparse_attend(const SparseParams& p, bool fp8, hipStream_t s);
 
 // ---- KV bridging ---------------------------------------------------------------
 struct BridgeParams {

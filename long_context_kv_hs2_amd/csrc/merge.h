@@ -1,6 +1,6 @@
-// Split-K merge of one (head, sequence, layer) problem, shared by the merge
-// kernels: the full layer's merge, the same merge fused with the selection's
-// first pass, and the sparse layers' merge.
+// Split-K merge of one (head, sequence) problem of the full layer, shared by
+// the plain merge kernel (score path) and the merge fused with the
+// selection's first pass (bound path), so both give bitwise the same (M, Z).
 //
 // A partial holds a reference max m, the sum z of exp2(l - m) and the
 // unnormalised output O[16][128] of its tokens (log2 domain).  With

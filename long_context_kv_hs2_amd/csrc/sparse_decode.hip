@@ -6,136 +6,251 @@
 // "Luo Fuli Teases Xiaomi MiMo-V3 Architecture", paragraphs on KV Reuse and on
 // token selection).  Each layer takes its softmax over the selected positions.
 //
-// One workgroup per (sequence, slice of 128 selected positions) gathers those
-// K and V rows from HBM into LDS once; its four waves then serve the sparse
-// layers (wave w takes layers w, w+4, ...), all 16 heads at a time, with the
-// same MFMA tile step as the full layer.  Split partials are merged after.
+// Workgroups of eight waves over (sparse layer, sequence, slice).  A workgroup
+// stages its slice of the selected positions in LDS; each wave takes 16 * TILES
+// consecutive selected rows and gathers their K and V rows straight into
+// registers (16-byte loads, a two-tile ring), with the full layer's tile step
+// for all 16 heads.  The eight waves' (m, z, O) are merged through LDS.  With
+// one slice per (layer, sequence) the output is written directly; when the
+// grid would be too small to fill the chip, the selected rows are cut into
+// 2, 4 or 8 slices whose partials a second launch merges.  The layers of a
+// sequence read the same rows at about the same time, so HBM serves each row
+// about once and the other layers hit in cache.
 #include "hs2_device.h"
 #include "hs2_internal.h"
+#include "merge.h"
 
 namespace hs2 {
 
-template <bool FP8>
-__global__ __launch_bounds__(256) void sparse_partial_kernel(SparseParams p) {
-  constexpr int kRowBytes = FP8 ? kDim : 2 * kDim;
-  constexpr int kPitch = kRowBytes + 16;  // pad rows so the 16 row reads of a K fragment spread over banks
-  __shared__ __attribute__((aligned(16))) uint8_t s_k[kSparseRows * kPitch];
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[kSparseRows * kPitch];
-  __shared__ float s_ks[kSparseRows];
-  __shared__ float s_vs[kSparseRows];
+namespace {
+constexpr int kSparseWaves = 8;
+constexpr int kSparseThreads = 64 * kSparseWaves;
+// Slices of the selection when each wave takes `tiles` tiles of 16 rows.
+constexpr int sparse_slices_for(int tiles) {
+  return (kBudget + 16 * kSparseWaves * tiles - 1) / (16 * kSparseWaves * tiles);
+}
+}  // namespace
 
-  const int split = blockIdx.x;
+template <bool FP8, int TILES>
+__global__ __launch_bounds__(kSparseThreads) void sparse_attend_kernel(SparseParams p) {
+  constexpr int kWaveRows = 16 * TILES;
+  constexpr int kSliceRows = kSparseWaves * kWaveRows;
+  __shared__ int32_t s_pos[kSliceRows];
+  __shared__ float s_m[kSparseWaves][kHeads];
+  __shared__ float s_z[kSparseWaves][kHeads];
+  __shared__ __attribute__((aligned(16))) float s_o[kSparseWaves][kHeads][kDim];
+  constexpr int kRowBytes = FP8 ? kDim : 2 * kDim;
+
+  const int layer = blockIdx.x;
   const int b = blockIdx.y;
+  const int slice = blockIdx.z;
+  const int t = threadIdx.x;
   int64_t base;
   int len;
   seq_bounds(p.seq_offsets, b, p.total_tokens, p.max_context, base, len);
   const int count = clamp_count(p.sel_count[b], len, p.budget);
-  const int r0 = split * kSparseRows;
-  if (r0 >= count) return;  // uniform
-  const int rows = min(kSparseRows, count - r0);
-  const int32_t* sel = p.sel_idx + static_cast<size_t>(b) * p.budget + r0;
-
-  // Gather: rows past `rows` copy the last valid row (masked out later).  All
-  // of a thread's loads are issued before any is stored to LDS.
-  constexpr int kChunks = kRowBytes / 16;
-  constexpr int kPer = kSparseRows * kChunks / 256;
-  u32x4 kv[kPer], vv[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int c = threadIdx.x + 256 * i;
-    const int row = c / kChunks;
-    const int part = c % kChunks;
-    const int64_t pos = base + min(max(sel[min(row, rows - 1)], 0), len - 1);
-    kv[i] = *reinterpret_cast<const u32x4*>(p.k + pos * kRowBytes + 16 * part);
-    vv[i] = *reinterpret_cast<const u32x4*>(p.v + pos * kRowBytes + 16 * part);
-  }
-  float ksc = 1.f, vsc = 1.f;
-  if constexpr (FP8) {
-    if (threadIdx.x < kSparseRows) {
-      const int64_t pos = base + min(max(sel[min(static_cast<int>(threadIdx.x), rows - 1)], 0), len - 1);
-      ksc = p.k_scale[pos];
-      vsc = p.v_scale[pos];
+  const int s0 = slice * kSliceRows;  // first selected row of the slice
+  const bool direct = gridDim.z == 1;
+  if (count == 0) {  // uniform: an empty sequence has a zero output
+    if (direct) {
+      float* out = p.out + (static_cast<size_t>(layer) * p.batch + b) * kHeads * kDim;
+      for (int i = t; i < kHeads * kDim; i += kSparseThreads) out[i] = 0.f;
     }
+    return;
   }
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int c = threadIdx.x + 256 * i;
-    const int row = c / kChunks;
-    const int part = c % kChunks;
-    *reinterpret_cast<u32x4*>(s_k + row * kPitch + 16 * part) = kv[i];
-    *reinterpret_cast<u32x4*>(s_v + row * kPitch + 16 * part) = vv[i];
-  }
-  if constexpr (FP8) {
-    if (threadIdx.x < kSparseRows) {
-      s_ks[threadIdx.x] = ksc;
-      s_vs[threadIdx.x] = vsc;
-    }
-  }
+  if (s0 >= count) return;  // uniform: the merge counts only slices with rows
+  // Positions, clamped into the sequence (rows past `count` repeat the last one
+  // and are masked out in the tile step), so every gather stays in the cache.
+  const int32_t* sel = p.sel_idx + static_cast<size_t>(b) * p.budget;
+  for (int i = t; i < kSliceRows; i += kSparseThreads) s_pos[i] = min(max(sel[min(s0 + i, count - 1)], 0), len - 1);
   __syncthreads();
 
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar loop control
-  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform
+  const int lane = t & 63;
   const int n = lane & 15;
   const int g = lane >> 4;
-  for (int layer = wave; layer < p.n_layers; layer += 4) {
+  const int r0 = wave * kWaveRows;                         // within the slice
+  const int rows = min(max(count - s0 - r0, 0), kWaveRows);
+  const int last = count - 1 - s0;                         // last valid slot of s_pos
+  const uint8_t* __restrict__ kbase = p.k + base * kRowBytes;
+  const uint8_t* __restrict__ vbase = p.v + base * kRowBytes;
+  const float* __restrict__ ksb = FP8 ? p.k_scale + base : nullptr;
+  const float* __restrict__ vsb = FP8 ? p.v_scale + base : nullptr;
+
+  struct Raw {
+    u32x4 k[FP8 ? 2 : 4];
+    u32x4 v[4];
+    float ks[4], vs[4];
+  };
+  // Tile t: K lane (n, g) holds selected row r0 + 16t + n at row bytes
+  // kload_offset(j, g); V lane (n, g) holds row r0 + 16t + 4g + r, dims 8n .. 8n + 7.
+  auto load_tile = [&](int tile, Raw& raw) {
+    const int i0 = r0 + 16 * tile;
+    const uint32_t krow = static_cast<uint32_t>(s_pos[min(i0 + n, last)]) * kRowBytes;
+#pragma unroll
+    for (int j = 0; j < (FP8 ? 2 : 4); ++j)
+      raw.k[j] = *reinterpret_cast<const u32x4*>(kbase + (krow + kload_offset(j, g)));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t tv = static_cast<uint32_t>(s_pos[min(i0 + 4 * g + r, last)]);
+      if constexpr (FP8) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(vbase + (tv * kRowBytes + 8 * n));
+        raw.v[r] = u32x4{w[0], w[1], 0u, 0u};
+        raw.ks[r] = ksb[tv];
+        raw.vs[r] = vsb[tv];
+      } else {
+        raw.v[r] = *reinterpret_cast<const u32x4*>(vbase + (tv * kRowBytes + 16 * n));
+        raw.ks[r] = 1.f;
+        raw.vs[r] = 1.f;
+      }
+    }
+  };
+
+  SoftmaxState st;
+  softmax_init(st);
+  if (rows > 0) {  // uniform over the wave
+    Raw ra, rb;
+    load_tile(0, ra);
+    if (TILES > 1) load_tile(1, rb);
     QRegs q;
     load_qregs<FP8>(p.q_sparse + ((static_cast<size_t>(layer) * p.batch + b) * kHeads + n) * kDim, p.qscale, g, q);
-    SoftmaxState st;
-    softmax_init(st);
-    for (int t0 = 0; t0 < rows; t0 += 16) {
-      const int nv = min(16, rows - t0);
+    auto step = [&](int tile, const Raw& cur) {
       bf16x8 kf[4];
-      const uint8_t* krow = s_k + (t0 + n) * kPitch;
       if constexpr (FP8) {
-        e4m3x16_to_bf16(*reinterpret_cast<const u32x4*>(krow + kload_offset(0, g)), kf[0], kf[1]);
-        e4m3x16_to_bf16(*reinterpret_cast<const u32x4*>(krow + kload_offset(1, g)), kf[2], kf[3]);
+        e4m3x16_to_bf16(cur.k[0], kf[0], kf[1]);
+        e4m3x16_to_bf16(cur.k[1], kf[2], kf[3]);
       } else {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) kf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + kload_offset(s, g)));
-      }
-      u32x4 vraw[4];
-      float ks[4], vs[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = t0 + 4 * g + r;
-        if constexpr (FP8) {
-          const u32x2 w = *reinterpret_cast<const u32x2*>(s_v + row * kPitch + 8 * n);
-          vraw[r] = u32x4{w[0], w[1], 0u, 0u};
-          ks[r] = s_ks[row];
-          vs[r] = s_vs[row];
-        } else {
-          vraw[r] = *reinterpret_cast<const u32x4*>(s_v + row * kPitch + 16 * n);
-          ks[r] = 1.f;
-          vs[r] = 1.f;
-        }
+        for (int s = 0; s < 4; ++s) kf[s] = as_bf16x8(cur.k[s]);
       }
       float lg[4], pr[4];
-      attend_tile<FP8>(q, kf, vraw, ks, vs, nv, g, st, lg, pr);
-    }
-    const float z = reduce_z(st.z);
-    float* out = p.partials + ((static_cast<size_t>(b) * p.n_layers + layer) * p.splits + split) * kPartialFloats;
-    if (g == 0) {
-      out[n] = st.m;
-      out[kHeads + n] = z;
-    }
-    // lane (n, g) holds O[head n][dims 32g .. 32g + 31] as o[t][i] -> dim 32g + 8i + t
-    float* orow = out + 2 * kHeads + n * kDim + 32 * g;
+      attend_tile<FP8>(q, kf, cur.v, cur.ks, cur.vs, rows - 16 * tile, g, st, lg, pr);
+    };
+    // Two-slot ring over the wave's tiles, fully unrolled so each slot keeps
+    // its registers; tiles wholly past the wave's rows are skipped.
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float4* o4 = reinterpret_cast<float4*>(orow + 8 * i);
-      o4[0] = make_float4(st.o[0][i], st.o[1][i], st.o[2][i], st.o[3][i]);
-      o4[1] = make_float4(st.o[4][i], st.o[5][i], st.o[6][i], st.o[7][i]);
+    for (int tile = 0; tile < TILES; ++tile) {
+      if (tile & 1) {
+        if (16 * tile < rows) step(tile, rb);
+        if (tile + 2 < TILES) load_tile(tile + 2, rb);
+      } else {
+        if (16 * tile < rows) step(tile, ra);
+        if (tile + 2 < TILES) load_tile(tile + 2, ra);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+  }
+
+  // Merge the waves through LDS (a wave with no rows has m = -inf).
+  const float z = reduce_z(st.z);
+  if (g == 0) {
+    s_m[wave][n] = st.m;
+    s_z[wave][n] = z;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_o[wave][n][32 * g + 8 * i + j] = st.o[j][i];
+  }
+  __syncthreads();
+  const int h = t >> 5;         // 16 heads x 32 threads
+  const int d0 = (t & 31) * 4;  // four dims each
+  float mx = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kSparseWaves; ++w) mx = fmaxf(mx, s_m[w][h]);
+  float zz = 0.f;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < kSparseWaves; ++w) {
+    const float mw = s_m[w][h];
+    if (mw == -INFINITY) continue;
+    const float f = exp2f(mw - mx);
+    zz += s_z[w][h] * f;
+    const float4 o4 = *reinterpret_cast<const float4*>(&s_o[w][h][d0]);
+    acc[0] += o4.x * f;
+    acc[1] += o4.y * f;
+    acc[2] += o4.z * f;
+    acc[3] += o4.w * f;
+  }
+  if (direct) {
+    float* out = p.out + (static_cast<size_t>(layer) * p.batch + b) * kHeads * kDim;
+    *reinterpret_cast<float4*>(out + h * kDim + d0) = make_float4(acc[0] / zz, acc[1] / zz, acc[2] / zz, acc[3] / zz);
+  } else {
+    // Partial of the slice: (m[16], z[16], O[16][128]) unnormalised.
+    float* part = p.partials + ((static_cast<size_t>(layer) * p.batch + b) * gridDim.z + slice) * kPartialFloats;
+    if ((t & 31) == 0) {
+      part[h] = mx;
+      part[kHeads + h] = zz;
+    }
+    *reinterpret_cast<float4*>(part + 2 * kHeads + h * kDim + d0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
   }
 }
 
-hipError_t launch_sparse_partial(const SparseParams& p, bool fp8, hipStream_t s) {
+__global__ __launch_bounds__(kMergeThreads) void sparse_merge_kernel(MergeParams p, int64_t stride_layer,
+                                                                     int64_t out_stride_layer) {
+  __shared__ MergeShared sh;
+  merge_one(p, blockIdx.x, blockIdx.y, blockIdx.z, stride_layer, out_stride_layer, sh);
+}
+
+// Tiles per wave: 9 (one slice per layer and sequence, output written
+// directly), else 5, 3, 2 or 1 (2, 3, 5 or 9 slices), the most tiles that
+// still give the grid at least kSparseFillWorkgroups workgroups.
+int sparse_wave_tiles(int batch, int n_layers) {
+  const int64_t wgs = static_cast<int64_t>(batch) * n_layers;
+  for (const int tiles : {9, 5, 3, 2})
+    if (wgs * sparse_slices_for(tiles) >= kSparseFillWorkgroups) return tiles;
+  return 1;
+}
+
+template <bool FP8, int TILES>
+static void launch_tiles(const SparseParams& p, hipStream_t s) {
+  const dim3 grid(p.n_layers, p.batch, sparse_slices_for(TILES));
+  hipLaunchKernelGGL((sparse_attend_kernel<FP8, TILES>), grid, dim3(kSparseThreads), 0, s, p);
+}
+
+template <bool FP8>
+static void launch_fp(const SparseParams& p, int tiles, hipStream_t s) {
+  switch (tiles) {
+    case 9: launch_tiles<FP8, 9>(p, s); break;
+    case 5: launch_tiles<FP8, 5>(p, s); break;
+    case 3: launch_tiles<FP8, 3>(p, s); break;
+    case 2: launch_tiles<FP8, 2>(p, s); break;
+    default: launch_tiles<FP8, 1>(p, s); break;
+  }
+}
+
+int sparse_slices(int batch, int n_layers) { return sparse_slices_for(sparse_wave_tiles(batch, n_layers)); }
+
+hipError_t launch_sparse_attend(const SparseParams& p, bool fp8, hipStream_t s) {
   if (p.batch == 0 || p.n_layers == 0) return hipSuccess;
-  const dim3 grid(p.splits, p.batch);
+  static_assert(sparse_slices_for(9) == 1, "nine tiles per wave cover the whole selection");
+  const int tiles = sparse_wave_tiles(p.batch, p.n_layers);
+  const int slices = sparse_slices_for(tiles);
+  if (slices > 1 && p.partials == nullptr) return hipErrorInvalidValue;
   if (fp8)
-    hipLaunchKernelGGL(sparse_partial_kernel<true>, grid, dim3(256), 0, s, p);
+    launch_fp<true>(p, tiles, s);
   else
-    hipLaunchKernelGGL(sparse_partial_kernel<false>, grid, dim3(256), 0, s, p);
+    launch_fp<false>(p, tiles, s);
+  const hipError_t e = hipGetLastError();
+  if (slices == 1 || e != hipSuccess) return e;
+  MergeParams mp{};
+  mp.seq_offsets = p.seq_offsets;
+  mp.total_tokens = p.total_tokens;
+  mp.max_context = p.max_context;
+  mp.budget = p.budget;
+  mp.partials = p.partials;
+  mp.chunk = 16 * kSparseWaves * tiles;  // selected rows per slice
+  mp.chunks_per_seq = slices;
+  mp.stride_seq = slices * kPartialFloats;
+  mp.stride_chunk = kPartialFloats;
+  mp.count_from_sel = 1;
+  mp.sel_count = p.sel_count;
+  mp.out = p.out;
+  mp.out_stride_seq = kHeads * kDim;
+  mp.stats = nullptr;
+  hipLaunchKernelGGL(sparse_merge_kernel, dim3(kHeads, p.batch, p.n_layers), dim3(kMergeThreads), 0, s, mp,
+                     static_cast<int64_t>(p.batch) * slices * kPartialFloats,
+                     static_cast<int64_t>(p.batch) * kHeads * kDim);
   return hipGetLastError();
 }
 
