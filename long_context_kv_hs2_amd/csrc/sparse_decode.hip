@@ -6,7 +6,7 @@
 // "Luo Fuli Teases Xiaomi MiMo-V3 Architecture", paragraphs on KV Reuse and on
 // token selection).  Each layer takes its softmax over the selected positions.
 //
-// Workgroups of eight waves over (sparse layer, sequence, slice).  A workgroup
+// Workgroups of eight waves over (sequence, sparse layer, slice).  A workgroup
 // stages its slice of the selected positions in LDS; each wave takes 16 * TILES
 // consecutive selected rows and gathers their K and V rows straight into
 // registers (16-byte loads, a two-tile ring), with the full layer's tile step
@@ -41,18 +41,26 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_attend_kernel(SparsePar
   __shared__ __attribute__((aligned(16))) float s_o[kSparseWaves][kHeads][kDim];
   constexpr int kRowBytes = FP8 ? kDim : 2 * kDim;
 
-  const int layer = blockIdx.x;
-  const int b = blockIdx.y;
-  const int slice = blockIdx.z;
+  // Work item j = (b * n_layers + layer) * slices + slice.  Consecutive items
+  // go to one XCD (workgroup id i runs on XCD i % 8), so the layers and slices
+  // of a sequence share that XCD's L2 when they gather the same rows.
+  constexpr int kSlices = sparse_slices_for(TILES);
+  const int items = p.batch * p.n_layers * kSlices;
+  const int per_xcd = (items + 7) / 8;
+  const int j = static_cast<int>(blockIdx.x & 7) * per_xcd + static_cast<int>(blockIdx.x >> 3);
+  if (j >= items) return;  // uniform
+  const int slice = j % kSlices;
+  const int layer = (j / kSlices) % p.n_layers;
+  const int b = j / (kSlices * p.n_layers);
   const int t = threadIdx.x;
   int64_t base;
   int len;
   seq_bounds(p.seq_offsets, b, p.total_tokens, p.max_context, base, len);
   const int count = clamp_count(p.sel_count[b], len, p.budget);
   const int s0 = slice * kSliceRows;  // first selected row of the slice
-  const bool direct = gridDim.z == 1;
+  constexpr bool direct = kSlices == 1;
   if (count == 0) {  // uniform: an empty sequence has a zero output
-    if (direct) {
+    if constexpr (direct) {
       float* out = p.out + (static_cast<size_t>(layer) * p.batch + b) * kHeads * kDim;
       for (int i = t; i < kHeads * kDim; i += kSparseThreads) out[i] = 0.f;
     }
@@ -172,12 +180,12 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_attend_kernel(SparsePar
     acc[2] += o4.z * f;
     acc[3] += o4.w * f;
   }
-  if (direct) {
+  if constexpr (direct) {
     float* out = p.out + (static_cast<size_t>(layer) * p.batch + b) * kHeads * kDim;
     *reinterpret_cast<float4*>(out + h * kDim + d0) = make_float4(acc[0] / zz, acc[1] / zz, acc[2] / zz, acc[3] / zz);
   } else {
     // Partial of the slice: (m[16], z[16], O[16][128]) unnormalised.
-    float* part = p.partials + ((static_cast<size_t>(layer) * p.batch + b) * gridDim.z + slice) * kPartialFloats;
+    float* part = p.partials + ((static_cast<size_t>(layer) * p.batch + b) * kSlices + slice) * kPartialFloats;
     if ((t & 31) == 0) {
       part[h] = mx;
       part[kHeads + h] = zz;
@@ -204,7 +212,8 @@ int sparse_wave_tiles(int batch, int n_layers) {
 
 template <bool FP8, int TILES>
 static void launch_tiles(const SparseParams& p, hipStream_t s) {
-  const dim3 grid(p.n_layers, p.batch, sparse_slices_for(TILES));
+  const int items = p.batch * p.n_layers * sparse_slices_for(TILES);
+  const dim3 grid(static_cast<unsigned>(8 * ((items + 7) / 8)));
   hipLaunchKernelGGL((sparse_attend_kernel<FP8, TILES>), grid, dim3(kSparseThreads), 0, s, p);
 }
 
