@@ -83,7 +83,8 @@ struct SelectParams {
 constexpr int kRadixBins = 2048;
 constexpr int kScoreBlockTokens = 2048;   // tokens per score-pass workgroup
 constexpr int kCollectBlockTokens = 8192; // tokens per collect workgroup
-constexpr int kBoundBlockTokens = 4096;   // tokens per bound-pass workgroup (one 16-token tile per thread)
+constexpr int kBoundBlockTokens = 4096;   // tokens per collect workgroup (one 16-token tile per thread)
+constexpr int64_t kHistLongContext = 1 << 19;  // longer: two tiles per thread in the lower-bound histogram
 constexpr int kRefineBlocks = 32;         // rescoring workgroups per sequence
 constexpr int kCandCap = 32768;           // threshold-bin keys kept per sequence (spill mode)
 hipError_t launch_select_init(const SelectParams& p, int batch, hipStream_t s);

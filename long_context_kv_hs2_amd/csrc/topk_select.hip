@@ -567,11 +567,14 @@ __device__ __forceinline__ void load_tile_bounds(const SelectParams& p, int64_t 
 // The full layer's merge and the bound selection's first pass in one launch.
 // Workgroups x < 16 merge head x of sequence y and write its (M, Z).  The
 // others histogram the first digit of the lower bounds lb_j = shat_j min_h F_h
-// over a block of kBoundBlockTokens out-of-window positions (one 16-token tile
-// per thread), with (M_h, Z_h) recomputed from the partials' (m, z), read
+// over a block of 4096 * TILES out-of-window positions (TILES 16-token tiles
+// per thread: two for very long sequences, whose many workgroups otherwise
+// queue on the global atomics of the sequence's one histogram), with (M_h, Z_h) recomputed from the partials' (m, z), read
 // from the full pass's packed copy: the merge's result is not written yet,
 // and the two differ by rounding order only, which the slack covers.
+template <int TILES>
 __global__ __launch_bounds__(256) void merge_bound_hist_kernel(MergeParams mp, SelectParams p) {
+  constexpr int kBlockTokens = 16 * 256 * TILES;
   __shared__ MergeShared msh;
   __shared__ uint32_t s_hist[kRadixBins];
   __shared__ float s_mx[kHeads], s_iz[kHeads];
@@ -585,14 +588,16 @@ __global__ __launch_bounds__(256) void merge_bound_hist_kernel(MergeParams mp, S
   seq_bounds(p.seq_offsets, b, p.total_tokens, p.max_context, base, len);
   if (len <= p.budget) return;
   const int dom = len - p.window;
-  const int j0 = (blockIdx.x - kHeads) * kBoundBlockTokens;
+  const int j0 = (blockIdx.x - kHeads) * kBlockTokens;
   if (j0 >= dom) return;
   const int t = threadIdx.x;
-  const int tile = (j0 >> 4) + t;
-  const bool valid = 16 * tile < dom;
-  const int nv = min(16, dom - 16 * tile);
-  float v[16], u[kHeads];
-  if (valid) load_tile_bounds(p, base, b, tile, nv, v, u);
+  // TILES tiles per thread, 256 tiles apart, all loads issued up front.
+  float v[TILES][16], u[TILES][kHeads];
+#pragma unroll
+  for (int k = 0; k < TILES; ++k) {
+    const int tile = (j0 >> 4) + t + 256 * k;
+    if (16 * tile < dom) load_tile_bounds(p, base, b, tile, min(16, dom - 16 * tile), v[k], u[k]);
+  }
   for (int i = t; i < kRadixBins; i += 256) s_hist[i] = 0;
   {
     // (M_h, Z_h): 16 lanes per head, partials c = l, l + 16, ..., eight
@@ -634,15 +639,19 @@ __global__ __launch_bounds__(256) void merge_bound_hist_kernel(MergeParams mp, S
     }
   }
   __syncthreads();
-  if (valid) {
+#pragma unroll
+  for (int k = 0; k < TILES; ++k) {
+    const int tile = (j0 >> 4) + t + 256 * k;
+    if (16 * tile >= dom) continue;
+    const int nv = min(16, dom - 16 * tile);
     float fmin, fmax;
-    tile_factors(u, s_mx, s_iz, fmin, fmax);
+    tile_factors(u[k], s_mx, s_iz, fmin, fmax);
     float tmax = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (i < nv) {
-        atomicAdd(&s_hist[digit0(v[i] * fmin)], 1u);
-        tmax = fmaxf(tmax, v[i] * fmax);
+        atomicAdd(&s_hist[digit0(v[k][i] * fmin)], 1u);
+        tmax = fmaxf(tmax, v[k][i] * fmax);
       }
     }
     // the tile's largest upper bound, so the collection can skip whole tiles
@@ -659,8 +668,15 @@ __global__ __launch_bounds__(256) void merge_bound_hist_kernel(MergeParams mp, S
 hipError_t launch_merge_bound_hist(const MergeParams& mp, const SelectParams& p, int batch, int64_t max_context,
                                    hipStream_t s) {
   if (batch == 0) return hipSuccess;
-  const unsigned blocks = static_cast<unsigned>((max_context + kBoundBlockTokens - 1) / kBoundBlockTokens);
-  hipLaunchKernelGGL(merge_bound_hist_kernel, dim3(kHeads + blocks, batch), dim3(256), 0, s, mp, p);
+  // Two tiles per thread only past kHistLongContext tokens: elsewhere the
+  // extra parallelism of one tile per thread wins.
+  const int tiles = max_context > kHistLongContext ? 2 : 1;
+  const int64_t block_tokens = 16 * 256 * tiles;
+  const dim3 grid(static_cast<unsigned>(kHeads + (max_context + block_tokens - 1) / block_tokens), batch);
+  if (tiles == 2)
+    hipLaunchKernelGGL(merge_bound_hist_kernel<2>, grid, dim3(256), 0, s, mp, p);
+  else
+    hipLaunchKernelGGL(merge_bound_hist_kernel<1>, grid, dim3(256), 0, s, mp, p);
   return hipGetLastError();
 }
 
