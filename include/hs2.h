@@ -157,15 +157,19 @@ hs2_status hs2_bridge_kv(int64_t n_tokens, int32_t d_model, int32_t head_dim, in
                          void* const* k_out, void* const* v_out,
                          void* workspace, size_t workspace_bytes, void* stream);
 
-/* Per-stage kernel timing of hs2_decode_block, for benchmarks.  While
- * enabled, each call records HIP events around its stages on its stream
+/* Per-stage kernel timing of hs2_decode_block, for benchmarks.  Mode 1:
+ * each call records HIP events around its stages on its stream
  * (HS2_N_STAGES stages: 0 full-attention partial pass, 1 full-attention
- * merge, 2 score and selection, 3 sparse layers).  hs2_stage_timing_read
- * waits for the recorded events and returns, per stage, the mean duration in
- * milliseconds over the calls recorded since the last read (at most 1024),
- * and the number of calls in *n_calls; it then clears the record.           */
+ * merge, 2 score and selection, 3 sparse layers).  Mode 2: only the two
+ * events around stage 0 (each marker costs the step about 1.5 us).  Mode 0:
+ * off.  Other modes: HS2_ERR_INVALID_ARGUMENT.  The events are timing-only
+ * (no system-scope fence).  hs2_stage_timing_read waits for the recorded
+ * events and returns, per stage, the mean duration in milliseconds over the
+ * calls recorded since the last read (at most 1024; 0 for stages a call did
+ * not record), and the number of calls in *n_calls; it then clears the
+ * record.                                                                  */
 #define HS2_N_STAGES 4
-hs2_status hs2_stage_timing_enable(int32_t on);
+hs2_status hs2_stage_timing_enable(int32_t mode);
 hs2_status hs2_stage_timing_read(float* mean_ms /* [HS2_N_STAGES] (host) */, int32_t* n_calls);
 
 const char* hs2_status_string(hs2_status status);

@@ -167,9 +167,10 @@ uint8_t* ws_at(void* ws, size_t off) { return static_cast<uint8_t*>(ws) + off; }
 // ---- stage timing -------------------------------------------------------------
 struct TimingRecord {
   hipEvent_t ev[HS2_N_STAGES + 1];
+  int last;  // events ev[0 .. last] are recorded
 };
 std::mutex g_timing_mu;
-bool g_timing_on = false;
+int32_t g_timing_mode = 0;  // 0 off, 1 every stage, 2 the full-attention partial pass only
 std::vector<TimingRecord> g_records;
 int g_records_used = 0;
 constexpr int kMaxRecords = 1024;
@@ -178,18 +179,23 @@ constexpr int kMaxRecords = 1024;
 hs2_status timing_begin(TimingRecord** out) {
   *out = nullptr;
   std::lock_guard<std::mutex> lock(g_timing_mu);
-  if (!g_timing_on || g_records_used >= kMaxRecords) return HS2_OK;
+  if (g_timing_mode == 0 || g_records_used >= kMaxRecords) return HS2_OK;
   if (g_records_used == static_cast<int>(g_records.size())) {
     TimingRecord r;
-    for (int i = 0; i <= HS2_N_STAGES; ++i) HS2_HIP(hipEventCreate(&r.ev[i]), "hipEventCreate");
+    // Timing-only events: no system-scope fence (a cache writeback and
+    // invalidate) when each is recorded, so the markers neither slow the step
+    // nor add that writeback to the stage before them.
+    for (int i = 0; i <= HS2_N_STAGES; ++i)
+      HS2_HIP(hipEventCreateWithFlags(&r.ev[i], hipEventDisableSystemFence), "hipEventCreateWithFlags");
     g_records.push_back(r);
   }
   *out = &g_records[g_records_used++];
+  (*out)->last = g_timing_mode == 2 ? 1 : HS2_N_STAGES;
   return HS2_OK;
 }
 
 hs2_status mark(TimingRecord* rec, int i, hipStream_t s) {
-  if (rec) HS2_HIP(hipEventRecord(rec->ev[i], s), "hipEventRecord");
+  if (rec && i <= rec->last) HS2_HIP(hipEventRecord(rec->ev[i], s), "hipEventRecord");
   return HS2_OK;
 }
 
@@ -490,9 +496,10 @@ hs2_status hs2_bridge_kv(int64_t n_tokens, int32_t d_model, int32_t head_dim, in
   return HS2_OK;
 }
 
-hs2_status hs2_stage_timing_enable(int32_t on) {
+hs2_status hs2_stage_timing_enable(int32_t mode) {
+  if (mode < 0 || mode > 2) return fail(HS2_ERR_INVALID_ARGUMENT, "timing mode %d (0, 1 or 2)", mode);
   std::lock_guard<std::mutex> lock(g_timing_mu);
-  g_timing_on = on != 0;
+  g_timing_mode = mode;
   return HS2_OK;
 }
 
@@ -501,8 +508,9 @@ hs2_status hs2_stage_timing_read(float* mean_ms, int32_t* n_calls) {
   std::lock_guard<std::mutex> lock(g_timing_mu);
   double sum[HS2_N_STAGES] = {0, 0, 0, 0};
   for (int r = 0; r < g_records_used; ++r) {
-    HS2_HIP(hipEventSynchronize(g_records[r].ev[HS2_N_STAGES]), "hipEventSynchronize");
-    for (int sidx = 0; sidx < HS2_N_STAGES; ++sidx) {
+    const int last = g_records[r].last;
+    HS2_HIP(hipEventSynchronize(g_records[r].ev[last]), "hipEventSynchronize");
+    for (int sidx = 0; sidx < last; ++sidx) {
       float ms = 0.f;
       HS2_HIP(hipEventElapsedTime(&ms, g_records[r].ev[sidx], g_records[r].ev[sidx + 1]), "hipEventElapsedTime");
       sum[sidx] += ms;

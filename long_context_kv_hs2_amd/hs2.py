@@ -227,8 +227,9 @@ def bridge_kv(hidden, w_k, w_v, k_out=None, v_out=None, workspace=None):
     return k_out, v_out
 
 
-def stage_timing(on: bool):
-    check(load().hs2_stage_timing_enable(1 if on else 0))
+def stage_timing(on: bool, full_pass_only: bool = False):
+    """Record HIP events around the decode stages (or only around the full pass)."""
+    check(load().hs2_stage_timing_enable(0 if not on else 2 if full_pass_only else 1))
 
 
 def stage_timing_read():

@@ -142,3 +142,18 @@ def test_status_strings():
     assert lib.hs2_status_string(0) == b"HS2_OK"
     assert lib.hs2_status_string(3) == b"HS2_ERR_WORKSPACE_TOO_SMALL"
     assert lib.hs2_status_string(99) == b"HS2_UNKNOWN_STATUS"
+
+
+def test_stage_timing_modes():
+    # mode 0 off, 1 every stage, 2 the full pass only; nothing recorded yet,
+    # so reading makes no HIP call and returns zeros.
+    lib = hs2.load()
+    assert lib.hs2_stage_timing_enable(3) == INVALID
+    assert lib.hs2_stage_timing_enable(-1) == INVALID
+    for mode in (2, 1, 0):
+        assert lib.hs2_stage_timing_enable(mode) == 0
+    out = (ctypes.c_float * hs2.N_STAGES)()
+    n = ctypes.c_int32(-1)
+    assert lib.hs2_stage_timing_read(out, ctypes.byref(n)) == 0
+    assert n.value == 0 and list(out) == [0.0] * hs2.N_STAGES
+    assert lib.hs2_stage_timing_read(None, ctypes.byref(n)) == INVALID
