@@ -33,7 +33,6 @@ namespace hs2 {
 // Bound-mode outputs of one wave's tiles wait in LDS until the loop ends: on
 // CDNA loads and stores share one in-order completion counter, so stores in
 // the streaming loop would put their write latency into every load wait.
-constexpr int kMaxWaveTiles = kMaxChunk / 64;
 constexpr int kTileOut = 2 * kHeads;  // shat[16], u[16]
 
 // Work item wg of the 1-D grid: the non-empty (sequence, chunk) pairs of the
@@ -72,6 +71,7 @@ __device__ bool find_work(const FullParams& p, int wg, int& b, int& c) {
 
 template <bool FP8, bool BOUND>
 __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
+  constexpr int kMaxWaveTiles = max_chunk(FP8) / 64;
   __shared__ float s_m[4][kHeads];
   __shared__ float s_z[4][kHeads];
   // the merge buffer O[4][16][128] and, before it, the bound-mode tile outputs

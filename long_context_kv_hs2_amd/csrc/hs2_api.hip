@@ -39,19 +39,26 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 // Tokens per full-attention workgroup.  The pass runs best as one round of
-// workgroups, two per CU of a 256-CU part: a workgroup's end (writing its
-// per-tile outputs, merging its waves) overlaps no streaming, so it should
-// happen once, and a partly filled second round would leave CUs idle.  A
-// batch takes sum_b ceil(L_b / chunk) < N / chunk + B workgroups, so
-// chunk >= N / (512 - B) keeps them within 512.  Chunks are multiples of 64
-// tokens (four waves of 16-token tiles) in [256, kMaxChunk].  The choice
-// affects speed only, never results.
-int choose_chunk(int64_t total_tokens, int batch) {
-  constexpr int64_t kSlots = 512;
-  const int64_t denom = std::max<int64_t>(kSlots - batch, kSlots / 4);
+// workgroups: a workgroup's end (writing its per-tile outputs, merging its
+// waves) overlaps no streaming, so it should happen once, and a partly filled
+// second round would leave CUs idle.  With a bf16 cache the round is one
+// workgroup per CU of a 256-CU part: two co-resident workgroups progress
+// unevenly (on each SIMD the older wave's loads are served first, about 2.3x
+// as fast), so the younger one streams its last ~quarter alone at a lower
+// rate; one workgroup's four waves, one per SIMD, keep pace with each other.
+// An E4M3 tile carries half the bytes per load, and one workgroup per CU
+// keeps too few in flight, so E4M3 runs two per CU.  A batch takes
+// sum_b ceil(L_b / chunk) < N / chunk + B workgroups, so
+// chunk >= N / (slots - B) keeps them within the round.  Chunks are multiples
+// of 64 tokens (four waves of 16-token tiles) in [256, max_chunk].  The
+// choice affects speed, and the rounding of the outputs (never the
+// selection), and depends on nothing but N, B and the cache type.
+int choose_chunk(int64_t total_tokens, int batch, bool fp8) {
+  const int64_t slots = fp8 ? 512 : 256;
+  const int64_t denom = std::max<int64_t>(slots - batch, slots / 4);
   int64_t c = (total_tokens + denom - 1) / denom;
   c = (c + 63) / 64 * 64;
-  return static_cast<int>(std::min<int64_t>(std::max<int64_t>(c, 256), kMaxChunk));
+  return static_cast<int>(std::min<int64_t>(std::max<int64_t>(c, 256), max_chunk(fp8)));
 }
 
 struct DecodeLayout {
@@ -65,7 +72,7 @@ DecodeLayout decode_layout(const hs2_decode_desc& d) {
   DecodeLayout L;
   const size_t B = static_cast<size_t>(d.batch);
   const size_t N = static_cast<size_t>(d.total_tokens);
-  L.chunk = choose_chunk(d.total_tokens, d.batch);
+  L.chunk = choose_chunk(d.total_tokens, d.batch, d.kv_dtype == HS2_KV_FP8_E4M3);
   L.chunks_per_seq = static_cast<int>((d.max_context + L.chunk - 1) / L.chunk);
   if (L.chunks_per_seq < 1) L.chunks_per_seq = 1;
   size_t off = 0;

@@ -8,7 +8,11 @@
 namespace hs2 {
 
 // ---- full-attention layer: split-K partial pass and merge -------------------
-constexpr int kMaxChunk = 8192;  // most tokens one full-attention workgroup takes
+// Most tokens one full-attention workgroup takes: bf16 caches run one
+// workgroup per CU, E4M3 caches two (their bound-mode LDS is sized by this).
+constexpr int kMaxChunkBf16 = 16384;
+constexpr int kMaxChunkFp8 = 8192;
+constexpr int max_chunk(bool fp8) { return fp8 ? kMaxChunkFp8 : kMaxChunkBf16; }
 struct FullParams {
   const int64_t* seq_offsets;
   int64_t total_tokens;
