@@ -40,7 +40,9 @@ HBM_PEAK_GBS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_PROFILE = {2: "profiles/full_partial_b32_ctx128k_bf16_hbm_traffic.md",
                    3: "profiles/full_partial_b4_ctx1m_fp8_hbm_traffic.md"}
-KERNEL_SOURCES = ("long_context_kv_hs2_amd/csrc/full_decode.hip", "long_context_kv_hs2_amd/csrc/hs2_device.h")
+# the kernel and what sets its launch (chunk size, grid)
+KERNEL_SOURCES = ("long_context_kv_hs2_amd/csrc/full_decode.hip", "long_context_kv_hs2_amd/csrc/hs2_device.h",
+                  "long_context_kv_hs2_amd/csrc/hs2_internal.h", "long_context_kv_hs2_amd/csrc/hs2_api.hip")
 METRIC = "hybrid-block decode tokens/s at 128K/1M ctx; achieved HBM GB/s vs peak"
 WORKLOADS = {2: "b32_ctx128k_bf16", 3: "b4_ctx1m_fp8", 4: "b64_ragged_2k_256k_bf16",
              5: "bridge_262144x4096_3layers_then_b8x32k_decode"}
