@@ -69,13 +69,23 @@ __device__ bool find_work(const FullParams& p, int wg, int& b, int& c) {
   return false;
 }
 
+// Waves per workgroup and tile streams per workgroup (see the kernel).
+template <bool FP8> constexpr int full_waves() { return FP8 ? 8 : 4; }
+template <bool FP8> constexpr int full_streams() { return FP8 ? 28 : 4; }
+
 template <bool FP8, bool BOUND>
-__global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
-  constexpr int kMaxWaveTiles = max_chunk(FP8) / 64;
-  __shared__ float s_m[4][kHeads];
-  __shared__ float s_z[4][kHeads];
-  // the merge buffer O[4][16][128] and, before it, the bound-mode tile outputs
-  __shared__ __attribute__((aligned(16))) float s_raw[BOUND ? 4 * kMaxWaveTiles * kTileOut : 4 * kHeads * kDim];
+__global__ __launch_bounds__(64 * full_waves<FP8>()) void full_partial_kernel(FullParams p) {
+  constexpr int kWaves = full_waves<FP8>();
+  constexpr int kStreams = full_streams<FP8>();
+  constexpr int kThreads = 64 * kWaves;
+  // Tiles of one workgroup (bound-mode LDS slots), and of one wave (a bound
+  // for the flush loop): a workgroup holds at most chunk / 16 + kStreams.
+  constexpr int kLocalTiles = max_chunk(FP8) / 16 + kStreams;
+  constexpr int kMaxWaveTiles = ((FP8 ? 4 : 1) * (max_chunk(FP8) / (16 * kStreams) + 1) + 15) / 16 * 16;
+  __shared__ float s_m[kWaves][kHeads];
+  __shared__ float s_z[kWaves][kHeads];
+  // the merge buffer O[kWaves][16][128] and, before it, the bound-mode tile outputs
+  __shared__ __attribute__((aligned(16))) float s_raw[BOUND ? kLocalTiles * kTileOut : kWaves * kHeads * kDim];
   __shared__ u32x4 s_q[kQLdsVecs];
   float(*s_o)[kHeads][kDim] = reinterpret_cast<float(*)[kHeads][kDim]>(s_raw);
 
@@ -91,15 +101,32 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;
   const int g = lane >> 4;
-  // Tiles of 16 tokens are dealt round-robin over all waves of the sequence's
-  // workgroups (tile 4c + w + k * 4 * nblk), so at any moment they stream one
-  // compact region of the cache (better DRAM locality than a contiguous range
-  // per wave).  The split-K merge does not depend on which tokens a partial holds.
+  // Tiles of 16 tokens are dealt round-robin over the tile streams of all the
+  // sequence's workgroups (tile kStreams * (k * nblk + c) + v is the k-th of
+  // stream v of workgroup c), so at any moment they stream one compact region
+  // of the cache (better DRAM locality than a contiguous range per wave).
+  // With a bf16 cache each of the four waves (one per SIMD) takes one stream.
+  // With E4M3 two waves share each SIMD, and the older one's loads are served
+  // about 4/3 as fast, so on each SIMD the older wave takes four streams and
+  // the younger three of seven: the two finish together.  A wave visits its
+  // streams' k-th tiles in stream order, then the (k + 1)-th.  The split-K
+  // merge does not depend on which tokens a partial holds.
   const int nblk = (len + p.chunk - 1) / p.chunk;
-  const int tile_stride = 16 * 4 * nblk;
-  const int w0 = 16 * (4 * c + wave);
-  const int nt = w0 < len ? (len - 1 - w0) / tile_stride + 1 : 0;  // this wave's tiles
-  auto tok0 = [&](int k) { return k < nt ? w0 + k * tile_stride : len; };  // len: past the end
+  const int simd = FP8 ? (wave & 3) : wave;
+  const int per = FP8 ? (wave < 4 ? 4 : 3) : 1;                 // streams of this wave
+  const int v0 = FP8 ? 7 * simd + (wave < 4 ? 0 : 4) : wave;    // its first stream
+  const int stream_stride = 16 * kStreams * nblk;               // tokens between a stream's tiles
+  int nt = 0;                                                   // this wave's tiles
+  for (int j = 0; j < per; ++j) {
+    const int s0 = 16 * (kStreams * c + v0 + j);
+    nt += s0 < len ? (len - 1 - s0) / stream_stride + 1 : 0;
+  }
+  // The i-th tile of the wave; a wave's tiles are in increasing token order,
+  // so the valid ones are i < nt.  len: past the end.
+  auto tok0 = [&](int i) {
+    return i < nt ? 16 * (kStreams * c + v0 + i % per) + (i / per) * stream_stride : len;
+  };
+  auto local = [&](int i) { return (i / per) * kStreams + v0 + i % per; };  // LDS slot of the i-th tile
 
   const QShared q{s_q, lane};  // filled below, after the first tile's loads are issued
 
@@ -175,7 +202,7 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
       for (int r = 0; r < 4; ++r) x[r] = pr[r] * cfac;
       const float sh = row_sums4(x, n);
       if (nv <= 0) return;  // the masked tile past the end has no slot
-      float* out = s_raw + (wave * kMaxWaveTiles + ti) * kTileOut;
+      float* out = s_raw + local(ti) * kTileOut;
       if ((n & 3) == 0) out[4 * g + (n >> 2)] = sh;
       if (g == 0) out[kHeads + n] = st.m - lcf;  // u_h = m_h - log2 c_h
     } else {
@@ -199,7 +226,7 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
   // masked (zero weights, no outputs).
   Raw ra, rb;
   load_tile(tok0(0), ra);  // in flight while the query operand is built
-  build_q_lds<FP8>(p.q + static_cast<size_t>(b) * kHeads * kDim, p.qscale, s_q);
+  if (threadIdx.x < 256) build_q_lds<FP8>(p.q + static_cast<size_t>(b) * kHeads * kDim, p.qscale, s_q);
   __syncthreads();
   if (nt > 0) {
     for (int k = 0;; k += 2) {
@@ -221,14 +248,13 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
     // 16-byte stores, all issued before any completes: the flush is on the
     // critical path of the workgroup's end.
     const int ntiles = nt;
-    const float* wraw = s_raw + wave * kMaxWaveTiles * kTileOut;
 #pragma unroll
     for (int it = 0; it < kMaxWaveTiles * 4 / 64; ++it) {
       const int i = lane + 64 * it;  // float4 i: tile i / 4, tokens 4 (i % 4) ..
       const int ti = i >> 2, e = 4 * (i & 3);
       if (ti < ntiles) {
-        const float4 v = *reinterpret_cast<const float4*>(wraw + ti * kTileOut + e);
-        const int tok = w0 + ti * tile_stride + e;
+        const float4 v = *reinterpret_cast<const float4*>(s_raw + local(ti) * kTileOut + e);
+        const int tok = tok0(ti) + e;
         // bf16, round to nearest even: the selection's slack covers the 2^-9
         // relative rounding
         const uint32_t b01 = bf16_rne(v.x) | (bf16_rne(v.y) << 16), b23 = bf16_rne(v.z) | (bf16_rne(v.w) << 16);
@@ -246,15 +272,15 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
       const int i = lane + 64 * it;  // float4 i: tile i / 4, heads 4 (i % 4) ..
       const int ti = i >> 2, e = 4 * (i & 3);
       if (ti < ntiles) {
-        const int tile = (w0 + ti * tile_stride) >> 4;
+        const int tile = tok0(ti) >> 4;
         *reinterpret_cast<float4*>(p.tile_stats + tile_slot(base, b, tile) * kHeads + e) =
-            *reinterpret_cast<const float4*>(wraw + ti * kTileOut + kHeads + e);
+            *reinterpret_cast<const float4*>(s_raw + local(ti) * kTileOut + kHeads + e);
       }
     }
     __syncthreads();  // the merge below reuses this LDS
   }
 
-  // Merge the four waves through LDS.
+  // Merge the waves through LDS.
   const float z = reduce_z(st.z);
   if (g == 0) {
     s_m[wave][n] = st.m;
@@ -267,36 +293,40 @@ __global__ __launch_bounds__(256) void full_partial_kernel(FullParams p) {
   }
   __syncthreads();
 
-  const int h = threadIdx.x >> 4;
-  const int d0 = (threadIdx.x & 15) * 8;
+  // thread -> (head h, dims d0 .. d0 + kDims - 1)
+  constexpr int kDims = kDim * kHeads / kThreads;  // 8 (bf16) or 4 (E4M3)
+  const int h = threadIdx.x / (kDim / kDims);
+  const int d0 = (threadIdx.x % (kDim / kDims)) * kDims;
   float mx = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) mx = fmaxf(mx, s_m[w][h]);
+  for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, s_m[w][h]);
   float zz = 0.f;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float acc[kDims];
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int j = 0; j < kDims; ++j) acc[j] = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
     const float mw = s_m[w][h];
     if (mw == -INFINITY) continue;  // a wave with no tokens
     const float f = exp2f(mw - mx);
     zz += s_z[w][h] * f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] += s_o[w][h][d0 + j] * f;
+    for (int j = 0; j < kDims; ++j) acc[j] += s_o[w][h][d0 + j] * f;
   }
   const size_t item = static_cast<size_t>(b) * p.chunks_per_seq + c;
   float* out = p.partials + item * kPartialFloats;
-  if ((threadIdx.x & 15) == 0) {
+  if (d0 == 0) {
     out[h] = mx;
     out[kHeads + h] = zz;
     p.pstats[item * 2 * kHeads + h] = mx;  // compact copy for the selection's first pass
     p.pstats[item * 2 * kHeads + kHeads + h] = zz;
   }
   float4* o4 = reinterpret_cast<float4*>(out + 2 * kHeads + h * kDim + d0);
-  o4[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-  o4[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+#pragma unroll
+  for (int j = 0; j < kDims / 4; ++j) o4[j] = make_float4(acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]);
   if (c == 0) {
     uint4* hz = reinterpret_cast<uint4*>(p.hist0 + static_cast<size_t>(b) * kRadixBins);
-    for (int i = threadIdx.x; i < kRadixBins / 4; i += 256) hz[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = threadIdx.x; i < kRadixBins / 4; i += kThreads) hz[i] = make_uint4(0u, 0u, 0u, 0u);
     if (threadIdx.x < 4) p.counters[b * 4 + threadIdx.x] = 0u;
   }
 }
@@ -308,13 +338,13 @@ hipError_t launch_full_partial(const FullParams& p, int batch, bool fp8, bool bo
                                           (p.total_tokens + p.chunk - 1) / p.chunk + batch);
   const dim3 grid(static_cast<unsigned>(items));
   if (fp8 && bound_mode)
-    hipLaunchKernelGGL((full_partial_kernel<true, true>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((full_partial_kernel<true, true>), grid, dim3(64 * full_waves<true>()), 0, s, p);
   else if (fp8)
-    hipLaunchKernelGGL((full_partial_kernel<true, false>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((full_partial_kernel<true, false>), grid, dim3(64 * full_waves<true>()), 0, s, p);
   else if (bound_mode)
-    hipLaunchKernelGGL((full_partial_kernel<false, true>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((full_partial_kernel<false, true>), grid, dim3(64 * full_waves<false>()), 0, s, p);
   else
-    hipLaunchKernelGGL((full_partial_kernel<false, false>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((full_partial_kernel<false, false>), grid, dim3(64 * full_waves<false>()), 0, s, p);
   return hipGetLastError();
 }
 

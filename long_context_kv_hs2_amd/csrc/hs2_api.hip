@@ -39,25 +39,23 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 // Tokens per full-attention workgroup.  The pass runs best as one round of
-// workgroups: a workgroup's end (writing its per-tile outputs, merging its
-// waves) overlaps no streaming, so it should happen once, and a partly filled
-// second round would leave CUs idle.  With a bf16 cache the round is one
-// workgroup per CU of a 256-CU part: two co-resident workgroups progress
-// unevenly (on each SIMD the older wave's loads are served first, about 2.3x
-// as fast), so the younger one streams its last ~quarter alone at a lower
-// rate; one workgroup's four waves, one per SIMD, keep pace with each other.
-// An E4M3 tile carries half the bytes per load, and one workgroup per CU
-// keeps too few in flight, so E4M3 runs two per CU.  A batch takes
-// sum_b ceil(L_b / chunk) < N / chunk + B workgroups, so
-// chunk >= N / (slots - B) keeps them within the round.  Chunks are multiples
-// of 64 tokens (four waves of 16-token tiles) in [256, max_chunk].  The
-// choice affects speed, and the rounding of the outputs (never the
-// selection), and depends on nothing but N, B and the cache type.
+// workgroups, one per CU of a 256-CU part: a workgroup's end (writing its
+// per-tile outputs, merging its waves) overlaps no streaming, so it should
+// happen once, and a partly filled second round would leave CUs idle.  (Two
+// co-resident workgroups progress unevenly: on each SIMD the older wave's
+// loads are served first, so the younger workgroup streams the last part of
+// the pass alone at a lower rate.  Within one workgroup the kernel deals the
+// tiles to match.)  A batch takes sum_b ceil(L_b / chunk) < N / chunk + B
+// workgroups, so chunk >= N / (256 - B) keeps them within the round.  Chunks
+// are multiples of chunk_quantum in [256, max_chunk].  The choice affects
+// speed, and the rounding of the outputs (never the selection), and depends
+// on nothing but N, B and the cache type.
 int choose_chunk(int64_t total_tokens, int batch, bool fp8) {
-  const int64_t slots = fp8 ? 512 : 256;
-  const int64_t denom = std::max<int64_t>(slots - batch, slots / 4);
+  constexpr int64_t kSlots = 256;
+  const int64_t denom = std::max<int64_t>(kSlots - batch, kSlots / 4);
+  const int64_t quantum = chunk_quantum(fp8);
   int64_t c = (total_tokens + denom - 1) / denom;
-  c = (c + 63) / 64 * 64;
+  c = (c + quantum - 1) / quantum * quantum;
   return static_cast<int>(std::min<int64_t>(std::max<int64_t>(c, 256), max_chunk(fp8)));
 }
 

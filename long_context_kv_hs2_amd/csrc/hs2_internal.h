@@ -8,11 +8,13 @@
 namespace hs2 {
 
 // ---- full-attention layer: split-K partial pass and merge -------------------
-// Most tokens one full-attention workgroup takes: bf16 caches run one
-// workgroup per CU, E4M3 caches two (their bound-mode LDS is sized by this).
+// Most tokens one full-attention workgroup takes (its bound-mode LDS is sized
+// by this), and the multiple a chunk is rounded to: one 16-token tile per
+// tile stream (4 streams for bf16, 28 for E4M3).
 constexpr int kMaxChunkBf16 = 16384;
-constexpr int kMaxChunkFp8 = 8192;
+constexpr int kMaxChunkFp8 = 39 * 448;
 constexpr int max_chunk(bool fp8) { return fp8 ? kMaxChunkFp8 : kMaxChunkBf16; }
+constexpr int chunk_quantum(bool fp8) { return fp8 ? 448 : 64; }
 struct FullParams {
   const int64_t* seq_offsets;
   int64_t total_tokens;
