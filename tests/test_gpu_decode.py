@@ -69,17 +69,18 @@ def test_empty_sequences_in_batch():
     parity.check_decode(d, out)
 
 
-def test_large_batch_of_short_sequences():
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_large_batch_of_short_sequences(kv):
     # More sequences than one wave scans at once (the full pass deals its
-    # workgroups by a prefix over 64 sequences at a time) and than the 512
+    # workgroups by a prefix over 64 sequences at a time) and than the 256
     # workgroup slots the chunk size aims at; lengths around the selection
     # budget, a few empty.
     rng = np.random.default_rng(61)
     lengths = [int(x) for x in rng.integers(0, 2600, size=600)]
     lengths[5] = lengths[300] = 0
     lengths[7] = 1153
-    say(f"case: 600 sequences, lengths 0..2600 (total {sum(lengths)})")
-    d = inputs.make_decode(lengths=lengths, n_sparse=1, seed=61, needles=4)
+    say(f"case: 600 sequences, lengths 0..2600 (total {sum(lengths)}) kv={kv}")
+    d = inputs.make_decode(lengths=lengths, n_sparse=1, kv=kv, seed=61, needles=4)
     out, _, _ = run(d)
     w = parity.check_decode(d, out)
     say(f"worst {w}")
