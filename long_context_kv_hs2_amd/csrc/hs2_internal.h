@@ -77,7 +77,10 @@ struct SelectParams {
   uint32_t* counters;         // [B][4]: winners emitted, candidates seen
   int32_t* selbuf;            // [B][top_k]: positions emitted so far
   unsigned long long* cand;   // spill mode: [B][kCandCap] threshold-bin keys; bound mode: [N] exact candidate keys
-  int32_t* cand_idx;          // bound mode: [N] candidate positions
+  int32_t* cand_idx;          // bound mode: [N + B * kBoundBlockTokens] candidate positions, one
+                              // segment of kBoundBlockTokens per collect workgroup
+  uint32_t* cand_cnt;         // bound mode: [B][cand_blocks] candidates per collect workgroup
+  int cand_blocks;            // collect workgroups of the longest sequence
   int32_t* sel_idx;           // [B][budget]
   int32_t* sel_count;         // [B]
   // exact rescoring of candidates (bound mode)
@@ -90,6 +93,8 @@ constexpr int kRadixBins = 2048;
 constexpr int kScoreBlockTokens = 2048;   // tokens per score-pass workgroup
 constexpr int kCollectBlockTokens = 8192; // tokens per collect workgroup
 constexpr int kBoundBlockTokens = 4096;   // tokens per collect workgroup (one 16-token tile per thread)
+constexpr int kMaxCollectBlocks = (1 << 24) / kBoundBlockTokens;  // collect workgroups of the longest context
+constexpr int kSharedListBlocks = 128;    // more collect workgroups per sequence: per-workgroup candidate segments
 constexpr int64_t kHistLongContext = 1 << 19;  // longer: two tiles per thread in the lower-bound histogram
 constexpr int kRefineBlocks = 32;         // rescoring workgroups per sequence
 constexpr int kCandCap = 32768;           // threshold-bin keys kept per sequence (spill mode)

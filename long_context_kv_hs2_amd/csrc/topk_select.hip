@@ -680,6 +680,14 @@ hipError_t launch_merge_bound_hist(const MergeParams& mp, const SelectParams& p,
   return hipGetLastError();
 }
 
+// Segment of collect workgroup j of sequence b (base: its first row) in the
+// candidate room: sequence b's region starts at row base + b * kBoundBlockTokens
+// and holds nb * kBoundBlockTokens <= len + kBoundBlockTokens slots, so the
+// regions of consecutive sequences do not overlap.
+__device__ __forceinline__ int32_t* cand_segment(const SelectParams& p, int64_t base, int b, int j) {
+  return p.cand_idx + base + static_cast<int64_t>(b + j) * kBoundBlockTokens;
+}
+
 // Candidates: workgroup j of a sequence takes the 16-token tiles j, j + nb,
 // j + 2 nb, ... of its out-of-window positions (nb workgroups, one tile per
 // thread).  The tiles each wave of the full pass visited first have the
@@ -691,8 +699,8 @@ hipError_t launch_merge_bound_hist(const MergeParams& mp, const SelectParams& p,
 // upper bound reaches it, so every position of the exact top-k (ties
 // included) is kept; a tile whose largest upper bound (from the first pass)
 // misses the threshold is skipped without reading its tokens.  The kept
-// positions are gathered in LDS and placed in the sequence's list (room for
-// every position) with one atomic.
+// positions are gathered in LDS and written to the workgroup's own segment
+// of the sequence's candidate room, with their count.
 __global__ __launch_bounds__(256) void collect_bound_kernel(SelectParams p) {
   __shared__ uint32_t s_hist[kRadixBins];
   __shared__ uint32_t s_scan[256];
@@ -749,10 +757,19 @@ __global__ __launch_bounds__(256) void collect_bound_kernel(SelectParams p) {
   }
   __syncthreads();
   const uint32_t ncand = s_cnt;
-  if (t == 0) s_base = ncand ? atomicAdd(p.counters + b * 4 + 1, ncand) : 0u;
-  __syncthreads();
-  int32_t* ci = p.cand_idx + base;  // the sequence's region: one slot per position
-  for (uint32_t i = t; i < ncand; i += 256) ci[s_base + i] = s_list[i];
+  int32_t* ci;
+  if (nb <= kSharedListBlocks) {
+    // One list for the sequence, room taken with one atomic per workgroup.
+    if (t == 0) s_base = ncand ? atomicAdd(p.counters + b * 4 + 1, ncand) : 0u;
+    __syncthreads();
+    ci = cand_segment(p, base, b, 0) + s_base;
+  } else {
+    // Many workgroups would queue on that one counter (a 1M-token sequence
+    // has 256): each writes its own segment and its count instead.
+    if (t == 0) p.cand_cnt[static_cast<size_t>(b) * p.cand_blocks + blockIdx.x] = ncand;
+    ci = cand_segment(p, base, b, blockIdx.x);
+  }
+  for (uint32_t i = t; i < ncand; i += 256) ci[i] = s_list[i];
 }
 
 // Exact keys of the candidates, 16 per MFMA tile: the split query from LDS
@@ -761,28 +778,61 @@ __global__ __launch_bounds__(256) void collect_bound_kernel(SelectParams p) {
 // are bitwise those of the spill path.  kRefineBlocks workgroups per
 // sequence deal the candidate tiles round-robin over their waves; each wave
 // has its next tile's loads in flight while it scores the current one.
-template <bool FP8>
+template <bool FP8, bool SEG>
 __global__ __launch_bounds__(256) void refine_kernel(SelectParams p) {
   __shared__ u32x4 s_q[kQLdsVecs];
   __shared__ float s_lg[4][16][17];
   __shared__ float s_mx[kHeads];
   __shared__ float s_iz[kHeads];
+  __shared__ uint32_t s_pre[SEG ? kMaxCollectBlocks + 1 : 1];  // (LDS only where some sequence needs it)
+  __shared__ uint32_t s_scan[4];
   const int b = blockIdx.y;
   int64_t base;
   int len;
   seq_bounds(p.seq_offsets, b, p.total_tokens, p.max_context, base, len);
   if (len <= p.budget) return;
   const int dom = len - p.window;
-  const int ncand = static_cast<int>(min(p.counters[b * 4 + 1], static_cast<uint32_t>(dom)));
+  // With per-workgroup segments, candidate i of the sequence lives in the
+  // segment of the collect workgroup j with s_pre[j] <= i < s_pre[j + 1]
+  // (exclusive prefix of the per-workgroup counts, in workgroup order).
+  const int nb = (dom + kBoundBlockTokens - 1) / kBoundBlockTokens;
+  const bool segmented = SEG && nb > kSharedListBlocks;  // uniform
+  int ncand;
+  if (!segmented) {
+    ncand = static_cast<int>(min(p.counters[b * 4 + 1], static_cast<uint32_t>(dom)));
+  } else {
+    const uint32_t* cnt = p.cand_cnt + static_cast<size_t>(b) * p.cand_blocks;
+    const int per = (nb + 255) / 256;
+    const int j0 = static_cast<int>(threadIdx.x) * per;
+    uint32_t sum = 0;
+    for (int j = j0; j < min(j0 + per, nb); ++j) sum += cnt[j];
+    uint32_t run = block_exclusive_scan<256>(sum, s_scan);
+    for (int j = j0; j < min(j0 + per, nb); ++j) {
+      s_pre[j] = run;
+      run += cnt[j];
+    }
+    if (j0 < nb && j0 + per >= nb) s_pre[nb] = run;  // the thread holding the last workgroup
+    __syncthreads();
+    ncand = static_cast<int>(min(s_pre[nb], static_cast<uint32_t>(dom)));
+    if (blockIdx.x == 0 && threadIdx.x == 0) p.counters[b * 4 + 1] = static_cast<uint32_t>(ncand);  // for the finish
+  }
   const int ntiles = (ncand + 15) >> 4;
   if (static_cast<int>(blockIdx.x) * 4 >= ntiles) return;  // uniform
+  auto cand_at = [&](int i) {  // position of candidate i (0 <= i < ncand)
+    if (!segmented) return cand_segment(p, base, b, 0)[i];
+    int lo = 0, hi = nb - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pre[mid] <= static_cast<uint32_t>(i)) lo = mid; else hi = mid - 1;
+    }
+    return cand_segment(p, base, b, lo)[i - static_cast<int>(s_pre[lo])];
+  };
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar loop control
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;
   const int g = lane >> 4;
   constexpr int kRowBytes = FP8 ? kDim : 2 * kDim;
   const uint8_t* __restrict__ kbase = p.k + base * kRowBytes;
-  const int32_t* ci = p.cand_idx + base;
   const int stride = gridDim.x * 4;
 
   struct Raw {
@@ -794,7 +844,7 @@ __global__ __launch_bounds__(256) void refine_kernel(SelectParams p) {
   // kload_offset(j, g); ks[r]: the K scale of candidate 4g + r
   auto load = [&](int tile, Raw& r) {
     const int i0 = min(tile, ntiles - 1) * 16;
-    r.pos = min(max(ci[i0 + min(n, ncand - 1 - i0)], 0), dom - 1);
+    r.pos = min(max(cand_at(i0 + min(n, ncand - 1 - i0)), 0), dom - 1);
     const uint32_t krow = static_cast<uint32_t>(r.pos) * kRowBytes;
 #pragma unroll
     for (int j = 0; j < (FP8 ? 2 : 4); ++j) r.k[j] = *reinterpret_cast<const u32x4*>(kbase + (krow + kload_offset(j, g)));
@@ -865,10 +915,18 @@ hipError_t launch_bound_select(const SelectParams& p, int batch, int64_t max_con
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 rgrid(kRefineBlocks, batch);
-    if (fp8)
-      hipLaunchKernelGGL(refine_kernel<true>, rgrid, dim3(256), 0, s, p);
+    // Per-workgroup candidate segments exist only past kSharedListBlocks
+    // collect workgroups; below that the prefix array's LDS would only cost
+    // occupancy.
+    const bool seg = (max_context + kBoundBlockTokens - 1) / kBoundBlockTokens > kSharedListBlocks;
+    if (fp8 && seg)
+      hipLaunchKernelGGL((refine_kernel<true, true>), rgrid, dim3(256), 0, s, p);
+    else if (fp8)
+      hipLaunchKernelGGL((refine_kernel<true, false>), rgrid, dim3(256), 0, s, p);
+    else if (seg)
+      hipLaunchKernelGGL((refine_kernel<false, true>), rgrid, dim3(256), 0, s, p);
     else
-      hipLaunchKernelGGL(refine_kernel<false>, rgrid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((refine_kernel<false, false>), rgrid, dim3(256), 0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -86,6 +86,18 @@ def test_large_batch_of_short_sequences(kv):
     say(f"worst {w}")
 
 
+def test_long_and_short_sequences_in_one_batch():
+    # A sequence past 512K tokens takes the selection's per-workgroup
+    # candidate segments and the two-tile histogram; the short ones in the
+    # same batch take the one shared candidate list.
+    lengths = [700000, 2500, 150000, 0, 1153]
+    say(f"case: mixed long and short {lengths}")
+    d = inputs.make_decode(lengths=lengths, n_sparse=2, seed=71, needles=64)
+    out, _, _ = run(d)
+    w = parity.check_decode(d, out)
+    say(f"worst {w}")
+
+
 def test_all_empty_batch():
     say("case: all-empty batch")
     dev = "cuda"
