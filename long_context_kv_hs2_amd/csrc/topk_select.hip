@@ -443,7 +443,7 @@ __global__ __launch_bounds__(1024) void finish_kernel(SelectParams p) {
   // room, free by now) and read them back in order: each thread counts the
   // bits of its run of at most four words, a block scan gives its first
   // output slot, and it emits its positions.  (Longer runs per thread cost
-  // more in LDS bank conflicts than the sort below.)
+  // more in LDS bank conflicts than the ranking below.)
   const uint32_t nwords = (static_cast<uint32_t>(dom) + 31) >> 5;
   if (nwords <= 4u * 1024u) {
     uint32_t* bm = reinterpret_cast<uint32_t*>(s_keys);
@@ -469,31 +469,35 @@ __global__ __launch_bounds__(1024) void finish_kernel(SelectParams p) {
     if (t == 0) p.sel_count[b] = p.budget;
     return;
   }
-  // Otherwise a bitonic sort, one position per thread: partners within a wave
-  // trade by lane shuffle, partners in other waves through LDS (the
-  // histogram's room, free by now, as two buffers taken in turn: one barrier
-  // per such stage).
+  // Otherwise each wave sorts its 64 positions by a bitonic network of lane
+  // shuffles, and a position's output slot is the number of positions below
+  // it over the 16 sorted runs (a binary search in each, through LDS).
   int32_t x = s_sel[t];
-  int32_t* xbuf = reinterpret_cast<int32_t*>(s_hist);  // [2][kTopK]
-  static_assert(kRadixBins >= 2 * kTopK, "two sort buffers fit in the histogram");
-  int nb = 0;
-  for (int size = 2; size <= kTopK; size <<= 1) {
+  const int lane = t & 63;
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      int32_t y;
-      if (stride >= 64) {
-        xbuf[nb * kTopK + t] = x;
-        __syncthreads();
-        y = xbuf[nb * kTopK + (t ^ stride)];
-        nb ^= 1;
-      } else {
-        y = __shfl_xor(x, stride);
-      }
-      const bool up = (t & size) == 0;
-      const bool lower = (t & stride) == 0;
+      const int32_t y = __shfl_xor(x, stride);
+      const bool up = (lane & size) == 0;
+      const bool lower = (lane & stride) == 0;
       x = (lower == up) ? min(x, y) : max(x, y);
     }
   }
-  out[t] = x;
+  int32_t* runs = reinterpret_cast<int32_t*>(s_hist);  // [16][64]
+  runs[t] = x;
+  __syncthreads();
+  int slot_out = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < 16; ++w2) {
+    const int32_t* run = runs + 64 * w2;
+    int lo = 0;
+#pragma unroll
+    for (int step = 32; step > 0; step >>= 1)
+      if (run[lo + step - 1] < x) lo += step;
+    slot_out += lo + ((lo == 63 && run[63] < x) ? 1 : 0);
+  }
+  out[slot_out] = x;
   if (t < p.window) out[p.top_k + t] = dom + t;
   if (t == 0) p.sel_count[b] = p.budget;
 }
