@@ -255,6 +255,7 @@ SelectParams select_params(const DecodeArgs& a, const DecodeLayout& L, float* sc
   p.seq_offsets = a.offs;
   p.total_tokens = a.d->total_tokens;
   p.max_context = a.d->max_context;
+  p.batch = a.d->batch;
   p.window = a.d->window;
   p.top_k = a.d->top_k;
   p.budget = a.d->window + a.d->top_k;

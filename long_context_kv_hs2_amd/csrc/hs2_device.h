@@ -28,6 +28,42 @@ __device__ __forceinline__ void seq_bounds(const int64_t* offs, int b, int64_t t
   len = static_cast<int>(e - a);
 }
 
+// Work item wg of a 1-D grid over the items of a ragged batch, numbered
+// sequence by sequence, count(len) items for a sequence of len tokens: the
+// sequence b of the item and its index j there.  A 2-D grid sized by the
+// longest sequence would dispatch every hole as a workgroup that loads its
+// bounds and exits.  Every lane of the wave computes the same answer (a wave
+// prefix over 64 sequences at a time); false past the last item.
+template <class CountFn>
+__device__ bool find_item(const int64_t* offs, int batch, int64_t total, int64_t max_ctx, int wg, CountFn count,
+                          int& b, int& j) {
+  const int lane = threadIdx.x & 63;
+  int carry = 0;  // items of the sequences before this pass
+  for (int s0 = 0; s0 < batch; s0 += 64) {
+    const int sb = s0 + lane;
+    int64_t sbase = 0;
+    int slen = 0;
+    if (sb < batch) seq_bounds(offs, sb, total, max_ctx, sbase, slen);
+    const int nb = sb < batch ? count(slen) : 0;
+    int incl = nb;  // inclusive prefix sum over the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    const int tot = __shfl(incl, 63);
+    if (wg < carry + tot) {
+      const uint64_t hit = __ballot(carry + incl > wg);
+      const int src = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+      b = s0 + src;
+      j = wg - carry - __shfl(incl - nb, src);
+      return true;
+    }
+    carry += tot;
+  }
+  return false;
+}
+
 // Number of selected rows of a sequence, clamped to what the sequence can hold.
 __device__ __forceinline__ int clamp_count(int count, int len, int budget) {
   const int cap = len < budget ? len : budget;

@@ -64,6 +64,7 @@ struct SelectParams {
   const int64_t* seq_offsets;
   int64_t total_tokens;
   int64_t max_context;
+  int batch;
   int window, top_k, budget;
   const float* spill;         // [N][16] (spill mode)
   const float* stats;         // [B][16][2] global (max, sum) per head

@@ -576,15 +576,29 @@ __device__ __forceinline__ void load_tile_bounds(const SelectParams& p, int64_t 
 // queue on the global atomics of the sequence's one histogram), with (M_h, Z_h) recomputed from the partials' (m, z), read
 // from the full pass's packed copy: the merge's result is not written yet,
 // and the two differ by rounding order only, which the slack covers.
-template <int TILES>
+template <int TILES, bool COMPACT>
 __global__ __launch_bounds__(256) void merge_bound_hist_kernel(MergeParams mp, SelectParams p) {
   constexpr int kBlockTokens = 16 * 256 * TILES;
   __shared__ MergeShared msh;
   __shared__ uint32_t s_hist[kRadixBins];
   __shared__ float s_mx[kHeads], s_iz[kHeads];
-  const int b = blockIdx.y;
-  if (blockIdx.x < kHeads) {
-    merge_one(mp, blockIdx.x, b, 0, 0, 0, msh);
+  // Item j of sequence b: j < 16 merges head j, j >= 16 is histogram block
+  // j - 16.  COMPACT: a 1-D grid over the batch's items (ragged batches);
+  // otherwise (blockIdx.x, blockIdx.y).
+  int b, j;
+  if constexpr (COMPACT) {
+    auto items = [&](int l) {
+      return kHeads + (l > p.budget ? (l - p.window + kBlockTokens - 1) / kBlockTokens : 0);
+    };
+    if (!find_item(p.seq_offsets, p.batch, p.total_tokens, p.max_context, blockIdx.x, items, b, j)) return;
+    b = __builtin_amdgcn_readfirstlane(b);
+    j = __builtin_amdgcn_readfirstlane(j);
+  } else {
+    b = blockIdx.y;
+    j = blockIdx.x;
+  }
+  if (j < kHeads) {
+    merge_one(mp, j, b, 0, 0, 0, msh);
     return;
   }
   int64_t base;
@@ -592,7 +606,7 @@ __global__ __launch_bounds__(256) void merge_bound_hist_kernel(MergeParams mp, S
   seq_bounds(p.seq_offsets, b, p.total_tokens, p.max_context, base, len);
   if (len <= p.budget) return;
   const int dom = len - p.window;
-  const int j0 = (blockIdx.x - kHeads) * kBlockTokens;
+  const int j0 = (j - kHeads) * kBlockTokens;
   if (j0 >= dom) return;
   const int t = threadIdx.x;
   // TILES tiles per thread, 256 tiles apart, all loads issued up front.
@@ -669,6 +683,12 @@ __global__ __launch_bounds__(256) void merge_bound_hist_kernel(MergeParams mp, S
   }
 }
 
+// A batch whose 2-D grid (longest sequence x batch) would be mostly holes
+// runs the selection's per-block kernels on a compact 1-D grid instead.
+static bool ragged_batch(const SelectParams& p, int batch, int64_t max_context) {
+  return static_cast<double>(batch) * static_cast<double>(max_context) > 2.0 * static_cast<double>(p.total_tokens);
+}
+
 hipError_t launch_merge_bound_hist(const MergeParams& mp, const SelectParams& p, int batch, int64_t max_context,
                                    hipStream_t s) {
   if (batch == 0) return hipSuccess;
@@ -676,11 +696,21 @@ hipError_t launch_merge_bound_hist(const MergeParams& mp, const SelectParams& p,
   // extra parallelism of one tile per thread wins.
   const int tiles = max_context > kHistLongContext ? 2 : 1;
   const int64_t block_tokens = 16 * 256 * tiles;
-  const dim3 grid(static_cast<unsigned>(kHeads + (max_context + block_tokens - 1) / block_tokens), batch);
-  if (tiles == 2)
-    hipLaunchKernelGGL(merge_bound_hist_kernel<2>, grid, dim3(256), 0, s, mp, p);
-  else
-    hipLaunchKernelGGL(merge_bound_hist_kernel<1>, grid, dim3(256), 0, s, mp, p);
+  if (ragged_batch(p, batch, max_context)) {
+    // at most sum_b (16 + ceil(L_b / block)) < 17 B + N / block items
+    const int64_t items = static_cast<int64_t>(kHeads + 1) * batch + p.total_tokens / block_tokens;
+    const dim3 grid(static_cast<unsigned>(items));
+    if (tiles == 2)
+      hipLaunchKernelGGL((merge_bound_hist_kernel<2, true>), grid, dim3(256), 0, s, mp, p);
+    else
+      hipLaunchKernelGGL((merge_bound_hist_kernel<1, true>), grid, dim3(256), 0, s, mp, p);
+  } else {
+    const dim3 grid(static_cast<unsigned>(kHeads + (max_context + block_tokens - 1) / block_tokens), batch);
+    if (tiles == 2)
+      hipLaunchKernelGGL((merge_bound_hist_kernel<2, false>), grid, dim3(256), 0, s, mp, p);
+    else
+      hipLaunchKernelGGL((merge_bound_hist_kernel<1, false>), grid, dim3(256), 0, s, mp, p);
+  }
   return hipGetLastError();
 }
 
@@ -705,22 +735,34 @@ __device__ __forceinline__ int32_t* cand_segment(const SelectParams& p, int64_t 
 // misses the threshold is skipped without reading its tokens.  The kept
 // positions are gathered in LDS and written to the workgroup's own segment
 // of the sequence's candidate room, with their count.
+template <bool COMPACT>
 __global__ __launch_bounds__(256) void collect_bound_kernel(SelectParams p) {
   __shared__ uint32_t s_hist[kRadixBins];
   __shared__ uint32_t s_scan[256];
   __shared__ Resolved s_res;
   __shared__ int32_t s_list[kBoundBlockTokens];
   __shared__ uint32_t s_cnt, s_base;
-  const int b = blockIdx.y;
+  // Workgroup j of sequence b: a compact 1-D grid for ragged batches,
+  // (blockIdx.x, blockIdx.y) otherwise.
+  int b, j;
+  if constexpr (COMPACT) {
+    auto blocks = [&](int l) { return l > p.budget ? (l - p.window + kBoundBlockTokens - 1) / kBoundBlockTokens : 0; };
+    if (!find_item(p.seq_offsets, p.batch, p.total_tokens, p.max_context, blockIdx.x, blocks, b, j)) return;
+    b = __builtin_amdgcn_readfirstlane(b);
+    j = __builtin_amdgcn_readfirstlane(j);
+  } else {
+    b = blockIdx.y;
+    j = blockIdx.x;
+  }
   int64_t base;
   int len;
   seq_bounds(p.seq_offsets, b, p.total_tokens, p.max_context, base, len);
   if (len <= p.budget) return;
   const int dom = len - p.window;
   const int nb = (dom + kBoundBlockTokens - 1) / kBoundBlockTokens;
-  if (static_cast<int>(blockIdx.x) >= nb) return;
+  if (j >= nb) return;
   const int t = threadIdx.x;
-  const int tile = blockIdx.x + t * nb;
+  const int tile = j + t * nb;
   const bool valid = 16 * tile < dom;
   const int nv = min(16, dom - 16 * tile);
   float2 ubf = make_float2(0.f, 0.f);  // (tile's largest upper bound, its max_h F_h)
@@ -770,8 +812,8 @@ __global__ __launch_bounds__(256) void collect_bound_kernel(SelectParams p) {
   } else {
     // Many workgroups would queue on that one counter (a 1M-token sequence
     // has 256): each writes its own segment and its count instead.
-    if (t == 0) p.cand_cnt[static_cast<size_t>(b) * p.cand_blocks + blockIdx.x] = ncand;
-    ci = cand_segment(p, base, b, blockIdx.x);
+    if (t == 0) p.cand_cnt[static_cast<size_t>(b) * p.cand_blocks + j] = ncand;
+    ci = cand_segment(p, base, b, j);
   }
   for (uint32_t i = t; i < ncand; i += 256) ci[i] = s_list[i];
 }
@@ -914,8 +956,14 @@ __global__ __launch_bounds__(256) void refine_kernel(SelectParams p) {
 hipError_t launch_bound_select(const SelectParams& p, int batch, int64_t max_context, bool fp8, hipStream_t s) {
   if (batch == 0) return hipSuccess;
   if (max_context > 0) {
-    const dim3 grid(static_cast<unsigned>((max_context + kBoundBlockTokens - 1) / kBoundBlockTokens), batch);
-    hipLaunchKernelGGL(collect_bound_kernel, grid, dim3(256), 0, s, p);
+    if (ragged_batch(p, batch, max_context)) {
+      // at most sum_b ceil(L_b / block) < N / block + B items
+      const dim3 grid(static_cast<unsigned>(p.total_tokens / kBoundBlockTokens + batch));
+      hipLaunchKernelGGL(collect_bound_kernel<true>, grid, dim3(256), 0, s, p);
+    } else {
+      const dim3 grid(static_cast<unsigned>((max_context + kBoundBlockTokens - 1) / kBoundBlockTokens), batch);
+      hipLaunchKernelGGL(collect_bound_kernel<false>, grid, dim3(256), 0, s, p);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 rgrid(kRefineBlocks, batch);
