@@ -63,7 +63,7 @@ struct DecodeLayout {
   int chunk = 0;
   int chunks_per_seq = 0;
   size_t partials = 0, stats = 0, pstats = 0, spill = 0, score = 0, hist0 = 0, counters = 0, selbuf = 0, cand = 0,
-         shat = 0, tile_stats = 0, tile_ub = 0, cand_idx = 0, cand_cnt = 0, sparse = 0, total = 0;
+         shat = 0, tile_stats = 0, tile_ub = 0, cand_cnt = 0, sparse = 0, total = 0;
   int cand_blocks = 0;
 };
 
@@ -90,8 +90,7 @@ DecodeLayout decode_layout(const hs2_decode_desc& d) {
   L.selbuf = take(B * kTopK * sizeof(int32_t));
   // spill mode: [B][kCandCap] keys of the threshold bin; bound mode: one slot
   // per position (every candidate's exact key, sequence b's from row base_b)
-  L.cand = take(std::max(B * kCandCap, N) * sizeof(unsigned long long));
-  L.cand_idx = take((N + B * kBoundBlockTokens) * sizeof(int32_t));
+  L.cand = take(std::max(B * kCandCap, N + B * kBoundBlockTokens) * sizeof(unsigned long long));
   L.cand_blocks = static_cast<int>(std::max<int64_t>((d.max_context + kBoundBlockTokens - 1) / kBoundBlockTokens, 1));
   L.cand_cnt = take(B * static_cast<size_t>(L.cand_blocks) * sizeof(uint32_t));
   L.shat = take(N * sizeof(uint16_t));
@@ -271,7 +270,6 @@ SelectParams select_params(const DecodeArgs& a, const DecodeLayout& L, float* sc
   p.shat = reinterpret_cast<const uint16_t*>(ws_at(a.ws, L.shat));
   p.tile_stats = reinterpret_cast<const float*>(ws_at(a.ws, L.tile_stats));
   p.tile_ub = reinterpret_cast<float*>(ws_at(a.ws, L.tile_ub));
-  p.cand_idx = reinterpret_cast<int32_t*>(ws_at(a.ws, L.cand_idx));
   p.cand_cnt = reinterpret_cast<uint32_t*>(ws_at(a.ws, L.cand_cnt));
   p.cand_blocks = L.cand_blocks;
   p.k = static_cast<const uint8_t*>(a.k);

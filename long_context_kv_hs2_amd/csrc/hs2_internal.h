@@ -77,11 +77,10 @@ struct SelectParams {
   uint32_t* hist0;            // [B][kRadixBins]: first-digit histogram
   uint32_t* counters;         // [B][4]: winners emitted, candidates seen
   int32_t* selbuf;            // [B][top_k]: positions emitted so far
-  unsigned long long* cand;   // spill mode: [B][kCandCap] threshold-bin keys; bound mode: [N] exact candidate keys
-  int32_t* cand_idx;          // bound mode: [N + B * kBoundBlockTokens] candidate positions, one
-                              // segment of kBoundBlockTokens per collect workgroup
-  uint32_t* cand_cnt;         // bound mode: [B][cand_blocks] candidates per collect workgroup
-  int cand_blocks;            // collect workgroups of the longest sequence
+  unsigned long long* cand;   // spill mode: [B][kCandCap] threshold-bin keys; bound mode: [N + B * kBoundBlockTokens]
+                              // exact candidate keys, one list per sequence or one segment per candidate workgroup
+  uint32_t* cand_cnt;         // bound mode: [B][cand_blocks] candidates per candidate workgroup (segmented lists)
+  int cand_blocks;            // ceil(longest context / kBoundBlockTokens)
   int32_t* sel_idx;           // [B][budget]
   int32_t* sel_count;         // [B]
   // exact rescoring of candidates (bound mode)
@@ -97,7 +96,7 @@ constexpr int kBoundBlockTokens = 4096;   // tokens per collect workgroup (one 1
 constexpr int kMaxCollectBlocks = (1 << 24) / kBoundBlockTokens;  // collect workgroups of the longest context
 constexpr int kSharedListBlocks = 128;    // more collect workgroups per sequence: per-workgroup candidate segments
 constexpr int64_t kHistLongContext = 1 << 19;  // longer: two tiles per thread in the lower-bound histogram
-constexpr int kRefineBlocks = 32;         // rescoring workgroups per sequence
+constexpr int kMinCollectBlocks = 32;     // candidate workgroups per sequence, at least (from 8K tokens on)
 constexpr int kCandCap = 32768;           // threshold-bin keys kept per sequence (spill mode)
 hipError_t launch_select_init(const SelectParams& p, int batch, hipStream_t s);
 // Spill mode: score_j from the spilled logits (compute_score) or read from

@@ -317,10 +317,23 @@ __global__ __launch_bounds__(256) void collect_kernel(SelectParams p) {
 // The radix passes read the candidates from LDS when they fit there.
 constexpr int kFinishLdsKeys = 16384;
 
+// Keys of sequence b (base: its first row) in the key room: its region starts
+// at row base + b * kBoundBlockTokens and holds len + kBoundBlockTokens
+// slots, so the regions of consecutive sequences do not overlap.  A
+// sequence's one list starts at the region's start (at most len - window
+// keys); past kSharedListBlocks candidate workgroups, workgroup j's segment
+// starts kBoundBlockTokens * j further in (nb = ceil((len - window) /
+// kBoundBlockTokens) segments of at most kBoundBlockTokens keys each).
+__device__ __forceinline__ int64_t key_segment(int64_t base, int b, int j) {
+  return base + static_cast<int64_t>(b + j) * kBoundBlockTokens;
+}
+
 template <bool BOUND>
 __global__ __launch_bounds__(1024) void finish_kernel(SelectParams p) {
   __shared__ uint32_t s_hist[kRadixBins];
-  __shared__ uint32_t s_scan[1024];
+  __shared__ uint32_t s_scan[16];
+  // bound mode, keys in per-workgroup segments: exclusive prefix of the counts
+  __shared__ uint32_t s_pre[BOUND ? kMaxCollectBlocks + 1 : 1];
   __shared__ Resolved s_res;
   __shared__ int32_t s_sel[kTopK];
   __shared__ uint32_t s_n;
@@ -337,13 +350,44 @@ __global__ __launch_bounds__(1024) void finish_kernel(SelectParams p) {
     return;
   }
   const int dom = len - p.window;
-  // Bound mode: the keys fill the sequence's region cand[base, base + ncand),
-  // which has room for every position.  Spill mode: cand[b][0, kCandCap),
-  // and a scan of the D0 bin's scores when that overflowed.
-  uint32_t ncand = p.counters[b * 4 + 1];
+  // Bound mode: the keys fill the start of the sequence's region, which has
+  // room for every position, or (past kSharedListBlocks candidate
+  // workgroups) one segment per workgroup, key i in the segment of the
+  // workgroup j with s_pre[j] <= i < s_pre[j + 1].  Spill mode:
+  // cand[b][0, kCandCap), and a scan of the D0 bin's scores when that
+  // overflowed.
+  const int nseg = (dom + kBoundBlockTokens - 1) / kBoundBlockTokens;
+  const bool segmented = BOUND && nseg > kSharedListBlocks;  // uniform
+  uint32_t ncand;
+  if (segmented) {
+    const uint32_t* cnt = p.cand_cnt + static_cast<size_t>(b) * p.cand_blocks;
+    const int per = (nseg + 1023) / 1024;
+    const int j0 = t * per;
+    uint32_t sum = 0;
+    for (int jj = j0; jj < min(j0 + per, nseg); ++jj) sum += cnt[jj];
+    uint32_t run = block_exclusive_scan<1024>(sum, s_scan);
+    for (int jj = j0; jj < min(j0 + per, nseg); ++jj) {
+      s_pre[jj] = run;
+      run += cnt[jj];
+    }
+    if (j0 < nseg && j0 + per >= nseg) s_pre[nseg] = run;  // the thread holding the last workgroup
+    __syncthreads();
+    ncand = s_pre[nseg];
+  } else {
+    ncand = p.counters[b * 4 + 1];
+  }
   if (BOUND) ncand = min(ncand, static_cast<uint32_t>(dom));
   const bool overflow = !BOUND && ncand > static_cast<uint32_t>(kCandCap);
-  const unsigned long long* cand = BOUND ? p.cand + base : p.cand + static_cast<size_t>(b) * kCandCap;
+  const unsigned long long* cand = BOUND ? p.cand + key_segment(base, b, 0) : p.cand + static_cast<size_t>(b) * kCandCap;
+  auto key_at = [&](uint32_t i) {  // key i of the candidate list, i < ncand
+    if (!segmented) return cand[i];
+    int lo = 0, hi = nseg - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pre[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    return p.cand[key_segment(base, b, lo) + (i - s_pre[lo])];
+  };
   const float* score = p.score + base;
   const bool staged = !overflow && ncand <= static_cast<uint32_t>(kFinishLdsKeys);
   if (staged) {
@@ -353,7 +397,7 @@ __global__ __launch_bounds__(1024) void finish_kernel(SelectParams p) {
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const uint32_t i = i0 + u * 1024 + t;
-        k8[u] = i < ncand ? cand[i] : 0ull;
+        k8[u] = i < ncand ? key_at(i) : 0ull;
       }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
@@ -395,7 +439,7 @@ __global__ __launch_bounds__(1024) void finish_kernel(SelectParams p) {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
           const uint32_t i = i0 + u * 1024 + t;
-          k8[u] = i < ncand ? cand[i] : 0ull;
+          k8[u] = i < ncand ? key_at(i) : 0ull;
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u)
@@ -714,39 +758,60 @@ hipError_t launch_merge_bound_hist(const MergeParams& mp, const SelectParams& p,
   return hipGetLastError();
 }
 
-// Segment of collect workgroup j of sequence b (base: its first row) in the
-// candidate room: sequence b's region starts at row base + b * kBoundBlockTokens
-// and holds nb * kBoundBlockTokens <= len + kBoundBlockTokens slots, so the
-// regions of consecutive sequences do not overlap.
-__device__ __forceinline__ int32_t* cand_segment(const SelectParams& p, int64_t base, int b, int j) {
-  return p.cand_idx + base + static_cast<int64_t>(b + j) * kBoundBlockTokens;
+// Workgroups of the candidate pass for a sequence of len tokens: one per
+// 4096 out-of-window positions, and at least one per 256 tokens up to
+// kMinCollectBlocks.  Short sequences have many candidates for their length
+// (the bounds are loosest on each wave's first tiles: ~40% of a 4K-token
+// sequence), and near-uniform scores make most positions candidates, so the
+// rescoring needs more waves than the collection; but every workgroup also
+// pays for resolving the threshold and building the query, so a batch of
+// many short sequences is better served by fewer.
+__device__ __forceinline__ int collect_blocks(const SelectParams& p, int len) {
+  return len > p.budget ? max((len - p.window + kBoundBlockTokens - 1) / kBoundBlockTokens,
+                              min(kMinCollectBlocks, (len + 255) / 256))
+                        : 0;
 }
 
-// Candidates: workgroup j of a sequence takes the 16-token tiles j, j + nb,
-// j + 2 nb, ... of its out-of-window positions (nb workgroups, one tile per
-// thread).  The tiles each wave of the full pass visited first have the
-// loosest bounds and sit together at the start of the sequence; striding
-// spreads them.  Each workgroup resolves the pruning threshold from the
-// finished lower-bound histogram (every workgroup of the sequence finds the
-// same one): the lower edge of the bin holding the k-th largest lower bound,
-// so at least k positions score at or above it.  It keeps the positions whose
-// upper bound reaches it, so every position of the exact top-k (ties
-// included) is kept; a tile whose largest upper bound (from the first pass)
-// misses the threshold is skipped without reading its tokens.  The kept
-// positions are gathered in LDS and written to the workgroup's own segment
-// of the sequence's candidate room, with their count.
-template <bool COMPACT>
-__global__ __launch_bounds__(256) void collect_bound_kernel(SelectParams p) {
-  __shared__ uint32_t s_hist[kRadixBins];
-  __shared__ uint32_t s_scan[256];
+
+// Candidates and their exact keys.  Workgroup j of a sequence (nb of them)
+// takes the 16-token tiles j, j + nb, j + 2 nb, ... of its out-of-window
+// positions, one tile per thread.  The tiles each wave of the full pass
+// visited first have the loosest bounds and sit together at the start of the
+// sequence; striding spreads them.  Each workgroup resolves the pruning
+// threshold from the finished lower-bound histogram (every workgroup of the
+// sequence finds the same one): the lower edge of the bin holding the k-th
+// largest lower bound, so at least k positions score at or above it.  It
+// keeps the positions whose upper bound reaches it, so every position of the
+// exact top-k (ties included) is kept; a tile whose largest upper bound (from
+// the first pass) misses the threshold is skipped without reading its
+// tokens.  The kept positions gather in LDS, and the workgroup's four waves
+// then compute their exact keys, 16 per MFMA tile: the split query from LDS
+// and the same MFMA sequence as the full pass give the same logits, and the
+// same head-ordered sum as the score pass gives the same score, so the keys
+// are bitwise those of the spill path.  Each wave has its next tile's loads in
+// flight while it scores the current one.  The keys go to the sequence's one
+// list (room taken with one atomic per workgroup) or, past
+// kSharedListBlocks workgroups (which would queue on that one counter), to
+// the workgroup's own segment with its count.
+template <bool FP8, bool COMPACT>
+__global__ __launch_bounds__(256) void collect_rescore_kernel(SelectParams p) {
+  // the histogram, then (once the threshold is resolved) the candidate list
+  __shared__ int32_t s_buf[kBoundBlockTokens];
+  static_assert(kBoundBlockTokens >= kRadixBins, "the histogram fits in the list's room");
+  __shared__ u32x4 s_q[kQLdsVecs];
+  __shared__ float s_lg[4][16][17];
+  __shared__ float s_mx[kHeads];
+  __shared__ float s_iz[kHeads];
+  __shared__ uint32_t s_scan[4];
   __shared__ Resolved s_res;
-  __shared__ int32_t s_list[kBoundBlockTokens];
   __shared__ uint32_t s_cnt, s_base;
+  uint32_t* s_hist = reinterpret_cast<uint32_t*>(s_buf);
+  int32_t* s_list = s_buf;
   // Workgroup j of sequence b: a compact 1-D grid for ragged batches,
   // (blockIdx.x, blockIdx.y) otherwise.
   int b, j;
   if constexpr (COMPACT) {
-    auto blocks = [&](int l) { return l > p.budget ? (l - p.window + kBoundBlockTokens - 1) / kBoundBlockTokens : 0; };
+    auto blocks = [&](int l) { return collect_blocks(p, l); };
     if (!find_item(p.seq_offsets, p.batch, p.total_tokens, p.max_context, blockIdx.x, blocks, b, j)) return;
     b = __builtin_amdgcn_readfirstlane(b);
     j = __builtin_amdgcn_readfirstlane(j);
@@ -759,7 +824,7 @@ __global__ __launch_bounds__(256) void collect_bound_kernel(SelectParams p) {
   seq_bounds(p.seq_offsets, b, p.total_tokens, p.max_context, base, len);
   if (len <= p.budget) return;
   const int dom = len - p.window;
-  const int nb = (dom + kBoundBlockTokens - 1) / kBoundBlockTokens;
+  const int nb = collect_blocks(p, len);
   if (j >= nb) return;
   const int t = threadIdx.x;
   const int tile = j + t * nb;
@@ -770,6 +835,12 @@ __global__ __launch_bounds__(256) void collect_bound_kernel(SelectParams p) {
   const uint32_t* gh = p.hist0 + static_cast<size_t>(b) * kRadixBins;
   for (int i = t; i < kRadixBins; i += 256) s_hist[i] = gh[i];
   if (t == 0) s_cnt = 0;
+  // the rescoring's query operand and (M, Z), loaded while the threshold resolves
+  build_q_lds<FP8>(p.q + static_cast<size_t>(b) * kHeads * kDim, p.qscale, s_q);
+  if (t < kHeads) {
+    s_mx[t] = p.stats[(static_cast<int64_t>(b) * kHeads + t) * 2];
+    s_iz[t] = 1.f / p.stats[(static_cast<int64_t>(b) * kHeads + t) * 2 + 1];
+  }
   __syncthreads();
   const Resolved r0 = block_resolve<256>(s_hist, kRadixBins, static_cast<uint32_t>(p.top_k), s_scan, &s_res);
   const float thr = __uint_as_float(static_cast<uint32_t>(r0.digit) << 20) * kLowSlack;
@@ -781,7 +852,8 @@ __global__ __launch_bounds__(256) void collect_bound_kernel(SelectParams p) {
     for (int i = 0; i < 16; ++i)
       if (i < nv && v[i] * ubf.y * kHighSlack >= thr) mine |= 1u << i;
   }
-  // Room in the LDS list: one atomic per wave, lane offsets by a wave prefix
+  // Room in the LDS list (the histogram is no longer read: block_resolve
+  // ended on a barrier): one atomic per wave, lane offsets by a wave prefix
   // sum (per-candidate atomics on one counter serialise).
   {
     const int lane = t & 63;
@@ -802,85 +874,22 @@ __global__ __launch_bounds__(256) void collect_bound_kernel(SelectParams p) {
     }
   }
   __syncthreads();
-  const uint32_t ncand = s_cnt;
-  int32_t* ci;
-  if (nb <= kSharedListBlocks) {
-    // One list for the sequence, room taken with one atomic per workgroup.
-    if (t == 0) s_base = ncand ? atomicAdd(p.counters + b * 4 + 1, ncand) : 0u;
-    __syncthreads();
-    ci = cand_segment(p, base, b, 0) + s_base;
-  } else {
-    // Many workgroups would queue on that one counter (a 1M-token sequence
-    // has 256): each writes its own segment and its count instead.
-    if (t == 0) p.cand_cnt[static_cast<size_t>(b) * p.cand_blocks + j] = ncand;
-    ci = cand_segment(p, base, b, j);
-  }
-  for (uint32_t i = t; i < ncand; i += 256) ci[i] = s_list[i];
-}
-
-// Exact keys of the candidates, 16 per MFMA tile: the split query from LDS
-// and the same MFMA sequence as the full pass give the same logits, and the
-// same head-ordered sum as the score pass gives the same score, so the keys
-// are bitwise those of the spill path.  kRefineBlocks workgroups per
-// sequence deal the candidate tiles round-robin over their waves; each wave
-// has its next tile's loads in flight while it scores the current one.
-template <bool FP8, bool SEG>
-__global__ __launch_bounds__(256) void refine_kernel(SelectParams p) {
-  __shared__ u32x4 s_q[kQLdsVecs];
-  __shared__ float s_lg[4][16][17];
-  __shared__ float s_mx[kHeads];
-  __shared__ float s_iz[kHeads];
-  __shared__ uint32_t s_pre[SEG ? kMaxCollectBlocks + 1 : 1];  // (LDS only where some sequence needs it)
-  __shared__ uint32_t s_scan[4];
-  const int b = blockIdx.y;
-  int64_t base;
-  int len;
-  seq_bounds(p.seq_offsets, b, p.total_tokens, p.max_context, base, len);
-  if (len <= p.budget) return;
-  const int dom = len - p.window;
-  // With per-workgroup segments, candidate i of the sequence lives in the
-  // segment of the collect workgroup j with s_pre[j] <= i < s_pre[j + 1]
-  // (exclusive prefix of the per-workgroup counts, in workgroup order).
-  const int nb = (dom + kBoundBlockTokens - 1) / kBoundBlockTokens;
-  const bool segmented = SEG && nb > kSharedListBlocks;  // uniform
-  int ncand;
-  if (!segmented) {
-    ncand = static_cast<int>(min(p.counters[b * 4 + 1], static_cast<uint32_t>(dom)));
-  } else {
-    const uint32_t* cnt = p.cand_cnt + static_cast<size_t>(b) * p.cand_blocks;
-    const int per = (nb + 255) / 256;
-    const int j0 = static_cast<int>(threadIdx.x) * per;
-    uint32_t sum = 0;
-    for (int j = j0; j < min(j0 + per, nb); ++j) sum += cnt[j];
-    uint32_t run = block_exclusive_scan<256>(sum, s_scan);
-    for (int j = j0; j < min(j0 + per, nb); ++j) {
-      s_pre[j] = run;
-      run += cnt[j];
-    }
-    if (j0 < nb && j0 + per >= nb) s_pre[nb] = run;  // the thread holding the last workgroup
-    __syncthreads();
-    ncand = static_cast<int>(min(s_pre[nb], static_cast<uint32_t>(dom)));
-    if (blockIdx.x == 0 && threadIdx.x == 0) p.counters[b * 4 + 1] = static_cast<uint32_t>(ncand);  // for the finish
+  const int ncand = static_cast<int>(s_cnt);
+  const bool shared = nb <= kSharedListBlocks;  // uniform
+  if (t == 0) {
+    if (shared)
+      s_base = ncand ? atomicAdd(p.counters + b * 4 + 1, static_cast<uint32_t>(ncand)) : 0u;
+    else
+      p.cand_cnt[static_cast<size_t>(b) * p.cand_blocks + j] = static_cast<uint32_t>(ncand);
   }
   const int ntiles = (ncand + 15) >> 4;
-  if (static_cast<int>(blockIdx.x) * 4 >= ntiles) return;  // uniform
-  auto cand_at = [&](int i) {  // position of candidate i (0 <= i < ncand)
-    if (!segmented) return cand_segment(p, base, b, 0)[i];
-    int lo = 0, hi = nb - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_pre[mid] <= static_cast<uint32_t>(i)) lo = mid; else hi = mid - 1;
-    }
-    return cand_segment(p, base, b, lo)[i - static_cast<int>(s_pre[lo])];
-  };
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar loop control
-  const int lane = threadIdx.x & 63;
+
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: scalar loop control
+  const int lane = t & 63;
   const int n = lane & 15;
   const int g = lane >> 4;
   constexpr int kRowBytes = FP8 ? kDim : 2 * kDim;
   const uint8_t* __restrict__ kbase = p.k + base * kRowBytes;
-  const int stride = gridDim.x * 4;
-
   struct Raw {
     u32x4 k[FP8 ? 2 : 4];
     float ks[4];
@@ -888,28 +897,25 @@ __global__ __launch_bounds__(256) void refine_kernel(SelectParams p) {
   };
   // lane (n, g): candidate n of the tile (clamped to the last one), row bytes
   // kload_offset(j, g); ks[r]: the K scale of candidate 4g + r
-  auto load = [&](int tile, Raw& r) {
-    const int i0 = min(tile, ntiles - 1) * 16;
-    r.pos = min(max(cand_at(i0 + min(n, ncand - 1 - i0)), 0), dom - 1);
+  auto load = [&](int ct, Raw& r) {
+    const int i0 = min(ct, ntiles - 1) * 16;
+    r.pos = min(max(s_list[i0 + min(n, ncand - 1 - i0)], 0), dom - 1);
     const uint32_t krow = static_cast<uint32_t>(r.pos) * kRowBytes;
 #pragma unroll
-    for (int j = 0; j < (FP8 ? 2 : 4); ++j) r.k[j] = *reinterpret_cast<const u32x4*>(kbase + (krow + kload_offset(j, g)));
+    for (int jj = 0; jj < (FP8 ? 2 : 4); ++jj)
+      r.k[jj] = *reinterpret_cast<const u32x4*>(kbase + (krow + kload_offset(jj, g)));
 #pragma unroll
-    for (int q = 0; q < 4; ++q) r.ks[q] = FP8 ? p.k_scale[base + __shfl(r.pos, 4 * g + q)] : 1.f;
+    for (int q4 = 0; q4 < 4; ++q4) r.ks[q4] = FP8 ? p.k_scale[base + __shfl(r.pos, 4 * g + q4)] : 1.f;
   };
+  int ct = wave;
   Raw ra, rb;
-  int tile = blockIdx.x * 4 + wave;
-  load(tile, ra);
-  build_q_lds<FP8>(p.q + static_cast<size_t>(b) * kHeads * kDim, p.qscale, s_q);
-  if (threadIdx.x < kHeads) {
-    s_mx[threadIdx.x] = p.stats[(static_cast<int64_t>(b) * kHeads + threadIdx.x) * 2];
-    s_iz[threadIdx.x] = 1.f / p.stats[(static_cast<int64_t>(b) * kHeads + threadIdx.x) * 2 + 1];
-  }
-  __syncthreads();
+  if (ct < ntiles) load(ct, ra);  // uniform over the wave
+  __syncthreads();                // s_base
+  if (ct >= ntiles) return;       // uniform over the wave; no barrier follows
   const QShared q{s_q, lane};
-  unsigned long long* ck = p.cand + base;  // the sequence's region: one slot per position
-  auto score = [&](int tile, const Raw& r) {
-    const int i0 = tile * 16;
+  unsigned long long* keys = p.cand + (shared ? key_segment(base, b, 0) + s_base : key_segment(base, b, j));
+  auto score = [&](int tl, const Raw& r) {
+    const int i0 = tl * 16;
     const int nvc = min(16, ncand - i0);
     bf16x8 kf[4];
     if constexpr (FP8) {
@@ -923,7 +929,7 @@ __global__ __launch_bounds__(256) void refine_kernel(SelectParams p) {
 #pragma unroll
     for (int part = 0; part < 3; ++part) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) sacc = mfma_bf16_16x16x32(kf[k], q.get(part, k), sacc);
+      for (int kq = 0; kq < 4; ++kq) sacc = mfma_bf16_16x16x32(kf[kq], q.get(part, kq), sacc);
     }
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) s_lg[wave][4 * g + q4][n] = sacc[q4] * r.ks[q4];
@@ -932,54 +938,45 @@ __global__ __launch_bounds__(256) void refine_kernel(SelectParams p) {
       float acc = 0.f;
 #pragma unroll
       for (int h = 0; h < kHeads; ++h) acc = __builtin_fmaf(exp2f(s_lg[wave][lane][h] - s_mx[h]), s_iz[h], acc);
-      if (lane < nvc) ck[i0 + lane] = select_key(acc, r.pos);
+      if (lane < nvc) keys[i0 + lane] = select_key(acc, r.pos);
     }
     asm volatile("" ::: "memory");  // the next tile's writes must follow these reads
   };
-  // two-slot ring; a load past the last tile re-reads the last one (unused)
+  // two-slot ring over the wave's tiles ct, ct + 4, ...; a load past the last
+  // tile re-reads the last one (unused)
   for (;;) {
-    load(tile + stride, rb);
+    load(ct + 4, rb);
     __builtin_amdgcn_sched_barrier(0);
-    score(tile, ra);
+    score(ct, ra);
     __builtin_amdgcn_sched_barrier(0);
-    tile += stride;
-    if (tile >= ntiles) break;
-    load(tile + stride, ra);
+    ct += 4;
+    if (ct >= ntiles) break;
+    load(ct + 4, ra);
     __builtin_amdgcn_sched_barrier(0);
-    score(tile, rb);
+    score(ct, rb);
     __builtin_amdgcn_sched_barrier(0);
-    tile += stride;
-    if (tile >= ntiles) break;
+    ct += 4;
+    if (ct >= ntiles) break;
   }
 }
 
 hipError_t launch_bound_select(const SelectParams& p, int batch, int64_t max_context, bool fp8, hipStream_t s) {
   if (batch == 0) return hipSuccess;
   if (max_context > 0) {
-    if (ragged_batch(p, batch, max_context)) {
-      // at most sum_b ceil(L_b / block) < N / block + B items
-      const dim3 grid(static_cast<unsigned>(p.total_tokens / kBoundBlockTokens + batch));
-      hipLaunchKernelGGL(collect_bound_kernel<true>, grid, dim3(256), 0, s, p);
-    } else {
-      const dim3 grid(static_cast<unsigned>((max_context + kBoundBlockTokens - 1) / kBoundBlockTokens), batch);
-      hipLaunchKernelGGL(collect_bound_kernel<false>, grid, dim3(256), 0, s, p);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const dim3 rgrid(kRefineBlocks, batch);
-    // Per-workgroup candidate segments exist only past kSharedListBlocks
-    // collect workgroups; below that the prefix array's LDS would only cost
-    // occupancy.
-    const bool seg = (max_context + kBoundBlockTokens - 1) / kBoundBlockTokens > kSharedListBlocks;
-    if (fp8 && seg)
-      hipLaunchKernelGGL((refine_kernel<true, true>), rgrid, dim3(256), 0, s, p);
+    const bool compact = ragged_batch(p, batch, max_context);
+    // compact: at most sum_b (ceil(L_b / block) + kMinCollectBlocks) < N / block + (kMinCollectBlocks + 1) B items
+    const int64_t per_seq = std::max<int64_t>((max_context + kBoundBlockTokens - 1) / kBoundBlockTokens, kMinCollectBlocks);
+    const dim3 grid = compact ? dim3(static_cast<unsigned>(p.total_tokens / kBoundBlockTokens + (kMinCollectBlocks + 1) * batch))
+                              : dim3(static_cast<unsigned>(per_seq), batch);
+    if (fp8 && compact)
+      hipLaunchKernelGGL((collect_rescore_kernel<true, true>), grid, dim3(256), 0, s, p);
     else if (fp8)
-      hipLaunchKernelGGL((refine_kernel<true, false>), rgrid, dim3(256), 0, s, p);
-    else if (seg)
-      hipLaunchKernelGGL((refine_kernel<false, true>), rgrid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((collect_rescore_kernel<true, false>), grid, dim3(256), 0, s, p);
+    else if (compact)
+      hipLaunchKernelGGL((collect_rescore_kernel<false, true>), grid, dim3(256), 0, s, p);
     else
-      hipLaunchKernelGGL((refine_kernel<false, false>), rgrid, dim3(256), 0, s, p);
-    e = hipGetLastError();
+      hipLaunchKernelGGL((collect_rescore_kernel<false, false>), grid, dim3(256), 0, s, p);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(finish_kernel<true>, dim3(batch), dim3(kTopK), 0, s, p);
