@@ -224,9 +224,14 @@ __global__ __launch_bounds__(64 * full_waves<FP8>()) void full_partial_kernel(Fu
   // issued, every iteration.  So the second half always runs; when a wave has
   // an odd number of tiles its last step sees a tile past the end, fully
   // masked (zero weights, no outputs).
+  // The query's loads go first, then the first tile's, which stay in flight
+  // while the query operand is built: a wait for data counts loads in issue
+  // order, so the other order would hold the build until the tile arrived.
+  float4 qa, qc;
+  if (threadIdx.x < 256) load_q_lds_raw<FP8>(p.q + static_cast<size_t>(b) * kHeads * kDim, qa, qc);
   Raw ra, rb;
-  load_tile(tok0(0), ra);  // in flight while the query operand is built
-  if (threadIdx.x < 256) build_q_lds<FP8>(p.q + static_cast<size_t>(b) * kHeads * kDim, p.qscale, s_q);
+  load_tile(tok0(0), ra);
+  if (threadIdx.x < 256) store_q_lds(qa, qc, p.qscale, s_q);
   __syncthreads();
   if (nt > 0) {
     for (int k = 0;; k += 2) {

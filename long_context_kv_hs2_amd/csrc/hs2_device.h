@@ -141,13 +141,10 @@ __device__ __forceinline__ int kdim0(int s, int g) {
   return FP8 ? 64 * (s >> 1) + 16 * g + 8 * (s & 1) : 32 * s + 8 * g;
 }
 
-// Three bf16 parts of (q * qscale) for the 8 dims of (k-step s, group g).
-template <bool FP8>
-__device__ __forceinline__ void split_q8(const float* __restrict__ q_head, int s, int g, float qscale, u32x4& ph,
-                                         u32x4& pm, u32x4& pl) {
-  const float* src = q_head + kdim0<FP8>(s, g);
-  const float4 a = *reinterpret_cast<const float4*>(src);
-  const float4 c = *reinterpret_cast<const float4*>(src + 4);
+// Three bf16 parts of (q * qscale) for 8 query values (those of one k-step
+// and lane group, see load_q8).
+__device__ __forceinline__ void split_q8(const float4& a, const float4& c, float qscale, u32x4& ph, u32x4& pm,
+                                         u32x4& pl) {
   const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -160,18 +157,34 @@ __device__ __forceinline__ void split_q8(const float* __restrict__ q_head, int s
   }
 }
 
+// The eight query values of k-step s for lane group g (raw fp32).  Loaded
+// apart from their split so that callers can issue these loads ahead of the
+// first tile's: a wait for data counts loads in issue order.
+template <bool FP8>
+__device__ __forceinline__ void load_q8(const float* __restrict__ q_head, int s, int g, float4& a, float4& c) {
+  const float* src = q_head + kdim0<FP8>(s, g);
+  a = *reinterpret_cast<const float4*>(src);
+  c = *reinterpret_cast<const float4*>(src + 4);
+}
+
 // Query operand held in registers (one wave's own query).
 struct QRegs {
   bf16x8 part[3][4];
   __device__ __forceinline__ bf16x8 get(int p, int s) const { return part[p][s]; }
 };
-
+struct QRaw {
+  float4 a[4], c[4];
+};
 template <bool FP8>
-__device__ __forceinline__ void load_qregs(const float* __restrict__ q_head, float qscale, int g, QRegs& f) {
+__device__ __forceinline__ void load_qraw(const float* __restrict__ q_head, int g, QRaw& r) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) load_q8<FP8>(q_head, s, g, r.a[s], r.c[s]);
+}
+__device__ __forceinline__ void qregs_from(const QRaw& r, float qscale, QRegs& f) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     u32x4 ph, pm, pl;
-    split_q8<FP8>(q_head, s, g, qscale, ph, pm, pl);
+    split_q8(r.a[s], r.c[s], qscale, ph, pm, pl);
     f.part[0][s] = as_bf16x8(ph);
     f.part[1][s] = as_bf16x8(pm);
     f.part[2][s] = as_bf16x8(pl);
@@ -186,16 +199,27 @@ struct QShared {
   __device__ __forceinline__ bf16x8 get(int p, int s) const { return as_bf16x8(s_q[(p * 4 + s) * 64 + lane]); }
 };
 
-// Build the LDS query operand of heads [16][128] with 256 threads.
+// Build the LDS query operand of heads [16][128] with 256 threads: the raw
+// loads (thread t: k-step t / 64), then the split and the LDS stores.
 template <bool FP8>
-__device__ __forceinline__ void build_q_lds(const float* __restrict__ q_heads, float qscale, u32x4* s_q) {
+__device__ __forceinline__ void load_q_lds_raw(const float* __restrict__ q_heads, float4& a, float4& c) {
+  const int lane = threadIdx.x & 63;
+  load_q8<FP8>(q_heads + (lane & 15) * kDim, threadIdx.x >> 6, lane >> 4, a, c);
+}
+__device__ __forceinline__ void store_q_lds(const float4& a, const float4& c, float qscale, u32x4* s_q) {
   const int s = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   u32x4 ph, pm, pl;
-  split_q8<FP8>(q_heads + (lane & 15) * kDim, s, lane >> 4, qscale, ph, pm, pl);
+  split_q8(a, c, qscale, ph, pm, pl);
   s_q[(0 * 4 + s) * 64 + lane] = ph;
   s_q[(1 * 4 + s) * 64 + lane] = pm;
   s_q[(2 * 4 + s) * 64 + lane] = pl;
+}
+template <bool FP8>
+__device__ __forceinline__ void build_q_lds(const float* __restrict__ q_heads, float qscale, u32x4* s_q) {
+  float4 a, c;
+  load_q_lds_raw<FP8>(q_heads, a, c);
+  store_q_lds(a, c, qscale, s_q);
 }
 
 // Row byte offset of the j-th 16-byte K load of lane group g (bf16: j = s,

@@ -117,11 +117,16 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_attend_kernel(SparsePar
   SoftmaxState st;
   softmax_init(st);
   if (rows > 0) {  // uniform over the wave
+    // The query's loads go first: a wait for data counts loads in issue
+    // order, so a query loaded after the first two tiles would hold the
+    // first step until the second tile had arrived too.
+    QRaw qr;
+    load_qraw<FP8>(p.q_sparse + ((static_cast<size_t>(layer) * p.batch + b) * kHeads + n) * kDim, g, qr);
     Raw ra, rb;
     load_tile(0, ra);
     if (TILES > 1) load_tile(1, rb);
     QRegs q;
-    load_qregs<FP8>(p.q_sparse + ((static_cast<size_t>(layer) * p.batch + b) * kHeads + n) * kDim, p.qscale, g, q);
+    qregs_from(qr, p.qscale, q);
     auto step = [&](int tile, const Raw& cur) {
       bf16x8 kf[4];
       if constexpr (FP8) {
