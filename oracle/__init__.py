@@ -36,6 +36,8 @@ from .hs2_oracle import (  # noqa: F401
     f64_to_bf16_bits,
     e4m3_value_table,
     e4m3_bytes_to_f64,
+    f64_to_e4m3,
+    quantize_rows_e4m3,
     decode_kv,
     full_attention,
     token_scores,
@@ -44,4 +46,5 @@ from .hs2_oracle import (  # noqa: F401
     decode_sequence,
     decode_block,
     bridge_kv,
+    bridge_kv_fp8,
 )

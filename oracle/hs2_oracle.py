@@ -112,6 +112,43 @@ def e4m3_bytes_to_f64(codes: np.ndarray) -> np.ndarray:
     return _E4M3[np.asarray(codes, dtype=np.uint8)]
 
 
+def f64_to_e4m3(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to OCP E4M3 codes (uint8): the nearest of the
+    format's finite values, ties to the even code (the one whose mantissa
+    field is even), magnitudes beyond 448 saturating to +-448.
+
+    Written from the format definition (see ``e4m3_value_table``); the sign
+    is kept, so a negative value that rounds to zero gives the code of -0.  The 127
+    non-negative finite values, codes 0x00..0x7E, increase with the code, so
+    the two candidates around |x| are adjacent codes.  Saturation is the
+    reading taken for a cache encoder (the pages say only "FP8 cache").
+    """
+    x = np.asarray(x, dtype=np.float64)
+    pos = _E4M3[:0x7F]  # codes 0x00..0x7E, increasing
+    a = np.minimum(np.abs(x), 448.0)
+    hi = np.clip(np.searchsorted(pos, a, side="left"), 0, 0x7E)  # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - pos[lo]
+    d_hi = pos[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(x), code | np.uint8(0x80), code).astype(np.uint8)  # the sign survives rounding to 0
+
+
+def quantize_rows_e4m3(x: np.ndarray):
+    """Per-row E4M3 with an fp32 scale, the FP8 cache layout the decode path
+    reads ([en] paragraph on cost and [pt]: the 1M-token footprints assume an
+    FP8 cache; the per-token scale is the reading taken): scale = (largest
+    |value| of the row) / 448, stored as fp32 (1 for an all-zero row), and
+    codes = E4M3(value / scale) with the stored scale.  Returns (codes uint8
+    [rows, cols], scales float32 [rows])."""
+    x = np.asarray(x, dtype=np.float64)
+    amax = np.abs(x).max(axis=1)
+    scale = np.where(amax > 0, amax / 448.0, 1.0).astype(np.float32)
+    codes = f64_to_e4m3(x / scale.astype(np.float64)[:, None])
+    return codes, scale
+
+
 def decode_kv(raw: np.ndarray, kv_dtype: str, scale: np.ndarray | None = None) -> np.ndarray:
     """Stored cache rows -> exact float64 rows.
 
@@ -273,3 +310,11 @@ def bridge_kv(h_bits: np.ndarray, w_k_bits, w_v_bits, rows=None):
     ks = [h @ bf16_bits_to_f64(w) for w in w_k_bits]
     vs = [h @ bf16_bits_to_f64(w) for w in w_v_bits]
     return ks, vs
+
+
+def bridge_kv_fp8(h_bits: np.ndarray, w_k_bits, w_v_bits, rows=None):
+    """The bridge projection stored as the FP8 cache: ``bridge_kv``'s float64
+    products, each row quantised by ``quantize_rows_e4m3``.  Returns
+    (list of (codes, scales) for K_l, the same for V_l)."""
+    ks, vs = bridge_kv(h_bits, w_k_bits, w_v_bits, rows)
+    return [quantize_rows_e4m3(k) for k in ks], [quantize_rows_e4m3(v) for v in vs]

@@ -125,3 +125,62 @@ def test_bridge_rows_subset_matches_full():
     rows = np.array([0, 7, 49])
     part, _ = O.bridge_kv(h, w, w, rows=rows)
     np.testing.assert_array_equal(part[0], full[0][rows])
+
+
+def test_e4m3_encode_hand_cases(golden):
+    for ln in golden("e4m3_rounding_cases.txt"):
+        x, code = ln.split("#")[0].split()[:-1], ln.split("#")[0].split()[-1]
+        val = _expr(" ".join(x))
+        got = int(O.f64_to_e4m3(np.array([val]))[0])
+        assert got == int(code, 16), (ln, hex(got))
+
+
+def test_e4m3_encode_round_trips_every_finite_code():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = O.e4m3_bytes_to_f64(codes)
+    np.testing.assert_array_equal(O.f64_to_e4m3(vals), codes)
+
+
+def test_e4m3_encode_matches_torch_within_range():
+    # torch's float8_e4m3fn cast rounds to nearest even; within +-448 (where
+    # no saturation question arises) the two encoders must agree everywhere.
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(200000) * 40.0, rng.standard_normal(50000) * 2.0 ** -7,
+                        (np.arange(-2000, 2000) + 0.5) * 2.0 ** -9])
+    x = x[np.abs(x) < 448]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = O.f64_to_e4m3(x)
+    zero = (ref & 0x7F) == 0
+    assert np.array_equal(got[~zero], ref[~zero])
+    assert np.array_equal(got[zero] & 0x7F, ref[zero] & 0x7F)  # signed zeros aside
+
+
+def test_quantize_rows_closed_forms():
+    x = np.array([[3.0] * 128, [0.0] * 128, [-5.0] + [1.0] * 127], dtype=np.float64)
+    codes, scale = O.quantize_rows_e4m3(x)
+    assert scale.dtype == np.float32
+    np.testing.assert_array_equal(scale, np.float32([3.0 / 448, 1.0, 5.0 / 448]))
+    assert (codes[0] == 0x7E).all()          # every value is the row maximum: 448 * scale
+    assert (codes[1] == 0x00).all()          # an all-zero row: scale 1, code 0
+    assert codes[2, 0] == 0xFE                # the largest magnitude maps to -448
+    # 1 / (5/448) = 89.6, between 88 (0x6B) and 96 (0x6C), nearer 88
+    assert (codes[2, 1:] == 0x6B).all()
+    back = O.e4m3_bytes_to_f64(codes) * scale.astype(np.float64)[:, None]
+    np.testing.assert_allclose(back[0], 3.0, rtol=1e-7)
+    np.testing.assert_allclose(back[2, 0], -5.0, rtol=1e-7)
+
+
+def test_bridge_fp8_one_hot_columns():
+    # One-hot W: K_l = the selected columns of H, then quantised per row;
+    # compare with quantising those columns directly.
+    rng = np.random.default_rng(7)
+    h = O.f64_to_bf16_bits(rng.standard_normal((40, 256)) * 0.1)
+    w = np.zeros((256, 128))
+    cols = rng.permutation(256)[:128]
+    w[cols, np.arange(128)] = 1.0
+    wb = O.f64_to_bf16_bits(w)
+    (kq,), (vq,) = O.bridge_kv_fp8(h, [wb], [wb])
+    want = O.quantize_rows_e4m3(O.bf16_bits_to_f64(h)[:, cols])
+    np.testing.assert_array_equal(kq[0], want[0])
+    np.testing.assert_array_equal(kq[1], want[1])
+    np.testing.assert_array_equal(vq[0], want[0])
