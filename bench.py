@@ -129,6 +129,39 @@ def bench_bridge(args, torch, hs2, inputs, dev):
     e1.record()
     torch.cuda.synchronize()
     bridge_ms = e0.elapsed_time(e1) / args.steps
+    # The same projection written as the E4M3 cache with per-token scales
+    # (diagnostic line: its own buffers, timed the same way).
+    k8 = [torch.empty((t_rows, 128), dtype=torch.uint8, device=dev) for _ in range(n_l)]
+    v8 = [torch.empty((t_rows, 128), dtype=torch.uint8, device=dev) for _ in range(n_l)]
+    ks8 = [torch.empty((t_rows,), dtype=torch.float32, device=dev) for _ in range(n_l)]
+    vs8 = [torch.empty((t_rows,), dtype=torch.float32, device=dev) for _ in range(n_l)]
+
+    def bridge_fp8():
+        hs2.bridge_kv_fp8(h, wk, wv, k8, ks8, v8, vs8, ws)
+
+    for _ in range(min(args.warmup, 5)):
+        bridge_fp8()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        bridge_fp8()
+    e1.record()
+    torch.cuda.synchronize()
+    bridge_fp8_ms = e0.elapsed_time(e1) / args.steps
+    blocks8 = [hs2.DecodeBlock(offs, k8[l], v8[l], torch.from_numpy(queries[l][0]).to(dev),
+                               torch.from_numpy(queries[l][1]).to(dev), ks8[l], vs8[l], t_rows // batch)
+               for l in range(n_l)]
+    for _ in range(min(args.warmup, 5)):
+        for blk in blocks8:
+            blk()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for blk in blocks8:
+            blk()
+    torch.cuda.synchronize()
+    decode_fp8_ms = (time.perf_counter() - t0) / args.steps * 1e3
+    del blocks8, k8, v8, ks8, vs8
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -158,6 +191,8 @@ def bench_bridge(args, torch, hs2, inputs, dev):
                      "kernel": "bridge_gemm_kernel (hs2_bridge_kv)", "alg_flops_per_launch": flops,
                      "mean_launch_ms": bridge_ms},
         "bridge_ms": bridge_ms,
+        "bridge_fp8_ms": bridge_fp8_ms,
+        "fp8_cache_decode_ms_per_step": decode_fp8_ms,
         "decode_stages_ms_per_layer": {k: round(v, 5) for k, v in stages.items()},
     }
 

@@ -157,6 +157,24 @@ hs2_status hs2_bridge_kv(int64_t n_tokens, int32_t d_model, int32_t head_dim, in
                          void* const* k_out, void* const* v_out,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* KV-Bridging projection writing the FP8 cache the pages' 1M-token
+ * footprints assume ([en] paragraph on cost; [pt]): the same products as
+ * hs2_bridge_kv, each output row (one token of one matrix) stored as OCP
+ * E4M3 codes with an fp32 scale: scale = (largest |value| of the row) / 448
+ * (1 for an all-zero row), code = E4M3(value / scale), round to nearest,
+ * ties to even, saturating at +-448; values from the fp32 products.
+ * k_out, v_out (host arrays of n_bridged device pointers) uint8
+ *   [n_tokens][head_dim]; k_scale, v_scale (host arrays of n_bridged device
+ *   pointers) fp32 [n_tokens], 4-byte aligned.  These are the cache and
+ *   scale arrays hs2_decode_block reads with kv_dtype HS2_KV_FP8_E4M3.
+ * Same support, workspace and errors as hs2_bridge_kv; NULL scale arrays:
+ * HS2_ERR_INVALID_ARGUMENT.                                                   */
+hs2_status hs2_bridge_kv_fp8(int64_t n_tokens, int32_t d_model, int32_t head_dim, int32_t n_bridged,
+                             const void* hidden, const void* const* w_k, const void* const* w_v,
+                             void* const* k_out, float* const* k_scale,
+                             void* const* v_out, float* const* v_scale,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Per-stage kernel timing of hs2_decode_block, for benchmarks.  Mode 1:
  * each call records HIP events around its stages on its stream
  * (HS2_N_STAGES stages: 0 full-attention partial pass, 1 full-attention

@@ -65,9 +65,28 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// fp32 -> OCP E4M3 code (1 sign, 4 exponent bits with bias 7, 3 mantissa
+// bits; exponent field 0 holds the subnormals m * 2^-9; no infinities, and
+// S.1111.111 is NaN, so the largest finite value is 448): round to nearest,
+// ties to the even code, magnitudes above 448 (and NaN) saturate to +-448.
+// Branch-free: from 2^-6 up, the fp32 bit pattern rounded at its 20th bit is
+// the code with the exponent bias 127 in place of 7 (the carry of a mantissa
+// that rounds up moves into the exponent); below 2^-6 the code is the
+// magnitude in units of 2^-9, rounded (a code of 8 is the smallest normal).
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t mag = u & 0x7FFFFFFFu;
+  const uint32_t normal = ((mag + 0x7FFFFu + ((mag >> 20) & 1u)) >> 20) - ((127u - 7u) << 3);
+  const uint32_t sub = static_cast<uint32_t>(__builtin_rintf(__uint_as_float(mag) * 512.f));
+  const uint32_t code = mag < 0x3C800000u ? sub : min(normal, 0x7Eu);  // 0x3C800000 = 2^-6
+  return ((u >> 24) & 0x80u) | code;
+}
+
+template <bool FP8OUT>
 __global__ __launch_bounds__(512) void bridge_gemm_kernel(BridgeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t s_a[2][kBM * kPitch];
   __shared__ __attribute__((aligned(16))) uint8_t s_b[2][kBN * kPitch];
+  __shared__ float s_amax[2][2][kBM];  // E4M3 output: [matrix][half of its columns][row] partial row maxima
 
   // XCD-aware order: workgroup id i runs on XCD i % 8; give the column tiles
   // of one row block consecutive slots on one XCD, so they share its L2.
@@ -175,19 +194,78 @@ __global__ __launch_bounds__(512) void bridge_gemm_kernel(BridgeParams p) {
     load_tile(ks + 4, sa);
   }
 
-  // Epilogue: D[row 4g + e][col n] of fragment (i, j) -> bf16, round to
-  // nearest even; column c of the tile belongs to output matrix c / 128.
-#pragma unroll
-  for (int j = 0; j < kFN; ++j) {
-    const int col = ct * kBN + wn + 16 * j + n;
-    uint16_t* out = p.out[col >> 7] + (col & (kDim - 1));
+  // Epilogue.  Fragment (i, j) holds D[row 4g + e][col n] in lane (n, g);
+  // tile column c belongs to output matrix c / 128 (two per workgroup).  The
+  // rounded values are staged in LDS (the operand buffers are free: the loop
+  // ended on a barrier), matrix 0 in s_a and matrix 1 in s_b, as [row][128]
+  // elements, and then written out row by row with 16-byte stores.
+  //   bf16: round to nearest even.
+  //   E4M3: per row and matrix, scale = (largest |value|) / 448 in fp32 (1 for
+  //   an all-zero row), code = E4M3(value / scale); the row maxima are reduced
+  //   over the 16 lanes of a fragment row and then over the two waves that
+  //   share the matrix, through LDS.
+  constexpr int kElemBytes = FP8OUT ? 1 : 2;
+  constexpr int kRowBytes = kDim * kElemBytes;  // staged bytes per row and matrix
+  static_assert(kBM * kRowBytes <= 2 * kBM * kPitch, "one matrix of the tile fits in one operand buffer");
+  const int mat = wn >> 7;         // output matrix of this wave (local: 0 or 1)
+  const int half = (wn >> 6) & 1;  // which 64 of its 128 columns
+  uint8_t* stage = mat == 0 ? &s_a[0][0] : &s_b[0][0];
+  float scale[kFM][4];
+  if constexpr (FP8OUT) {
 #pragma unroll
     for (int i = 0; i < kFM; ++i) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int64_t row = m0 + wm + 16 * i + 4 * g + e;
-        if (row < p.n_tokens) out[row * kDim] = f32_to_bf16_rne(acc[i][j][e]);
+        float a = 0.f;
+#pragma unroll
+        for (int j = 0; j < kFN; ++j) a = fmaxf(a, fabsf(acc[i][j][e]));
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));  // over the 16 lanes n
+        if (n == 0) s_amax[mat][half][wm + 16 * i + 4 * g + e] = a;
       }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kFM; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = wm + 16 * i + 4 * g + e;
+        const float a = fmaxf(s_amax[mat][0][r], s_amax[mat][1][r]);
+        scale[i][e] = a > 0.f ? a / 448.f : 1.f;
+        const int64_t row = m0 + r;
+        if (half == 0 && n == 0 && row < p.n_tokens) p.scale[ct * (kBN / kDim) + mat][row] = scale[i][e];
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kFN; ++j) {
+    const int c = (wn & (kDim - 1)) + 16 * j + n;  // column within the matrix
+#pragma unroll
+    for (int i = 0; i < kFM; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = wm + 16 * i + 4 * g + e;
+        if constexpr (FP8OUT) {
+          stage[r * kRowBytes + c] = static_cast<uint8_t>(f32_to_e4m3_rne_sat(acc[i][j][e] / scale[i][e]));
+        } else {
+          *reinterpret_cast<uint16_t*>(stage + r * kRowBytes + 2 * c) = f32_to_bf16_rne(acc[i][j][e]);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int kChunks = kRowBytes / 16;  // 16-byte pieces per row
+#pragma unroll
+  for (int k = 0; k < 2 * kBM * kChunks / 512; ++k) {
+    const int idx = tid + 512 * k;
+    const int mm = idx / (kBM * kChunks);
+    const int r = (idx / kChunks) % kBM;
+    const int q = idx % kChunks;
+    const int64_t row = m0 + r;
+    if (row < p.n_tokens) {
+      const uint8_t* src = (mm == 0 ? &s_a[0][0] : &s_b[0][0]) + r * kRowBytes + 16 * q;
+      uint8_t* dst = reinterpret_cast<uint8_t*>(p.out[ct * (kBN / kDim) + mm]) + row * kRowBytes + 16 * q;
+      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
     }
   }
 }
@@ -197,7 +275,10 @@ hipError_t launch_bridge_gemm(const BridgeParams& p, hipStream_t s) {
   const int64_t m_tiles = (p.n_tokens + kBM - 1) / kBM;
   const int64_t groups = (m_tiles + 7) / 8;  // row blocks per XCD, rounded up
   const int64_t blocks = groups * 8 * (p.n_out * kDim / kBN);
-  hipLaunchKernelGGL(bridge_gemm_kernel, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, p);
+  if (p.fp8)
+    hipLaunchKernelGGL(bridge_gemm_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, p);
+  else
+    hipLaunchKernelGGL(bridge_gemm_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, p);
   return hipGetLastError();
 }
 

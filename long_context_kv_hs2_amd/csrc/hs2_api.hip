@@ -465,26 +465,35 @@ size_t hs2_bridge_workspace_bytes(int64_t n_tokens, int32_t d_model, int32_t hea
   return align_up(static_cast<size_t>(2 * n_bridged) * kDim * d_model * sizeof(uint16_t));
 }
 
-hs2_status hs2_bridge_kv(int64_t n_tokens, int32_t d_model, int32_t head_dim, int32_t n_bridged, const void* hidden,
-                         const void* const* w_k, const void* const* w_v, void* const* k_out, void* const* v_out,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+// The bridge projection, with bf16 or E4M3 (per-token scales) outputs.
+static hs2_status bridge_run(int64_t n_tokens, int32_t d_model, int32_t head_dim, int32_t n_bridged,
+                             const void* hidden, const void* const* w_k, const void* const* w_v,
+                             void* const* k_out, void* const* v_out, float* const* k_scale, float* const* v_scale,
+                             bool fp8, void* workspace, size_t workspace_bytes, void* stream) {
   if (n_tokens < 0) return fail(HS2_ERR_INVALID_ARGUMENT, "n_tokens < 0");
   if (head_dim != kDim) return fail(HS2_ERR_UNSUPPORTED, "head_dim %d (only 128 is supported)", head_dim);
   if (d_model <= 0 || d_model % 64) return fail(HS2_ERR_UNSUPPORTED, "d_model %d must be a positive multiple of 64", d_model);
   if (n_bridged < 1 || n_bridged > 4) return fail(HS2_ERR_UNSUPPORTED, "n_bridged %d (1..4 supported)", n_bridged);
   if (n_tokens > (int64_t(1) << 31)) return fail(HS2_ERR_UNSUPPORTED, "n_tokens above 2^31");
   if (!w_k || !w_v || !k_out || !v_out) return fail(HS2_ERR_INVALID_ARGUMENT, "weight/output pointer array is NULL");
+  if (fp8 && (!k_scale || !v_scale)) return fail(HS2_ERR_INVALID_ARGUMENT, "scale pointer array is NULL");
   const uint16_t* ws[8];
-  uint16_t* outs[8];
+  void* outs[8];
+  float* scales[8] = {};
   for (int l = 0; l < n_bridged; ++l) {
     ws[2 * l] = static_cast<const uint16_t*>(w_k[l]);
     ws[2 * l + 1] = static_cast<const uint16_t*>(w_v[l]);
-    outs[2 * l] = static_cast<uint16_t*>(k_out[l]);
-    outs[2 * l + 1] = static_cast<uint16_t*>(v_out[l]);
+    outs[2 * l] = k_out[l];
+    outs[2 * l + 1] = v_out[l];
+    if (fp8) {
+      scales[2 * l] = k_scale[l];
+      scales[2 * l + 1] = v_scale[l];
+    }
   }
   for (int i = 0; i < 2 * n_bridged; ++i) {
     HS2_TRY(check_ptr(ws[i], true, 16, "w_k/w_v entry"));
     HS2_TRY(check_ptr(outs[i], n_tokens > 0, 16, "k_out/v_out entry"));
+    if (fp8) HS2_TRY(check_ptr(scales[i], n_tokens > 0, 4, "k_scale/v_scale entry"));
   }
   HS2_TRY(check_ptr(hidden, n_tokens > 0, 16, "hidden"));
   const size_t need = hs2_bridge_workspace_bytes(n_tokens, d_model, head_dim, n_bridged);
@@ -500,9 +509,28 @@ hs2_status hs2_bridge_kv(int64_t n_tokens, int32_t d_model, int32_t head_dim, in
   p.n_out = 2 * n_bridged;
   p.hidden = static_cast<const uint16_t*>(hidden);
   p.w_t = w_t;
-  for (int i = 0; i < 8; ++i) p.out[i] = i < 2 * n_bridged ? outs[i] : nullptr;
+  p.fp8 = fp8 ? 1 : 0;
+  for (int i = 0; i < 8; ++i) {
+    p.out[i] = i < 2 * n_bridged ? outs[i] : nullptr;
+    p.scale[i] = i < 2 * n_bridged ? scales[i] : nullptr;
+  }
   HS2_HIP(launch_bridge_gemm(p, s), "bridge GEMM");
   return HS2_OK;
+}
+
+hs2_status hs2_bridge_kv(int64_t n_tokens, int32_t d_model, int32_t head_dim, int32_t n_bridged, const void* hidden,
+                         const void* const* w_k, const void* const* w_v, void* const* k_out, void* const* v_out,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return bridge_run(n_tokens, d_model, head_dim, n_bridged, hidden, w_k, w_v, k_out, v_out, nullptr, nullptr, false,
+                    workspace, workspace_bytes, stream);
+}
+
+hs2_status hs2_bridge_kv_fp8(int64_t n_tokens, int32_t d_model, int32_t head_dim, int32_t n_bridged,
+                             const void* hidden, const void* const* w_k, const void* const* w_v, void* const* k_out,
+                             float* const* k_scale, void* const* v_out, float* const* v_scale, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return bridge_run(n_tokens, d_model, head_dim, n_bridged, hidden, w_k, w_v, k_out, v_out, k_scale, v_scale, true,
+                    workspace, workspace_bytes, stream);
 }
 
 hs2_status hs2_stage_timing_enable(int32_t mode) {

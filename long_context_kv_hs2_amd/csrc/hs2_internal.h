@@ -143,7 +143,9 @@ struct BridgeParams {
   int n_out;                  // 2 * n_bridged column blocks of 128
   const uint16_t* hidden;     // [T][d_model]
   const uint16_t* w_t;        // workspace: [n_out * 128][d_model] (W transposed)
-  uint16_t* out[8];           // [T][128] each
+  void* out[8];               // [T][128] each: bf16, or E4M3 codes when fp8
+  float* scale[8];            // fp8: [T] per-token scale of each output
+  int fp8;                    // 1: E4M3 output with per-token scales
 };
 hipError_t launch_bridge_transpose_w(const uint16_t* const* w, int n_out, int d_model, uint16_t* w_t,
                                      hipStream_t s);

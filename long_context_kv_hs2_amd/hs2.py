@@ -25,7 +25,7 @@ STAGE_NAMES = ("full_partial", "full_merge", "score_select", "sparse")
 
 EXPORTED = (
     "hs2_decode_workspace_bytes", "hs2_decode_block", "hs2_full_decode_score", "hs2_topk_select",
-    "hs2_sparse_decode", "hs2_bridge_workspace_bytes", "hs2_bridge_kv", "hs2_stage_timing_enable",
+    "hs2_sparse_decode", "hs2_bridge_workspace_bytes", "hs2_bridge_kv", "hs2_bridge_kv_fp8", "hs2_stage_timing_enable",
     "hs2_stage_timing_read", "hs2_status_string", "hs2_last_error_message",
 )
 
@@ -77,6 +77,10 @@ def load(path: str = LIB_PATH):
     lib.hs2_bridge_kv.argtypes = [i64, i32, i32, i32, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                   ctypes.POINTER(vp), ctypes.POINTER(vp), vp, sz, vp]
     lib.hs2_bridge_kv.restype = ctypes.c_int
+    lib.hs2_bridge_kv_fp8.argtypes = [i64, i32, i32, i32, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                      ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                      vp, sz, vp]
+    lib.hs2_bridge_kv_fp8.restype = ctypes.c_int
     lib.hs2_stage_timing_enable.argtypes = [i32]
     lib.hs2_stage_timing_enable.restype = ctypes.c_int
     lib.hs2_stage_timing_read.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
@@ -225,6 +229,27 @@ def bridge_kv(hidden, w_k, w_v, k_out=None, v_out=None, workspace=None):
                                arr(*[w.data_ptr() for w in w_v]), arr(*[o.data_ptr() for o in k_out]),
                                arr(*[o.data_ptr() for o in v_out]), _ptr(ws), ws.numel(), _stream()))
     return k_out, v_out
+
+
+def bridge_kv_fp8(hidden, w_k, w_v, k_out=None, k_sc=None, v_out=None, v_sc=None, workspace=None):
+    """The bridge projection stored as E4M3 with per-token fp32 scales:
+    returns (k_codes, k_scales, v_codes, v_scales), lists of uint8 [T, 128]
+    and fp32 [T] tensors, one per bridged layer (allocated when not given)."""
+    dev = hidden.device
+    t, d_model = hidden.shape
+    n = len(w_k)
+    new = lambda shape, dt: [torch.empty(shape, dtype=dt, device=dev) for _ in range(n)]
+    k_out = new((t, 128), torch.uint8) if k_out is None else k_out
+    v_out = new((t, 128), torch.uint8) if v_out is None else v_out
+    k_sc = new((t,), torch.float32) if k_sc is None else k_sc
+    v_sc = new((t,), torch.float32) if v_sc is None else v_sc
+    arr = ctypes.c_void_p * n
+    ws = _workspace(bridge_workspace_bytes(t, d_model, n), dev, workspace)
+    check(load().hs2_bridge_kv_fp8(t, d_model, 128, n, _ptr(hidden), arr(*[w.data_ptr() for w in w_k]),
+                                   arr(*[w.data_ptr() for w in w_v]), arr(*[o.data_ptr() for o in k_out]),
+                                   arr(*[o.data_ptr() for o in k_sc]), arr(*[o.data_ptr() for o in v_out]),
+                                   arr(*[o.data_ptr() for o in v_sc]), _ptr(ws), ws.numel(), _stream()))
+    return k_out, k_sc, v_out, v_sc
 
 
 def stage_timing(on: bool, full_pass_only: bool = False):

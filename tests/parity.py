@@ -169,3 +169,42 @@ def check_bridge(h_bits, w_bits, out_bits, rows):
     frac1 = float((ulps <= 1).mean())
     assert frac1 >= 0.999, f"only {frac1:.5f} of elements within 1 ulp"
     return int(ulps.max()), frac1
+
+
+def e4m3_ordinal(codes):
+    """E4M3 codes -> integers in value order (sign-magnitude; both zeros 0)."""
+    c = np.asarray(codes, dtype=np.int32)
+    mag = c & 0x7F
+    return np.where(c & 0x80, -mag, mag)
+
+
+def check_bridge_fp8(h_bits, w_bits, codes, scales, rows):
+    """FP8 bridge outputs (E4M3 codes [T, 128], fp32 scales [T]) for the given
+    rows against the oracle's quantisation of the float64 products.  The GPU
+    quantises its fp32 products, each within gamma_n * sum|h w| of the exact
+    value (see check_bridge), so its row maxima, hence its scales, differ
+    from the oracle's by at most that much relative to the row maximum plus
+    one fp32 rounding; and a code can differ only where a value sits within
+    that error of a rounding boundary: there by one step of the code order.
+    Bar: scales within that relative bound, every code within one step, at
+    least 99.5 % of the codes equal.  Returns (fraction of equal codes,
+    worst relative scale difference)."""
+    h = O.bf16_bits_to_f64(h_bits[rows])
+    w = O.bf16_bits_to_f64(w_bits)
+    ref = h @ w
+    abs_sum = np.abs(h) @ np.abs(w)
+    n = h.shape[1]
+    u = 2.0 ** -24
+    gamma = n * u / (1 - n * u)
+    ref_codes, ref_scale = O.quantize_rows_e4m3(ref)
+    got_codes = np.asarray(codes)[rows]
+    got_scale = np.asarray(scales)[rows].astype(np.float64)
+    amax = np.abs(ref).max(axis=1)
+    rel_bound = np.where(amax > 0, gamma * abs_sum.max(axis=1) / np.where(amax > 0, amax, 1.0), 0.0) + 2.0 ** -22
+    rel = np.abs(got_scale - ref_scale.astype(np.float64)) / ref_scale.astype(np.float64)
+    assert (rel <= rel_bound).all(), f"scale off by {rel.max():.3e} (bound {rel_bound[rel.argmax()]:.3e})"
+    steps = np.abs(e4m3_ordinal(got_codes) - e4m3_ordinal(ref_codes))
+    assert steps.max() <= 1, f"a code {steps.max()} steps from the oracle's"
+    same = float((steps == 0).mean())
+    assert same >= 0.995, f"only {same:.5f} of the codes equal the oracle's"
+    return same, float(rel.max())

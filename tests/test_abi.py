@@ -157,3 +157,19 @@ def test_stage_timing_modes():
     assert lib.hs2_stage_timing_read(out, ctypes.byref(n)) == 0
     assert n.value == 0 and list(out) == [0.0] * hs2.N_STAGES
     assert lib.hs2_stage_timing_read(None, ctypes.byref(n)) == INVALID
+
+
+def test_bridge_fp8_validation():
+    # E4M3 outputs: the same checks as the bf16 call, plus the scale arrays
+    # (NULL array, NULL or misaligned entry); nothing reaches the GPU.
+    lib = hs2.load()
+    arr = ctypes.c_void_p * 1
+    one = arr(FAKE)
+    f = lib.hs2_bridge_kv_fp8
+    assert f(10, 4096, 64, 1, FAKE, one, one, one, one, one, one, FAKE, 1 << 30, None) == UNSUPPORTED
+    assert f(10, 4096, 128, 5, FAKE, one, one, one, one, one, one, FAKE, 1 << 30, None) == UNSUPPORTED
+    assert f(10, 4096, 128, 1, FAKE, one, one, one, None, one, one, FAKE, 1 << 30, None) == INVALID
+    assert f(10, 4096, 128, 1, FAKE, one, one, one, one, one, None, FAKE, 1 << 30, None) == INVALID
+    assert f(10, 4096, 128, 1, FAKE, one, one, one, arr(None), one, one, FAKE, 1 << 30, None) == INVALID
+    assert f(10, 4096, 128, 1, FAKE, one, one, one, arr(FAKE + 2), one, one, FAKE, 1 << 30, None) == INVALID
+    assert f(10, 4096, 128, 1, FAKE, one, one, one, one, one, one, FAKE, 100, None) == SMALL_WS

@@ -47,3 +47,41 @@ def test_bridge_one_hot_weights_copy_columns():
     torch.cuda.synchronize()
     got = k_out[0].view(torch.int16).cpu().numpy().view(np.uint16)
     np.testing.assert_array_equal(got, br["h"][:, cols])
+
+
+@pytest.mark.parametrize("tokens,d_model,n_bridged", [(1000, 256, 2), (128, 64, 1), (1, 4096, 3), (5000, 4096, 4)])
+def test_bridge_fp8_small_shapes(tokens, d_model, n_bridged):
+    print(f"case: bridge fp8 T={tokens} d_model={d_model} n_bridged={n_bridged}", flush=True)
+    br = inputs.make_bridge(tokens=tokens, d_model=d_model, n_bridged=n_bridged, seed=tokens + d_model + 1)
+    k_c, k_s, v_c, v_s = hs2.bridge_kv_fp8(to_dev(br["h"]), [to_dev(w) for w in br["w_k"]],
+                                           [to_dev(w) for w in br["w_v"]])
+    torch.cuda.synchronize()
+    rows = np.arange(tokens)
+    for l in range(n_bridged):
+        for w_bits, c, s in ((br["w_k"][l], k_c[l], k_s[l]), (br["w_v"][l], v_c[l], v_s[l])):
+            parity.check_bridge_fp8(br["h"], w_bits, c.cpu().numpy(), s.cpu().numpy(), rows)
+
+
+def test_bridge_fp8_special_rows():
+    # A zero row (scale 1, codes 0) and a row whose largest value saturates to
+    # exactly +-448 under its own scale; the bf16 and E4M3 calls share the
+    # product, so the decoded codes must match the bf16 output closely.
+    d_model = 256
+    rng = np.random.default_rng(11)
+    h = rng.standard_normal((300, d_model)) * 0.05
+    h[7] = 0.0
+    hb = inputs.to_bf16_bits(h.astype(np.float32))
+    w = inputs.to_bf16_bits((rng.standard_normal((d_model, 128)) * 0.05).astype(np.float32))
+    k_c, k_s, _, _ = hs2.bridge_kv_fp8(to_dev(hb), [to_dev(w)], [to_dev(w)])
+    k_b, _ = hs2.bridge_kv(to_dev(hb), [to_dev(w)], [to_dev(w)])
+    torch.cuda.synchronize()
+    codes, scales = k_c[0].cpu().numpy(), k_s[0].cpu().numpy()
+    assert scales[7] == 1.0 and (codes[7] == 0).all()
+    mags = (codes & 0x7F).max(axis=1)
+    assert (mags[np.arange(300) != 7] == 0x7E).all()   # each row's largest magnitude encodes to 448
+    from oracle import hs2_oracle as O
+    dec = O.e4m3_bytes_to_f64(codes) * scales.astype(np.float64)[:, None]
+    bf = O.bf16_bits_to_f64(k_b[0].view(torch.int16).cpu().numpy().view(np.uint16))
+    rowmax = np.abs(bf).max(axis=1, keepdims=True)
+    assert (np.abs(dec - bf) <= rowmax * 2.0 ** -4 + 1e-30).all()   # within E4M3's half step at the top
+    parity.check_bridge_fp8(hb, w, codes, scales, np.arange(300))

@@ -66,6 +66,36 @@ def test_workload4_b64_ragged_agent_mix():
     say(f"worst {w}")
 
 
+def test_workload5_fp8_bridge_then_decode():
+    # The bridge written as the FP8 cache (E4M3 + per-token scales), then the
+    # decode over it for one bridged layer (8 x 32768 packed).
+    say("case: workload 5 FP8 bridge (262144 x 4096 -> 3 x (K, V) E4M3), sampled rows, then decode")
+    br = inputs.make_bridge()
+    dev = "cuda"
+    h = torch.from_numpy(br["h"].view(np.int16)).view(torch.bfloat16).to(dev)
+    wk = [torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).to(dev) for w in br["w_k"]]
+    wv = [torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).to(dev) for w in br["w_v"]]
+    k_c, k_s, v_c, v_s = hs2.bridge_kv_fp8(h, wk, wv)
+    torch.cuda.synchronize()
+    del h
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([rng.choice(262144, 1500, replace=False), np.arange(64),
+                                     262144 - 1 - np.arange(64)]))
+    for l in range(3):
+        for name, w_bits, c, s in (("K", br["w_k"][l], k_c[l], k_s[l]), ("V", br["w_v"][l], v_c[l], v_s[l])):
+            same, rel = parity.check_bridge_fp8(br["h"], w_bits, c.cpu().numpy(), s.cpu().numpy(), rows)
+            say(f"fp8 bridge layer {l} {name}: {same:.5f} codes equal, scales within {rel:.2e}")
+    del br
+    queries = inputs.make_bridge_queries()
+    offs = np.arange(9, dtype=np.int64) * 32768
+    l = 1
+    d = dict(seq_offsets=offs, k=k_c[l].cpu().numpy(), v=v_c[l].cpu().numpy(), k_scale=k_s[l].cpu().numpy(),
+             v_scale=v_s[l].cpu().numpy(), q_full=queries[l][0], q_sparse=queries[l][1], kv="fp8_e4m3")
+    say("case: workload 5 decode over the FP8 bridged cache, layer 1; oracle on sequences 2 and 7")
+    w, _ = run_workload(d, [2, 7])
+    say(f"worst {w}")
+
+
 def test_workload5_bridge_then_decode():
     say("case: workload 5 bridge (262144 x 4096 -> 3 x (K, V)), sampled rows")
     br = inputs.make_bridge()
