@@ -43,6 +43,7 @@ N_Q_HEADS = 16
 WINDOW = 128  # [zh] forced recent window paragraph; [fr]/[ko] "Ce que fait"/"한 일"
 TOP_K = 1024  # same passages: 1024 tokens from before the window
 BAND_REL = 1e-5  # relative band around the k-th score inside which ties may differ
+BLOCK = 64  # gen-1 HySparse's selection unit ([en] paragraph on how the sparse layers select)
 
 
 # --------------------------------------------------------------------------
@@ -234,6 +235,50 @@ def select_tokens(score: np.ndarray, window: int = WINDOW, top_k: int = TOP_K):
     return {"sel": sel.astype(np.int64), "s_k": s_k, "band": band.astype(np.int64)}
 
 
+def select_blocks(score: np.ndarray, window: int = WINDOW, top_k: int = TOP_K, block: int = BLOCK):
+    """Gen-1 (block-level) selection under the same budget, the ablation
+    comparator of ``select_tokens``.
+
+    The previous generation picked whole 64-token blocks, so one relevant
+    token costs its block's share of the budget; the ablation keeps the
+    backbone and the attention budget and changes only the granularity
+    ([en] paragraphs on how the sparse layers select and on the ablation;
+    [zh] paragraph on block versus token selection; [fr] "Ce que fait
+    HySparse2").  Readings, where the pages are silent:
+
+    * blocks are [64 i, 64 i + 64), aligned to position 0; the candidates are
+      the complete blocks that end before the window, i = 0 .. (L - window) // 64 - 1;
+    * a block's score is the sum of its positions' scores (its share of the
+      attention mass);
+    * the budget is the token-level one: the window, plus top_k // 64 blocks,
+      ranked by block score descending, ties to the lower block;
+    * L <= window + top_k selects every position, as at token level.
+
+    score [L] -> dict(sel, s_k, band, band_blocks, block_scores) with ``sel``
+    ascending positions, ``s_k`` the last chosen block's score, and
+    ``band``/``band_blocks`` the positions/indices of the candidate blocks whose
+    score is within BAND_REL * s_k of s_k (where a selection may differ).
+    """
+    score = np.asarray(score, dtype=np.float64)
+    n = score.shape[0]
+    none = np.zeros(0, dtype=np.int64)
+    if n <= window + top_k:
+        return {"sel": np.arange(n, dtype=np.int64), "s_k": None, "band": none, "band_blocks": none,
+                "block_scores": np.zeros(0)}
+    nb = (n - window) // block
+    bs = score[:nb * block].reshape(nb, block).sum(axis=1)
+    kb = top_k // block
+    order = np.lexsort((np.arange(nb), -bs))  # block score descending, then block index ascending
+    top = order[:kb]
+    pos = (top[:, None] * block + np.arange(block)[None, :]).ravel()
+    sel = np.sort(np.concatenate([pos, np.arange(n - window, n)]))
+    s_k = float(bs[order[kb - 1]])
+    band_blocks = np.nonzero(np.abs(bs - s_k) <= BAND_REL * s_k)[0]
+    band = (band_blocks[:, None] * block + np.arange(block)[None, :]).ravel()
+    return {"sel": sel.astype(np.int64), "s_k": s_k, "band": band.astype(np.int64),
+            "band_blocks": band_blocks.astype(np.int64), "block_scores": bs}
+
+
 def sparse_attention(q: np.ndarray, k_sel: np.ndarray, v_sel: np.ndarray) -> np.ndarray:
     """One sparse layer: attention of its own query over the selected rows only.
 
@@ -247,18 +292,24 @@ def sparse_attention(q: np.ndarray, k_sel: np.ndarray, v_sel: np.ndarray) -> np.
 
 
 def decode_sequence(q_full: np.ndarray, q_sparse: np.ndarray, k: np.ndarray, v: np.ndarray,
-                    window: int = WINDOW, top_k: int = TOP_K, sel_override=None):
+                    window: int = WINDOW, top_k: int = TOP_K, sel_override=None, selection: str = "token"):
     """One sequence through one hybrid block at decode.
 
     q_full [H, D]; q_sparse [n_s, H, D]; k, v [L, D] decoded float64 rows.
-    Steps: full attention and scores, selection, then every sparse layer over
-    the same selection.  ``sel_override`` (ascending positions) replaces the
-    oracle's own selection in the sparse step; tests use it when a GPU list
-    differs from this one only inside the tie band.
+    Steps: full attention and scores, selection ("token": ``select_tokens``;
+    "block": the gen-1 comparator ``select_blocks``), then every sparse layer
+    over the same selection.  ``sel_override`` (ascending positions) replaces
+    the oracle's own selection in the sparse step; tests use it when a GPU
+    list differs from this one only inside the tie band.
     """
     o_full, p = full_attention(q_full, k, v)
     score = token_scores(p)
-    s = select_tokens(score, window, top_k)
+    if selection == "token":
+        s = select_tokens(score, window, top_k)
+    elif selection == "block":
+        s = select_blocks(score, window, top_k)
+    else:
+        raise ValueError(f"unknown selection {selection!r}")
     sel = s["sel"] if sel_override is None else np.asarray(sel_override, dtype=np.int64)
     ks, vs = k[sel], v[sel]
     o_sparse = np.stack([sparse_attention(q_sparse[l], ks, vs) for l in range(q_sparse.shape[0])]) \
@@ -268,7 +319,7 @@ def decode_sequence(q_full: np.ndarray, q_sparse: np.ndarray, k: np.ndarray, v: 
 
 
 def decode_block(seq_offsets, k_raw, v_raw, q_full, q_sparse, kv_dtype="bf16",
-                 k_scale=None, v_scale=None, seqs=None, window=WINDOW, top_k=TOP_K):
+                 k_scale=None, v_scale=None, seqs=None, window=WINDOW, top_k=TOP_K, selection="token"):
     """The hybrid block for a packed batch, one sequence at a time.
 
     seq_offsets [B+1] (packed rows), k_raw/v_raw [N, D] stored values,
@@ -288,7 +339,7 @@ def decode_block(seq_offsets, k_raw, v_raw, q_full, q_sparse, kv_dtype="bf16",
         v = decode_kv(v_raw[a:e], kv_dtype, vs)
         qf = np.asarray(q_full[b], dtype=np.float64)
         qs = np.asarray(q_sparse[:, b], dtype=np.float64)
-        out[b] = decode_sequence(qf, qs, k, v, window, top_k)
+        out[b] = decode_sequence(qf, qs, k, v, window, top_k, selection=selection)
     return out
 
 
