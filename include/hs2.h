@@ -130,6 +130,23 @@ hs2_status hs2_topk_select(const hs2_decode_desc* desc, const int64_t* seq_offse
                            const float* score, int32_t* sel_idx, int32_t* sel_count,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Stage call: gen-1 (block-level) selection from given scores, the
+ * comparator the pages' ablation sets against the token-level selection at
+ * the same attention budget ("Luo Fuli Teases Xiaomi MiMo-V3 Architecture",
+ * paragraphs on how the sparse layers select and on the ablation;
+ * readaitime.com news of 2026-09-24, paragraph on block versus token
+ * selection).  Sequence b selects the last `window` positions plus the
+ * top_k / 64 = 16 complete 64-token blocks [64 i, 64 i + 64) that end before
+ * the window, ranked by the sum of their positions' scores (descending;
+ * ties to the lower block); a context of at most window + top_k positions
+ * selects every position.  Arguments, workspace, errors and output format
+ * (ascending, -1 padded, sel_count = min(L_b, window + top_k)) as
+ * hs2_topk_select.  hs2_full_decode_score, then this, then
+ * hs2_sparse_decode is the hybrid block with gen-1 selection.               */
+hs2_status hs2_block_select(const hs2_decode_desc* desc, const int64_t* seq_offsets,
+                            const float* score, int32_t* sel_idx, int32_t* sel_count,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* Stage call: the sparse layers over a given selection.  desc->n_sparse_layers
  * queries in q_sparse; sel_idx/sel_count as written by hs2_topk_select (the
  * caller may keep them across calls: one selection serves every layer).

@@ -63,7 +63,7 @@ struct DecodeLayout {
   int chunk = 0;
   int chunks_per_seq = 0;
   size_t partials = 0, stats = 0, pstats = 0, spill = 0, score = 0, hist0 = 0, counters = 0, selbuf = 0, cand = 0,
-         shat = 0, tile_stats = 0, tile_ub = 0, cand_cnt = 0, sparse = 0, total = 0;
+         shat = 0, tile_stats = 0, tile_ub = 0, cand_cnt = 0, sparse = 0, blocks = 0, total = 0;
   int cand_blocks = 0;
 };
 
@@ -99,6 +99,7 @@ DecodeLayout decode_layout(const hs2_decode_desc& d) {
   const int n_sparse = d.n_sparse_layers > 0 ? d.n_sparse_layers : 1;
   const int slices = sparse_slices(d.batch, n_sparse);
   L.sparse = take(slices > 1 ? B * n_sparse * static_cast<size_t>(slices) * kPartialFloats * sizeof(float) : 0);
+  L.blocks = take(((N >> 6) + B + 1) * sizeof(float));  // gen-1 block selection: per-block score sums
   L.total = off;
   return L;
 }
@@ -437,6 +438,33 @@ hs2_status hs2_topk_select(const hs2_decode_desc* desc, const int64_t* seq_offse
   HS2_HIP(launch_select_init(sp, d.batch, a.stream), "selection init");
   HS2_HIP(launch_score_hist(sp, d.batch, d.max_context, false, true, a.stream), "score histogram");
   HS2_HIP(launch_collect_finish(sp, d.batch, d.max_context, a.stream), "selection");
+  return HS2_OK;
+}
+
+hs2_status hs2_block_select(const hs2_decode_desc* desc, const int64_t* seq_offsets, const float* score,
+                            int32_t* sel_idx, int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  HS2_TRY(check_desc(desc));
+  const hs2_decode_desc& d = *desc;
+  const bool any = d.batch > 0;
+  if (any && !seq_offsets) return fail(HS2_ERR_INVALID_ARGUMENT, "seq_offsets is NULL");
+  if (seq_offsets && !aligned(seq_offsets, 8)) return fail(HS2_ERR_INVALID_ARGUMENT, "seq_offsets not 8-byte aligned");
+  HS2_TRY(check_ptr(score, d.total_tokens > 0, 4, "score"));
+  HS2_TRY(check_ptr(sel_idx, any, 4, "sel_idx"));
+  HS2_TRY(check_ptr(sel_count, any, 4, "sel_count"));
+  DecodeLayout L;
+  HS2_TRY(check_workspace(d, workspace, workspace_bytes, L));
+  if (!any) return HS2_OK;
+  BlockParams p{};
+  p.seq_offsets = seq_offsets;
+  p.total_tokens = d.total_tokens;
+  p.max_context = d.max_context;
+  p.batch = d.batch;
+  p.score = score;
+  p.block_scores = reinterpret_cast<float*>(ws_at(workspace, L.blocks));
+  p.sel_idx = sel_idx;
+  p.sel_count = sel_count;
+  HS2_HIP(launch_block_select(p, static_cast<hipStream_t>(stream)), "block selection");
   return HS2_OK;
 }
 

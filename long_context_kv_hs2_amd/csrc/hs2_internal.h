@@ -60,6 +60,21 @@ struct MergeParams {
 hipError_t launch_merge(const MergeParams& p, int batch, hipStream_t s);
 
 // ---- score and token selection ---------------------------------------------
+// Gen-1 block-level selection (the ablation comparator): 64-token blocks.
+constexpr int kSelectBlock = 64;
+constexpr int kTopBlocks = kTopK / kSelectBlock;
+struct BlockParams {
+  const int64_t* seq_offsets;
+  int64_t total_tokens;
+  int64_t max_context;
+  int batch;
+  const float* score;         // [N] per-token scores
+  float* block_scores;        // [N / 64 + B]: block i of the sequence at row base_b in slot (base_b >> 6) + b + i
+  int32_t* sel_idx;           // [B][window + top_k]
+  int32_t* sel_count;         // [B]
+};
+hipError_t launch_block_select(const BlockParams& p, hipStream_t s);
+
 struct SelectParams {
   const int64_t* seq_offsets;
   int64_t total_tokens;

@@ -24,7 +24,7 @@ N_STAGES = 4
 STAGE_NAMES = ("full_partial", "full_merge", "score_select", "sparse")
 
 EXPORTED = (
-    "hs2_decode_workspace_bytes", "hs2_decode_block", "hs2_full_decode_score", "hs2_topk_select",
+    "hs2_decode_workspace_bytes", "hs2_decode_block", "hs2_full_decode_score", "hs2_topk_select", "hs2_block_select",
     "hs2_sparse_decode", "hs2_bridge_workspace_bytes", "hs2_bridge_kv", "hs2_bridge_kv_fp8", "hs2_stage_timing_enable",
     "hs2_stage_timing_read", "hs2_status_string", "hs2_last_error_message",
 )
@@ -70,6 +70,8 @@ def load(path: str = LIB_PATH):
     lib.hs2_full_decode_score.restype = ctypes.c_int
     lib.hs2_topk_select.argtypes = [dp, vp, vp, vp, vp, vp, sz, vp]
     lib.hs2_topk_select.restype = ctypes.c_int
+    lib.hs2_block_select.argtypes = [dp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hs2_block_select.restype = ctypes.c_int
     lib.hs2_sparse_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hs2_sparse_decode.restype = ctypes.c_int
     lib.hs2_bridge_workspace_bytes.argtypes = [i64, i32, i32, i32]
@@ -194,6 +196,58 @@ def topk_select(seq_offsets, score, batch, max_context):
     check(load().hs2_topk_select(ctypes.byref(desc), _ptr(seq_offsets), _ptr(score), _ptr(sel_idx),
                                  _ptr(sel_count), _ptr(ws), ws.numel(), _stream()))
     return sel_idx, sel_count
+
+
+def block_select(seq_offsets, score, batch, max_context):
+    """Gen-1 block-level selection (16 blocks of 64 + the window) from given scores."""
+    dev = score.device
+    desc = make_desc(batch, score.shape[0], max_context, 0)
+    sel_idx = torch.empty((batch, 1152), dtype=torch.int32, device=dev)
+    sel_count = torch.empty((batch,), dtype=torch.int32, device=dev)
+    ws = _workspace(decode_workspace_bytes(desc), dev)
+    check(load().hs2_block_select(ctypes.byref(desc), _ptr(seq_offsets), _ptr(score), _ptr(sel_idx),
+                                  _ptr(sel_count), _ptr(ws), ws.numel(), _stream()))
+    return sel_idx, sel_count
+
+
+class BlockSelectDecode:
+    """The hybrid block with gen-1 selection, as three stage calls sharing one
+    workspace and fixed outputs: full attention with scores, block selection,
+    then the sparse layers over that list."""
+
+    def __init__(self, seq_offsets, k, v, q_full, q_sparse, k_scale=None, v_scale=None, max_context=None):
+        dev = k.device
+        self.seq_offsets, self.k, self.v, self.k_scale, self.v_scale = seq_offsets, k, v, k_scale, v_scale
+        self.q_full, self.q_sparse = q_full, q_sparse
+        batch = q_full.shape[0]
+        n_s = 0 if q_sparse is None else q_sparse.shape[0]
+        if max_context is None:
+            max_context = int((seq_offsets[1:] - seq_offsets[:-1]).max().item()) if batch else 0
+        self.desc = make_desc(batch, k.shape[0], max_context, n_s, kv_dtype_of(k))
+        self.o_full = torch.empty((batch, 16, 128), dtype=torch.float32, device=dev)
+        self.o_sparse = torch.empty((n_s, batch, 16, 128), dtype=torch.float32, device=dev) if n_s else None
+        self.sel_idx = torch.empty((batch, 1152), dtype=torch.int32, device=dev)
+        self.sel_count = torch.empty((batch,), dtype=torch.int32, device=dev)
+        self.score = torch.empty((k.shape[0],), dtype=torch.float32, device=dev)
+        self.workspace = _workspace(decode_workspace_bytes(self.desc), dev)
+
+    def __call__(self):
+        lib, d, ws, st = load(), ctypes.byref(self.desc), _ptr(self.workspace), _stream()
+        n = self.workspace.numel()
+        check(lib.hs2_full_decode_score(d, _ptr(self.seq_offsets), _ptr(self.k), _ptr(self.v), _ptr(self.k_scale),
+                                        _ptr(self.v_scale), _ptr(self.q_full), _ptr(self.o_full), _ptr(self.score),
+                                        ws, n, st))
+        check(lib.hs2_block_select(d, _ptr(self.seq_offsets), _ptr(self.score), _ptr(self.sel_idx),
+                                   _ptr(self.sel_count), ws, n, st))
+        if self.desc.n_sparse_layers:
+            check(lib.hs2_sparse_decode(d, _ptr(self.seq_offsets), _ptr(self.k), _ptr(self.v), _ptr(self.k_scale),
+                                        _ptr(self.v_scale), _ptr(self.q_sparse), _ptr(self.sel_idx),
+                                        _ptr(self.sel_count), _ptr(self.o_sparse), ws, n, st))
+        return self
+
+    def outputs(self):
+        return dict(o_full=self.o_full, o_sparse=self.o_sparse, sel_idx=self.sel_idx,
+                    sel_count=self.sel_count, score=self.score)
 
 
 def sparse_decode(seq_offsets, k, v, q_sparse, sel_idx, sel_count, k_scale=None, v_scale=None, max_context=None):

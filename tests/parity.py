@@ -65,11 +65,12 @@ def check_selection(sel_gpu, count, length, ref):
     return got
 
 
-def check_decode(d, out, seqs=None, tol=None, score_tol=5e-6, oracle_cache=None):
+def check_decode(d, out, seqs=None, tol=None, score_tol=5e-6, oracle_cache=None, selection="token"):
     """Compare GPU outputs (dict of tensors) with the oracle on `seqs`.
 
     Returns a dict of the worst errors seen.  ``oracle_cache`` may hold
-    per-sequence oracle results already computed (keyed by sequence)."""
+    per-sequence oracle results already computed (keyed by sequence).
+    ``selection`` names the oracle's rule ("token", or "block" for gen-1)."""
     kv = d["kv"]
     tol = TOL[kv] if tol is None else tol
     offs = d["seq_offsets"]
@@ -97,7 +98,8 @@ def check_decode(d, out, seqs=None, tol=None, score_tol=5e-6, oracle_cache=None)
             vs = None if d["v_scale"] is None else d["v_scale"][a:e]
             kf = O.decode_kv(d["k"][a:e], kv, ks)
             vf = O.decode_kv(d["v"][a:e], kv, vs)
-            ref = O.decode_sequence(d["q_full"][b].astype(np.float64), d["q_sparse"][:, b].astype(np.float64), kf, vf)
+            ref = O.decode_sequence(d["q_full"][b].astype(np.float64), d["q_sparse"][:, b].astype(np.float64), kf, vf,
+                                    selection=selection)
             ref["_k"], ref["_v"] = kf, vf
             if oracle_cache is not None:
                 oracle_cache[b] = ref
@@ -106,7 +108,7 @@ def check_decode(d, out, seqs=None, tol=None, score_tol=5e-6, oracle_cache=None)
         worst["o_full"] = max(worst["o_full"], err)
         got = check_selection(sel_idx[b], int(sel_count[b]), length, ref)
         if score is not None:
-            s_k = ref["s_k"] if ref["s_k"] else ref["score"].max()
+            s_k = O.select_tokens(ref["score"])["s_k"] or ref["score"].max()  # the token-level k-th score
             den = np.maximum(ref["score"], s_k)
             serr = float((np.abs(score[a:e].astype(np.float64) - ref["score"]) / den).max())
             assert serr <= score_tol, f"score seq {b}: {serr:.3e} (relative, floored at s_k) > {score_tol}"

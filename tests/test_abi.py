@@ -131,6 +131,12 @@ def test_stage_calls_validate():
     d = desc()
     n = lib.hs2_decode_workspace_bytes(ctypes.byref(d))
     assert lib.hs2_topk_select(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, n, None) == INVALID
+    assert lib.hs2_block_select(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, n, None) == INVALID
+    assert lib.hs2_block_select(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, n, None) == INVALID
+    assert lib.hs2_block_select(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, n - 256, None) == SMALL_WS
+    bad = desc()
+    bad.top_k = 512
+    assert lib.hs2_block_select(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, n, None) == UNSUPPORTED
     assert lib.hs2_full_decode_score(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None, FAKE, n,
                                      None) == INVALID
     assert lib.hs2_sparse_decode(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, None, FAKE, FAKE, FAKE, n,

@@ -1,0 +1,92 @@
+"""GPU parity of the gen-1 (block-level) selection, the ablation comparator:
+exact on given scores, and the hybrid block with gen-1 selection against the
+oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_kv_hs2_amd import hs2, inputs
+from oracle import hs2_oracle as O
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def run_block_select(lengths, scores):
+    offs = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    t_offs = torch.from_numpy(offs).cuda()
+    t_score = torch.from_numpy(scores.astype(np.float32)).cuda()
+    sel, cnt = hs2.block_select(t_offs, t_score, len(lengths), int(max(lengths)) if len(lengths) else 0)
+    torch.cuda.synchronize()
+    return offs, sel.cpu().numpy(), cnt.cpu().numpy()
+
+
+LENGTHS = [0, 5, 1152, 1153, 1216, 1217, 5000, 70001, 131072]
+
+
+@pytest.mark.parametrize("kind", ["integers", "constant", "descending"])
+def test_block_select_exact_on_given_scores(kind):
+    # Scores whose block sums are exact in fp32 (small integers, or equal
+    # powers of two), with heavy ties: the list must match bit for bit.
+    print(f"case: block select, {kind} scores, lengths {LENGTHS}", flush=True)
+    rng = np.random.default_rng(3)
+    n = sum(LENGTHS)
+    if kind == "integers":
+        scores = rng.integers(0, 4, size=n).astype(np.float32)
+    elif kind == "constant":
+        scores = np.full(n, 0.25, dtype=np.float32)
+    else:
+        scores = np.concatenate([np.arange(l, 0, -1) for l in LENGTHS]).astype(np.float32) if n else np.zeros(0)
+    offs, sel, cnt = run_block_select(LENGTHS, scores)
+    for b, length in enumerate(LENGTHS):
+        ref = O.select_blocks(scores[offs[b]:offs[b + 1]].astype(np.float64))
+        assert cnt[b] == min(length, 1152)
+        np.testing.assert_array_equal(sel[b, :cnt[b]], ref["sel"], err_msg=f"{kind} L={length}")
+        assert np.all(sel[b, cnt[b]:] == -1)
+
+
+def test_block_select_random_scores_outside_band():
+    lengths = [3000, 131072, 40000, 1048576]
+    print(f"case: block select, exponential scores, lengths {lengths}", flush=True)
+    rng = np.random.default_rng(4)
+    scores = (rng.exponential(size=sum(lengths)) * 1e-5).astype(np.float32)
+    offs, sel, cnt = run_block_select(lengths, scores)
+    for b, length in enumerate(lengths):
+        ref = O.select_blocks(scores[offs[b]:offs[b + 1]].astype(np.float64))
+        parity.check_selection(sel[b], int(cnt[b]), length, ref)
+
+
+def test_block_select_empty_batch_and_zero_tokens():
+    offs, sel, cnt = run_block_select([0, 0, 0], np.zeros(0, dtype=np.float32))
+    assert np.all(cnt == 0) and np.all(sel == -1)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_hybrid_block_with_block_selection(kv):
+    lengths = [300, 1500, 4000, 20000, 0, 70000]
+    print(f"case: gen-1 hybrid block, {kv}, lengths {lengths}", flush=True)
+    d = inputs.make_decode(lengths=lengths, n_sparse=3, kv=kv, seed=17, needles=40)
+    t = parity.to_device(d)
+    blk = hs2.BlockSelectDecode(t["seq_offsets"], t["k"], t["v"], t["q_full"], t["q_sparse"], t["k_scale"],
+                                t["v_scale"], t["max_context"])
+    blk()
+    torch.cuda.synchronize()
+    w = parity.check_decode(d, blk.outputs(), selection="block")
+    print(f"worst {w}", flush=True)
+
+
+def test_block_selection_differs_from_token_selection():
+    # On a needle workload the two rules pick different lists (the ablation's
+    # point); both are checked against their own oracle above.
+    d = inputs.make_decode(lengths=[20000], n_sparse=1, seed=18, needles=40)
+    t = parity.to_device(d)
+    blk = hs2.BlockSelectDecode(t["seq_offsets"], t["k"], t["v"], t["q_full"], t["q_sparse"], None, None,
+                                t["max_context"])
+    blk()
+    tok = hs2.decode_block(t["seq_offsets"], t["k"], t["v"], t["q_full"], t["q_sparse"], max_context=t["max_context"])
+    torch.cuda.synchronize()
+    a = set(blk.sel_idx[0].cpu().numpy().tolist())
+    b = set(tok["sel_idx"][0].cpu().numpy().tolist())
+    assert len(a ^ b) > 0
+    assert torch.equal(blk.o_full, tok["o_full"])  # the full layer is the same call
