@@ -17,7 +17,13 @@ rocprofv3 FETCH_SIZE/WRITE_SIZE runs summarised under profiles/ (scaled by a
 The cpu_baseline leg times the fp64 oracle on a bounded sample of the same
 workload (whole sequences, one after another, until about 15 s have passed).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 2|3|4|5]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 2|3|4|5] [--selection token|block]
+
+``--selection block`` times the same workload through the gen-1 (block-level)
+selection instead, the comparator of the pages' ablation: the full layer with
+every score (hs2_full_decode_score), hs2_block_select, then the sparse layers.
+Each line also carries per-launch percentiles of the full pass, a "cold"
+full-pass time (after 1 GiB of writes has evicted the caches), and the device.
 
 Workload 5 times the KV-Bridging projection (262144 x 4096 hidden states into
 3 layers' K and V, one bf16 MFMA GEMM) and then each bridged layer's decode
@@ -66,6 +72,38 @@ def measured_traffic(workload):
     if fields.get("source_sha256", "").strip() != sha:
         return None
     return int(fields["traffic_bytes_per_launch"])
+
+
+def pct(x):
+    """Mean, p10, median and p90 (ms) of per-call durations."""
+    x = np.asarray(x, dtype=np.float64)
+    if x.size == 0:
+        return None
+    return {"mean": round(float(x.mean()), 5), "p10": round(float(np.percentile(x, 10)), 5),
+            "median": round(float(np.median(x)), 5), "p90": round(float(np.percentile(x, 90)), 5), "n": int(x.size)}
+
+
+def device_info(torch):
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "clock_khz": getattr(p, "clock_rate", None), "hip": torch.version.hip, "torch": torch.__version__}
+
+
+def cold_full_pass(torch, hs2, step, dev, reps=5):
+    """The full pass right after 1 GiB of writes (more than the 256 MB
+    Infinity Cache and the L2s hold), so its K/V reads start cold."""
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    times = []
+    for i in range(reps):
+        scratch.fill_(i + 1)
+        torch.cuda.synchronize()
+        hs2.stage_timing(True, full_pass_only=True)
+        step()
+        torch.cuda.synchronize()
+        hs2.stage_timing(False)
+        times.extend(hs2.stage_timing_read_calls()[:, 0].tolist())
+    del scratch
+    return pct(times)
 
 
 def cpu_baseline(d, budget_s=15.0):
@@ -161,6 +199,24 @@ def bench_bridge(args, torch, hs2, inputs, dev):
             blk()
     torch.cuda.synchronize()
     decode_fp8_ms = (time.perf_counter() - t0) / args.steps * 1e3
+    # Decode-time bridging: the current token's hidden row of each of the
+    # batch's sequences projected into the 3 bridged layers' caches.
+    h_step = h[:batch].contiguous()
+    aws = torch.empty(hs2.load().hs2_bridge_append_workspace_bytes(batch, d_model, 128, n_l), dtype=torch.uint8,
+                      device=dev)
+
+    def time_append(kc, vc, ksc, vsc):
+        for _ in range(5):
+            hs2.bridge_append(offs, h_step, wk, wv, kc, vc, ksc, vsc, aws)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            hs2.bridge_append(offs, h_step, wk, wv, kc, vc, ksc, vsc, aws)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    append_fp8_ms = time_append(k8, v8, ks8, vs8)
     del blocks8, k8, v8, ks8, vs8
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -169,6 +225,7 @@ def bench_bridge(args, torch, hs2, inputs, dev):
             blk()
     torch.cuda.synchronize()
     decode_s = (time.perf_counter() - t0) / args.steps
+    append_ms = time_append(k_out, v_out, None, None)
     # Per-stage breakdown (diagnostic), from extra untimed steps.
     hs2.stage_timing(True)
     hs2.stage_timing_read()
@@ -190,9 +247,12 @@ def bench_bridge(args, torch, hs2, inputs, dev):
                      "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
                      "kernel": "bridge_gemm_kernel (hs2_bridge_kv)", "alg_flops_per_launch": flops,
                      "mean_launch_ms": bridge_ms},
+        "device": device_info(torch),
         "bridge_ms": bridge_ms,
         "bridge_fp8_ms": bridge_fp8_ms,
         "fp8_cache_decode_ms_per_step": decode_fp8_ms,
+        "decode_bridge_append_ms": {"bf16": append_ms, "fp8_e4m3": append_fp8_ms, "rows": batch,
+                                    "weight_bytes": 2 * n_l * d_model * 128 * 2},
         "decode_stages_ms_per_layer": {k: round(v, 5) for k, v in stages.items()},
     }
 
@@ -203,6 +263,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOADS))
+    ap.add_argument("--selection", choices=("token", "block"), default="token",
+                    help="token: the method's selection; block: the gen-1 64-token-block comparator")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy before the timed region (for HBM counter scaling)")
@@ -247,6 +309,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if args.selection == "block":
+        blk = hs2.BlockSelectDecode(offs_t, k, v, q_full, q_sparse, ks, vs, int(lens.max()))
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     for _ in range(args.warmup):
         blk()
     torch.cuda.synchronize()
@@ -261,18 +326,35 @@ def main():
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     hs2.stage_timing(False)
-    k1_stages, n_rec = hs2.stage_timing_read()
+    k1_calls = hs2.stage_timing_read_calls()[:, 0]
+    n_rec = int(k1_calls.shape[0])
     # Per-stage breakdown (diagnostic), from extra untimed steps.
     hs2.stage_timing(True)
+    extra = []
     for _ in range(min(args.steps, 20)):
-        blk()
+        if args.selection == "block":
+            blk(marks)
+            torch.cuda.synchronize()
+            extra.append((marks[0].elapsed_time(marks[1]), marks[1].elapsed_time(marks[2])))
+        else:
+            blk()
     torch.cuda.synchronize()
     hs2.stage_timing(False)
-    stages, _ = hs2.stage_timing_read()
+    calls = hs2.stage_timing_read_calls()
+    stage_pct = {name: pct(calls[:, i]) for i, name in enumerate(hs2.STAGE_NAMES)}
+    stages = {name: (stage_pct[name] or {}).get("mean", 0.0) for name in hs2.STAGE_NAMES}
+    if args.selection == "block":
+        # hs2_full_decode_score records partial pass, merge and score pass; the
+        # block selection and the sparse layers are separate calls
+        stage_pct = {"full_partial": stage_pct["full_partial"], "full_merge": stage_pct["full_merge"],
+                     "score_pass": stage_pct["score_select"], "block_select": pct([e[0] for e in extra]),
+                     "sparse": pct([e[1] for e in extra])}
+        stages = {name: v["mean"] for name, v in stage_pct.items()}
+    cold = cold_full_pass(torch, hs2, blk, dev)
 
     ms_per_step = dt * 1e3 / args.steps
     value = batch * args.steps / dt
-    k1_ms = k1_stages["full_partial"]
+    k1_ms = float(k1_calls.mean())
     alg_bytes = n_tokens * KV_ROW_BYTES[kv] + batch * 16 * 128 * 4
     achieved = alg_bytes / (k1_ms * 1e-3) / 1e9
     result = {
@@ -290,15 +372,22 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOADS[args.workload], "batch": batch, "context_tokens": n_tokens,
                    "max_context": int(lens.max()), "kv_cache": kv, "q_heads": 16, "kv_heads": 1,
-                   "head_dim": 128, "window": 128, "top_k": 1024, "n_sparse_layers": int(q_sparse.shape[0])},
+                   "head_dim": 128, "window": 128, "top_k": 1024, "n_sparse_layers": int(q_sparse.shape[0]),
+                   "selection": "token" if args.selection == "token" else "block64 (gen-1 comparator)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload),
-                     "kernel": "full_partial_kernel (hs2_full_decode_score split-K pass)",
-                     "alg_bytes_per_launch": alg_bytes, "mean_launch_ms": k1_ms},
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(args.workload) if args.selection == "token" else None,
+                     "kernel": ("full_partial_kernel (split-K pass, score bounds)" if args.selection == "token"
+                                else "full_partial_kernel (split-K pass, every logit kept for the scores)"),
+                     "alg_bytes_per_launch": alg_bytes, "mean_launch_ms": k1_ms,
+                     "launch_ms": pct(k1_calls)},
         "stages_ms": {k2: round(v2, 5) for k2, v2 in stages.items()},  # untimed extra steps
+        "stages_ms_percentiles": stage_pct,
+        "cold_full_partial_ms": cold,
         "stage_calls_timed": n_rec,
+        "device": device_info(torch),
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.selection == "token":
         result["cpu_baseline"] = cpu_baseline(d)
     print(json.dumps(result), flush=True)
 

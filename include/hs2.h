@@ -192,20 +192,55 @@ hs2_status hs2_bridge_kv_fp8(int64_t n_tokens, int32_t d_model, int32_t head_dim
                              void* const* v_out, float* const* v_scale,
                              void* workspace, size_t workspace_bytes, void* stream);
 
-/* Per-stage kernel timing of hs2_decode_block, for benchmarks.  Mode 1:
- * each call records HIP events around its stages on its stream
- * (HS2_N_STAGES stages: 0 full-attention partial pass, 1 full-attention
- * merge, 2 score and selection, 3 sparse layers).  Mode 2: only the two
- * events around stage 0 (each marker costs the step about 1.5 us).  Mode 0:
- * off.  Other modes: HS2_ERR_INVALID_ARGUMENT.  The events are timing-only
- * (no system-scope fence).  hs2_stage_timing_read waits for the recorded
- * events and returns, per stage, the mean duration in milliseconds over the
- * calls recorded since the last read (at most 1024; 0 for stages a call did
- * not record), and the number of calls in *n_calls; it then clears the
- * record.                                                                  */
+/* Decode-time KV Bridging: each decode step, the current token's hidden
+ * state is projected by every bridged layer's W_k and W_v (the products of
+ * hs2_bridge_kv, one row per sequence) and written into that layer's cache at
+ * the current token's row, seq_offsets[b + 1] - 1, where hs2_decode_block
+ * reads it (toolnavs.com (ko), section "HySparse2가 한 일"; [en] paragraph on
+ * KV Bridging).  Sequences with L_b == 0 are skipped; no other row changes.
+ * hidden (device) bf16 [batch][d_model]; w_k, w_v (host arrays of n_bridged
+ *   device pointers) bf16 [d_model][head_dim];
+ * k_cache, v_cache (host arrays of n_bridged device pointers, 16-byte
+ *   aligned) [total_tokens]
+ *   [head_dim] rows, bf16 or E4M3 codes per kv_dtype (hs2_kv_dtype);
+ * k_scale, v_scale (host arrays of device pointers) fp32 [total_tokens] for
+ *   E4M3 (the row's scale is written: row max |value| / 448, 1 for a zero
+ *   row, codes rounded to nearest even and saturated, as hs2_bridge_kv_fp8),
+ *   NULL for bf16 (round to nearest even).
+ * seq_offsets (device) int64 [batch + 1], as in hs2_decode_block.
+ * Supported: head_dim 128, d_model a multiple of 128 up to 16384,
+ * 1 <= n_bridged <= 4, batch >= 0.  workspace (device) >=
+ * hs2_bridge_append_workspace_bytes(...), 256-byte aligned.  fp32
+ * accumulation; the summation order differs from hs2_bridge_kv's, so a row
+ * can differ from the prefill bridge's in the last bit.                     */
+size_t hs2_bridge_append_workspace_bytes(int32_t batch, int32_t d_model, int32_t head_dim,
+                                         int32_t n_bridged);
+hs2_status hs2_bridge_append(int32_t batch, int32_t d_model, int32_t head_dim, int32_t n_bridged,
+                             int32_t kv_dtype, const int64_t* seq_offsets, int64_t total_tokens,
+                             const void* hidden, const void* const* w_k, const void* const* w_v,
+                             void* const* k_cache, void* const* v_cache,
+                             float* const* k_scale, float* const* v_scale,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Per-stage kernel timing of hs2_decode_block and hs2_full_decode_score, for
+ * benchmarks.  Mode 1: each call records HIP events around its stages on its
+ * stream (HS2_N_STAGES stages: 0 full-attention partial pass, 1 full-attention
+ * merge, 2 score and selection (hs2_full_decode_score: the score pass),
+ * 3 sparse layers (hs2_full_decode_score: none)).  Mode 2: only the two events
+ * around stage 0 (each marker costs the step about 1.5 us).  Mode 0: off.
+ * Other modes: HS2_ERR_INVALID_ARGUMENT.  The events are timing-only (no
+ * system-scope fence).  At most 1024 calls are recorded between reads.
+ * hs2_stage_timing_read waits for the recorded events and returns, per stage,
+ * the mean duration in milliseconds over the calls recorded since the last
+ * read (a stage a call did not record counts as 0), and the number of calls
+ * in *n_calls; it then clears the record.  hs2_stage_timing_read_calls does
+ * the same but writes each call's durations, ms[r * HS2_N_STAGES + stage] for
+ * the first max_calls calls r (host array), instead of the means.           */
 #define HS2_N_STAGES 4
 hs2_status hs2_stage_timing_enable(int32_t mode);
 hs2_status hs2_stage_timing_read(float* mean_ms /* [HS2_N_STAGES] (host) */, int32_t* n_calls);
+hs2_status hs2_stage_timing_read_calls(float* ms /* [max_calls][HS2_N_STAGES] (host) */, int32_t max_calls,
+                                       int32_t* n_calls);
 
 const char* hs2_status_string(hs2_status status);
 const char* hs2_last_error_message(void);

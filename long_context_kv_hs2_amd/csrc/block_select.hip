@@ -15,21 +15,25 @@
 //     selects every position, as the token-level rule does.
 //
 // Two launches:
-//   block_pool_kernel    one 16-lane group per candidate block sums its 64
-//                        scores in a fixed order (coalesced loads, then a
-//                        butterfly over the 16 lanes), over a compact 1-D grid
-//                        of the non-empty (sequence, 16-block group) items.
-//   block_select_kernel  one 1024-thread workgroup per sequence: exact top-16
-//                        of the 64-bit keys (block-sum bits above the
+//   block_pool_kernel    one workgroup per (sequence, 4 groups of 16 candidate
+//                        blocks), over a compact 1-D grid of the non-empty
+//                        items: each 16-lane group sums one block's 64 scores
+//                        in a fixed order (coalesced loads, then a butterfly
+//                        over the 16 lanes), and each 256-thread quarter also
+//                        writes its group's largest key.
+//   block_select_kernel  one 1024-thread workgroup per sequence: the exact
+//                        top 16 of the 64-bit keys (block-sum bits above the
 //                        complement of the block index, so keys are distinct,
 //                        larger is better and equal sums go to the lower
-//                        block).  Each thread keeps the best key of the blocks
-//                        it owns (strided); t0 = the 16th largest of those
-//                        maxima is a lower bound on the 16th largest key (the
-//                        16 maxima at or above it are distinct keys), and only
-//                        the 16 threads whose maximum reaches t0 can hold keys
-//                        >= t0.  Those keys (at most 16 per thread's share)
-//                        are sorted and the first 16 taken.
+//                        block).  t0 = the 16th largest of the per-thread
+//                        maxima of the group keys bounds the 16th largest key
+//                        from below (those 16 maxima are distinct keys), so
+//                        only blocks of groups whose key reaches t0 can be
+//                        chosen: at most 16 groups per thread stride.  The
+//                        thread maxima and the candidates are ranked with
+//                        in-wave bitonic sorts (shuffles, no barriers); more
+//                        than 256 candidates (contexts past 1M tokens) take a
+//                        workgroup-wide LDS sort.
 #include "hs2_device.h"
 #include "hs2_internal.h"
 
@@ -37,26 +41,92 @@ namespace hs2 {
 
 namespace {
 
-constexpr int kPoolBlocks = 16;  // candidate blocks per pool workgroup (16 lanes each)
+constexpr int kPoolBlocks = 16;  // candidate blocks per group (16 lanes each)
+constexpr int kPoolGroups = 4;   // groups per pool workgroup (256 threads each)
 constexpr int kSelThreads = 1024;
-constexpr int kSortCap = 4096;   // candidate keys: <= 16 * ceil(blocks / 1024) <= 4096 for 2^24 tokens
+constexpr int kSortCap = 4096;   // candidates: <= 16 * 16 * ceil(groups / 1024) <= 4096 for 2^24 tokens
+typedef unsigned long long u64;
 
 __device__ __forceinline__ int64_t block_slot(int64_t base, int b, int i) { return (base >> 6) + b + i; }
+__device__ __forceinline__ int64_t group_slot(int64_t base, int b, int g) { return (base >> 10) + b + g; }
 
 __device__ __forceinline__ int candidate_blocks(int len) {
   return len > kBudget ? (len - kWindow) / kSelectBlock : 0;
 }
 
-__global__ __launch_bounds__(256) void block_pool_kernel(BlockParams p) {
-  int b, j;
+__device__ __forceinline__ u64 block_key(float sum, int i) {
+  return (static_cast<u64>(__float_as_uint(sum)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(i));
+}
+
+__device__ __forceinline__ u64 shfl_xor64(u64 v, int m) {
+  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m);
+  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m);
+  return (static_cast<u64>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ u64 shfl64(u64 v, int src) {
+  const uint32_t lo = __shfl(static_cast<uint32_t>(v), src);
+  const uint32_t hi = __shfl(static_cast<uint32_t>(v >> 32), src);
+  return (static_cast<u64>(hi) << 32) | lo;
+}
+
+// Bitonic sort across the 64 lanes: afterwards lane i holds the i-th largest.
+__device__ __forceinline__ u64 wave_sort_desc(u64 v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const u64 o = shfl_xor64(v, j);
+      const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
+      v = keep_max ? (v > o ? v : o) : (v < o ? v : o);
+    }
+  }
+  return v;
+}
+
+// a, b sorted descending across lanes -> the 64 largest of both, sorted
+// descending (a max with b reversed is bitonic; one merge network sorts it).
+__device__ __forceinline__ u64 wave_merge_desc(u64 a, u64 b) {
+  const int lane = threadIdx.x & 63;
+  const u64 r = shfl64(b, 63 - lane);
+  u64 v = a > r ? a : r;
+#pragma unroll
+  for (int j = 32; j > 0; j >>= 1) {
+    const u64 o = shfl_xor64(v, j);
+    v = (lane & j) == 0 ? (v > o ? v : o) : (v < o ? v : o);
+  }
+  return v;
+}
+
+// Merge tree over the sorted lists of waves [0, waves) (a power of two): wave
+// 0 ends with the 64 largest of them, sorted descending.  Every thread of the
+// workgroup calls it (one barrier per level); slots: waves x 64 LDS keys.
+__device__ u64 tree_top64(u64 v, int waves, u64* slots) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  for (int step = 1; step < waves; step <<= 1) {
+    if (wave < waves && wave % (2 * step) == step) slots[wave * 64 + lane] = v;  // each slot written once
+    __syncthreads();
+    if (wave < waves && wave % (2 * step) == 0) v = wave_merge_desc(v, slots[(wave + step) * 64 + lane]);
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(256 * kPoolGroups) void block_pool_kernel(BlockParams p) {
+  __shared__ u64 s_wave_max[4 * kPoolGroups];
+  int b, item;
   if (!find_item(p.seq_offsets, p.batch, p.total_tokens, p.max_context, blockIdx.x,
-                 [](int len) { return (candidate_blocks(len) + kPoolBlocks - 1) / kPoolBlocks; }, b, j))
+                 [](int len) { return (candidate_blocks(len) + kPoolBlocks * kPoolGroups - 1) / (kPoolBlocks * kPoolGroups); },
+                 b, item))
     return;
   int64_t base;
   int len;
   seq_bounds(p.seq_offsets, b, p.total_tokens, p.max_context, base, len);
   const int nb = candidate_blocks(len);
-  const int i = j * kPoolBlocks + (threadIdx.x >> 4);
+  const int quarter = threadIdx.x >> 8;
+  const int g = item * kPoolGroups + quarter;
+  const int i = g * kPoolBlocks + ((threadIdx.x & 255) >> 4);
   const int l = threadIdx.x & 15;
   float s = 0.f;
   if (i < nb) {
@@ -66,16 +136,24 @@ __global__ __launch_bounds__(256) void block_pool_kernel(BlockParams p) {
 #pragma unroll
   for (int off = 8; off > 0; off >>= 1) s += __shfl_xor(s, off);  // every lane ends with the same sum
   if (i < nb && l == 0) p.block_scores[block_slot(base, b, i)] = s;
+  u64 key = i < nb ? block_key(s, i) : 0ull;
+  key = max(key, shfl_xor64(key, 16));
+  key = max(key, shfl_xor64(key, 32));
+  if ((threadIdx.x & 63) == 0) s_wave_max[threadIdx.x >> 6] = key;
+  __syncthreads();
+  const u64* w = s_wave_max + 4 * quarter;
+  if ((threadIdx.x & 255) == 0 && g * kPoolBlocks < nb)
+    p.group_keys[group_slot(base, b, g)] = max(max(w[0], w[1]), max(w[2], w[3]));
 }
 
 // Sorts s[0, m) descending; m a power of two <= kSortCap; every thread calls it.
-__device__ void bitonic_sort_desc(unsigned long long* s, int m) {
+__device__ void bitonic_sort_desc(u64* s, int m) {
   for (int k = 2; k <= m; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       for (int i = threadIdx.x; i < m; i += kSelThreads) {
         const int o = i ^ j;
         if (o > i) {
-          const unsigned long long a = s[i], c = s[o];
+          const u64 a = s[i], c = s[o];
           const bool down = (i & k) == 0;  // this run ends up descending
           if (down ? a < c : a > c) {
             s[i] = c;
@@ -89,11 +167,14 @@ __device__ void bitonic_sort_desc(unsigned long long* s, int m) {
 }
 
 __global__ __launch_bounds__(kSelThreads) void block_select_kernel(BlockParams p) {
-  __shared__ unsigned long long s_keys[kSortCap];
+  __shared__ u64 s_keys[kSortCap];
+  __shared__ u64 s_t0;
   __shared__ int s_n;
   __shared__ int s_blk[kTopBlocks];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   int64_t base;
   int len;
   seq_bounds(p.seq_offsets, b, p.total_tokens, p.max_context, base, len);
@@ -104,34 +185,50 @@ __global__ __launch_bounds__(kSelThreads) void block_select_kernel(BlockParams p
     return;
   }
   const int nb = candidate_blocks(len);  // >= 16
+  const int ng = (nb + kPoolBlocks - 1) / kPoolBlocks;
   const float* bs = p.block_scores + block_slot(base, b, 0);
-  auto key_of = [&](int i) {
-    return (static_cast<unsigned long long>(__float_as_uint(bs[i])) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(i));
-  };
-  unsigned long long best = 0;  // 0 is below every key (the low word is never 0)
-  for (int i = tid; i < nb; i += kSelThreads) {
-    const unsigned long long k = key_of(i);
-    best = k > best ? k : best;
-  }
-  s_keys[tid] = best;
+  const u64* gk = p.group_keys + group_slot(base, b, 0);
+  u64 best = 0;  // 0 is below every key (the low word of a key is never 0)
+  for (int g = tid; g < ng; g += kSelThreads) best = max(best, gk[g]);
+  // t0: the 16th largest thread maximum (each wave sorts its 64, then a merge tree)
   if (tid == 0) s_n = 0;
+  const u64 top = tree_top64(wave_sort_desc(best), kSelThreads / 64, s_keys);
+  if (tid == kTopBlocks - 1) s_t0 = top;
   __syncthreads();
-  bitonic_sort_desc(s_keys, kSelThreads);
-  const unsigned long long t0 = s_keys[kTopBlocks - 1];
-  __syncthreads();
-  if (best >= t0) {
-    for (int i = tid; i < nb; i += kSelThreads) {
-      const unsigned long long k = key_of(i);
-      if (k >= t0) s_keys[atomicAdd(&s_n, 1)] = k;
+  const u64 t0 = s_t0;
+  if (best >= t0) {  // the blocks of groups reaching t0: the candidates
+    for (int g = tid; g < ng; g += kSelThreads) {
+      if (gk[g] < t0) continue;
+      float v[kPoolBlocks];
+#pragma unroll
+      for (int q = 0; q < kPoolBlocks; ++q) {
+        const int i = g * kPoolBlocks + q;
+        v[q] = i < nb ? bs[i] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < kPoolBlocks; ++q) {
+        const int i = g * kPoolBlocks + q;
+        if (i < nb) {
+          const u64 k = block_key(v[q], i);
+          if (k >= t0) s_keys[atomicAdd(&s_n, 1)] = k;
+        }
+      }
     }
   }
   __syncthreads();
-  const int n = s_n;
-  int m = kTopBlocks;
-  while (m < n) m <<= 1;
-  for (int e = n + tid; e < m; e += kSelThreads) s_keys[e] = 0;
-  __syncthreads();
-  bitonic_sort_desc(s_keys, m);
+  const int n = s_n;  // 16 <= n <= kSortCap
+  if (n <= 256) {  // four waves sort 64 candidates each, then merge
+    const u64 v = wave < 4 && tid < n ? s_keys[tid] : 0ull;
+    const u64 top = tree_top64(wave_sort_desc(v), 4, s_keys + 256);
+    if (tid < kTopBlocks) s_keys[tid] = top;  // wave 0 alone reads LDS from here on until the barrier
+    __syncthreads();
+  } else {
+    int m = 512;
+    while (m < n) m <<= 1;
+    for (int e = n + tid; e < m; e += kSelThreads) s_keys[e] = 0;
+    __syncthreads();
+    bitonic_sort_desc(s_keys, m);
+  }
   if (tid < kTopBlocks) {  // the 16 chosen blocks, placed in index order
     const int blk = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(s_keys[tid]));
     int r = 0;
@@ -148,9 +245,9 @@ __global__ __launch_bounds__(kSelThreads) void block_select_kernel(BlockParams p
 
 hipError_t launch_block_select(const BlockParams& p, hipStream_t s) {
   if (p.batch <= 0) return hipSuccess;
-  const int64_t pool_grid = p.total_tokens / (kPoolBlocks * kSelectBlock) + p.batch;
+  const int64_t pool_grid = p.total_tokens / (kPoolGroups * kPoolBlocks * kSelectBlock) + p.batch;
   if (p.total_tokens > kBudget) {
-    hipLaunchKernelGGL(block_pool_kernel, dim3(static_cast<unsigned>(pool_grid)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(block_pool_kernel, dim3(static_cast<unsigned>(pool_grid)), dim3(256 * kPoolGroups), 0, s, p);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(block_select_kernel, dim3(p.batch), dim3(kSelThreads), 0, s, p);

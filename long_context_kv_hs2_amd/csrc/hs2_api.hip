@@ -63,7 +63,7 @@ struct DecodeLayout {
   int chunk = 0;
   int chunks_per_seq = 0;
   size_t partials = 0, stats = 0, pstats = 0, spill = 0, score = 0, hist0 = 0, counters = 0, selbuf = 0, cand = 0,
-         shat = 0, tile_stats = 0, tile_ub = 0, cand_cnt = 0, sparse = 0, blocks = 0, total = 0;
+         shat = 0, tile_stats = 0, tile_ub = 0, cand_cnt = 0, sparse = 0, blocks = 0, groups = 0, total = 0;
   int cand_blocks = 0;
 };
 
@@ -100,6 +100,7 @@ DecodeLayout decode_layout(const hs2_decode_desc& d) {
   const int slices = sparse_slices(d.batch, n_sparse);
   L.sparse = take(slices > 1 ? B * n_sparse * static_cast<size_t>(slices) * kPartialFloats * sizeof(float) : 0);
   L.blocks = take(((N >> 6) + B + 1) * sizeof(float));  // gen-1 block selection: per-block score sums
+  L.groups = take(((N >> 10) + B + 1) * sizeof(unsigned long long));  // and each 16-block group's largest key
   L.total = off;
   return L;
 }
@@ -413,9 +414,14 @@ hs2_status hs2_full_decode_score(const hs2_decode_desc* desc, const int64_t* seq
   if (!any) return HS2_OK;
   DecodeArgs a{desc, seq_offsets, k_cache, v_cache, k_scale, v_scale, q_full, nullptr, o_full, nullptr,
                nullptr, nullptr, score_out, workspace, static_cast<hipStream_t>(stream)};
-  HS2_TRY(run_full(a, L, nullptr, nullptr));
+  TimingRecord* rec = nullptr;
+  HS2_TRY(timing_begin(&rec));
+  if (rec && rec->last > 3) rec->last = 3;  // stages 0 partial pass, 1 merge, 2 score pass
+  HS2_TRY(mark(rec, 0, a.stream));
+  HS2_TRY(run_full(a, L, nullptr, rec));
   const SelectParams sp = select_params(a, L, score_out);
   HS2_HIP(launch_score_hist(sp, d.batch, d.max_context, true, false, a.stream), "score pass");
+  HS2_TRY(mark(rec, 3, a.stream));
   return HS2_OK;
 }
 
@@ -462,6 +468,7 @@ hs2_status hs2_block_select(const hs2_decode_desc* desc, const int64_t* seq_offs
   p.batch = d.batch;
   p.score = score;
   p.block_scores = reinterpret_cast<float*>(ws_at(workspace, L.blocks));
+  p.group_keys = reinterpret_cast<unsigned long long*>(ws_at(workspace, L.groups));
   p.sel_idx = sel_idx;
   p.sel_count = sel_count;
   HS2_HIP(launch_block_select(p, static_cast<hipStream_t>(stream)), "block selection");
@@ -561,6 +568,68 @@ hs2_status hs2_bridge_kv_fp8(int64_t n_tokens, int32_t d_model, int32_t head_dim
                     workspace, workspace_bytes, stream);
 }
 
+size_t hs2_bridge_append_workspace_bytes(int32_t batch, int32_t d_model, int32_t head_dim, int32_t n_bridged) {
+  if (batch < 0 || d_model < kAppendSliceK || d_model > kMaxAppendDModel || d_model % kAppendSliceK ||
+      head_dim != kDim || n_bridged < 1 || n_bridged > 4)
+    return 0;
+  const size_t partials = static_cast<size_t>(d_model / kAppendSliceK) * batch * 2 * n_bridged * kDim * sizeof(float);
+  return std::max<size_t>(align_up(partials), 256);
+}
+
+hs2_status hs2_bridge_append(int32_t batch, int32_t d_model, int32_t head_dim, int32_t n_bridged, int32_t kv_dtype,
+                             const int64_t* seq_offsets, int64_t total_tokens, const void* hidden,
+                             const void* const* w_k, const void* const* w_v, void* const* k_cache,
+                             void* const* v_cache, float* const* k_scale, float* const* v_scale, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (batch < 0) return fail(HS2_ERR_INVALID_ARGUMENT, "batch %d < 0", batch);
+  if (total_tokens < 0) return fail(HS2_ERR_INVALID_ARGUMENT, "total_tokens < 0");
+  if (head_dim != kDim) return fail(HS2_ERR_UNSUPPORTED, "head_dim %d (only 128 is supported)", head_dim);
+  if (d_model < kAppendSliceK || d_model > kMaxAppendDModel || d_model % kAppendSliceK)
+    return fail(HS2_ERR_UNSUPPORTED, "d_model %d must be a multiple of 128 in [128, 16384]", d_model);
+  if (n_bridged < 1 || n_bridged > 4) return fail(HS2_ERR_UNSUPPORTED, "n_bridged %d (1..4 supported)", n_bridged);
+  if (kv_dtype != HS2_KV_BF16 && kv_dtype != HS2_KV_FP8_E4M3)
+    return fail(HS2_ERR_INVALID_ARGUMENT, "kv_dtype %d unknown", kv_dtype);
+  const bool fp8 = kv_dtype == HS2_KV_FP8_E4M3;
+  const bool any = batch > 0;
+  if (any && !seq_offsets) return fail(HS2_ERR_INVALID_ARGUMENT, "seq_offsets is NULL");
+  if (seq_offsets && !aligned(seq_offsets, 8)) return fail(HS2_ERR_INVALID_ARGUMENT, "seq_offsets not 8-byte aligned");
+  if (!w_k || !w_v || !k_cache || !v_cache) return fail(HS2_ERR_INVALID_ARGUMENT, "weight/cache pointer array is NULL");
+  if (fp8 && (!k_scale || !v_scale)) return fail(HS2_ERR_INVALID_ARGUMENT, "E4M3 caches need k_scale and v_scale");
+  if (!fp8 && (k_scale || v_scale)) return fail(HS2_ERR_INVALID_ARGUMENT, "bf16 caches take no scales (pass NULL)");
+  AppendParams p{};
+  for (int l = 0; l < n_bridged; ++l) {
+    p.w[2 * l] = static_cast<const uint16_t*>(w_k[l]);
+    p.w[2 * l + 1] = static_cast<const uint16_t*>(w_v[l]);
+    p.out[2 * l] = k_cache[l];
+    p.out[2 * l + 1] = v_cache[l];
+    if (fp8) {
+      p.scale[2 * l] = k_scale[l];
+      p.scale[2 * l + 1] = v_scale[l];
+    }
+  }
+  const bool rows = any && total_tokens > 0;
+  for (int i = 0; i < 2 * n_bridged; ++i) {
+    HS2_TRY(check_ptr(p.w[i], true, 16, "w_k/w_v entry"));
+    HS2_TRY(check_ptr(p.out[i], rows, 16, "k_cache/v_cache entry"));
+    if (fp8) HS2_TRY(check_ptr(p.scale[i], rows, 4, "k_scale/v_scale entry"));
+  }
+  HS2_TRY(check_ptr(hidden, any, 16, "hidden"));
+  const size_t need = hs2_bridge_append_workspace_bytes(batch, d_model, head_dim, n_bridged);
+  if (workspace_bytes < need) return fail(HS2_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  HS2_TRY(check_ptr(workspace, true, 256, "workspace"));
+  if (!any || total_tokens == 0) return HS2_OK;
+  p.seq_offsets = seq_offsets;
+  p.total_tokens = total_tokens;
+  p.batch = batch;
+  p.d_model = d_model;
+  p.n_out = 2 * n_bridged;
+  p.hidden = static_cast<const uint16_t*>(hidden);
+  p.fp8 = fp8 ? 1 : 0;
+  p.partials = static_cast<float*>(workspace);
+  HS2_HIP(launch_bridge_append(p, static_cast<hipStream_t>(stream)), "bridge append");
+  return HS2_OK;
+}
+
 hs2_status hs2_stage_timing_enable(int32_t mode) {
   if (mode < 0 || mode > 2) return fail(HS2_ERR_INVALID_ARGUMENT, "timing mode %d (0, 1 or 2)", mode);
   std::lock_guard<std::mutex> lock(g_timing_mu);
@@ -568,24 +637,43 @@ hs2_status hs2_stage_timing_enable(int32_t mode) {
   return HS2_OK;
 }
 
-hs2_status hs2_stage_timing_read(float* mean_ms, int32_t* n_calls) {
-  if (!mean_ms || !n_calls) return fail(HS2_ERR_INVALID_ARGUMENT, "NULL output");
-  std::lock_guard<std::mutex> lock(g_timing_mu);
+namespace {
+// Waits for the recorded calls and writes each call's stage durations (0 for
+// stages it did not record) to per_call[r][stage] for r < max_calls (when
+// per_call is not NULL) and their means to mean_ms (when not NULL); clears the
+// record.  Caller holds g_timing_mu.
+hs2_status read_records(float* mean_ms, float* per_call, int32_t max_calls, int32_t* n_calls) {
   double sum[HS2_N_STAGES] = {0, 0, 0, 0};
   for (int r = 0; r < g_records_used; ++r) {
     const int last = g_records[r].last;
     HS2_HIP(hipEventSynchronize(g_records[r].ev[last]), "hipEventSynchronize");
-    for (int sidx = 0; sidx < last; ++sidx) {
+    for (int sidx = 0; sidx < HS2_N_STAGES; ++sidx) {
       float ms = 0.f;
-      HS2_HIP(hipEventElapsedTime(&ms, g_records[r].ev[sidx], g_records[r].ev[sidx + 1]), "hipEventElapsedTime");
+      if (sidx < last)
+        HS2_HIP(hipEventElapsedTime(&ms, g_records[r].ev[sidx], g_records[r].ev[sidx + 1]), "hipEventElapsedTime");
       sum[sidx] += ms;
+      if (per_call && r < max_calls) per_call[static_cast<size_t>(r) * HS2_N_STAGES + sidx] = ms;
     }
   }
-  for (int sidx = 0; sidx < HS2_N_STAGES; ++sidx)
-    mean_ms[sidx] = g_records_used ? static_cast<float>(sum[sidx] / g_records_used) : 0.f;
+  if (mean_ms)
+    for (int sidx = 0; sidx < HS2_N_STAGES; ++sidx)
+      mean_ms[sidx] = g_records_used ? static_cast<float>(sum[sidx] / g_records_used) : 0.f;
   *n_calls = g_records_used;
   g_records_used = 0;
   return HS2_OK;
+}
+}  // namespace
+
+hs2_status hs2_stage_timing_read(float* mean_ms, int32_t* n_calls) {
+  if (!mean_ms || !n_calls) return fail(HS2_ERR_INVALID_ARGUMENT, "NULL output");
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  return read_records(mean_ms, nullptr, 0, n_calls);
+}
+
+hs2_status hs2_stage_timing_read_calls(float* ms, int32_t max_calls, int32_t* n_calls) {
+  if (!ms || !n_calls || max_calls < 0) return fail(HS2_ERR_INVALID_ARGUMENT, "NULL output or max_calls < 0");
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  return read_records(nullptr, ms, max_calls, n_calls);
 }
 
 const char* hs2_status_string(hs2_status status) {

@@ -106,6 +106,23 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// fp32 -> OCP E4M3 code (1 sign, 4 exponent bits with bias 7, 3 mantissa
+// bits; exponent field 0 holds the subnormals m * 2^-9; no infinities, and
+// S.1111.111 is NaN, so the largest finite value is 448): round to nearest,
+// ties to the even code, magnitudes above 448 (and NaN) saturate to +-448.
+// Branch-free: from 2^-6 up, the fp32 bit pattern rounded at its 20th bit is
+// the code with the exponent bias 127 in place of 7 (the carry of a mantissa
+// that rounds up moves into the exponent); below 2^-6 the code is the
+// magnitude in units of 2^-9, rounded (a code of 8 is the smallest normal).
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t mag = u & 0x7FFFFFFFu;
+  const uint32_t normal = ((mag + 0x7FFFFu + ((mag >> 20) & 1u)) >> 20) - ((127u - 7u) << 3);
+  const uint32_t sub = static_cast<uint32_t>(__builtin_rintf(__uint_as_float(mag) * 512.f));
+  const uint32_t code = mag < 0x3C800000u ? sub : min(normal, 0x7Eu);  // 0x3C800000 = 2^-6
+  return ((u >> 24) & 0x80u) | code;
+}
+
 // Byte permute of the pair {hi_word, lo_word}: selector byte i picks byte
 // sel_i of the 8-byte value lo_word | hi_word << 32.
 __device__ __forceinline__ uint32_t perm(uint32_t hi_word, uint32_t lo_word, uint32_t sel) {

@@ -70,6 +70,7 @@ struct BlockParams {
   int batch;
   const float* score;         // [N] per-token scores
   float* block_scores;        // [N / 64 + B]: block i of the sequence at row base_b in slot (base_b >> 6) + b + i
+  unsigned long long* group_keys;  // [N / 1024 + B]: largest key of blocks [16 g, 16 g + 16), slot (base_b >> 10) + b + g
   int32_t* sel_idx;           // [B][window + top_k]
   int32_t* sel_count;         // [B]
 };
@@ -165,5 +166,23 @@ struct BridgeParams {
 hipError_t launch_bridge_transpose_w(const uint16_t* const* w, int n_out, int d_model, uint16_t* w_t,
                                      hipStream_t s);
 hipError_t launch_bridge_gemm(const BridgeParams& p, hipStream_t s);
+
+// Decode-time bridging: one hidden row per sequence, appended at its last row.
+constexpr int kAppendSliceK = 128;  // d_model rows per split-K slice
+constexpr int kMaxAppendDModel = 16384;
+struct AppendParams {
+  const int64_t* seq_offsets;  // [B + 1]: row seq_offsets[b + 1] - 1 takes sequence b's projection
+  int64_t total_tokens;
+  int batch;
+  int d_model;                 // multiple of kAppendSliceK
+  int n_out;                   // 2 * n_bridged output matrices (K0, V0, K1, ...)
+  const uint16_t* hidden;      // [B][d_model] bf16
+  const uint16_t* w[8];        // [d_model][128] bf16 each
+  void* out[8];                // caches [N][128]: bf16, or E4M3 codes when fp8
+  float* scale[8];             // fp8: [N] per-token scales
+  int fp8;
+  float* partials;             // workspace: [d_model / kAppendSliceK][B][n_out * 128]
+};
+hipError_t launch_bridge_append(const AppendParams& p, hipStream_t s);
 
 }  // namespace hs2

@@ -25,8 +25,9 @@ STAGE_NAMES = ("full_partial", "full_merge", "score_select", "sparse")
 
 EXPORTED = (
     "hs2_decode_workspace_bytes", "hs2_decode_block", "hs2_full_decode_score", "hs2_topk_select", "hs2_block_select",
-    "hs2_sparse_decode", "hs2_bridge_workspace_bytes", "hs2_bridge_kv", "hs2_bridge_kv_fp8", "hs2_stage_timing_enable",
-    "hs2_stage_timing_read", "hs2_status_string", "hs2_last_error_message",
+    "hs2_sparse_decode", "hs2_bridge_workspace_bytes", "hs2_bridge_kv", "hs2_bridge_kv_fp8",
+    "hs2_bridge_append_workspace_bytes", "hs2_bridge_append", "hs2_stage_timing_enable",
+    "hs2_stage_timing_read", "hs2_stage_timing_read_calls", "hs2_status_string", "hs2_last_error_message",
 )
 
 
@@ -83,10 +84,17 @@ def load(path: str = LIB_PATH):
                                       ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
                                       vp, sz, vp]
     lib.hs2_bridge_kv_fp8.restype = ctypes.c_int
+    lib.hs2_bridge_append_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.hs2_bridge_append_workspace_bytes.restype = sz
+    pp = ctypes.POINTER(vp)
+    lib.hs2_bridge_append.argtypes = [i32, i32, i32, i32, i32, vp, i64, vp, pp, pp, pp, pp, pp, pp, vp, sz, vp]
+    lib.hs2_bridge_append.restype = ctypes.c_int
     lib.hs2_stage_timing_enable.argtypes = [i32]
     lib.hs2_stage_timing_enable.restype = ctypes.c_int
     lib.hs2_stage_timing_read.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
     lib.hs2_stage_timing_read.restype = ctypes.c_int
+    lib.hs2_stage_timing_read_calls.argtypes = [ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(i32)]
+    lib.hs2_stage_timing_read_calls.restype = ctypes.c_int
     lib.hs2_status_string.argtypes = [ctypes.c_int]
     lib.hs2_status_string.restype = ctypes.c_char_p
     lib.hs2_last_error_message.argtypes = []
@@ -231,18 +239,26 @@ class BlockSelectDecode:
         self.score = torch.empty((k.shape[0],), dtype=torch.float32, device=dev)
         self.workspace = _workspace(decode_workspace_bytes(self.desc), dev)
 
-    def __call__(self):
+    def __call__(self, marks=None):
+        """marks: optional three torch.cuda.Event recorded before the block
+        selection, between it and the sparse layers, and after them."""
         lib, d, ws, st = load(), ctypes.byref(self.desc), _ptr(self.workspace), _stream()
         n = self.workspace.numel()
         check(lib.hs2_full_decode_score(d, _ptr(self.seq_offsets), _ptr(self.k), _ptr(self.v), _ptr(self.k_scale),
                                         _ptr(self.v_scale), _ptr(self.q_full), _ptr(self.o_full), _ptr(self.score),
                                         ws, n, st))
+        if marks:
+            marks[0].record()
         check(lib.hs2_block_select(d, _ptr(self.seq_offsets), _ptr(self.score), _ptr(self.sel_idx),
                                    _ptr(self.sel_count), ws, n, st))
+        if marks:
+            marks[1].record()
         if self.desc.n_sparse_layers:
             check(lib.hs2_sparse_decode(d, _ptr(self.seq_offsets), _ptr(self.k), _ptr(self.v), _ptr(self.k_scale),
                                         _ptr(self.v_scale), _ptr(self.q_sparse), _ptr(self.sel_idx),
                                         _ptr(self.sel_count), _ptr(self.o_sparse), ws, n, st))
+        if marks:
+            marks[2].record()
         return self
 
     def outputs(self):
@@ -306,9 +322,35 @@ def bridge_kv_fp8(hidden, w_k, w_v, k_out=None, k_sc=None, v_out=None, v_sc=None
     return k_out, k_sc, v_out, v_sc
 
 
+def bridge_append(seq_offsets, hidden, w_k, w_v, k_cache, v_cache, k_scale=None, v_scale=None, workspace=None):
+    """Project each sequence's current hidden row (bf16 [B, d_model]) by every
+    bridged layer's W_k, W_v and write it at row seq_offsets[b+1]-1 of the
+    layer's cache (bf16, or uint8 E4M3 codes with fp32 per-token scales)."""
+    dev = hidden.device
+    batch, d_model = hidden.shape
+    n = len(w_k)
+    fp8 = k_cache[0].dtype == torch.uint8
+    arr = ctypes.c_void_p * n
+    need = load().hs2_bridge_append_workspace_bytes(batch, d_model, 128, n)
+    ws = _workspace(need, dev, workspace)
+    ptrs = lambda ts: arr(*[t.data_ptr() for t in ts]) if ts is not None else None
+    check(load().hs2_bridge_append(batch, d_model, 128, n, KV_FP8_E4M3 if fp8 else KV_BF16, _ptr(seq_offsets),
+                                   k_cache[0].shape[0], _ptr(hidden), ptrs(w_k), ptrs(w_v), ptrs(k_cache),
+                                   ptrs(v_cache), ptrs(k_scale), ptrs(v_scale), _ptr(ws), ws.numel(), _stream()))
+
+
 def stage_timing(on: bool, full_pass_only: bool = False):
     """Record HIP events around the decode stages (or only around the full pass)."""
     check(load().hs2_stage_timing_enable(0 if not on else 2 if full_pass_only else 1))
+
+
+def stage_timing_read_calls(max_calls: int = 1024):
+    """Per-call stage durations (ms) since the last read: float32 [n_calls, 4]."""
+    import numpy as np
+    buf = (ctypes.c_float * (max_calls * N_STAGES))()
+    n = ctypes.c_int32(0)
+    check(load().hs2_stage_timing_read_calls(buf, max_calls, ctypes.byref(n)))
+    return np.frombuffer(buf, dtype=np.float32).reshape(max_calls, N_STAGES)[:min(n.value, max_calls)].copy()
 
 
 def stage_timing_read():

@@ -140,9 +140,11 @@ def check_bridge(h_bits, w_bits, out_bits, rows):
     oracle.  Element-wise bound from the arithmetic: fp32 accumulation of
     d_model exact bf16 products is within gamma_n * sum|h w| of the exact sum
     (gamma_n = n u / (1 - n u), u = 2^-24), and the final rounding to bf16
-    adds at most one bf16 ulp.  Also: at least 99.9 % of elements within one
-    ulp of the correctly rounded value (catches a systematic error such as
-    truncation).  No max-abs-relative bar: bf16 output alone is off by up to
+    adds at most one bf16 ulp.  Also: at most 0.1 % of the elements (at least
+    one, for small samples) more than one ulp from the correctly rounded value
+    (a statistical guard against a systematic error; elements with a large
+    sum|h w| against a small value may miss by two within the bound above).
+    No max-abs-relative bar: bf16 output alone is off by up to
     half an ulp, 2^-9 of the largest element, which a 2e-3 bar would not
     reliably admit.  Returns (worst ulps, fraction within 1 ulp)."""
     h = O.bf16_bits_to_f64(h_bits[rows])
@@ -169,7 +171,8 @@ def check_bridge(h_bits, w_bits, out_bits, rows):
         raise AssertionError(msg)
     ulps = np.abs(bf16_ordinal(got_bits) - bf16_ordinal(O.f64_to_bf16_bits(ref)))
     frac1 = float((ulps <= 1).mean())
-    assert frac1 >= 0.999, f"only {frac1:.5f} of elements within 1 ulp"
+    allowed = max(1, int(0.001 * ulps.size))
+    assert int((ulps > 1).sum()) <= allowed, f"only {frac1:.5f} of elements within 1 ulp"
     return int(ulps.max()), frac1
 
 

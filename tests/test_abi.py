@@ -126,6 +126,35 @@ def test_bridge_validation():
     assert lib.hs2_bridge_kv(10, 4096, 128, 1, FAKE, one, one, None, one, FAKE, 1 << 30, None) == INVALID
 
 
+def test_bridge_append_validation():
+    lib = hs2.load()
+    one = (ctypes.c_void_p * 1)(FAKE)
+    ws = lib.hs2_bridge_append_workspace_bytes(8, 4096, 128, 1)
+    assert ws == 32 * 8 * 2 * 128 * 4
+    assert lib.hs2_bridge_append_workspace_bytes(8, 4000, 128, 1) == 0
+    assert lib.hs2_bridge_append_workspace_bytes(8, 4096, 128, 5) == 0
+    ok = dict(batch=8, d=4096, hd=128, nb=1, kv=0)
+
+    def call(batch=8, d=4096, hd=128, nb=1, kv=0, offs=FAKE, total=100, hidden=FAKE, wk=one, wv=one, kc=one,
+             vc=one, ks=None, vs=None, w=FAKE, nbytes=ws):
+        return lib.hs2_bridge_append(batch, d, hd, nb, kv, offs, total, hidden, wk, wv, kc, vc, ks, vs, w, nbytes,
+                                     None)
+
+    assert call(batch=-1) == INVALID
+    assert call(hd=64) == UNSUPPORTED
+    assert call(d=4000) == UNSUPPORTED
+    assert call(d=32768) == UNSUPPORTED
+    assert call(nb=0) == UNSUPPORTED
+    assert call(kv=7) == INVALID
+    assert call(offs=None) == INVALID
+    assert call(hidden=None) == INVALID
+    assert call(kc=None) == INVALID
+    assert call(kv=1) == INVALID            # E4M3 without scale arrays
+    assert call(ks=one, vs=one) == INVALID  # bf16 with scale arrays
+    assert call(nbytes=ws - 1) == SMALL_WS
+    assert call(total=-1) == INVALID
+
+
 def test_stage_calls_validate():
     lib = hs2.load()
     d = desc()
@@ -163,6 +192,12 @@ def test_stage_timing_modes():
     assert lib.hs2_stage_timing_read(out, ctypes.byref(n)) == 0
     assert n.value == 0 and list(out) == [0.0] * hs2.N_STAGES
     assert lib.hs2_stage_timing_read(None, ctypes.byref(n)) == INVALID
+    per = (ctypes.c_float * (4 * hs2.N_STAGES))()
+    n.value = -1
+    assert lib.hs2_stage_timing_read_calls(per, 4, ctypes.byref(n)) == 0 and n.value == 0
+    assert lib.hs2_stage_timing_read_calls(None, 4, ctypes.byref(n)) == INVALID
+    assert lib.hs2_stage_timing_read_calls(per, -1, ctypes.byref(n)) == INVALID
+    assert hs2.stage_timing_read_calls().shape == (0, hs2.N_STAGES)
 
 
 def test_bridge_fp8_validation():

@@ -90,3 +90,20 @@ def test_block_selection_differs_from_token_selection():
     b = set(tok["sel_idx"][0].cpu().numpy().tolist())
     assert len(a ^ b) > 0
     assert torch.equal(blk.o_full, tok["o_full"])  # the full layer is the same call
+
+
+def test_block_select_past_256_candidates():
+    # Over 1M tokens a thread ranks several 16-block groups.  Here thread 0's
+    # four groups (0, 1024, 2048, 3072) hold the largest block sums and groups
+    # 1..15 the next ones, so 19 groups reach the threshold: 304 candidates,
+    # the workgroup-wide sort.  Block sums are exact in fp32.
+    length = 4 * 1024 * 1024 + 1000
+    print(f"case: block select, {length} tokens, 304 candidates", flush=True)
+    score = np.zeros(length, dtype=np.float32)
+    for g in (0, 1024, 2048, 3072):
+        score[g * 1024:(g + 1) * 1024] = 1000.0 / 64
+    score[1024:16 * 1024] = 500.0 / 64
+    offs, sel, cnt = run_block_select([length], score)
+    ref = O.select_blocks(score.astype(np.float64))
+    assert cnt[0] == 1152
+    np.testing.assert_array_equal(sel[0], ref["sel"])

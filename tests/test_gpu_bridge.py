@@ -85,3 +85,67 @@ def test_bridge_fp8_special_rows():
     rowmax = np.abs(bf).max(axis=1, keepdims=True)
     assert (np.abs(dec - bf) <= rowmax * 2.0 ** -4 + 1e-30).all()   # within E4M3's half step at the top
     parity.check_bridge_fp8(hb, w, codes, scales, np.arange(300))
+
+
+def _append_case(lengths, d_model, n_bridged, fp8, seed):
+    rng = np.random.default_rng(seed)
+    batch = len(lengths)
+    offs = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    n = int(offs[-1])
+    br = inputs.make_bridge(tokens=batch, d_model=d_model, n_bridged=n_bridged, seed=seed)
+    # caches full of other rows, which the call must leave alone
+    if fp8:
+        caches = [torch.from_numpy(rng.integers(0, 255, size=(n, 128), dtype=np.uint8)).cuda()
+                  for _ in range(2 * n_bridged)]
+        scales = [torch.from_numpy(rng.random(n, dtype=np.float32) + 0.5).cuda() for _ in range(2 * n_bridged)]
+    else:
+        caches = [to_dev(inputs.to_bf16_bits(rng.standard_normal((n, 128), dtype=np.float32)))
+                  for _ in range(2 * n_bridged)]
+        scales = None
+    before = [c.clone() for c in caches]
+    before_s = [s.clone() for s in scales] if fp8 else None
+    hs2.bridge_append(torch.from_numpy(offs).cuda(), to_dev(br["h"]), [to_dev(w) for w in br["w_k"]],
+                      [to_dev(w) for w in br["w_v"]], caches[0::2], caches[1::2],
+                      scales[0::2] if fp8 else None, scales[1::2] if fp8 else None)
+    torch.cuda.synchronize()
+    last = offs[1:] - 1
+    live = np.nonzero(np.asarray(lengths) > 0)[0]
+    for m in range(2 * n_bridged):
+        w_bits = (br["w_k"] if m % 2 == 0 else br["w_v"])[m // 2]
+        host = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16) if t.dtype == torch.bfloat16 \
+            else t.cpu().numpy()
+        got = host(caches[m])
+        old = host(before[m])
+        keep = np.ones(n, dtype=bool)
+        keep[last[live]] = False
+        if fp8:
+            assert np.array_equal(got[keep], old[keep])
+            sc, old_sc = scales[m].cpu().numpy(), before_s[m].cpu().numpy()
+            assert np.array_equal(sc[keep], old_sc[keep])
+            rows_out = np.zeros((batch, 128), dtype=np.uint8)
+            rows_sc = np.ones(batch, dtype=np.float32)
+            rows_out[live], rows_sc[live] = got[last[live]], sc[last[live]]
+            if live.size:
+                parity.check_bridge_fp8(br["h"], w_bits, rows_out, rows_sc, live)
+        else:
+            bits = got
+            assert np.array_equal(bits[keep], old[keep])
+            rows_out = np.zeros((batch, 128), dtype=np.uint16)
+            rows_out[live] = bits[last[live]]
+            if live.size:
+                parity.check_bridge(br["h"], w_bits, rows_out, live)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("lengths", [[5, 0, 300, 1, 64, 2000, 17, 900], [3], list(range(1, 41)),
+                                     [int(x) for x in np.arange(100) * 7 % 50 + 1]])
+def test_bridge_append_writes_the_current_rows(lengths, fp8):
+    print(f"case: bridge append, batch {len(lengths)}, fp8 {fp8}", flush=True)
+    _append_case(lengths, 4096, 3, fp8, seed=len(lengths) + 7 * fp8)
+
+
+def test_bridge_append_small_model_and_empty_batch():
+    print("case: bridge append, d_model 256, 1 bridged layer; empty batch", flush=True)
+    _append_case([10, 20, 0, 5], 256, 1, False, seed=3)
+    _append_case([10, 20, 0, 5], 256, 1, True, seed=4)
+    _append_case([0, 0], 256, 2, False, seed=5)
