@@ -38,6 +38,9 @@ from .hs2_oracle import (  # noqa: F401
     e4m3_bytes_to_f64,
     f64_to_e4m3,
     quantize_rows_e4m3,
+    SWA_WINDOW,
+    swa_ring_slots,
+    swa_attention,
     decode_kv,
     full_attention,
     token_scores,

@@ -29,7 +29,13 @@ plainest reading is taken; each such reading is named where it is used:
   mesures": HySparse2 uses a more compact MQA setting);
 * the bridge is a plain product of the shared hidden state with each bridged
   layer's own W_k and W_v, no norm, bias or rotary step ([ko] "í•œ ì¼": one
-  source hidden state, independent K/V projections per target layer).
+  source hidden state, independent K/V projections per target layer);
+* gen-1 block selection (the ablation comparator): 64-token blocks aligned
+  to position 0, block score = sum of its token scores, 16 blocks plus the
+  window under the same budget;
+* a Self-Decoder sliding-window layer attends to the 128 most recent
+  positions (no window size is given; the pages' local window is used),
+  kept in a ring buffer at slot position mod 128.
 """
 
 from __future__ import annotations
@@ -44,6 +50,7 @@ WINDOW = 128  # [zh] forced recent window paragraph; [fr]/[ko] "Ce que fait"/"í•
 TOP_K = 1024  # same passages: 1024 tokens from before the window
 BAND_REL = 1e-5  # relative band around the k-th score inside which ties may differ
 BLOCK = 64  # gen-1 HySparse's selection unit ([en] paragraph on how the sparse layers select)
+SWA_WINDOW = 128  # Self-Decoder sliding window: the pages give none; their local window (128) is taken
 
 
 # --------------------------------------------------------------------------
@@ -189,6 +196,34 @@ def full_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray):
     p = e / z
     o = p.T @ v  # [H, D]
     return o, p
+
+
+def swa_ring_slots(length: int, window: int = SWA_WINDOW) -> np.ndarray:
+    """Ring slots holding the positions a sliding window of ``window`` covers
+    at decode, position p being kept in slot p mod window: positions
+    [max(0, L - window), L), in position order."""
+    return np.arange(max(0, length - window), length) % window
+
+
+def swa_attention(q: np.ndarray, ring_k: np.ndarray, ring_v: np.ndarray, length: int,
+                  window: int = SWA_WINDOW) -> np.ndarray:
+    """One Self-Decoder sliding-window attention layer at decode.
+
+    The front half of the model (the Self-Decoder) mixes full-attention and
+    sliding-window layers ([fr] "Ce que fait HySparse2"; [en] paragraph on
+    the self-decoder and cross-decoder split).  At decode a window layer
+    attends to the ``window`` most recent positions, current token included,
+    which a ring buffer of ``window`` rows holds (the reading taken: the
+    pages give no window size, so the local window they do give, 128, is
+    used).  q [H, D]; ring_k, ring_v [window, D] decoded float64 rows;
+    length = positions so far (the current token included).  Returns
+    o [H, D]; a sequence with no positions gives zeros.
+    """
+    if length == 0:
+        return np.zeros_like(q, dtype=np.float64)
+    slots = swa_ring_slots(length, window)
+    o, _ = full_attention(q, ring_k[slots], ring_v[slots])
+    return o
 
 
 def token_scores(p: np.ndarray) -> np.ndarray:
