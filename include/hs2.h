@@ -192,6 +192,48 @@ hs2_status hs2_bridge_kv_fp8(int64_t n_tokens, int32_t d_model, int32_t head_dim
                              void* const* v_out, float* const* v_scale,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* Self-Decoder layers at decode.  The model's front half (the Self-Decoder)
+ * mixes full-attention and sliding-window layers; in the pages' 49-layer
+ * model the first 25 layers hold one full-attention layer, whose input hidden
+ * state is the bridge source ([fr] "Ce que fait HySparse2" and "Le Prefill
+ * s'arrête à mi-chemin"; [en] paragraphs on the self-decoder split and on
+ * early prefill exit).
+ *
+ * hs2_full_decode: the Self-Decoder's full-attention layer: full attention
+ * alone (o_full), no score and no selection.  Arguments, workspace and
+ * errors as hs2_decode_block.  Stage timing records stages 0 and 1.
+ *
+ * hs2_swa_decode: one sliding-window layer for a batch: each sequence's
+ * query attends to its `window` most recent positions, the current token
+ * included (the pages give no window size; the workloads use 128, the local
+ * window the pages do give).  The layer's cache is a ring per sequence:
+ *   ring_k, ring_v (device) [batch][window][128] rows, bf16 or E4M3 codes per
+ *     kv_dtype, 16-byte aligned; position p lives in slot p mod window;
+ *   ring_k_scale, ring_v_scale (device) fp32 [batch][window] (E4M3), else NULL;
+ *   lengths (device) int64 [batch]: positions so far, the current one
+ *     included (0: zero output);
+ *   k_new, v_new (device) [batch][128] the current token's rows (with
+ *     k_new_scale, v_new_scale fp32 [batch] for E4M3), written into slot
+ *     (lengths[b] - 1) mod window before the attention; NULL when the caller
+ *     has already written them;
+ *   q (device) fp32 [batch][16][128]; o (device) fp32 [batch][16][128];
+ *   softmax_scale multiplies q.k (1/sqrt(128) in the workloads).
+ * Supported: 1 <= window <= 1152, 16 query heads, head_dim 128.  workspace
+ * (device) >= hs2_swa_workspace_bytes(batch, window), 256-byte aligned.     */
+hs2_status hs2_full_decode(const hs2_decode_desc* desc, const int64_t* seq_offsets,
+                           const void* k_cache, const void* v_cache,
+                           const float* k_scale, const float* v_scale,
+                           const float* q_full, float* o_full,
+                           void* workspace, size_t workspace_bytes, void* stream);
+size_t hs2_swa_workspace_bytes(int32_t batch, int32_t window);
+hs2_status hs2_swa_decode(int32_t batch, int32_t window, int32_t kv_dtype, float softmax_scale,
+                          const int64_t* lengths, void* ring_k, void* ring_v,
+                          float* ring_k_scale, float* ring_v_scale,
+                          const void* k_new, const void* v_new,
+                          const float* k_new_scale, const float* v_new_scale,
+                          const float* q, float* o,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Decode-time KV Bridging: each decode step, the current token's hidden
  * state is projected by every bridged layer's W_k and W_v (the products of
  * hs2_bridge_kv, one row per sequence) and written into that layer's cache at

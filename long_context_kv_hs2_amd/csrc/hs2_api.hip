@@ -630,6 +630,116 @@ hs2_status hs2_bridge_append(int32_t batch, int32_t d_model, int32_t head_dim, i
   return HS2_OK;
 }
 
+size_t hs2_swa_workspace_bytes(int32_t batch, int32_t window) {
+  if (batch < 0 || window < 1 || window > kBudget) return 0;
+  const size_t B = static_cast<size_t>(batch);
+  return align_up((B + 1) * sizeof(int64_t)) + align_up(B * window * sizeof(int32_t)) +
+         std::max<size_t>(align_up(B * sizeof(int32_t)), 256);
+}
+
+hs2_status hs2_swa_decode(int32_t batch, int32_t window, int32_t kv_dtype, float softmax_scale,
+                          const int64_t* lengths, void* ring_k, void* ring_v, float* ring_k_scale,
+                          float* ring_v_scale, const void* k_new, const void* v_new, const float* k_new_scale,
+                          const float* v_new_scale, const float* q, float* o, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (batch < 0) return fail(HS2_ERR_INVALID_ARGUMENT, "batch %d < 0", batch);
+  if (window < 1 || window > kBudget) return fail(HS2_ERR_UNSUPPORTED, "window %d (1..1152 supported)", window);
+  if (kv_dtype != HS2_KV_BF16 && kv_dtype != HS2_KV_FP8_E4M3)
+    return fail(HS2_ERR_INVALID_ARGUMENT, "kv_dtype %d unknown", kv_dtype);
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale))
+    return fail(HS2_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
+  const bool fp8 = kv_dtype == HS2_KV_FP8_E4M3;
+  const bool any = batch > 0;
+  HS2_TRY(check_ptr(lengths, any, 8, "lengths"));
+  HS2_TRY(check_ptr(ring_k, any, 16, "ring_k"));
+  HS2_TRY(check_ptr(ring_v, any, 16, "ring_v"));
+  HS2_TRY(check_ptr(q, any, 16, "q"));
+  HS2_TRY(check_ptr(o, any, 16, "o"));
+  if (fp8) {
+    HS2_TRY(check_ptr(ring_k_scale, any, 4, "ring_k_scale"));
+    HS2_TRY(check_ptr(ring_v_scale, any, 4, "ring_v_scale"));
+  } else if (ring_k_scale || ring_v_scale || k_new_scale || v_new_scale) {
+    return fail(HS2_ERR_INVALID_ARGUMENT, "bf16 rings take no scales (pass NULL)");
+  }
+  if ((k_new == nullptr) != (v_new == nullptr)) return fail(HS2_ERR_INVALID_ARGUMENT, "k_new and v_new: both or neither");
+  if (k_new) {
+    HS2_TRY(check_ptr(k_new, any, 4, "k_new"));
+    HS2_TRY(check_ptr(v_new, any, 4, "v_new"));
+    if (fp8) {
+      HS2_TRY(check_ptr(k_new_scale, any, 4, "k_new_scale"));
+      HS2_TRY(check_ptr(v_new_scale, any, 4, "v_new_scale"));
+    }
+  }
+  const size_t need = hs2_swa_workspace_bytes(batch, window);
+  if (workspace_bytes < need) return fail(HS2_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  HS2_TRY(check_ptr(workspace, true, 256, "workspace"));
+  if (!any) return HS2_OK;
+  const size_t B = static_cast<size_t>(batch);
+  SwaParams w{};
+  w.lengths = lengths;
+  w.batch = batch;
+  w.window = window;
+  w.fp8 = fp8 ? 1 : 0;
+  w.ring_k = static_cast<uint8_t*>(ring_k);
+  w.ring_v = static_cast<uint8_t*>(ring_v);
+  w.ring_ks = ring_k_scale;
+  w.ring_vs = ring_v_scale;
+  w.k_new = static_cast<const uint8_t*>(k_new);
+  w.v_new = static_cast<const uint8_t*>(v_new);
+  w.k_new_scale = k_new_scale;
+  w.v_new_scale = v_new_scale;
+  w.offs = reinterpret_cast<int64_t*>(workspace);
+  w.sel_idx = reinterpret_cast<int32_t*>(ws_at(workspace, align_up((B + 1) * sizeof(int64_t))));
+  w.sel_count = reinterpret_cast<int32_t*>(
+      ws_at(workspace, align_up((B + 1) * sizeof(int64_t)) + align_up(B * window * sizeof(int32_t))));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  HS2_HIP(launch_swa_prep(w, st), "sliding-window ring update");
+  SparseParams sp{};
+  sp.seq_offsets = w.offs;
+  sp.total_tokens = static_cast<int64_t>(batch) * window;
+  sp.max_context = window;
+  sp.k = w.ring_k;
+  sp.v = w.ring_v;
+  sp.k_scale = ring_k_scale;
+  sp.v_scale = ring_v_scale;
+  sp.q_sparse = q;
+  sp.qscale = static_cast<float>(static_cast<double>(softmax_scale) * kLog2e);
+  sp.batch = batch;
+  sp.n_layers = 1;
+  sp.budget = window;
+  sp.sel_idx = w.sel_idx;
+  sp.sel_count = w.sel_count;
+  sp.out = o;
+  sp.partials = nullptr;
+  HS2_HIP(launch_sparse_window(sp, fp8, st), "sliding-window attention");
+  return HS2_OK;
+}
+
+hs2_status hs2_full_decode(const hs2_decode_desc* desc, const int64_t* seq_offsets, const void* k_cache,
+                           const void* v_cache, const float* k_scale, const float* v_scale, const float* q_full,
+                           float* o_full, void* workspace, size_t workspace_bytes, void* stream) {
+  HS2_TRY(check_desc(desc));
+  const hs2_decode_desc& d = *desc;
+  HS2_TRY(check_kv(d, seq_offsets, k_cache, v_cache, k_scale, v_scale));
+  const bool any = d.batch > 0;
+  HS2_TRY(check_ptr(q_full, any, 16, "q_full"));
+  HS2_TRY(check_ptr(o_full, any, 16, "o_full"));
+  DecodeLayout L;
+  HS2_TRY(check_workspace(d, workspace, workspace_bytes, L));
+  if (!any) return HS2_OK;
+  DecodeArgs a{desc, seq_offsets, k_cache, v_cache, k_scale, v_scale, q_full, nullptr, o_full, nullptr,
+               nullptr, nullptr, nullptr, workspace, static_cast<hipStream_t>(stream)};
+  TimingRecord* rec = nullptr;
+  HS2_TRY(timing_begin(&rec));
+  if (rec && rec->last > 2) rec->last = 2;  // stages 0 partial pass, 1 merge
+  // The bound-mode pass: its per-token outputs (6 bytes a token) are the
+  // cheapest the kernel writes; no selection follows.
+  const SelectParams sp = select_params(a, L, reinterpret_cast<float*>(ws_at(workspace, L.score)));
+  HS2_TRY(mark(rec, 0, a.stream));
+  HS2_TRY(run_full(a, L, &sp, rec));
+  return HS2_OK;
+}
+
 hs2_status hs2_stage_timing_enable(int32_t mode) {
   if (mode < 0 || mode > 2) return fail(HS2_ERR_INVALID_ARGUMENT, "timing mode %d (0, 1 or 2)", mode);
   std::lock_guard<std::mutex> lock(g_timing_mu);

@@ -151,6 +151,29 @@ constexpr int kSparseFillWorkgroups = 128;  // slice the selection while the gri
 int sparse_slices(int batch, int n_layers);
 // Attention over the selected rows: one launch, plus a merge when sliced.
 hipError_t launch_sparse_attend(const SparseParams& p, bool fp8, hipStream_t s);
+// The same attention over at most p.budget (<= 1152) rows per sequence, in one
+// unsliced launch (sliding-window layers: the rows of a ring buffer).
+hipError_t launch_sparse_window(const SparseParams& p, bool fp8, hipStream_t s);
+
+// ---- Self-Decoder sliding-window layers ----------------------------------------
+struct SwaParams {
+  const int64_t* lengths;     // [B] positions so far, the current token included
+  int batch;
+  int window;                 // ring rows per sequence (<= 1152)
+  int fp8;
+  uint8_t* ring_k;            // [B][window][128] bf16 or E4M3; position p at slot p mod window
+  uint8_t* ring_v;
+  float* ring_ks;             // [B][window] (E4M3)
+  float* ring_vs;
+  const uint8_t* k_new;       // [B][128] the current token's row, or nullptr (already in the ring)
+  const uint8_t* v_new;
+  const float* k_new_scale;   // [B] (E4M3)
+  const float* v_new_scale;
+  int64_t* offs;              // workspace [B + 1]: ring row offsets b * window
+  int32_t* sel_idx;           // workspace [B][window]: the ring slots in the window
+  int32_t* sel_count;         // workspace [B]
+};
+hipError_t launch_swa_prep(const SwaParams& p, hipStream_t s);
 
 // ---- KV bridging ---------------------------------------------------------------
 struct BridgeParams {

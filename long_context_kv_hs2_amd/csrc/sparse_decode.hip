@@ -31,7 +31,7 @@ constexpr int sparse_slices_for(int tiles) {
 }
 }  // namespace
 
-template <bool FP8, int TILES>
+template <bool FP8, int TILES, int SLICES = sparse_slices_for(TILES)>
 __global__ __launch_bounds__(kSparseThreads) void sparse_attend_kernel(SparseParams p) {
   constexpr int kWaveRows = 16 * TILES;
   constexpr int kSliceRows = kSparseWaves * kWaveRows;
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_attend_kernel(SparsePar
   // Work item j = (b * n_layers + layer) * slices + slice.  Consecutive items
   // go to one XCD (workgroup id i runs on XCD i % 8), so the layers and slices
   // of a sequence share that XCD's L2 when they gather the same rows.
-  constexpr int kSlices = sparse_slices_for(TILES);
+  constexpr int kSlices = SLICES;
   const int items = p.batch * p.n_layers * kSlices;
   const int per_xcd = (items + 7) / 8;
   const int j = static_cast<int>(blockIdx.x & 7) * per_xcd + static_cast<int>(blockIdx.x >> 3);
@@ -234,6 +234,38 @@ static void launch_fp(const SparseParams& p, int tiles, hipStream_t s) {
 }
 
 int sparse_slices(int batch, int n_layers) { return sparse_slices_for(sparse_wave_tiles(batch, n_layers)); }
+
+template <bool FP8, int TILES>
+static void launch_window_tiles(const SparseParams& p, hipStream_t s) {
+  const int items = p.batch * p.n_layers;
+  const dim3 grid(static_cast<unsigned>(8 * ((items + 7) / 8)));
+  hipLaunchKernelGGL((sparse_attend_kernel<FP8, TILES, 1>), grid, dim3(kSparseThreads), 0, s, p);
+}
+
+template <bool FP8>
+static void launch_window_fp(const SparseParams& p, hipStream_t s) {
+  const int rows = 16 * kSparseWaves;  // rows per tile step of the eight waves
+  if (p.budget <= rows)
+    launch_window_tiles<FP8, 1>(p, s);
+  else if (p.budget <= 2 * rows)
+    launch_window_tiles<FP8, 2>(p, s);
+  else if (p.budget <= 3 * rows)
+    launch_window_tiles<FP8, 3>(p, s);
+  else if (p.budget <= 5 * rows)
+    launch_window_tiles<FP8, 5>(p, s);
+  else
+    launch_window_tiles<FP8, 9>(p, s);
+}
+
+hipError_t launch_sparse_window(const SparseParams& p, bool fp8, hipStream_t s) {
+  if (p.batch == 0 || p.n_layers == 0) return hipSuccess;
+  if (p.budget < 1 || p.budget > kBudget) return hipErrorInvalidValue;
+  if (fp8)
+    launch_window_fp<true>(p, s);
+  else
+    launch_window_fp<false>(p, s);
+  return hipGetLastError();
+}
 
 hipError_t launch_sparse_attend(const SparseParams& p, bool fp8, hipStream_t s) {
   if (p.batch == 0 || p.n_layers == 0) return hipSuccess;
