@@ -19,6 +19,8 @@ workload (whole sequences, one after another, until about 15 s have passed).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 2|3|4|5] [--selection token|block]
 
+``--part self-decoder`` times the model's front half at decode on the same
+batch: its one full-attention layer and 24 sliding-window layers (window 128).
 ``--selection block`` times the same workload through the gen-1 (block-level)
 selection instead, the comparator of the pages' ablation: the full layer with
 every score (hs2_full_decode_score), hs2_block_select, then the sparse layers.
@@ -257,12 +259,93 @@ def bench_bridge(args, torch, hs2, inputs, dev):
     }
 
 
+def bench_self_decoder(args, torch, hs2, inputs, dev):
+    """The Self-Decoder's attention at decode on a workload's batch: its one
+    full-attention layer over the whole context (hs2_full_decode) and 24
+    sliding-window layers (window 128, one ring per layer; hs2_swa_decode,
+    each also writing the current token's rows), per decode step."""
+    d = inputs.make_decode(args.workload)
+    kv = d["kv"]
+    offs = torch.from_numpy(d["seq_offsets"]).to(dev)
+    if kv == "bf16":
+        k = torch.from_numpy(d["k"].view(np.int16)).view(torch.bfloat16).to(dev)
+        v = torch.from_numpy(d["v"].view(np.int16)).view(torch.bfloat16).to(dev)
+        ks = vs = None
+    else:
+        k, v = torch.from_numpy(d["k"]).to(dev), torch.from_numpy(d["v"]).to(dev)
+        ks, vs = torch.from_numpy(d["k_scale"]).to(dev), torch.from_numpy(d["v_scale"]).to(dev)
+    q_full = torch.from_numpy(d["q_full"]).to(dev)
+    lens = np.diff(d["seq_offsets"])
+    batch, n_tokens, n_swa, window = int(lens.shape[0]), int(lens.sum()), 24, 128
+    desc = hs2.make_desc(batch, n_tokens, int(lens.max()), 0, hs2.kv_dtype_of(k))
+    ws = torch.empty(hs2.decode_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    o_full = torch.empty((batch, 16, 128), dtype=torch.float32, device=dev)
+    g = torch.Generator(device="cpu").manual_seed(7)
+    rings = [(torch.randn((batch, window, 128), generator=g).to(torch.bfloat16).to(dev),
+              torch.randn((batch, window, 128), generator=g).to(torch.bfloat16).to(dev)) for _ in range(n_swa)]
+    new_k = torch.randn((batch, 128), generator=g).to(torch.bfloat16).to(dev)
+    new_v = torch.randn((batch, 128), generator=g).to(torch.bfloat16).to(dev)
+    q_swa = torch.randn((n_swa, batch, 16, 128), generator=g).to(dev)
+    lengths = torch.from_numpy(lens.astype(np.int64)).to(dev)
+    o_swa = torch.empty((batch, 16, 128), dtype=torch.float32, device=dev)
+    sws = torch.empty(max(hs2.load().hs2_swa_workspace_bytes(batch, window), 256), dtype=torch.uint8, device=dev)
+
+    def step(marks=None):
+        hs2.full_decode(offs, k, v, q_full, ks, vs, int(lens.max()), o_full, ws)
+        if marks:
+            marks[0].record()
+        for layer in range(n_swa):
+            hs2.swa_decode(lengths, rings[layer][0], rings[layer][1], q_swa[layer], k_new=new_k, v_new=new_v,
+                           o=o_swa, workspace=sws)
+        if marks:
+            marks[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    hs2.stage_timing(True, full_pass_only=True)
+    hs2.stage_timing_read()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    hs2.stage_timing(False)
+    k1 = hs2.stage_timing_read_calls()[:, 0]
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    swa_ms = []
+    for _ in range(min(args.steps, 20)):
+        step(marks)
+        torch.cuda.synchronize()
+        swa_ms.append(marks[0].elapsed_time(marks[1]) / n_swa)
+    alg_bytes = n_tokens * KV_ROW_BYTES[kv] + batch * 16 * 128 * 4
+    k1_ms = float(k1.mean())
+    achieved = alg_bytes / (k1_ms * 1e-3) / 1e9
+    return {
+        "metric": "self-decoder attention tokens/s (1 full-attention + 24 sliding-window layers per step)",
+        "value": batch * args.steps / dt, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": dt * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if kv == "bf16" else "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.workload] + "_self_decoder", "batch": batch, "context_tokens": n_tokens,
+                   "full_layers": 1, "swa_layers": n_swa, "swa_window": window, "swa_kv": "bf16"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "full_partial_kernel (hs2_full_decode)", "alg_bytes_per_launch": alg_bytes,
+                     "mean_launch_ms": k1_ms, "launch_ms": pct(k1)},
+        "swa_layer_ms": pct(swa_ms),
+        "swa_alg_bytes_per_layer": batch * window * 2 * 128 * 2 + batch * 2 * 16 * 128 * 4,
+        "device": device_info(torch),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOADS))
+    ap.add_argument("--part", choices=("hybrid-block", "self-decoder"), default="hybrid-block",
+                    help="self-decoder: the front half's attention (1 full + 24 sliding-window layers)")
     ap.add_argument("--selection", choices=("token", "block"), default="token",
                     help="token: the method's selection; block: the gen-1 64-token-block comparator")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -283,6 +366,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.workload == 5:
         print(json.dumps(bench_bridge(args, torch, hs2, inputs, dev)), flush=True)
+        return
+    if args.part == "self-decoder":
+        print(json.dumps(bench_self_decoder(args, torch, hs2, inputs, dev)), flush=True)
         return
     d = inputs.make_decode(args.workload)
     kv = d["kv"]
