@@ -58,12 +58,6 @@ __device__ __forceinline__ u64 block_key(float sum, int i) {
   return (static_cast<u64>(__float_as_uint(sum)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(i));
 }
 
-__device__ __forceinline__ u64 shfl_xor64(u64 v, int m) {
-  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m);
-  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m);
-  return (static_cast<u64>(hi) << 32) | lo;
-}
-
 __device__ __forceinline__ u64 shfl64(u64 v, int src) {
   const uint32_t lo = __shfl(static_cast<uint32_t>(v), src);
   const uint32_t hi = __shfl(static_cast<uint32_t>(v >> 32), src);
@@ -77,7 +71,7 @@ __device__ __forceinline__ u64 wave_sort_desc(u64 v) {
   for (int k = 2; k <= 64; k <<= 1) {
 #pragma unroll
     for (int j = k >> 1; j > 0; j >>= 1) {
-      const u64 o = shfl_xor64(v, j);
+      const u64 o = shfl_xor_u64(v, j);
       const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
       v = keep_max ? (v > o ? v : o) : (v < o ? v : o);
     }
@@ -93,7 +87,7 @@ __device__ __forceinline__ u64 wave_merge_desc(u64 a, u64 b) {
   u64 v = a > r ? a : r;
 #pragma unroll
   for (int j = 32; j > 0; j >>= 1) {
-    const u64 o = shfl_xor64(v, j);
+    const u64 o = shfl_xor_u64(v, j);
     v = (lane & j) == 0 ? (v > o ? v : o) : (v < o ? v : o);
   }
   return v;
@@ -137,8 +131,8 @@ __global__ __launch_bounds__(256 * kPoolGroups) void block_pool_kernel(BlockPara
   for (int off = 8; off > 0; off >>= 1) s += __shfl_xor(s, off);  // every lane ends with the same sum
   if (i < nb && l == 0) p.block_scores[block_slot(base, b, i)] = s;
   u64 key = i < nb ? block_key(s, i) : 0ull;
-  key = max(key, shfl_xor64(key, 16));
-  key = max(key, shfl_xor64(key, 32));
+  key = max(key, shfl_xor_u64(key, 16));
+  key = max(key, shfl_xor_u64(key, 32));
   if ((threadIdx.x & 63) == 0) s_wave_max[threadIdx.x >> 6] = key;
   __syncthreads();
   const u64* w = s_wave_max + 4 * quarter;

@@ -123,6 +123,13 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float x) {
   return ((u >> 24) & 0x80u) | code;
 }
 
+// 64-bit lane exchange: the value of lane (lane ^ m).
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
+  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m);
+  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m);
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
 // Byte permute of the pair {hi_word, lo_word}: selector byte i picks byte
 // sel_i of the 8-byte value lo_word | hi_word << 32.
 __device__ __forceinline__ uint32_t perm(uint32_t hi_word, uint32_t lo_word, uint32_t sel) {

@@ -453,22 +453,60 @@ __global__ __launch_bounds__(1024) void finish_kernel(SelectParams p) {
     }
   };
 
-  // digits of the 63 key bits below the sign: 11, 11, 11, 11, 11, 8
-  for (int pass = first_pass; pass < 6 && !done; ++pass) {
-    const int bits = pass < 5 ? 11 : 8;
-    const int shift = pass < 5 ? 52 - 11 * pass : 0;
+  // The digits run over key - kmin, 11 bits at a time from bit top_bits down.
+  // Normally kmin = 0 and top_bits = 63 (the bits below the sign: 11, 11, 11,
+  // 11, 11, 8).  A large candidate list read from global memory (near-uniform
+  // attention, where the bounds prune little) takes its range first: keys
+  // that share an exponent would pile into one or two bins of the first digit,
+  // and a wave's 64 atomic adds to one LDS word serialise; over the span's bits
+  // the first digit spreads them.
+  unsigned long long kmin = 0;
+  int top_bits = 63;
+  if (BOUND && !staged && ncand > 1u) {
+    __shared__ unsigned long long s_lo[16], s_hi[16];
+    unsigned long long lo = ~0ull, hi = 0ull;
+    for_each_key([&](unsigned long long key) {
+      lo = min(lo, key);
+      hi = max(hi, key);
+    });
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      lo = min(lo, shfl_xor_u64(lo, off));
+      hi = max(hi, shfl_xor_u64(hi, off));
+    }
+    if ((t & 63) == 0) {
+      s_lo[t >> 6] = lo;
+      s_hi[t >> 6] = hi;
+    }
+    __syncthreads();
+    lo = s_lo[0];
+    hi = s_hi[0];
+    for (int w = 1; w < 16; ++w) {
+      lo = min(lo, s_lo[w]);
+      hi = max(hi, s_hi[w]);
+    }
+    kmin = lo;
+    top_bits = 64 - __clzll(hi - lo);  // keys are distinct, so hi > lo; hi - lo < 2^63
+    pshift = top_bits;
+  }
+  for (int pass = first_pass; !done; ++pass) {
+    const int top = top_bits - 11 * pass;
+    if (top <= 0) break;
+    const int bits = min(11, top);
+    const int shift = top - bits;
     const uint32_t mask = (1u << bits) - 1u;
     for (int i = t; i < kRadixBins; i += blockDim.x) s_hist[i] = 0;
     __syncthreads();
     for_each_key([&](unsigned long long key) {
-      if ((key >> pshift) == prefix) atomicAdd(&s_hist[static_cast<uint32_t>(key >> shift) & mask], 1u);
+      const unsigned long long rk = key - kmin;
+      if ((rk >> pshift) == prefix) atomicAdd(&s_hist[static_cast<uint32_t>(rk >> shift) & mask], 1u);
     });
     __syncthreads();
     const Resolved r = block_resolve<1024>(s_hist, 1 << bits, rank, s_scan, &s_res);
     rank -= r.above;
     prefix = (prefix << bits) | static_cast<unsigned long long>(r.digit);
     pshift = shift;
-    done = r.count == rank || pass == 5;
+    done = r.count == rank || shift == 0;
   }
 
   // Winners from collect (spill mode), then the keys at or above the threshold.
@@ -476,7 +514,7 @@ __global__ __launch_bounds__(1024) void finish_kernel(SelectParams p) {
   if (t == 0) s_n = 0;
   __syncthreads();
   for_each_key([&](unsigned long long key) {
-    if ((key >> pshift) >= prefix) {
+    if (((key - kmin) >> pshift) >= prefix) {
       const uint32_t slot = nwin + atomicAdd(&s_n, 1u);
       if (slot < static_cast<uint32_t>(p.top_k)) s_sel[slot] = key_pos(key);
     }

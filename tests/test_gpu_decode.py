@@ -122,12 +122,15 @@ def test_fp8_long_context():
 
 def test_constant_keys_all_tied():
     say("case: constant keys (every score tied)")
-    d = inputs.make_decode(lengths=[5000, 20000], n_sparse=2, seed=3)
+    # (20000 and 600000 tokens: candidate lists too long for LDS, the second
+    # also kept in per-workgroup segments)
+    lengths = [5000, 20000, 600000]
+    d = inputs.make_decode(lengths=lengths, n_sparse=2, seed=3)
     row = d["k"][0].copy()
     d["k"][:] = row
     out, _, _ = run(d)
     sel = out["sel_idx"].cpu().numpy()
-    for b, length in enumerate([5000, 20000]):
+    for b, length in enumerate(lengths):
         want = np.concatenate([np.arange(1024), np.arange(length - 128, length)])
         np.testing.assert_array_equal(sel[b], want)
     parity.check_decode(d, out)
@@ -135,11 +138,13 @@ def test_constant_keys_all_tied():
 
 def test_zero_queries_uniform_attention():
     say("case: all-zero full-layer queries")
-    d = inputs.make_decode(lengths=[4000], n_sparse=1, seed=8)
+    lengths = [4000, 40000]
+    d = inputs.make_decode(lengths=lengths, n_sparse=1, seed=8)
     d["q_full"][:] = 0
     out, _, _ = run(d)
-    sel = out["sel_idx"].cpu().numpy()[0]
-    np.testing.assert_array_equal(sel, np.concatenate([np.arange(1024), np.arange(4000 - 128, 4000)]))
+    for b, length in enumerate(lengths):
+        sel = out["sel_idx"].cpu().numpy()[b]
+        np.testing.assert_array_equal(sel, np.concatenate([np.arange(1024), np.arange(length - 128, length)]))
     parity.check_decode(d, out)
 
 
