@@ -288,7 +288,6 @@ def bench_self_decoder(args, torch, hs2, inputs, dev):
     q_swa = torch.randn((n_swa, batch, 16, 128), generator=g).to(dev)
     lengths = torch.from_numpy(lens.astype(np.int64)).to(dev)
     o_swa = torch.empty((batch, 16, 128), dtype=torch.float32, device=dev)
-    sws = torch.empty(max(hs2.load().hs2_swa_workspace_bytes(batch, window), 256), dtype=torch.uint8, device=dev)
 
     def step(marks=None):
         hs2.full_decode(offs, k, v, q_full, ks, vs, int(lens.max()), o_full, ws)
@@ -296,7 +295,7 @@ def bench_self_decoder(args, torch, hs2, inputs, dev):
             marks[0].record()
         for layer in range(n_swa):
             hs2.swa_decode(lengths, rings[layer][0], rings[layer][1], q_swa[layer], k_new=new_k, v_new=new_v,
-                           o=o_swa, workspace=sws)
+                           o=o_swa)
         if marks:
             marks[1].record()
 

@@ -212,27 +212,25 @@ hs2_status hs2_bridge_kv_fp8(int64_t n_tokens, int32_t d_model, int32_t head_dim
  *   ring_k_scale, ring_v_scale (device) fp32 [batch][window] (E4M3), else NULL;
  *   lengths (device) int64 [batch]: positions so far, the current one
  *     included (0: zero output);
- *   k_new, v_new (device) [batch][128] the current token's rows (with
- *     k_new_scale, v_new_scale fp32 [batch] for E4M3), written into slot
- *     (lengths[b] - 1) mod window before the attention; NULL when the caller
- *     has already written them;
+ *   k_new, v_new (device, 16-byte aligned) [batch][128] the current token's
+ *     rows (with k_new_scale, v_new_scale fp32 [batch] for E4M3): attended in
+ *     place of slot (lengths[b] - 1) mod window and stored there, by the same
+ *     launch; NULL when the caller has already written them into the ring;
  *   q (device) fp32 [batch][16][128]; o (device) fp32 [batch][16][128];
  *   softmax_scale multiplies q.k (1/sqrt(128) in the workloads).
- * Supported: 1 <= window <= 1152, 16 query heads, head_dim 128.  workspace
- * (device) >= hs2_swa_workspace_bytes(batch, window), 256-byte aligned.     */
+ * Supported: 1 <= window <= 1152, 16 query heads, head_dim 128.  No
+ * workspace.  Calls on the same ring must not overlap.                      */
 hs2_status hs2_full_decode(const hs2_decode_desc* desc, const int64_t* seq_offsets,
                            const void* k_cache, const void* v_cache,
                            const float* k_scale, const float* v_scale,
                            const float* q_full, float* o_full,
                            void* workspace, size_t workspace_bytes, void* stream);
-size_t hs2_swa_workspace_bytes(int32_t batch, int32_t window);
 hs2_status hs2_swa_decode(int32_t batch, int32_t window, int32_t kv_dtype, float softmax_scale,
                           const int64_t* lengths, void* ring_k, void* ring_v,
                           float* ring_k_scale, float* ring_v_scale,
                           const void* k_new, const void* v_new,
                           const float* k_new_scale, const float* v_new_scale,
-                          const float* q, float* o,
-                          void* workspace, size_t workspace_bytes, void* stream);
+                          const float* q, float* o, void* stream);
 
 /* Decode-time KV Bridging: each decode step, the current token's hidden
  * state is projected by every bridged layer's W_k and W_v (the products of

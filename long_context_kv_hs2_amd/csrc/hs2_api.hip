@@ -319,7 +319,7 @@ hs2_status run_full(const DecodeArgs& a, const DecodeLayout& L, const SelectPara
 hs2_status run_sparse(const DecodeArgs& a, const DecodeLayout& L, const int32_t* sel_idx, const int32_t* sel_count) {
   const hs2_decode_desc& d = *a.d;
   if (d.n_sparse_layers == 0 || d.batch == 0) return HS2_OK;
-  SparseParams sp;
+  SparseParams sp{};
   sp.seq_offsets = a.offs;
   sp.total_tokens = d.total_tokens;
   sp.max_context = d.max_context;
@@ -630,18 +630,10 @@ hs2_status hs2_bridge_append(int32_t batch, int32_t d_model, int32_t head_dim, i
   return HS2_OK;
 }
 
-size_t hs2_swa_workspace_bytes(int32_t batch, int32_t window) {
-  if (batch < 0 || window < 1 || window > kBudget) return 0;
-  const size_t B = static_cast<size_t>(batch);
-  return align_up((B + 1) * sizeof(int64_t)) + align_up(B * window * sizeof(int32_t)) +
-         std::max<size_t>(align_up(B * sizeof(int32_t)), 256);
-}
-
 hs2_status hs2_swa_decode(int32_t batch, int32_t window, int32_t kv_dtype, float softmax_scale,
                           const int64_t* lengths, void* ring_k, void* ring_v, float* ring_k_scale,
                           float* ring_v_scale, const void* k_new, const void* v_new, const float* k_new_scale,
-                          const float* v_new_scale, const float* q, float* o, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+                          const float* v_new_scale, const float* q, float* o, void* stream) {
   if (batch < 0) return fail(HS2_ERR_INVALID_ARGUMENT, "batch %d < 0", batch);
   if (window < 1 || window > kBudget) return fail(HS2_ERR_UNSUPPORTED, "window %d (1..1152 supported)", window);
   if (kv_dtype != HS2_KV_BF16 && kv_dtype != HS2_KV_FP8_E4M3)
@@ -663,43 +655,19 @@ hs2_status hs2_swa_decode(int32_t batch, int32_t window, int32_t kv_dtype, float
   }
   if ((k_new == nullptr) != (v_new == nullptr)) return fail(HS2_ERR_INVALID_ARGUMENT, "k_new and v_new: both or neither");
   if (k_new) {
-    HS2_TRY(check_ptr(k_new, any, 4, "k_new"));
-    HS2_TRY(check_ptr(v_new, any, 4, "v_new"));
+    HS2_TRY(check_ptr(k_new, any, 16, "k_new"));
+    HS2_TRY(check_ptr(v_new, any, 16, "v_new"));
     if (fp8) {
       HS2_TRY(check_ptr(k_new_scale, any, 4, "k_new_scale"));
       HS2_TRY(check_ptr(v_new_scale, any, 4, "v_new_scale"));
     }
   }
-  const size_t need = hs2_swa_workspace_bytes(batch, window);
-  if (workspace_bytes < need) return fail(HS2_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
-  HS2_TRY(check_ptr(workspace, true, 256, "workspace"));
   if (!any) return HS2_OK;
-  const size_t B = static_cast<size_t>(batch);
-  SwaParams w{};
-  w.lengths = lengths;
-  w.batch = batch;
-  w.window = window;
-  w.fp8 = fp8 ? 1 : 0;
-  w.ring_k = static_cast<uint8_t*>(ring_k);
-  w.ring_v = static_cast<uint8_t*>(ring_v);
-  w.ring_ks = ring_k_scale;
-  w.ring_vs = ring_v_scale;
-  w.k_new = static_cast<const uint8_t*>(k_new);
-  w.v_new = static_cast<const uint8_t*>(v_new);
-  w.k_new_scale = k_new_scale;
-  w.v_new_scale = v_new_scale;
-  w.offs = reinterpret_cast<int64_t*>(workspace);
-  w.sel_idx = reinterpret_cast<int32_t*>(ws_at(workspace, align_up((B + 1) * sizeof(int64_t))));
-  w.sel_count = reinterpret_cast<int32_t*>(
-      ws_at(workspace, align_up((B + 1) * sizeof(int64_t)) + align_up(B * window * sizeof(int32_t))));
-  const hipStream_t st = static_cast<hipStream_t>(stream);
-  HS2_HIP(launch_swa_prep(w, st), "sliding-window ring update");
   SparseParams sp{};
-  sp.seq_offsets = w.offs;
   sp.total_tokens = static_cast<int64_t>(batch) * window;
   sp.max_context = window;
-  sp.k = w.ring_k;
-  sp.v = w.ring_v;
+  sp.k = static_cast<const uint8_t*>(ring_k);
+  sp.v = static_cast<const uint8_t*>(ring_v);
   sp.k_scale = ring_k_scale;
   sp.v_scale = ring_v_scale;
   sp.q_sparse = q;
@@ -707,11 +675,17 @@ hs2_status hs2_swa_decode(int32_t batch, int32_t window, int32_t kv_dtype, float
   sp.batch = batch;
   sp.n_layers = 1;
   sp.budget = window;
-  sp.sel_idx = w.sel_idx;
-  sp.sel_count = w.sel_count;
   sp.out = o;
-  sp.partials = nullptr;
-  HS2_HIP(launch_sparse_window(sp, fp8, st), "sliding-window attention");
+  sp.lengths = lengths;
+  sp.k_new = static_cast<const uint8_t*>(k_new);
+  sp.v_new = static_cast<const uint8_t*>(v_new);
+  sp.k_new_scale = k_new_scale;
+  sp.v_new_scale = v_new_scale;
+  sp.ring_k = static_cast<uint8_t*>(ring_k);
+  sp.ring_v = static_cast<uint8_t*>(ring_v);
+  sp.ring_ks = ring_k_scale;
+  sp.ring_vs = ring_v_scale;
+  HS2_HIP(launch_sparse_window(sp, fp8, static_cast<hipStream_t>(stream)), "sliding-window attention");
   return HS2_OK;
 }
 

@@ -145,35 +145,29 @@ struct SparseParams {
   const int32_t* sel_count;   // [B]
   float* out;                 // [n_layers][B][16][128]
   float* partials;            // [n_layers][B][slices][kPartialFloats] when the selection is sliced
+  // Window mode (sliding-window layers; launch_sparse_window): k, v, k_scale,
+  // v_scale are rings of `budget` rows per sequence, position p in slot
+  // p mod budget; the window covers min(lengths[b], budget) slots (all once the
+  // ring is full, else slots 0 .. L-1); seq_offsets, sel_idx, sel_count unused.
+  const int64_t* lengths;     // [B] positions so far, the current token included
+  const uint8_t* k_new;       // [B][128] the current token's rows (read in place of its slot), or nullptr
+  const uint8_t* v_new;
+  const float* k_new_scale;   // [B] (E4M3)
+  const float* v_new_scale;
+  uint8_t* ring_k;            // writable aliases of k, v, k_scale, v_scale: the current rows are stored there
+  uint8_t* ring_v;
+  float* ring_ks;
+  float* ring_vs;
 };
 constexpr int kSparseFillWorkgroups = 128;  // slice the selection while the grid has fewer workgroups
 // Slices of each (layer, sequence) selection the sparse pass uses (1: no partials, no merge).
 int sparse_slices(int batch, int n_layers);
 // Attention over the selected rows: one launch, plus a merge when sliced.
 hipError_t launch_sparse_attend(const SparseParams& p, bool fp8, hipStream_t s);
-// The same attention over at most p.budget (<= 1152) rows per sequence, in one
-// unsliced launch (sliding-window layers: the rows of a ring buffer).
+// Window mode: one sliding-window layer over ring caches of p.budget (<= 1152)
+// rows per sequence, in one unsliced launch that also stores the current rows.
 hipError_t launch_sparse_window(const SparseParams& p, bool fp8, hipStream_t s);
 
-// ---- Self-Decoder sliding-window layers ----------------------------------------
-struct SwaParams {
-  const int64_t* lengths;     // [B] positions so far, the current token included
-  int batch;
-  int window;                 // ring rows per sequence (<= 1152)
-  int fp8;
-  uint8_t* ring_k;            // [B][window][128] bf16 or E4M3; position p at slot p mod window
-  uint8_t* ring_v;
-  float* ring_ks;             // [B][window] (E4M3)
-  float* ring_vs;
-  const uint8_t* k_new;       // [B][128] the current token's row, or nullptr (already in the ring)
-  const uint8_t* v_new;
-  const float* k_new_scale;   // [B] (E4M3)
-  const float* v_new_scale;
-  int64_t* offs;              // workspace [B + 1]: ring row offsets b * window
-  int32_t* sel_idx;           // workspace [B][window]: the ring slots in the window
-  int32_t* sel_count;         // workspace [B]
-};
-hipError_t launch_swa_prep(const SwaParams& p, hipStream_t s);
 
 // ---- KV bridging ---------------------------------------------------------------
 struct BridgeParams {

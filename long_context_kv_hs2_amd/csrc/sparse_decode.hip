@@ -16,6 +16,16 @@
 // 2, 4 or 8 slices whose partials a second launch merges.  The layers of a
 // sequence read the same rows at about the same time, so HBM serves each row
 // about once and the other layers hit in cache.
+//
+// Window mode serves the Self-Decoder's sliding-window layers, which the
+// model's front half mixes with full attention ("Luo Fuli Teases Xiaomi
+// MiMo-V3 Architecture", paragraph on the self-decoder / cross-decoder split;
+// toolnavs.com article 2080, section "Ce que fait HySparse2"): a layer's cache
+// is a ring of `window` rows per sequence (position p in slot p mod window),
+// and the rows attended are the window's slots, so no list is read.  The
+// current token's rows come from the caller's input (its slot's old row is
+// never read) and are stored into the ring by the same workgroup, one
+// workgroup per sequence, unsliced.
 #include "hs2_device.h"
 #include "hs2_internal.h"
 #include "merge.h"
@@ -31,7 +41,7 @@ constexpr int sparse_slices_for(int tiles) {
 }
 }  // namespace
 
-template <bool FP8, int TILES, int SLICES = sparse_slices_for(TILES)>
+template <bool FP8, int TILES, int SLICES = sparse_slices_for(TILES), bool WINDOW = false>
 __global__ __launch_bounds__(kSparseThreads) void sparse_attend_kernel(SparseParams p) {
   constexpr int kWaveRows = 16 * TILES;
   constexpr int kSliceRows = kSparseWaves * kWaveRows;
@@ -55,8 +65,18 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_attend_kernel(SparsePar
   const int t = threadIdx.x;
   int64_t base;
   int len;
-  seq_bounds(p.seq_offsets, b, p.total_tokens, p.max_context, base, len);
-  const int count = clamp_count(p.sel_count[b], len, p.budget);
+  int count;
+  int new_slot = -1;  // window mode: the ring slot of the current token, read from the caller's rows
+  if constexpr (WINDOW) {
+    const int64_t positions = max<int64_t>(p.lengths[b], 0);
+    base = static_cast<int64_t>(b) * p.budget;
+    len = p.budget;
+    count = static_cast<int>(min<int64_t>(positions, p.budget));
+    if (p.k_new && positions > 0) new_slot = static_cast<int>((positions - 1) % p.budget);
+  } else {
+    seq_bounds(p.seq_offsets, b, p.total_tokens, p.max_context, base, len);
+    count = clamp_count(p.sel_count[b], len, p.budget);
+  }
   const int s0 = slice * kSliceRows;  // first selected row of the slice
   constexpr bool direct = kSlices == 1;
   if (count == 0) {  // uniform: an empty sequence has a zero output
@@ -69,8 +89,21 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_attend_kernel(SparsePar
   if (s0 >= count) return;  // uniform: the merge counts only slices with rows
   // Positions, clamped into the sequence (rows past `count` repeat the last one
   // and are masked out in the tile step), so every gather stays in the cache.
-  const int32_t* sel = p.sel_idx + static_cast<size_t>(b) * p.budget;
-  for (int i = t; i < kSliceRows; i += kSparseThreads) s_pos[i] = min(max(sel[min(s0 + i, count - 1)], 0), len - 1);
+  if constexpr (WINDOW) {
+    for (int i = t; i < kSliceRows; i += kSparseThreads) s_pos[i] = min(s0 + i, count - 1);
+    if (new_slot >= 0 && t < kRowBytes / 4) {  // store the current rows into the ring (nothing here reads that slot)
+      const size_t at = (static_cast<size_t>(base) + new_slot) * kRowBytes / 4 + t;
+      reinterpret_cast<uint32_t*>(p.ring_k)[at] = reinterpret_cast<const uint32_t*>(p.k_new)[b * kRowBytes / 4 + t];
+      reinterpret_cast<uint32_t*>(p.ring_v)[at] = reinterpret_cast<const uint32_t*>(p.v_new)[b * kRowBytes / 4 + t];
+      if (FP8 && t == 0) {
+        p.ring_ks[base + new_slot] = p.k_new_scale[b];
+        p.ring_vs[base + new_slot] = p.v_new_scale[b];
+      }
+    }
+  } else {
+    const int32_t* sel = p.sel_idx + static_cast<size_t>(b) * p.budget;
+    for (int i = t; i < kSliceRows; i += kSparseThreads) s_pos[i] = min(max(sel[min(s0 + i, count - 1)], 0), len - 1);
+  }
   __syncthreads();
 
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform
@@ -94,22 +127,45 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_attend_kernel(SparsePar
   // kload_offset(j, g); V lane (n, g) holds row r0 + 16t + 4g + r, dims 8n .. 8n + 7.
   auto load_tile = [&](int tile, Raw& raw) {
     const int i0 = r0 + 16 * tile;
-    const uint32_t krow = static_cast<uint32_t>(s_pos[min(i0 + n, last)]) * kRowBytes;
+    if constexpr (WINDOW) {  // the current token's slot reads the caller's rows
+      const int kp = s_pos[min(i0 + n, last)];
+      const uint8_t* ksrc = kp == new_slot ? p.k_new + static_cast<size_t>(b) * kRowBytes : kbase + kp * kRowBytes;
 #pragma unroll
-    for (int j = 0; j < (FP8 ? 2 : 4); ++j)
-      raw.k[j] = *reinterpret_cast<const u32x4*>(kbase + (krow + kload_offset(j, g)));
+      for (int j = 0; j < (FP8 ? 2 : 4); ++j) raw.k[j] = *reinterpret_cast<const u32x4*>(ksrc + kload_offset(j, g));
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t tv = static_cast<uint32_t>(s_pos[min(i0 + 4 * g + r, last)]);
-      if constexpr (FP8) {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(vbase + (tv * kRowBytes + 8 * n));
-        raw.v[r] = u32x4{w[0], w[1], 0u, 0u};
-        raw.ks[r] = ksb[tv];
-        raw.vs[r] = vsb[tv];
-      } else {
-        raw.v[r] = *reinterpret_cast<const u32x4*>(vbase + (tv * kRowBytes + 16 * n));
-        raw.ks[r] = 1.f;
-        raw.vs[r] = 1.f;
+      for (int r = 0; r < 4; ++r) {
+        const int tv = s_pos[min(i0 + 4 * g + r, last)];
+        const bool cur = tv == new_slot;
+        const uint8_t* vsrc = cur ? p.v_new + static_cast<size_t>(b) * kRowBytes : vbase + tv * kRowBytes;
+        if constexpr (FP8) {
+          const u32x2 w = *reinterpret_cast<const u32x2*>(vsrc + 8 * n);
+          raw.v[r] = u32x4{w[0], w[1], 0u, 0u};
+          raw.ks[r] = cur ? p.k_new_scale[b] : ksb[tv];
+          raw.vs[r] = cur ? p.v_new_scale[b] : vsb[tv];
+        } else {
+          raw.v[r] = *reinterpret_cast<const u32x4*>(vsrc + 16 * n);
+          raw.ks[r] = 1.f;
+          raw.vs[r] = 1.f;
+        }
+      }
+    } else {
+      const uint32_t krow = static_cast<uint32_t>(s_pos[min(i0 + n, last)]) * kRowBytes;
+#pragma unroll
+      for (int j = 0; j < (FP8 ? 2 : 4); ++j)
+        raw.k[j] = *reinterpret_cast<const u32x4*>(kbase + (krow + kload_offset(j, g)));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t tv = static_cast<uint32_t>(s_pos[min(i0 + 4 * g + r, last)]);
+        if constexpr (FP8) {
+          const u32x2 w = *reinterpret_cast<const u32x2*>(vbase + (tv * kRowBytes + 8 * n));
+          raw.v[r] = u32x4{w[0], w[1], 0u, 0u};
+          raw.ks[r] = ksb[tv];
+          raw.vs[r] = vsb[tv];
+        } else {
+          raw.v[r] = *reinterpret_cast<const u32x4*>(vbase + (tv * kRowBytes + 16 * n));
+          raw.ks[r] = 1.f;
+          raw.vs[r] = 1.f;
+        }
       }
     }
   };
@@ -239,7 +295,7 @@ template <bool FP8, int TILES>
 static void launch_window_tiles(const SparseParams& p, hipStream_t s) {
   const int items = p.batch * p.n_layers;
   const dim3 grid(static_cast<unsigned>(8 * ((items + 7) / 8)));
-  hipLaunchKernelGGL((sparse_attend_kernel<FP8, TILES, 1>), grid, dim3(kSparseThreads), 0, s, p);
+  hipLaunchKernelGGL((sparse_attend_kernel<FP8, TILES, 1, true>), grid, dim3(kSparseThreads), 0, s, p);
 }
 
 template <bool FP8>
@@ -259,7 +315,7 @@ static void launch_window_fp(const SparseParams& p, hipStream_t s) {
 
 hipError_t launch_sparse_window(const SparseParams& p, bool fp8, hipStream_t s) {
   if (p.batch == 0 || p.n_layers == 0) return hipSuccess;
-  if (p.budget < 1 || p.budget > kBudget) return hipErrorInvalidValue;
+  if (p.budget < 1 || p.budget > kBudget || p.lengths == nullptr || p.n_layers != 1) return hipErrorInvalidValue;
   if (fp8)
     launch_window_fp<true>(p, s);
   else

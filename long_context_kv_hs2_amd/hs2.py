@@ -26,8 +26,7 @@ STAGE_NAMES = ("full_partial", "full_merge", "score_select", "sparse")
 EXPORTED = (
     "hs2_decode_workspace_bytes", "hs2_decode_block", "hs2_full_decode_score", "hs2_topk_select", "hs2_block_select",
     "hs2_sparse_decode", "hs2_bridge_workspace_bytes", "hs2_bridge_kv", "hs2_bridge_kv_fp8",
-    "hs2_bridge_append_workspace_bytes", "hs2_bridge_append", "hs2_full_decode", "hs2_swa_workspace_bytes",
-    "hs2_swa_decode", "hs2_stage_timing_enable",
+    "hs2_bridge_append_workspace_bytes", "hs2_bridge_append", "hs2_full_decode", "hs2_swa_decode", "hs2_stage_timing_enable",
     "hs2_stage_timing_read", "hs2_stage_timing_read_calls", "hs2_status_string", "hs2_last_error_message",
 )
 
@@ -92,10 +91,7 @@ def load(path: str = LIB_PATH):
     lib.hs2_bridge_append.restype = ctypes.c_int
     lib.hs2_full_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hs2_full_decode.restype = ctypes.c_int
-    lib.hs2_swa_workspace_bytes.argtypes = [i32, i32]
-    lib.hs2_swa_workspace_bytes.restype = sz
-    lib.hs2_swa_decode.argtypes = [i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
-                                   vp]
+    lib.hs2_swa_decode.argtypes = [i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.hs2_swa_decode.restype = ctypes.c_int
     lib.hs2_stage_timing_enable.argtypes = [i32]
     lib.hs2_stage_timing_enable.restype = ctypes.c_int
@@ -363,20 +359,18 @@ def full_decode(seq_offsets, k, v, q_full, k_scale=None, v_scale=None, max_conte
 
 
 def swa_decode(lengths, ring_k, ring_v, q, ring_k_scale=None, ring_v_scale=None, k_new=None, v_new=None,
-               k_new_scale=None, v_new_scale=None, o=None, workspace=None, softmax_scale=None):
+               k_new_scale=None, v_new_scale=None, o=None, softmax_scale=None):
     """One sliding-window layer over ring caches [B, window, 128] (bf16, or
-    uint8 E4M3 codes with [B, window] scales); writes the current rows first
-    when k_new/v_new are given.  Returns o [B, 16, 128] fp32."""
+    uint8 E4M3 codes with [B, window] scales); with k_new/v_new the current
+    rows are attended and stored into their slot.  Returns o [B, 16, 128] fp32."""
     batch, window = ring_k.shape[0], ring_k.shape[1]
     dev = ring_k.device
     fp8 = ring_k.dtype == torch.uint8
     o = torch.empty((batch, 16, 128), dtype=torch.float32, device=dev) if o is None else o
-    ws = _workspace(load().hs2_swa_workspace_bytes(batch, window), dev, workspace)
     scale = 1.0 / math.sqrt(128) if softmax_scale is None else softmax_scale
     check(load().hs2_swa_decode(batch, window, KV_FP8_E4M3 if fp8 else KV_BF16, scale, _ptr(lengths), _ptr(ring_k),
                                 _ptr(ring_v), _ptr(ring_k_scale), _ptr(ring_v_scale), _ptr(k_new), _ptr(v_new),
-                                _ptr(k_new_scale), _ptr(v_new_scale), _ptr(q), _ptr(o), _ptr(ws), ws.numel(),
-                                _stream()))
+                                _ptr(k_new_scale), _ptr(v_new_scale), _ptr(q), _ptr(o), _stream()))
     return o
 
 

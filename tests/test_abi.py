@@ -157,13 +157,10 @@ def test_bridge_append_validation():
 
 def test_swa_and_full_decode_validation():
     lib = hs2.load()
-    ws = lib.hs2_swa_workspace_bytes(4, 128)
-    assert ws > 0 and lib.hs2_swa_workspace_bytes(4, 0) == 0 and lib.hs2_swa_workspace_bytes(4, 1153) == 0
 
     def swa(batch=4, window=128, kv=0, scale=0.088, lengths=FAKE, rk=FAKE, rv=FAKE, rks=None, rvs=None, kn=None,
-            vn=None, kns=None, vns=None, q=FAKE, o=FAKE, w=FAKE, nbytes=ws):
-        return lib.hs2_swa_decode(batch, window, kv, scale, lengths, rk, rv, rks, rvs, kn, vn, kns, vns, q, o, w,
-                                  nbytes, None)
+            vn=None, kns=None, vns=None, q=FAKE, o=FAKE):
+        return lib.hs2_swa_decode(batch, window, kv, scale, lengths, rk, rv, rks, rvs, kn, vn, kns, vns, q, o, None)
 
     assert swa(batch=-1) == INVALID
     assert swa(window=0) == UNSUPPORTED
@@ -176,7 +173,8 @@ def test_swa_and_full_decode_validation():
     assert swa(kv=1) == INVALID               # E4M3 ring without scales
     assert swa(rks=FAKE, rvs=FAKE) == INVALID  # bf16 ring with scales
     assert swa(kn=FAKE) == INVALID            # k_new without v_new
-    assert swa(nbytes=ws - 1) == SMALL_WS
+    assert swa(kn=FAKE + 4, vn=FAKE) == INVALID  # current rows not 16-byte aligned
+    assert swa(batch=0, lengths=None, rk=None, rv=None, q=None, o=None) == 0  # nothing to do
     d = desc()
     n = lib.hs2_decode_workspace_bytes(ctypes.byref(d))
     assert lib.hs2_full_decode(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, n, None) == INVALID
