@@ -35,7 +35,10 @@ plainest reading is taken; each such reading is named where it is used:
   window under the same budget;
 * a Self-Decoder sliding-window layer attends to the 128 most recent
   positions (no window size is given; the pages' local window is used),
-  kept in a ring buffer at slot position mod 128.
+  kept in a ring buffer at slot position mod 128;
+* several query tokens of a sequence in one step (speculative verification,
+  which the pages do not describe for HySparse2): each token is a decode step
+  of its own over its causal prefix, with its own selection.
 """
 
 from __future__ import annotations
@@ -351,6 +354,29 @@ def decode_sequence(q_full: np.ndarray, q_sparse: np.ndarray, k: np.ndarray, v: 
         if q_sparse.shape[0] else np.zeros((0,) + q_full.shape)
     return {"o_full": o_full, "score": score, "sel": s["sel"], "s_k": s["s_k"],
             "band": s["band"], "o_sparse": o_sparse}
+
+
+def decode_multi_sequence(q_full: np.ndarray, q_sparse: np.ndarray, k: np.ndarray, v: np.ndarray,
+                          window: int = WINDOW, top_k: int = TOP_K):
+    """Several query tokens of one sequence in one decode step (speculative
+    verification).  The pages name no multi-token rule for HySparse2; the
+    reading taken: the T tokens occupy the last T positions of the cache and
+    token t, at position L - T + t, is a decode step of its own over the
+    prefix [0, L - T + t] (causal), with its own selection.
+
+    q_full [T, H, D]; q_sparse [n_s, T, H, D]; k, v [L, D] decoded rows.
+    Returns a list of T per-token dicts (see ``decode_sequence``); a token
+    whose position is below 0 (L < T) gets None.
+    """
+    n_tok, length = q_full.shape[0], k.shape[0]
+    out = []
+    for t in range(n_tok):
+        n = length - n_tok + t + 1
+        if n <= 0:
+            out.append(None)
+            continue
+        out.append(decode_sequence(q_full[t], q_sparse[:, t], k[:n], v[:n], window, top_k))
+    return out
 
 
 def decode_block(seq_offsets, k_raw, v_raw, q_full, q_sparse, kv_dtype="bf16",
