@@ -114,6 +114,30 @@ hs2_status hs2_decode_block(const hs2_decode_desc* desc, const int64_t* seq_offs
                             int32_t* sel_idx, int32_t* sel_count, float* score_out,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* Multi-token decode (speculative verification): n_query = T query tokens
+ * per sequence in one step.  The pages give no multi-token rule for
+ * HySparse2; the reading taken: the T tokens are the sequence's last T cache
+ * rows (already stored), and token t, at position L_b - T + t, is a decode
+ * step of its own over the causal prefix [0, L_b - T + t], with its own
+ * selection (window and top-k as hs2_decode_block).  Arguments as
+ * hs2_decode_block with the token index after the sequence index:
+ *   q_full, o_full fp32 [B][T][16][128]; q_sparse, o_sparse fp32
+ *   [n_s][B][T][16][128]; sel_idx int32 [B][T][window + top_k];
+ *   sel_count int32 [B][T].
+ * A token whose position would be below 0 (L_b < T) gets zero outputs and
+ * sel_count 0.  Supported: 1 <= n_query <= 16, batch * n_query <= 2^24.
+ * workspace >= hs2_decode_multi_workspace_bytes(desc, n_query) (it grows
+ * with T: each token keeps its own scores and candidates).  Every token
+ * streams its prefix's K/V rows (T x the full layer's bytes at most).      */
+size_t hs2_decode_multi_workspace_bytes(const hs2_decode_desc* desc, int32_t n_query);
+hs2_status hs2_decode_multi(const hs2_decode_desc* desc, int32_t n_query, const int64_t* seq_offsets,
+                            const void* k_cache, const void* v_cache,
+                            const float* k_scale, const float* v_scale,
+                            const float* q_full, const float* q_sparse,
+                            float* o_full, float* o_sparse,
+                            int32_t* sel_idx, int32_t* sel_count,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* Stage call: the full-attention layer alone.  Same arguments as
  * hs2_decode_block; writes o_full and score_out (required here).            */
 hs2_status hs2_full_decode_score(const hs2_decode_desc* desc, const int64_t* seq_offsets,

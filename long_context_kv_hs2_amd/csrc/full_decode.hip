@@ -133,10 +133,11 @@ __global__ __launch_bounds__(64 * full_waves<FP8>()) void full_partial_kernel(Fu
   constexpr int kRowBytes = FP8 ? kDim : 2 * kDim;
   // Uniform per-sequence bases; lanes address rows with 32-bit offsets
   // (a sequence spans at most 2^24 rows, so its bytes fit in 32 bits).
-  const uint8_t* __restrict__ kbase = p.k + base * kRowBytes;
-  const uint8_t* __restrict__ vbase = p.v + base * kRowBytes;
-  const float* __restrict__ ksb = FP8 ? p.k_scale + base : nullptr;
-  const float* __restrict__ vsb = FP8 ? p.v_scale + base : nullptr;
+  const int64_t kvb = p.kv_start ? p.kv_start[b] : base;  // the sequence's first K/V row
+  const uint8_t* __restrict__ kbase = p.k + kvb * kRowBytes;
+  const uint8_t* __restrict__ vbase = p.v + kvb * kRowBytes;
+  const float* __restrict__ ksb = FP8 ? p.k_scale + kvb : nullptr;
+  const float* __restrict__ vsb = FP8 ? p.v_scale + kvb : nullptr;
   float* __restrict__ spill = BOUND ? nullptr : p.spill + base * kHeads;
   uint16_t* __restrict__ shat = BOUND ? p.shat + base : nullptr;
 

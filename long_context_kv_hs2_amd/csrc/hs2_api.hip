@@ -225,10 +225,12 @@ struct DecodeArgs {
   float* score_out;
   void* ws;
   hipStream_t stream;
+  const int64_t* kv_start = nullptr;  // multi-token decode: real first K/V row of each virtual sequence
 };
 
 FullParams full_params(const DecodeArgs& a, const DecodeLayout& L) {
-  FullParams p;
+  FullParams p{};
+  p.kv_start = a.kv_start;
   p.seq_offsets = a.offs;
   p.total_tokens = a.d->total_tokens;
   p.max_context = a.d->max_context;
@@ -252,7 +254,8 @@ FullParams full_params(const DecodeArgs& a, const DecodeLayout& L) {
 }
 
 SelectParams select_params(const DecodeArgs& a, const DecodeLayout& L, float* score) {
-  SelectParams p;
+  SelectParams p{};
+  p.kv_start = a.kv_start;
   p.seq_offsets = a.offs;
   p.total_tokens = a.d->total_tokens;
   p.max_context = a.d->max_context;
@@ -336,9 +339,12 @@ hs2_status run_sparse(const DecodeArgs& a, const DecodeLayout& L, const int32_t*
   sp.sel_count = sel_count;
   sp.out = a.o_sparse;
   sp.partials = reinterpret_cast<float*>(ws_at(a.ws, L.sparse));
+  sp.kv_start = a.kv_start;
   HS2_HIP(launch_sparse_attend(sp, d.kv_dtype == HS2_KV_FP8_E4M3, a.stream), "sparse layers");
   return HS2_OK;
 }
+
+hs2_status run_block(const DecodeArgs& a, const DecodeLayout& L);
 
 }  // namespace
 
@@ -372,6 +378,17 @@ hs2_status hs2_decode_block(const hs2_decode_desc* desc, const int64_t* seq_offs
 
   DecodeArgs a{desc, seq_offsets, k_cache, v_cache, k_scale, v_scale, q_full, q_sparse, o_full, o_sparse,
                sel_idx, sel_count, score_out, workspace, static_cast<hipStream_t>(stream)};
+  return run_block(a, L);
+}
+
+}  // extern "C"
+
+namespace {
+// One hybrid block for the (validated) batch in `a`.
+hs2_status run_block(const DecodeArgs& a, const DecodeLayout& L) {
+  const hs2_decode_desc& d = *a.d;
+  void* workspace = a.ws;
+  float* score_out = a.score_out;
   TimingRecord* rec = nullptr;
   HS2_TRY(timing_begin(&rec));
   // Without a score output the full pass keeps only score bounds (2 + 4 bytes
@@ -393,9 +410,71 @@ hs2_status hs2_decode_block(const hs2_decode_desc* desc, const int64_t* seq_offs
     HS2_HIP(launch_collect_finish(sp, d.batch, d.max_context, a.stream), "selection");
   }
   HS2_TRY(mark(rec, 3, a.stream));
-  HS2_TRY(run_sparse(a, L, sel_idx, sel_count));
+  HS2_TRY(run_sparse(a, L, a.sel_idx, a.sel_count));
   HS2_TRY(mark(rec, 4, a.stream));
   return HS2_OK;
+}
+}  // namespace
+
+extern "C" {
+
+// Multi-token decode: the virtual batch's descriptor, and its layout followed
+// by the virtual offsets and K/V starts.
+static hs2_decode_desc multi_desc(const hs2_decode_desc& d, int32_t n_query) {
+  hs2_decode_desc v = d;
+  v.batch = d.batch * n_query;
+  v.total_tokens = d.total_tokens * n_query;  // bounds the packed prefix lengths
+  return v;
+}
+
+size_t hs2_decode_multi_workspace_bytes(const hs2_decode_desc* desc, int32_t n_query) {
+  if (check_desc(desc) != HS2_OK || n_query < 1 || n_query > kMaxQueryTokens) return 0;
+  const hs2_decode_desc v = multi_desc(*desc, n_query);
+  if (check_desc(&v) != HS2_OK) return 0;
+  const size_t n = static_cast<size_t>(v.batch);
+  return align_up(decode_layout(v).total) + align_up((n + 1) * sizeof(int64_t)) + align_up(n * sizeof(int64_t));
+}
+
+hs2_status hs2_decode_multi(const hs2_decode_desc* desc, int32_t n_query, const int64_t* seq_offsets,
+                            const void* k_cache, const void* v_cache, const float* k_scale, const float* v_scale,
+                            const float* q_full, const float* q_sparse, float* o_full, float* o_sparse,
+                            int32_t* sel_idx, int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  HS2_TRY(check_desc(desc));
+  const hs2_decode_desc& d = *desc;
+  if (n_query < 1 || n_query > kMaxQueryTokens)
+    return fail(HS2_ERR_UNSUPPORTED, "n_query %d (1..%d supported)", n_query, kMaxQueryTokens);
+  if (static_cast<int64_t>(d.batch) * n_query > (1 << 24))
+    return fail(HS2_ERR_UNSUPPORTED, "batch * n_query above 2^24");
+  HS2_TRY(check_kv(d, seq_offsets, k_cache, v_cache, k_scale, v_scale));
+  const hs2_decode_desc v = multi_desc(d, n_query);
+  HS2_TRY(check_desc(&v));
+  const bool any = d.batch > 0;
+  const bool sparse = any && d.n_sparse_layers > 0;
+  HS2_TRY(check_ptr(q_full, any, 16, "q_full"));
+  HS2_TRY(check_ptr(o_full, any, 16, "o_full"));
+  HS2_TRY(check_ptr(q_sparse, sparse, 16, "q_sparse"));
+  HS2_TRY(check_ptr(o_sparse, sparse, 16, "o_sparse"));
+  HS2_TRY(check_ptr(sel_idx, any, 4, "sel_idx"));
+  HS2_TRY(check_ptr(sel_count, any, 4, "sel_count"));
+  const size_t need = hs2_decode_multi_workspace_bytes(desc, n_query);
+  if (workspace_bytes < need) return fail(HS2_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  HS2_TRY(check_ptr(workspace, true, 256, "workspace"));
+  if (!any) return HS2_OK;
+  const DecodeLayout L = decode_layout(v);
+  const size_t n = static_cast<size_t>(v.batch);
+  MultiParams mp{};
+  mp.seq_offsets = seq_offsets;
+  mp.total_tokens = d.total_tokens;
+  mp.max_context = d.max_context;
+  mp.batch = d.batch;
+  mp.n_query = n_query;
+  mp.voffs = reinterpret_cast<int64_t*>(ws_at(workspace, align_up(L.total)));
+  mp.kv_start = reinterpret_cast<int64_t*>(ws_at(workspace, align_up(L.total) + align_up((n + 1) * sizeof(int64_t))));
+  HS2_HIP(launch_multi_prep(mp, static_cast<hipStream_t>(stream)), "multi-token offsets");
+  DecodeArgs a{&v, mp.voffs, k_cache, v_cache, k_scale, v_scale, q_full, q_sparse, o_full, o_sparse,
+               sel_idx, sel_count, nullptr, workspace, static_cast<hipStream_t>(stream), mp.kv_start};
+  return run_block(a, L);
 }
 
 hs2_status hs2_full_decode_score(const hs2_decode_desc* desc, const int64_t* seq_offsets, const void* k_cache,

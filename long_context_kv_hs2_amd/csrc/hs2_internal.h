@@ -35,6 +35,7 @@ struct FullParams {
   float* tile_stats;         // bound mode: [tile_slots][16] per head after each tile: running max - log2(~1/running sum)
   uint32_t* hist0;           // [B][kRadixBins] selection histogram, cleared here
   uint32_t* counters;        // [B][4] selection counters, cleared here
+  const int64_t* kv_start;   // [B] first K/V row of each sequence, or nullptr: the row seq_offsets[b]
 };
 // Slot of tile t (tokens [16t, 16t + 16)) of the sequence starting at row `base`:
 // unique over all sequences, at most N/16 + B.
@@ -104,6 +105,7 @@ struct SelectParams {
   const float* k_scale;
   const float* q;             // [B][16][128]
   float qscale;
+  const int64_t* kv_start;    // [B] first K/V row of each sequence, or nullptr: the row seq_offsets[b]
 };
 constexpr int kRadixBins = 2048;
 constexpr int kScoreBlockTokens = 2048;   // tokens per score-pass workgroup
@@ -145,6 +147,7 @@ struct SparseParams {
   const int32_t* sel_count;   // [B]
   float* out;                 // [n_layers][B][16][128]
   float* partials;            // [n_layers][B][slices][kPartialFloats] when the selection is sliced
+  const int64_t* kv_start;    // [B] first K/V row of each sequence, or nullptr: the row seq_offsets[b]
   // Window mode (sliding-window layers; launch_sparse_window): k, v, k_scale,
   // v_scale are rings of `budget` rows per sequence, position p in slot
   // p mod budget; the window covers min(lengths[b], budget) slots (all once the
@@ -201,5 +204,21 @@ struct AppendParams {
   float* partials;             // workspace: [d_model / kAppendSliceK][B][n_out * 128]
 };
 hipError_t launch_bridge_append(const AppendParams& p, hipStream_t s);
+
+// Multi-token decode: T query tokens per sequence, token t a decode step of
+// its own over the causal prefix [0, L_b - T + t]; run as a batch of B * T
+// virtual sequences whose workspace ranges are disjoint and whose K/V rows
+// start at their real sequence's first row.
+constexpr int kMaxQueryTokens = 16;
+struct MultiParams {
+  const int64_t* seq_offsets;  // [B + 1] real sequences
+  int64_t total_tokens;
+  int64_t max_context;
+  int batch;
+  int n_query;                 // T
+  int64_t* voffs;              // [B * T + 1] virtual offsets (prefix lengths, packed)
+  int64_t* kv_start;           // [B * T] real first row of each virtual sequence
+};
+hipError_t launch_multi_prep(const MultiParams& p, hipStream_t s);
 
 }  // namespace hs2

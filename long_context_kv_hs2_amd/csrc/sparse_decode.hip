@@ -113,10 +113,11 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_attend_kernel(SparsePar
   const int r0 = wave * kWaveRows;                         // within the slice
   const int rows = min(max(count - s0 - r0, 0), kWaveRows);
   const int last = count - 1 - s0;                         // last valid slot of s_pos
-  const uint8_t* __restrict__ kbase = p.k + base * kRowBytes;
-  const uint8_t* __restrict__ vbase = p.v + base * kRowBytes;
-  const float* __restrict__ ksb = FP8 ? p.k_scale + base : nullptr;
-  const float* __restrict__ vsb = FP8 ? p.v_scale + base : nullptr;
+  const int64_t kvb = !WINDOW && p.kv_start ? p.kv_start[b] : base;  // the sequence's first K/V row
+  const uint8_t* __restrict__ kbase = p.k + kvb * kRowBytes;
+  const uint8_t* __restrict__ vbase = p.v + kvb * kRowBytes;
+  const float* __restrict__ ksb = FP8 ? p.k_scale + kvb : nullptr;
+  const float* __restrict__ vsb = FP8 ? p.v_scale + kvb : nullptr;
 
   struct Raw {
     u32x4 k[FP8 ? 2 : 4];

@@ -927,7 +927,8 @@ __global__ __launch_bounds__(256) void collect_rescore_kernel(SelectParams p) {
   const int n = lane & 15;
   const int g = lane >> 4;
   constexpr int kRowBytes = FP8 ? kDim : 2 * kDim;
-  const uint8_t* __restrict__ kbase = p.k + base * kRowBytes;
+  const int64_t kvb = p.kv_start ? p.kv_start[b] : base;  // the sequence's first K/V row
+  const uint8_t* __restrict__ kbase = p.k + kvb * kRowBytes;
   struct Raw {
     u32x4 k[FP8 ? 2 : 4];
     float ks[4];
@@ -943,7 +944,7 @@ __global__ __launch_bounds__(256) void collect_rescore_kernel(SelectParams p) {
     for (int jj = 0; jj < (FP8 ? 2 : 4); ++jj)
       r.k[jj] = *reinterpret_cast<const u32x4*>(kbase + (krow + kload_offset(jj, g)));
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) r.ks[q4] = FP8 ? p.k_scale[base + __shfl(r.pos, 4 * g + q4)] : 1.f;
+    for (int q4 = 0; q4 < 4; ++q4) r.ks[q4] = FP8 ? p.k_scale[kvb + __shfl(r.pos, 4 * g + q4)] : 1.f;
   };
   int ct = wave;
   Raw ra, rb;

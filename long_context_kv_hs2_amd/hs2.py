@@ -26,7 +26,8 @@ STAGE_NAMES = ("full_partial", "full_merge", "score_select", "sparse")
 EXPORTED = (
     "hs2_decode_workspace_bytes", "hs2_decode_block", "hs2_full_decode_score", "hs2_topk_select", "hs2_block_select",
     "hs2_sparse_decode", "hs2_bridge_workspace_bytes", "hs2_bridge_kv", "hs2_bridge_kv_fp8",
-    "hs2_bridge_append_workspace_bytes", "hs2_bridge_append", "hs2_full_decode", "hs2_swa_decode", "hs2_stage_timing_enable",
+    "hs2_bridge_append_workspace_bytes", "hs2_bridge_append", "hs2_full_decode", "hs2_swa_decode",
+    "hs2_decode_multi_workspace_bytes", "hs2_decode_multi", "hs2_stage_timing_enable",
     "hs2_stage_timing_read", "hs2_stage_timing_read_calls", "hs2_status_string", "hs2_last_error_message",
 )
 
@@ -89,6 +90,10 @@ def load(path: str = LIB_PATH):
     pp = ctypes.POINTER(vp)
     lib.hs2_bridge_append.argtypes = [i32, i32, i32, i32, i32, vp, i64, vp, pp, pp, pp, pp, pp, pp, vp, sz, vp]
     lib.hs2_bridge_append.restype = ctypes.c_int
+    lib.hs2_decode_multi_workspace_bytes.argtypes = [dp, i32]
+    lib.hs2_decode_multi_workspace_bytes.restype = sz
+    lib.hs2_decode_multi.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hs2_decode_multi.restype = ctypes.c_int
     lib.hs2_full_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hs2_full_decode.restype = ctypes.c_int
     lib.hs2_swa_decode.argtypes = [i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -176,6 +181,37 @@ class DecodeBlock:
     def outputs(self):
         return dict(o_full=self.o_full, o_sparse=self.o_sparse, sel_idx=self.sel_idx,
                     sel_count=self.sel_count, score=self.score)
+
+
+class MultiDecode:
+    """Multi-token decode step: q_full [B, T, 16, 128], q_sparse [n_s, B, T,
+    16, 128]; each token decodes over its causal prefix with its own
+    selection.  Holds outputs and workspace across calls."""
+
+    def __init__(self, seq_offsets, k, v, q_full, q_sparse, k_scale=None, v_scale=None, max_context=None):
+        dev = k.device
+        self.seq_offsets, self.k, self.v, self.k_scale, self.v_scale = seq_offsets, k, v, k_scale, v_scale
+        self.q_full, self.q_sparse = q_full, q_sparse
+        batch, self.n_query = q_full.shape[0], q_full.shape[1]
+        n_s = 0 if q_sparse is None else q_sparse.shape[0]
+        if max_context is None:
+            max_context = int((seq_offsets[1:] - seq_offsets[:-1]).max().item()) if batch else 0
+        self.desc = make_desc(batch, k.shape[0], max_context, n_s, kv_dtype_of(k))
+        t = self.n_query
+        self.o_full = torch.empty((batch, t, 16, 128), dtype=torch.float32, device=dev)
+        self.o_sparse = torch.empty((n_s, batch, t, 16, 128), dtype=torch.float32, device=dev) if n_s else None
+        self.sel_idx = torch.empty((batch, t, 1152), dtype=torch.int32, device=dev)
+        self.sel_count = torch.empty((batch, t), dtype=torch.int32, device=dev)
+        need = load().hs2_decode_multi_workspace_bytes(ctypes.byref(self.desc), t)
+        self.workspace = _workspace(need, dev)
+
+    def __call__(self):
+        check(load().hs2_decode_multi(
+            ctypes.byref(self.desc), self.n_query, _ptr(self.seq_offsets), _ptr(self.k), _ptr(self.v),
+            _ptr(self.k_scale), _ptr(self.v_scale), _ptr(self.q_full), _ptr(self.q_sparse), _ptr(self.o_full),
+            _ptr(self.o_sparse), _ptr(self.sel_idx), _ptr(self.sel_count), _ptr(self.workspace),
+            self.workspace.numel(), _stream()))
+        return self
 
 
 def decode_block(seq_offsets, k, v, q_full, q_sparse, k_scale=None, v_scale=None, max_context=None,

@@ -182,6 +182,27 @@ def test_swa_and_full_decode_validation():
                                None) == SMALL_WS
 
 
+def test_decode_multi_validation():
+    lib = hs2.load()
+    d = desc()
+    n = lib.hs2_decode_multi_workspace_bytes(ctypes.byref(d), 4)
+    assert n > lib.hs2_decode_workspace_bytes(ctypes.byref(d))
+    assert lib.hs2_decode_multi_workspace_bytes(ctypes.byref(d), 0) == 0
+    assert lib.hs2_decode_multi_workspace_bytes(ctypes.byref(d), 17) == 0
+
+    def call(t=4, offs=FAKE, k=FAKE, q=FAKE, qs=FAKE, o=FAKE, os_=FAKE, si=FAKE, sc=FAKE, nbytes=n):
+        return lib.hs2_decode_multi(ctypes.byref(d), t, offs, k, k, None, None, q, qs, o, os_, si, sc, FAKE, nbytes,
+                                    None)
+
+    assert call(t=0) == UNSUPPORTED
+    assert call(t=17) == UNSUPPORTED
+    assert call(offs=None) == INVALID
+    assert call(q=None) == INVALID
+    assert call(qs=None) == INVALID
+    assert call(si=None) == INVALID
+    assert call(nbytes=n - 1) == SMALL_WS
+
+
 def test_stage_calls_validate():
     lib = hs2.load()
     d = desc()
