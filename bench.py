@@ -19,6 +19,8 @@ workload (whole sequences, one after another, until about 15 s have passed).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 2|3|4|5] [--selection token|block]
 
+``--tokens T`` (T > 1) times multi-token decode on the same cache: T query
+tokens per sequence, each over its causal prefix with its own selection.
 ``--part self-decoder`` times the model's front half at decode on the same
 batch: its one full-attention layer and 24 sliding-window layers (window 128).
 ``--selection block`` times the same workload through the gen-1 (block-level)
@@ -337,6 +339,66 @@ def bench_self_decoder(args, torch, hs2, inputs, dev):
     }
 
 
+def bench_multi(args, torch, hs2, inputs, dev):
+    """Multi-token decode on a workload's cache: T query tokens per sequence,
+    each a decode step over its causal prefix with its own selection."""
+    d = inputs.make_decode(args.workload)
+    kv = d["kv"]
+    offs = torch.from_numpy(d["seq_offsets"]).to(dev)
+    if kv == "bf16":
+        k = torch.from_numpy(d["k"].view(np.int16)).view(torch.bfloat16).to(dev)
+        v = torch.from_numpy(d["v"].view(np.int16)).view(torch.bfloat16).to(dev)
+        ks = vs = None
+    else:
+        k, v = torch.from_numpy(d["k"]).to(dev), torch.from_numpy(d["v"]).to(dev)
+        ks, vs = torch.from_numpy(d["k_scale"]).to(dev), torch.from_numpy(d["v_scale"]).to(dev)
+    lens = np.diff(d["seq_offsets"])
+    batch, n_tokens, t_q = int(lens.shape[0]), int(lens.sum()), args.tokens
+    n_s = d["q_sparse"].shape[0]
+    g = torch.Generator(device="cpu").manual_seed(11)
+    q_full = torch.randn((batch, t_q, 16, 128), generator=g).to(dev)
+    q_sparse = torch.randn((n_s, batch, t_q, 16, 128), generator=g).to(dev)
+    step = hs2.MultiDecode(offs, k, v, q_full, q_sparse, ks, vs, int(lens.max()))
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    hs2.stage_timing(True, full_pass_only=True)
+    hs2.stage_timing_read()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    hs2.stage_timing(False)
+    k1 = hs2.stage_timing_read_calls()[:, 0]
+    hs2.stage_timing(True)
+    for _ in range(min(args.steps, 20)):
+        step()
+    torch.cuda.synchronize()
+    hs2.stage_timing(False)
+    calls = hs2.stage_timing_read_calls()
+    stage_pct = {name: pct(calls[:, i]) for i, name in enumerate(hs2.STAGE_NAMES)}
+    # algorithmic bytes: every K/V row once for all T tokens (a multi-query pass
+    # would read no more), plus the T tokens' queries
+    alg_bytes = n_tokens * KV_ROW_BYTES[kv] + batch * t_q * 16 * 128 * 4
+    k1_ms = float(k1.mean())
+    achieved = alg_bytes / (k1_ms * 1e-3) / 1e9
+    return {
+        "metric": METRIC + " (multi-token step)", "value": batch * t_q * args.steps / dt, "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": dt * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if kv == "bf16" else "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.workload] + f"_multi{t_q}", "batch": batch, "query_tokens": t_q,
+                   "context_tokens": n_tokens, "kv_cache": kv, "n_sparse_layers": n_s},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "full_partial_kernel over the B x T causal prefixes", "alg_bytes_per_launch": alg_bytes,
+                     "mean_launch_ms": k1_ms, "launch_ms": pct(k1)},
+        "stages_ms_percentiles": stage_pct,
+        "device": device_info(torch),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -345,6 +407,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOADS))
     ap.add_argument("--part", choices=("hybrid-block", "self-decoder"), default="hybrid-block",
                     help="self-decoder: the front half's attention (1 full + 24 sliding-window layers)")
+    ap.add_argument("--tokens", type=int, default=1,
+                    help="query tokens per sequence and step (above 1: the multi-token decode line)")
     ap.add_argument("--selection", choices=("token", "block"), default="token",
                     help="token: the method's selection; block: the gen-1 64-token-block comparator")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -365,6 +429,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.workload == 5:
         print(json.dumps(bench_bridge(args, torch, hs2, inputs, dev)), flush=True)
+        return
+    if args.tokens > 1:
+        print(json.dumps(bench_multi(args, torch, hs2, inputs, dev)), flush=True)
         return
     if args.part == "self-decoder":
         print(json.dumps(bench_self_decoder(args, torch, hs2, inputs, dev)), flush=True)
