@@ -50,12 +50,20 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) &
 // are multiples of chunk_quantum in [256, max_chunk].  The choice affects
 // speed, and the rounding of the outputs (never the selection), and depends
 // on nothing but N, B and the cache type.
-int choose_chunk(int64_t total_tokens, int batch, bool fp8) {
+int choose_chunk(int64_t total_tokens, int64_t max_context, int batch, bool fp8) {
   constexpr int64_t kSlots = 256;
   const int64_t denom = std::max<int64_t>(kSlots - batch, kSlots / 4);
   const int64_t quantum = chunk_quantum(fp8);
-  int64_t c = (total_tokens + denom - 1) / denom;
-  c = (c + quantum - 1) / quantum * quantum;
+  auto round_up = [&](int64_t c) { return (c + quantum - 1) / quantum * quantum; };
+  int64_t c = round_up((total_tokens + denom - 1) / denom);
+  // Every sequence the same length (total = batch x longest, known here): the
+  // smallest chunk that still gives each sequence at most kSlots / batch items
+  // fills the slots exactly, where the rule above leaves room for a ragged tail
+  // per sequence (4 x 1M tokens: 256 items of 16576 tokens, not 248 of 17024).
+  if (batch > 0 && batch <= kSlots && max_context > 0 && total_tokens == static_cast<int64_t>(batch) * max_context) {
+    const int64_t per = kSlots / batch;
+    c = std::min(c, round_up((max_context + per - 1) / per));
+  }
   return static_cast<int>(std::min<int64_t>(std::max<int64_t>(c, 256), max_chunk(fp8)));
 }
 
@@ -71,7 +79,7 @@ DecodeLayout decode_layout(const hs2_decode_desc& d) {
   DecodeLayout L;
   const size_t B = static_cast<size_t>(d.batch);
   const size_t N = static_cast<size_t>(d.total_tokens);
-  L.chunk = choose_chunk(d.total_tokens, d.batch, d.kv_dtype == HS2_KV_FP8_E4M3);
+  L.chunk = choose_chunk(d.total_tokens, d.max_context, d.batch, d.kv_dtype == HS2_KV_FP8_E4M3);
   L.chunks_per_seq = static_cast<int>((d.max_context + L.chunk - 1) / L.chunk);
   if (L.chunks_per_seq < 1) L.chunks_per_seq = 1;
   size_t off = 0;
