@@ -245,3 +245,32 @@ def test_fp8_conversion_matches_ocp_table():
              q_sparse=rng.standard_normal((1, 1, 16, 128)).astype(np.float32) * 0.05, kv="fp8_e4m3")
     out, _, _ = run(d)
     parity.check_decode(d, out)
+
+
+@pytest.mark.parametrize("n_s", [0, 8])
+def test_sparse_layer_counts_at_the_limits(n_s):
+    # No sparse layer (the full layer and its selection only) and the most
+    # the descriptor allows; with a batch small enough that 8 layers slice.
+    lengths = [9000, 1153, 60000]
+    say(f"case: {n_s} sparse layers, lengths {lengths}")
+    d = inputs.make_decode(lengths=lengths, n_sparse=n_s, seed=51 + n_s, needles=32)
+    out, _, _ = run(d)
+    w = parity.check_decode(d, out)
+    say(f"worst {w}")
+
+
+def test_fp8_rows_of_zeros():
+    # All-zero K and V rows (scale 1, codes 0) among ordinary ones: logit 0 and
+    # zero values for those positions.
+    lengths = [5000, 1300]
+    say(f"case: E4M3 cache with zero rows, lengths {lengths}")
+    d = inputs.make_decode(lengths=lengths, n_sparse=2, kv="fp8_e4m3", seed=57, needles=16)
+    rng = np.random.default_rng(57)
+    zero = rng.choice(sum(lengths), 700, replace=False)
+    d["k"][zero] = 0
+    d["v"][zero] = 0
+    d["k_scale"][zero] = 1.0
+    d["v_scale"][zero] = 1.0
+    out, _, _ = run(d)
+    w = parity.check_decode(d, out)
+    say(f"worst {w}")
