@@ -336,7 +336,7 @@ __global__ __launch_bounds__(1024) void finish_kernel(SelectParams p) {
   __shared__ uint32_t s_pre[BOUND ? kMaxCollectBlocks + 1 : 1];
   __shared__ Resolved s_res;
   __shared__ int32_t s_sel[kTopK];
-  __shared__ uint32_t s_n;
+  __shared__ uint32_t s_n, s_nst;
   __shared__ unsigned long long s_keys[kFinishLdsKeys];
   const int b = blockIdx.x;
   const int t = threadIdx.x;
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(1024) void finish_kernel(SelectParams p) {
     return p.cand[key_segment(base, b, lo) + (i - s_pre[lo])];
   };
   const float* score = p.score + base;
-  const bool staged = !overflow && ncand <= static_cast<uint32_t>(kFinishLdsKeys);
+  bool staged = !overflow && ncand <= static_cast<uint32_t>(kFinishLdsKeys);
   if (staged) {
     constexpr int kBatch = 8;  // loads in flight per thread
     for (uint32_t i0 = 0; i0 < ncand; i0 += kBatch * 1024) {
@@ -507,10 +507,35 @@ __global__ __launch_bounds__(1024) void finish_kernel(SelectParams p) {
     prefix = (prefix << bits) | static_cast<unsigned long long>(r.digit);
     pshift = shift;
     done = r.count == rank || shift == 0;
+    // A list read from memory: after its first pass only the threshold bin is
+    // undecided.  One more read puts the keys above it into the selection and
+    // stages the bin's keys in LDS, so the remaining passes read LDS.
+    if (BOUND && !staged && !done && pass == first_pass && r.count <= static_cast<uint32_t>(kFinishLdsKeys)) {
+      if (t == 0) {
+        s_n = 0;
+        s_nst = 0;
+      }
+      __syncthreads();
+      for_each_key([&](unsigned long long key) {
+        const unsigned long long d = (key - kmin) >> pshift;
+        if (d > prefix) {
+          const uint32_t w = atomicAdd(&s_n, 1u);
+          if (w < static_cast<uint32_t>(p.top_k)) s_sel[w] = key_pos(key);
+        } else if (d == prefix) {
+          s_keys[atomicAdd(&s_nst, 1u)] = key;
+        }
+      });
+      __syncthreads();
+      nwin = min(s_n, static_cast<uint32_t>(p.top_k));
+      ncand = s_nst;
+      staged = true;
+    }
   }
 
-  // Winners from collect (spill mode), then the keys at or above the threshold.
-  for (uint32_t i = t; i < nwin; i += blockDim.x) s_sel[i] = p.selbuf[static_cast<size_t>(b) * p.top_k + i];
+  // Winners from collect (spill mode; bound mode put its own in s_sel when it
+  // staged the threshold bin), then the keys at or above the threshold.
+  if (!BOUND)
+    for (uint32_t i = t; i < nwin; i += blockDim.x) s_sel[i] = p.selbuf[static_cast<size_t>(b) * p.top_k + i];
   if (t == 0) s_n = 0;
   __syncthreads();
   for_each_key([&](unsigned long long key) {
