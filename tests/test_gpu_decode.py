@@ -61,6 +61,27 @@ def test_edge_lengths_ragged(kv):
     say(f"worst {w}")
 
 
+# 24 ragged sequences of 1.5K-40K tokens, about 530K in all: chunks of 2304
+# (bf16) or 2688 (E4M3) tokens, ~230 full-pass items with a ragged tail each,
+# every sequence checked against the oracle.
+MID_RAGGED_LENGTHS = {
+    "bf16": [3801, 31758, 25936, 22720, 32123, 10889, 34803, 14376, 38783, 13769, 15267, 16520, 14070, 32350,
+             8716, 4995, 36582, 15884, 9603, 31965, 29587, 30708, 29935, 24753],
+    "fp8_e4m3": [23558, 19473, 34303, 18869, 12631, 22217, 10581, 34798, 10835, 33912, 9680, 37613, 34787,
+                 32235, 22035, 3424, 26723, 12402, 26284, 13132, 32451, 6158, 14940, 38770],
+}
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_mid_size_ragged_batch(kv):
+    lengths = MID_RAGGED_LENGTHS[kv]
+    say(f"case: mid-size ragged batch, B=24, N={sum(lengths)} kv={kv}")
+    d = inputs.make_decode(lengths=lengths, n_sparse=2, kv=kv, seed=29, needles=64)
+    out, _, _ = run(d)
+    w = parity.check_decode(d, out)
+    say(f"worst {w}")
+
+
 def test_empty_sequences_in_batch():
     lengths = [0, 3000, 0, 1200]
     say(f"case: empty sequences {lengths}")
