@@ -416,7 +416,7 @@ def main():
                     help="run one 1 GiB device copy before the timed region (for HBM counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the decode batch would shard by sequence with no exchange).", file=sys.stderr)
         sys.exit(2)
 

@@ -8,7 +8,7 @@ no attention, score, selection or projection.  Both the GPU path (through
 the tests and the benchmark) and the CPU oracle consume what it returns.
 
 Recipe (per sequence, each from its own child of
-``SeedSequence(1000 + config_id)`` so sequences can be generated in parallel):
+``SeedSequence(1000 + workload)`` so sequences can be generated in parallel):
 
 1. q_full  fp32 N(0,1) [16, 128]
 2. K       fp32 N(0,1) [L, 128]
@@ -45,7 +45,7 @@ D_MODEL = 4096
 N_BRIDGED = 3
 
 # Workload table.  "needles" is a count per sequence, or a rule name.
-CONFIGS = {
+WORKLOAD_RECIPES = {
     1: dict(name="b1_ctx4k_bf16", batch=1, lengths="fixed", ctx=4096, kv="bf16", n_sparse=3,
             needles=64, needle_mode="uniform"),
     2: dict(name="b32_ctx128k_bf16", batch=32, lengths="fixed", ctx=131072, kv="bf16", n_sparse=4,
@@ -155,11 +155,11 @@ def _one_sequence(seed_seq, cfg, length, n_sparse, spans):
     return q_full, k_bits, v_bits, q_sparse, needles
 
 
-def make_decode(config_id: int = None, *, lengths=None, n_sparse=None, kv=None, seed=None,
+def make_decode(workload: int = None, *, lengths=None, n_sparse=None, kv=None, seed=None,
                 needles=None, needle_mode=None):
     """Build one decode batch.
 
-    Either a workload id from CONFIGS, or custom ``lengths`` (a list of
+    Either a workload id from WORKLOAD_RECIPES, or custom ``lengths`` (a list of
     context lengths) with ``n_sparse``, ``kv`` ("bf16" | "fp8_e4m3"), ``seed``
     and optional needle settings (used by the tests for small and ragged
     cases).  Returns a dict of host arrays:
@@ -168,9 +168,9 @@ def make_decode(config_id: int = None, *, lengths=None, n_sparse=None, kv=None, 
     codes); k_scale, v_scale fp32 [N] or None; q_full fp32 [B, 16, 128];
     q_sparse fp32 [n_s, B, 16, 128]; needles list of int64 arrays; kv str.
     """
-    if config_id is not None:
-        cfg = dict(CONFIGS[config_id])
-        base_seed = 1000 + config_id if seed is None else seed
+    if workload is not None:
+        cfg = dict(WORKLOAD_RECIPES[workload])
+        base_seed = 1000 + workload if seed is None else seed
     else:
         cfg = dict(batch=len(lengths), lengths="custom", kv=kv or "bf16", n_sparse=n_sparse or 0,
                    needles=needles if needles is not None else 0,

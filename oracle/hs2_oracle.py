@@ -167,7 +167,7 @@ def decode_kv(raw: np.ndarray, kv_dtype: str, scale: np.ndarray | None = None) -
     ``"fp8_e4m3"`` (raw = uint8 codes [L, D] and ``scale`` = per-token fp32
     scale [L]; the value is code_value * scale).  The FP8 cache is the one the
     pages quote their 1M-token footprints with ([en] paragraph on cost; [pt]);
-    the per-token fp32 scale is this build's reading of "FP8 cache".
+    the per-token fp32 scale is the reading of "FP8 cache" taken here.
     """
     if kv_dtype == "bf16":
         return bf16_bits_to_f64(raw)

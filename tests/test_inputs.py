@@ -48,7 +48,7 @@ def test_fp8_quantisation_per_token():
 
 
 def test_burst_needles_structure():
-    cfg = inputs.CONFIGS[3]
+    cfg = inputs.WORKLOAD_RECIPES[3]
     rng = np.random.default_rng(0)
     pos = inputs._needle_positions(rng, cfg, 1 << 20, None)
     assert pos.shape[0] == 1024
@@ -74,7 +74,7 @@ def test_agent_spans_and_lengths():
 
 
 def test_agent_needles_only_in_observations():
-    cfg = inputs.CONFIGS[4]
+    cfg = inputs.WORKLOAD_RECIPES[4]
     rng = np.random.default_rng(2)
     spans = inputs.agent_spans(rng, 40000)
     pos = inputs._needle_positions(rng, cfg, 40000, spans)
