@@ -4,15 +4,21 @@ A step is one hs2_decode_block call over one batch: the full-attention layer
 over every context token, the per-token score and the token selection, and
 the sparse layers over the selected rows.  Inputs are resident in HBM before
 the timed region.  Default workload: 32 sequences x 131072 tokens, bf16 MQA
-cache (16 query heads, head_dim 128), window 128 + top-1024, 4 sparse layers.
+cache (16 query heads, head_dim 128), window 128 + top-1024, 4 sparse layers;
+the same line then carries the metric's 1M-token half (4 sequences x 1048576
+tokens, E4M3 cache with per-token scales), timed the same way, as
+``roofline_ctx1m_fp8``.
 
-The roofline object is for the dominant kernel, the full-attention split-K
-pass: algorithmic bytes per launch = N x 512 B (each K and V row read once)
-+ B x 8 KiB (the queries), divided by that kernel's mean duration measured
-live with HIP events recorded by the library on the launch stream during
-the timed steps.  ``traffic`` is the kernel's HBM bytes per launch from the
+The roofline object covers the full layer and its score (K1 + K1b): the
+split-K partial pass and the launch that merges it and runs the selection's
+first pass over the score bounds.  Algorithmic bytes per launch = N x 512 B
+(each K and V row read once; 264 B with E4M3 and its two scales) + B x 16 KiB
+(the query and the output), divided by the two kernels' mean duration per
+step, measured live with HIP events recorded by the library on the launch
+stream during the timed steps.  ``k1_alone`` gives the partial pass by
+itself.  ``traffic`` is the two kernels' HBM bytes per launch from the
 rocprofv3 FETCH_SIZE/WRITE_SIZE runs summarised under profiles/ (scaled by a
-1 GiB copy), or null when the kernel source changed since they were taken.
+1 GiB copy), or null when their sources changed since they were taken.
 
 The cpu_baseline leg times the fp64 oracle on a bounded sample of the same
 workload (whole sequences, one after another, until about 15 s have passed).
@@ -26,8 +32,9 @@ batch: its one full-attention layer and 24 sliding-window layers (window 128).
 ``--selection block`` times the same workload through the gen-1 (block-level)
 selection instead, the comparator of the pages' ablation: the full layer with
 every score (hs2_full_decode_score), hs2_block_select, then the sparse layers.
-Each line also carries per-launch percentiles of the full pass, a "cold"
-full-pass time (after 1 GiB of writes has evicted the caches), and the device.
+Each line also carries per-launch percentiles, a "cold" full-pass time (after
+1 GiB of writes has evicted the caches), the clock levels sampled during the
+timed steps, and the device.
 
 Workload 5 times the KV-Bridging projection (262144 x 4096 hidden states into
 3 layers' K and V, one bf16 MFMA GEMM) and then each bridged layer's decode
@@ -52,7 +59,8 @@ TRAFFIC_PROFILE = {2: "profiles/full_partial_b32_ctx128k_bf16_hbm_traffic.md",
                    3: "profiles/full_partial_b4_ctx1m_fp8_hbm_traffic.md"}
 # the kernel and what sets its launch (chunk size, grid)
 KERNEL_SOURCES = ("long_context_kv_hs2_amd/csrc/full_decode.hip", "long_context_kv_hs2_amd/csrc/hs2_device.h",
-                  "long_context_kv_hs2_amd/csrc/hs2_internal.h", "long_context_kv_hs2_amd/csrc/hs2_api.hip")
+                  "long_context_kv_hs2_amd/csrc/hs2_internal.h", "long_context_kv_hs2_amd/csrc/hs2_api.hip",
+                  "long_context_kv_hs2_amd/csrc/topk_select.hip", "long_context_kv_hs2_amd/csrc/merge.h")
 METRIC = "hybrid-block decode tokens/s at 128K/1M ctx; achieved HBM GB/s vs peak"
 WORKLOADS = {2: "b32_ctx128k_bf16", 3: "b4_ctx1m_fp8", 4: "b64_ragged_2k_256k_bf16",
              5: "bridge_262144x4096_3layers_then_b8x32k_decode"}
@@ -97,7 +105,7 @@ def cold_full_pass(torch, hs2, step, dev, reps=5):
     """The full pass right after 1 GiB of writes (more than the 256 MB
     Infinity Cache and the L2s hold), so its K/V reads start cold."""
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    times = []
+    k1, both = [], []
     for i in range(reps):
         scratch.fill_(i + 1)
         torch.cuda.synchronize()
@@ -105,9 +113,11 @@ def cold_full_pass(torch, hs2, step, dev, reps=5):
         step()
         torch.cuda.synchronize()
         hs2.stage_timing(False)
-        times.extend(hs2.stage_timing_read_calls()[:, 0].tolist())
+        calls = hs2.stage_timing_read_calls()
+        k1.extend(calls[:, 0].tolist())
+        both.extend((calls[:, 0] + calls[:, 1]).tolist())
     del scratch
-    return pct(times)
+    return {"k1": pct(k1), "k1_k1b": pct(both)}
 
 
 def cpu_baseline(d, budget_s=15.0):
@@ -399,6 +409,134 @@ def bench_multi(args, torch, hs2, inputs, dev):
     }
 
 
+def load_cache(torch, d, dev):
+    """Device K/V (and scales) of a decode batch from the input generator."""
+    if d["kv"] == "bf16":
+        k = torch.from_numpy(d["k"].view(np.int16)).view(torch.bfloat16).to(dev)
+        v = torch.from_numpy(d["v"].view(np.int16)).view(torch.bfloat16).to(dev)
+        return k, v, None, None
+    return (torch.from_numpy(d["k"]).to(dev), torch.from_numpy(d["v"]).to(dev),
+            torch.from_numpy(d["k_scale"]).to(dev), torch.from_numpy(d["v_scale"]).to(dev))
+
+
+def clock_levels():
+    """The active shader, memory and fabric clock levels (the entries marked
+    '*' in the driver's pp_dpm_* tables), or None where not readable."""
+    import glob
+
+    out = {}
+    for name in ("sclk", "mclk", "fclk"):
+        for path in sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{name}")):
+            try:
+                text = open(path, encoding="utf-8").read()
+            except OSError:
+                continue
+            act = [ln.split(":", 1)[1].strip().rstrip("*").strip() for ln in text.splitlines() if ln.endswith("*")]
+            if act:
+                out[name] = act[0]
+                break
+    return out or None
+
+
+def hybrid_block_line(args, torch, hs2, d, dev, workload, selection="token", with_cpu=True):
+    """Time hs2_decode_block (or the gen-1 line) on one decode batch; returns
+    the JSON fields of its line."""
+    kv = d["kv"]
+    offs_t = torch.from_numpy(d["seq_offsets"]).to(dev)
+    k, v, ks, vs = load_cache(torch, d, dev)
+    q_full = torch.from_numpy(d["q_full"]).to(dev)
+    q_sparse = torch.from_numpy(d["q_sparse"]).to(dev)
+    lens = np.diff(d["seq_offsets"])
+    batch, n_tokens = int(lens.shape[0]), int(lens.sum())
+    if selection == "block":
+        blk = hs2.BlockSelectDecode(offs_t, k, v, q_full, q_sparse, ks, vs, int(lens.max()))
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    else:
+        blk = hs2.DecodeBlock(offs_t, k, v, q_full, q_sparse, ks, vs, int(lens.max()), with_score=False)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(args.warmup):
+        blk()
+    torch.cuda.synchronize()
+    # Timed region: HIP events around the full pass and its merge (the
+    # roofline's kernels) only; every extra marker would add ~1.5 us a step.
+    hs2.stage_timing(True, full_pass_only=True)
+    hs2.stage_timing_read()  # clear
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        blk()
+    clocks = clock_levels()  # sampled while the timed steps run
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    hs2.stage_timing(False)
+    calls = hs2.stage_timing_read_calls()
+    k1_calls, k1b_calls = calls[:, 0], calls[:, 1]
+    n_rec = int(k1_calls.shape[0])
+    # Per-stage breakdown (diagnostic), from extra untimed steps.
+    hs2.stage_timing(True)
+    extra = []
+    for _ in range(min(args.steps, 20)):
+        if selection == "block":
+            blk(marks)
+            torch.cuda.synchronize()
+            extra.append((marks[0].elapsed_time(marks[1]), marks[1].elapsed_time(marks[2])))
+        else:
+            blk()
+    torch.cuda.synchronize()
+    hs2.stage_timing(False)
+    calls = hs2.stage_timing_read_calls()
+    stage_pct = {name: pct(calls[:, i]) for i, name in enumerate(hs2.STAGE_NAMES)}
+    stages = {name: (stage_pct[name] or {}).get("mean", 0.0) for name in hs2.STAGE_NAMES}
+    if selection == "block":
+        # hs2_full_decode_score records partial pass, merge and score pass; the
+        # block selection and the sparse layers are separate calls
+        stage_pct = {"full_partial": stage_pct["full_partial"], "full_merge": stage_pct["full_merge"],
+                     "score_pass": stage_pct["score_select"], "block_select": pct([e[0] for e in extra]),
+                     "sparse": pct([e[1] for e in extra])}
+        stages = {name: val["mean"] for name, val in stage_pct.items()}
+    cold = cold_full_pass(torch, hs2, blk, dev)
+
+    ms_per_step = dt * 1e3 / args.steps
+    alg_bytes = n_tokens * KV_ROW_BYTES[kv] + batch * 2 * 16 * 128 * 4  # K/V once, query and output per sequence
+    both = k1_calls + k1b_calls
+    t_both, t_k1 = float(both.mean()), float(k1_calls.mean())
+    achieved = alg_bytes / (t_both * 1e-3) / 1e9
+    k1_achieved = alg_bytes / (t_k1 * 1e-3) / 1e9
+    name = ("full_partial_kernel + merge_bound_hist_kernel (the full layer and its score bounds, K1 + K1b)"
+            if selection == "token" else
+            "full_partial_kernel + merge_kernel (the full layer keeping every logit; the score pass is apart)")
+    return {
+        "value": batch * args.steps / dt,
+        "ms_per_step": ms_per_step,
+        "dtype": "bf16" if kv == "bf16" else "fp8_e4m3",
+        "config": {"workload": WORKLOADS[workload], "batch": batch, "context_tokens": n_tokens,
+                   "max_context": int(lens.max()), "kv_cache": kv, "q_heads": 16, "kv_heads": 1,
+                   "head_dim": 128, "window": 128, "top_k": 1024, "n_sparse_layers": int(q_sparse.shape[0]),
+                   "selection": "token" if selection == "token" else "block64 (gen-1 comparator)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(workload) if selection == "token" else None,
+                     "kernel": name, "alg_bytes_per_launch": alg_bytes, "mean_launch_ms": t_both,
+                     "launch_ms": pct(both),
+                     "k1_alone": {"kernel": "full_partial_kernel", "mean_launch_ms": t_k1,
+                                  "launch_ms": pct(k1_calls), "achieved": k1_achieved,
+                                  "frac": k1_achieved / HBM_PEAK_GBS}},
+        "stages_ms": {k2: round(v2, 5) for k2, v2 in stages.items()},  # untimed extra steps
+        "stages_ms_percentiles": stage_pct,
+        "cold_full_partial_ms": cold,
+        "stage_calls_timed": n_rec,
+        "clocks_during_timed_steps": clocks,
+        **({"cpu_baseline": cpu_baseline(d)} if with_cpu else {}),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -412,6 +550,8 @@ def main():
     ap.add_argument("--selection", choices=("token", "block"), default="token",
                     help="token: the method's selection; block: the gen-1 64-token-block comparator")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-1m", action="store_true",
+                    help="workload 2 only: skip the second (1M-token E4M3) roofline object")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy before the timed region (for HBM counter scaling)")
     args = ap.parse_args()
@@ -437,110 +577,28 @@ def main():
         print(json.dumps(bench_self_decoder(args, torch, hs2, inputs, dev)), flush=True)
         return
     d = inputs.make_decode(args.workload)
-    kv = d["kv"]
-    offs_t = torch.from_numpy(d["seq_offsets"]).to(dev)
-    if kv == "bf16":
-        k = torch.from_numpy(d["k"].view(np.int16)).view(torch.bfloat16).to(dev)
-        v = torch.from_numpy(d["v"].view(np.int16)).view(torch.bfloat16).to(dev)
-        ks = vs = None
-    else:
-        k = torch.from_numpy(d["k"]).to(dev)
-        v = torch.from_numpy(d["v"]).to(dev)
-        ks = torch.from_numpy(d["k_scale"]).to(dev)
-        vs = torch.from_numpy(d["v_scale"]).to(dev)
-    q_full = torch.from_numpy(d["q_full"]).to(dev)
-    q_sparse = torch.from_numpy(d["q_sparse"]).to(dev)
-    lens = np.diff(d["seq_offsets"])
-    batch, n_tokens = int(lens.shape[0]), int(lens.sum())
-    blk = hs2.DecodeBlock(offs_t, k, v, q_full, q_sparse, ks, vs, int(lens.max()), with_score=False)
-
-    if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    if args.selection == "block":
-        blk = hs2.BlockSelectDecode(offs_t, k, v, q_full, q_sparse, ks, vs, int(lens.max()))
-        marks = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    for _ in range(args.warmup):
-        blk()
-    torch.cuda.synchronize()
-    # Timed region: HIP events around the full pass only (the roofline's
-    # kernel); every extra marker would add ~1.5 us to each step.
-    hs2.stage_timing(True, full_pass_only=True)
-    hs2.stage_timing_read()  # clear
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        blk()
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    hs2.stage_timing(False)
-    k1_calls = hs2.stage_timing_read_calls()[:, 0]
-    n_rec = int(k1_calls.shape[0])
-    # Per-stage breakdown (diagnostic), from extra untimed steps.
-    hs2.stage_timing(True)
-    extra = []
-    for _ in range(min(args.steps, 20)):
-        if args.selection == "block":
-            blk(marks)
-            torch.cuda.synchronize()
-            extra.append((marks[0].elapsed_time(marks[1]), marks[1].elapsed_time(marks[2])))
-        else:
-            blk()
-    torch.cuda.synchronize()
-    hs2.stage_timing(False)
-    calls = hs2.stage_timing_read_calls()
-    stage_pct = {name: pct(calls[:, i]) for i, name in enumerate(hs2.STAGE_NAMES)}
-    stages = {name: (stage_pct[name] or {}).get("mean", 0.0) for name in hs2.STAGE_NAMES}
-    if args.selection == "block":
-        # hs2_full_decode_score records partial pass, merge and score pass; the
-        # block selection and the sparse layers are separate calls
-        stage_pct = {"full_partial": stage_pct["full_partial"], "full_merge": stage_pct["full_merge"],
-                     "score_pass": stage_pct["score_select"], "block_select": pct([e[0] for e in extra]),
-                     "sparse": pct([e[1] for e in extra])}
-        stages = {name: v["mean"] for name, v in stage_pct.items()}
-    cold = cold_full_pass(torch, hs2, blk, dev)
-
-    ms_per_step = dt * 1e3 / args.steps
-    value = batch * args.steps / dt
-    k1_ms = float(k1_calls.mean())
-    alg_bytes = n_tokens * KV_ROW_BYTES[kv] + batch * 16 * 128 * 4
-    achieved = alg_bytes / (k1_ms * 1e-3) / 1e9
-    result = {
-        "metric": METRIC,
-        "value": value,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if kv == "bf16" else "fp8_e4m3",
-        "data": "synthetic",
-        "config": {"workload": WORKLOADS[args.workload], "batch": batch, "context_tokens": n_tokens,
-                   "max_context": int(lens.max()), "kv_cache": kv, "q_heads": 16, "kv_heads": 1,
-                   "head_dim": 128, "window": 128, "top_k": 1024, "n_sparse_layers": int(q_sparse.shape[0]),
-                   "selection": "token" if args.selection == "token" else "block64 (gen-1 comparator)"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(args.workload) if args.selection == "token" else None,
-                     "kernel": ("full_partial_kernel (split-K pass, score bounds)" if args.selection == "token"
-                                else "full_partial_kernel (split-K pass, every logit kept for the scores)"),
-                     "alg_bytes_per_launch": alg_bytes, "mean_launch_ms": k1_ms,
-                     "launch_ms": pct(k1_calls)},
-        "stages_ms": {k2: round(v2, 5) for k2, v2 in stages.items()},  # untimed extra steps
-        "stages_ms_percentiles": stage_pct,
-        "cold_full_partial_ms": cold,
-        "stage_calls_timed": n_rec,
-        "device": device_info(torch),
-    }
-    if not args.no_cpu_baseline and args.selection == "token":
-        result["cpu_baseline"] = cpu_baseline(d)
+    line = hybrid_block_line(args, torch, hs2, d, dev, args.workload, args.selection,
+                             with_cpu=not args.no_cpu_baseline and args.selection == "token")
+    cpu = line.pop("cpu_baseline", None)
+    result = {"metric": METRIC, "value": line.pop("value"), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+              "warmup": args.warmup, "ms_per_step": line.pop("ms_per_step"), "higher_is_better": True,
+              "scaling": "weak", "vs_baseline": None, "dtype": line.pop("dtype"), "data": "synthetic"}
+    result.update(line)
+    del d
+    if args.workload == 2 and args.selection == "token" and not args.no_1m:
+        # The metric's 1M-token half: 4 sequences x 1048576 tokens, E4M3 cache
+        # with per-token scales, timed the same way (its own warmup and steps).
+        torch.cuda.empty_cache()
+        d3 = inputs.make_decode(3)
+        sub = hybrid_block_line(args, torch, hs2, d3, dev, 3, "token", with_cpu=False)
+        del d3
+        result["roofline_ctx1m_fp8"] = dict(sub["roofline"], workload=sub["config"]["workload"],
+                                            tokens_per_s=sub["value"], ms_per_step=sub["ms_per_step"],
+                                            steps=args.steps, warmup=args.warmup, dtype=sub["dtype"],
+                                            stages_ms=sub["stages_ms"], cold_full_partial_ms=sub["cold_full_partial_ms"])
+    result["device"] = device_info(torch)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 

@@ -79,9 +79,15 @@ typedef struct {
   int64_t max_context;      /* >= every L_b (host-known; sizes the grids)        */
 } hs2_decode_desc;
 
-/* Bytes of workspace hs2_decode_block (and every stage call) needs for
- * `desc`.  Returns 0 when desc is invalid.                                    */
+/* Bytes of workspace for `desc` (0 when desc is invalid):
+ *  - hs2_decode_workspace_bytes: hs2_decode_block with score_out == NULL, and
+ *    hs2_topk_select, hs2_block_select, hs2_sparse_decode, hs2_full_decode;
+ *  - hs2_decode_score_workspace_bytes: the calls that return per-token scores,
+ *    hs2_decode_block with score_out != NULL and hs2_full_decode_score; it adds
+ *    64 bytes a token (every logit of the full layer) to the first size.
+ * A workspace of the larger size serves every call.                          */
 size_t hs2_decode_workspace_bytes(const hs2_decode_desc* desc);
+size_t hs2_decode_score_workspace_bytes(const hs2_decode_desc* desc);
 
 /* One decode step of one hybrid block for a packed batch.
  *
@@ -103,8 +109,9 @@ size_t hs2_decode_workspace_bytes(const hs2_decode_desc* desc);
  * sel_count (device) int32 [B]: min(L_b, window + top_k).
  * score_out (device) fp32 [N] or NULL: per-token score (sum over heads of the
  *   softmax probability), for every position of every sequence.
- * workspace (device), workspace_bytes >= hs2_decode_workspace_bytes(desc),
- *   256-byte aligned; its contents on entry do not matter.
+ * workspace (device), workspace_bytes >= hs2_decode_workspace_bytes(desc)
+ *   (hs2_decode_score_workspace_bytes(desc) when score_out != NULL), 256-byte
+ *   aligned; its contents on entry do not matter.
  * A sequence with L_b == 0 yields zero outputs, sel_count 0 and all -1.      */
 hs2_status hs2_decode_block(const hs2_decode_desc* desc, const int64_t* seq_offsets,
                             const void* k_cache, const void* v_cache,
@@ -139,7 +146,8 @@ hs2_status hs2_decode_multi(const hs2_decode_desc* desc, int32_t n_query, const 
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Stage call: the full-attention layer alone.  Same arguments as
- * hs2_decode_block; writes o_full and score_out (required here).            */
+ * hs2_decode_block; writes o_full and score_out (required here).  workspace
+ * >= hs2_decode_score_workspace_bytes(desc).                                 */
 hs2_status hs2_full_decode_score(const hs2_decode_desc* desc, const int64_t* seq_offsets,
                                  const void* k_cache, const void* v_cache,
                                  const float* k_scale, const float* v_scale,
@@ -147,9 +155,10 @@ hs2_status hs2_full_decode_score(const hs2_decode_desc* desc, const int64_t* seq
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* Stage call: token selection from given scores.  score (device) fp32 [N]
- * non-negative; writes sel_idx and sel_count as hs2_decode_block does: the
- * last `window` positions plus the top_k positions before them by (score
- * descending, position ascending).                                           */
+ * non-negative (-0.0, negative values and NaN are ranked as +0.0); writes
+ * sel_idx and sel_count as hs2_decode_block does: the last `window` positions
+ * plus the top_k positions before them by (score descending, position
+ * ascending).  seq_offsets 8-byte aligned.                                    */
 hs2_status hs2_topk_select(const hs2_decode_desc* desc, const int64_t* seq_offsets,
                            const float* score, int32_t* sel_idx, int32_t* sel_count,
                            void* workspace, size_t workspace_bytes, void* stream);
@@ -224,8 +233,9 @@ hs2_status hs2_bridge_kv_fp8(int64_t n_tokens, int32_t d_model, int32_t head_dim
  * early prefill exit).
  *
  * hs2_full_decode: the Self-Decoder's full-attention layer: full attention
- * alone (o_full), no score and no selection.  Arguments, workspace and
- * errors as hs2_decode_block.  Stage timing records stages 0 and 1.
+ * alone (o_full), no score and no selection: the workspace receives the
+ * split-K partials only.  Arguments, workspace and errors as
+ * hs2_decode_block.  Stage timing records stages 0 and 1.
  *
  * hs2_swa_decode: one sliding-window layer for a batch: each sequence's
  * query attends to its `window` most recent positions, the current token
@@ -289,11 +299,16 @@ hs2_status hs2_bridge_append(int32_t batch, int32_t d_model, int32_t head_dim, i
 /* Per-stage kernel timing of hs2_decode_block and hs2_full_decode_score, for
  * benchmarks.  Mode 1: each call records HIP events around its stages on its
  * stream (HS2_N_STAGES stages: 0 full-attention partial pass, 1 full-attention
- * merge, 2 score and selection (hs2_full_decode_score: the score pass),
- * 3 sparse layers (hs2_full_decode_score: none)).  Mode 2: only the two events
- * around stage 0 (each marker costs the step about 1.5 us).  Mode 0: off.
- * Other modes: HS2_ERR_INVALID_ARGUMENT.  The events are timing-only (no
- * system-scope fence).  At most 1024 calls are recorded between reads.
+ * merge (with the selection's first pass when no score is returned), 2 score
+ * and selection (hs2_full_decode_score: the score pass), 3 sparse layers
+ * (hs2_full_decode_score: none)).  Mode 2: only the events around stages 0 and
+ * 1 (each marker costs the step about 1.5 us).  Mode 0: off.  Other modes:
+ * HS2_ERR_INVALID_ARGUMENT.  The events are timing-only (no system-scope
+ * fence).  At most 1024 calls are recorded between reads.
+ * This is the library's one piece of process-global state: the mode and the
+ * record are shared by every thread and device (guarded by a mutex); with
+ * timing on, calls from several threads land in one record in the order they
+ * take it.  With timing off (the default) the calls keep no state at all.
  * hs2_stage_timing_read waits for the recorded events and returns, per stage,
  * the mean duration in milliseconds over the calls recorded since the last
  * read (a stage a call did not record counts as 0), and the number of calls

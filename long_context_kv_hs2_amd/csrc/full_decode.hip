@@ -13,9 +13,11 @@
 // three exact bf16 parts (fp32-accurate logits), an online softmax per head in
 // registers, and O^T += V^T P^T on bf16 MFMA with each weight split into a
 // bf16 head and tail (16 significant bits).  The four waves' (m, z, O) are
-// merged through LDS into one partial per workgroup.  The first workgroup of
-// each sequence also clears the sequence's selection histogram and counters
-// for the kernels that follow.
+// merged through LDS into one partial per workgroup.  Three modes: BOUND keeps
+// per-token score bounds for the selection, SPILL keeps every logit for the
+// score pass, PLAIN keeps nothing (full attention alone).  In the first two
+// the first workgroup of each sequence also clears the sequence's selection
+// histogram and counters for the kernels that follow.
 #include <algorithm>
 
 #include "hs2_device.h"
@@ -73,8 +75,10 @@ __device__ bool find_work(const FullParams& p, int wg, int& b, int& c) {
 template <bool FP8> constexpr int full_waves() { return FP8 ? 8 : 4; }
 template <bool FP8> constexpr int full_streams() { return FP8 ? 28 : 4; }
 
-template <bool FP8, bool BOUND>
+template <bool FP8, int MODE>
 __global__ __launch_bounds__(64 * full_waves<FP8>()) void full_partial_kernel(FullParams p) {
+  constexpr bool BOUND = MODE == kFullBound;
+  constexpr bool SPILL = MODE == kFullSpill;
   constexpr int kWaves = full_waves<FP8>();
   constexpr int kStreams = full_streams<FP8>();
   constexpr int kThreads = 64 * kWaves;
@@ -138,7 +142,7 @@ __global__ __launch_bounds__(64 * full_waves<FP8>()) void full_partial_kernel(Fu
   const uint8_t* __restrict__ vbase = p.v + kvb * kRowBytes;
   const float* __restrict__ ksb = FP8 ? p.k_scale + kvb : nullptr;
   const float* __restrict__ vsb = FP8 ? p.v_scale + kvb : nullptr;
-  float* __restrict__ spill = BOUND ? nullptr : p.spill + base * kHeads;
+  float* __restrict__ spill = SPILL ? p.spill + base * kHeads : nullptr;
   uint16_t* __restrict__ shat = BOUND ? p.shat + base : nullptr;
 
   SoftmaxState st;
@@ -206,7 +210,7 @@ __global__ __launch_bounds__(64 * full_waves<FP8>()) void full_partial_kernel(Fu
       float* out = s_raw + local(ti) * kTileOut;
       if ((n & 3) == 0) out[4 * g + (n >> 2)] = sh;
       if (g == 0) out[kHeads + n] = st.m - lcf;  // u_h = m_h - log2 c_h
-    } else {
+    } else if constexpr (SPILL) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if (4 * g + r < nv) spill[static_cast<uint32_t>(t0 + 4 * g + r) * kHeads + n] = lg[r];
@@ -324,33 +328,38 @@ __global__ __launch_bounds__(64 * full_waves<FP8>()) void full_partial_kernel(Fu
   if (d0 == 0) {
     out[h] = mx;
     out[kHeads + h] = zz;
-    p.pstats[item * 2 * kHeads + h] = mx;  // compact copy for the selection's first pass
-    p.pstats[item * 2 * kHeads + kHeads + h] = zz;
+    if constexpr (MODE != kFullPlain) {
+      p.pstats[item * 2 * kHeads + h] = mx;  // compact copy for the selection's first pass
+      p.pstats[item * 2 * kHeads + kHeads + h] = zz;
+    }
   }
   float4* o4 = reinterpret_cast<float4*>(out + 2 * kHeads + h * kDim + d0);
 #pragma unroll
   for (int j = 0; j < kDims / 4; ++j) o4[j] = make_float4(acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]);
-  if (c == 0) {
+  if (MODE != kFullPlain && c == 0) {
     uint4* hz = reinterpret_cast<uint4*>(p.hist0 + static_cast<size_t>(b) * kRadixBins);
     for (int i = threadIdx.x; i < kRadixBins / 4; i += kThreads) hz[i] = make_uint4(0u, 0u, 0u, 0u);
     if (threadIdx.x < 4) p.counters[b * 4 + threadIdx.x] = 0u;
   }
 }
 
-hipError_t launch_full_partial(const FullParams& p, int batch, bool fp8, bool bound_mode, hipStream_t s) {
+template <bool FP8, int MODE>
+static void launch_mode(const FullParams& p, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((full_partial_kernel<FP8, MODE>), grid, dim3(64 * full_waves<FP8>()), 0, s, p);
+}
+
+hipError_t launch_full_partial(const FullParams& p, int batch, bool fp8, int mode, hipStream_t s) {
   if (batch == 0) return hipSuccess;
   // at most sum_b ceil(L_b / chunk) < N / chunk + B work items
   const int64_t items = std::min<int64_t>(static_cast<int64_t>(batch) * p.chunks_per_seq,
                                           (p.total_tokens + p.chunk - 1) / p.chunk + batch);
   const dim3 grid(static_cast<unsigned>(items));
-  if (fp8 && bound_mode)
-    hipLaunchKernelGGL((full_partial_kernel<true, true>), grid, dim3(64 * full_waves<true>()), 0, s, p);
-  else if (fp8)
-    hipLaunchKernelGGL((full_partial_kernel<true, false>), grid, dim3(64 * full_waves<true>()), 0, s, p);
-  else if (bound_mode)
-    hipLaunchKernelGGL((full_partial_kernel<false, true>), grid, dim3(64 * full_waves<false>()), 0, s, p);
-  else
-    hipLaunchKernelGGL((full_partial_kernel<false, false>), grid, dim3(64 * full_waves<false>()), 0, s, p);
+  switch (mode) {
+    case kFullBound: fp8 ? launch_mode<true, kFullBound>(p, grid, s) : launch_mode<false, kFullBound>(p, grid, s); break;
+    case kFullSpill: fp8 ? launch_mode<true, kFullSpill>(p, grid, s) : launch_mode<false, kFullSpill>(p, grid, s); break;
+    case kFullPlain: fp8 ? launch_mode<true, kFullPlain>(p, grid, s) : launch_mode<false, kFullPlain>(p, grid, s); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

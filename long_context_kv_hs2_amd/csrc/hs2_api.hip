@@ -70,12 +70,15 @@ int choose_chunk(int64_t total_tokens, int64_t max_context, int batch, bool fp8)
 struct DecodeLayout {
   int chunk = 0;
   int chunks_per_seq = 0;
-  size_t partials = 0, stats = 0, pstats = 0, spill = 0, score = 0, hist0 = 0, counters = 0, selbuf = 0, cand = 0,
-         shat = 0, tile_stats = 0, tile_ub = 0, cand_cnt = 0, sparse = 0, blocks = 0, groups = 0, total = 0;
+  size_t partials = 0, stats = 0, pstats = 0, spill = 0, hist0 = 0, counters = 0, selbuf = 0, cand = 0, shat = 0,
+         tile_stats = 0, tile_ub = 0, cand_cnt = 0, sparse = 0, blocks = 0, groups = 0, total = 0;
   int cand_blocks = 0;
 };
 
-DecodeLayout decode_layout(const hs2_decode_desc& d) {
+// with_spill: room for the score path's logits ([N][16] fp32, 64 bytes a
+// token), only for calls that return per-token scores.  It comes last, so the
+// layout without it is a prefix of the layout with it.
+DecodeLayout decode_layout(const hs2_decode_desc& d, bool with_spill) {
   DecodeLayout L;
   const size_t B = static_cast<size_t>(d.batch);
   const size_t N = static_cast<size_t>(d.total_tokens);
@@ -91,8 +94,6 @@ DecodeLayout decode_layout(const hs2_decode_desc& d) {
   L.partials = take(B * L.chunks_per_seq * kPartialFloats * sizeof(float));
   L.stats = take(B * kHeads * 2 * sizeof(float));
   L.pstats = take(B * L.chunks_per_seq * 2 * kHeads * sizeof(float));
-  L.spill = take(N * kHeads * sizeof(float));
-  L.score = take(N * sizeof(float));
   L.hist0 = take(B * kRadixBins * sizeof(uint32_t));
   L.counters = take(B * 4 * sizeof(uint32_t));
   L.selbuf = take(B * kTopK * sizeof(int32_t));
@@ -109,6 +110,7 @@ DecodeLayout decode_layout(const hs2_decode_desc& d) {
   L.sparse = take(slices > 1 ? B * n_sparse * static_cast<size_t>(slices) * kPartialFloats * sizeof(float) : 0);
   L.blocks = take(((N >> 6) + B + 1) * sizeof(float));  // gen-1 block selection: per-block score sums
   L.groups = take(((N >> 10) + B + 1) * sizeof(unsigned long long));  // and each 16-block group's largest key
+  L.spill = with_spill ? take(N * kHeads * sizeof(float)) : off;
   L.total = off;
   return L;
 }
@@ -158,8 +160,9 @@ hs2_status check_ptr(const void* p, bool needed, size_t align, const char* name)
   return HS2_OK;
 }
 
-hs2_status check_workspace(const hs2_decode_desc& d, const void* ws, size_t bytes, DecodeLayout& L) {
-  L = decode_layout(d);
+hs2_status check_workspace(const hs2_decode_desc& d, const void* ws, size_t bytes, DecodeLayout& L,
+                           bool with_spill = false) {
+  L = decode_layout(d, with_spill);
   if (bytes < L.total)
     return fail(HS2_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", bytes, L.total);
   if (L.total > 0 && !ws) return fail(HS2_ERR_INVALID_ARGUMENT, "workspace is NULL");
@@ -197,6 +200,9 @@ hs2_status timing_begin(TimingRecord** out) {
   *out = nullptr;
   std::lock_guard<std::mutex> lock(g_timing_mu);
   if (g_timing_mode == 0 || g_records_used >= kMaxRecords) return HS2_OK;
+  // Room for every record up front: a later push_back must not move the
+  // records that calls in flight on other threads are filling.
+  if (g_records.capacity() < static_cast<size_t>(kMaxRecords)) g_records.reserve(kMaxRecords);
   if (g_records_used == static_cast<int>(g_records.size())) {
     TimingRecord r;
     // Timing-only events: no system-scope fence (a cache writeback and
@@ -207,7 +213,7 @@ hs2_status timing_begin(TimingRecord** out) {
     g_records.push_back(r);
   }
   *out = &g_records[g_records_used++];
-  (*out)->last = g_timing_mode == 2 ? 1 : HS2_N_STAGES;
+  (*out)->last = g_timing_mode == 2 ? 2 : HS2_N_STAGES;
   return HS2_OK;
 }
 
@@ -294,13 +300,16 @@ SelectParams select_params(const DecodeArgs& a, const DecodeLayout& L, float* sc
   return p;
 }
 
-// Full-attention pass and merge.  With `bound_sel` (bound mode) the merge
-// launch also runs the selection's first pass.
-hs2_status run_full(const DecodeArgs& a, const DecodeLayout& L, const SelectParams* bound_sel, TimingRecord* rec) {
-  const bool bound_mode = bound_sel != nullptr;
+// Full-attention pass and merge.  `mode`: kFullBound (the merge launch also
+// runs the selection's first pass, with `bound_sel`), kFullSpill (every logit
+// kept for the score pass) or kFullPlain (full attention alone: partials and
+// o_full only).
+hs2_status run_full(const DecodeArgs& a, const DecodeLayout& L, int mode, const SelectParams* bound_sel,
+                    TimingRecord* rec) {
+  const bool bound_mode = mode == kFullBound;
   const hs2_decode_desc& d = *a.d;
   const FullParams fp = full_params(a, L);
-  HS2_HIP(launch_full_partial(fp, d.batch, d.kv_dtype == HS2_KV_FP8_E4M3, bound_mode, a.stream),
+  HS2_HIP(launch_full_partial(fp, d.batch, d.kv_dtype == HS2_KV_FP8_E4M3, mode, a.stream),
           "full-attention partial pass");
   HS2_TRY(mark(rec, 1, a.stream));
   MergeParams mp;
@@ -317,7 +326,7 @@ hs2_status run_full(const DecodeArgs& a, const DecodeLayout& L, const SelectPara
   mp.sel_count = nullptr;
   mp.out = a.o_full;
   mp.out_stride_seq = kHeads * kDim;
-  mp.stats = reinterpret_cast<float*>(ws_at(a.ws, L.stats));
+  mp.stats = mode == kFullPlain ? nullptr : reinterpret_cast<float*>(ws_at(a.ws, L.stats));
   if (bound_mode) {
     HS2_HIP(launch_merge_bound_hist(mp, *bound_sel, d.batch, d.max_context, a.stream), "merge and bound histogram");
   } else {
@@ -360,7 +369,12 @@ extern "C" {
 
 size_t hs2_decode_workspace_bytes(const hs2_decode_desc* desc) {
   if (check_desc(desc) != HS2_OK) return 0;
-  return decode_layout(*desc).total;
+  return decode_layout(*desc, false).total;
+}
+
+size_t hs2_decode_score_workspace_bytes(const hs2_decode_desc* desc) {
+  if (check_desc(desc) != HS2_OK) return 0;
+  return decode_layout(*desc, true).total;
 }
 
 hs2_status hs2_decode_block(const hs2_decode_desc* desc, const int64_t* seq_offsets, const void* k_cache,
@@ -381,7 +395,7 @@ hs2_status hs2_decode_block(const hs2_decode_desc* desc, const int64_t* seq_offs
   HS2_TRY(check_ptr(sel_count, any, 4, "sel_count"));
   if (score_out && !aligned(score_out, 4)) return fail(HS2_ERR_INVALID_ARGUMENT, "score_out not 4-byte aligned");
   DecodeLayout L;
-  HS2_TRY(check_workspace(d, workspace, workspace_bytes, L));
+  HS2_TRY(check_workspace(d, workspace, workspace_bytes, L, score_out != nullptr));
   if (!any) return HS2_OK;
 
   DecodeArgs a{desc, seq_offsets, k_cache, v_cache, k_scale, v_scale, q_full, q_sparse, o_full, o_sparse,
@@ -405,12 +419,11 @@ hs2_status run_block(const DecodeArgs& a, const DecodeLayout& L) {
   // every score computed.  Both give the same scores for the positions that
   // matter, hence the same selection.
   const bool bound_mode = score_out == nullptr;
-  float* score = score_out ? score_out : reinterpret_cast<float*>(ws_at(workspace, L.score));
-  const SelectParams sp = select_params(a, L, score);
+  const SelectParams sp = select_params(a, L, score_out);  // bound mode reads no score array
   // (bound mode: the full pass itself clears the selection's histogram and counters)
   if (!bound_mode) HS2_HIP(launch_select_init(sp, d.batch, a.stream), "selection init");
   HS2_TRY(mark(rec, 0, a.stream));
-  HS2_TRY(run_full(a, L, bound_mode ? &sp : nullptr, rec));
+  HS2_TRY(run_full(a, L, bound_mode ? kFullBound : kFullSpill, bound_mode ? &sp : nullptr, rec));
   if (bound_mode) {
     HS2_HIP(launch_bound_select(sp, d.batch, d.max_context, d.kv_dtype == HS2_KV_FP8_E4M3, a.stream), "selection");
   } else {
@@ -440,7 +453,7 @@ size_t hs2_decode_multi_workspace_bytes(const hs2_decode_desc* desc, int32_t n_q
   const hs2_decode_desc v = multi_desc(*desc, n_query);
   if (check_desc(&v) != HS2_OK) return 0;
   const size_t n = static_cast<size_t>(v.batch);
-  return align_up(decode_layout(v).total) + align_up((n + 1) * sizeof(int64_t)) + align_up(n * sizeof(int64_t));
+  return align_up(decode_layout(v, false).total) + align_up((n + 1) * sizeof(int64_t)) + align_up(n * sizeof(int64_t));
 }
 
 hs2_status hs2_decode_multi(const hs2_decode_desc* desc, int32_t n_query, const int64_t* seq_offsets,
@@ -469,7 +482,7 @@ hs2_status hs2_decode_multi(const hs2_decode_desc* desc, int32_t n_query, const 
   if (workspace_bytes < need) return fail(HS2_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   HS2_TRY(check_ptr(workspace, true, 256, "workspace"));
   if (!any) return HS2_OK;
-  const DecodeLayout L = decode_layout(v);
+  const DecodeLayout L = decode_layout(v, false);
   const size_t n = static_cast<size_t>(v.batch);
   MultiParams mp{};
   mp.seq_offsets = seq_offsets;
@@ -497,7 +510,7 @@ hs2_status hs2_full_decode_score(const hs2_decode_desc* desc, const int64_t* seq
   HS2_TRY(check_ptr(o_full, any, 16, "o_full"));
   HS2_TRY(check_ptr(score_out, d.total_tokens > 0, 4, "score_out"));
   DecodeLayout L;
-  HS2_TRY(check_workspace(d, workspace, workspace_bytes, L));
+  HS2_TRY(check_workspace(d, workspace, workspace_bytes, L, true));
   if (!any) return HS2_OK;
   DecodeArgs a{desc, seq_offsets, k_cache, v_cache, k_scale, v_scale, q_full, nullptr, o_full, nullptr,
                nullptr, nullptr, score_out, workspace, static_cast<hipStream_t>(stream)};
@@ -505,7 +518,7 @@ hs2_status hs2_full_decode_score(const hs2_decode_desc* desc, const int64_t* seq
   HS2_TRY(timing_begin(&rec));
   if (rec && rec->last > 3) rec->last = 3;  // stages 0 partial pass, 1 merge, 2 score pass
   HS2_TRY(mark(rec, 0, a.stream));
-  HS2_TRY(run_full(a, L, nullptr, rec));
+  HS2_TRY(run_full(a, L, kFullSpill, nullptr, rec));
   const SelectParams sp = select_params(a, L, score_out);
   HS2_HIP(launch_score_hist(sp, d.batch, d.max_context, true, false, a.stream), "score pass");
   HS2_TRY(mark(rec, 3, a.stream));
@@ -519,6 +532,7 @@ hs2_status hs2_topk_select(const hs2_decode_desc* desc, const int64_t* seq_offse
   const hs2_decode_desc& d = *desc;
   const bool any = d.batch > 0;
   if (any && !seq_offsets) return fail(HS2_ERR_INVALID_ARGUMENT, "seq_offsets is NULL");
+  if (seq_offsets && !aligned(seq_offsets, 8)) return fail(HS2_ERR_INVALID_ARGUMENT, "seq_offsets not 8-byte aligned");
   HS2_TRY(check_ptr(score, d.total_tokens > 0, 4, "score"));
   HS2_TRY(check_ptr(sel_idx, any, 4, "sel_idx"));
   HS2_TRY(check_ptr(sel_count, any, 4, "sel_count"));
@@ -793,11 +807,10 @@ hs2_status hs2_full_decode(const hs2_decode_desc* desc, const int64_t* seq_offse
   TimingRecord* rec = nullptr;
   HS2_TRY(timing_begin(&rec));
   if (rec && rec->last > 2) rec->last = 2;  // stages 0 partial pass, 1 merge
-  // The bound-mode pass: its per-token outputs (6 bytes a token) are the
-  // cheapest the kernel writes; no selection follows.
-  const SelectParams sp = select_params(a, L, reinterpret_cast<float*>(ws_at(workspace, L.score)));
+  // The plain pass: partials only, then the merge into o_full; no score
+  // bounds, statistics or selection state.
   HS2_TRY(mark(rec, 0, a.stream));
-  HS2_TRY(run_full(a, L, &sp, rec));
+  HS2_TRY(run_full(a, L, kFullPlain, nullptr, rec));
   return HS2_OK;
 }
 

@@ -40,7 +40,10 @@ struct FullParams {
 // Slot of tile t (tokens [16t, 16t + 16)) of the sequence starting at row `base`:
 // unique over all sequences, at most N/16 + B.
 __host__ __device__ inline int64_t tile_slot(int64_t base, int b, int t) { return (base >> 4) + b + t; }
-hipError_t launch_full_partial(const FullParams& p, int batch, bool fp8, bool bound_mode, hipStream_t s);
+// What the partial pass keeps beside its partials: score bounds (the default
+// selection path), every logit (the score path), or nothing (full attention alone).
+enum FullMode { kFullBound = 0, kFullSpill = 1, kFullPlain = 2 };
+hipError_t launch_full_partial(const FullParams& p, int batch, bool fp8, int mode, hipStream_t s);
 
 struct MergeParams {
   const int64_t* seq_offsets;

@@ -66,6 +66,14 @@ __device__ __forceinline__ int key_pos(unsigned long long key) {
 
 __device__ __forceinline__ uint32_t digit0(float score) { return (__float_as_uint(score) >> 20) & (kRadixBins - 1); }
 
+// A caller-given score as the selection ranks it: -0.0, negative values and
+// NaN count as +0.0, so the first digit and the 64-bit key of a score always
+// agree (both read the bit pattern with the sign bit clear).
+__device__ __forceinline__ float canon_score(float score) {
+  const uint32_t u = __float_as_uint(score);
+  return (u & 0x80000000u) || u > 0x7F800000u ? 0.f : score;
+}
+
 struct Resolved {
   int digit;        // the bin holding the rank-th largest key
   uint32_t above;   // keys in higher bins
@@ -208,7 +216,7 @@ __global__ __launch_bounds__(256) void score_hist_kernel(SelectParams p, int his
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int j = min(j0 + (i0 + u) * 256 + static_cast<int>(threadIdx.x), j1 - 1);
-        sc[u] = p.score[base + j];
+        sc[u] = canon_score(p.score[base + j]);
       }
     }
 #pragma unroll
@@ -277,7 +285,8 @@ __global__ __launch_bounds__(256) void collect_kernel(SelectParams p) {
     for (int i0 = c0; i0 < c1; i0 += kBatch * 256) {
       float sc[kBatch];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) sc[u] = p.score[base + min(i0 + u * 256 + static_cast<int>(threadIdx.x), c1 - 1)];
+      for (int u = 0; u < kBatch; ++u)
+        sc[u] = canon_score(p.score[base + min(i0 + u * 256 + static_cast<int>(threadIdx.x), c1 - 1)]);
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int j = i0 + u * 256 + static_cast<int>(threadIdx.x);
@@ -350,6 +359,7 @@ __global__ __launch_bounds__(1024) void finish_kernel(SelectParams p) {
     return;
   }
   const int dom = len - p.window;
+  s_sel[t] = -1;  // a slot no emission fills stays out of the bitmap below (blockDim.x == kTopK)
   // Bound mode: the keys fill the start of the sequence's region, which has
   // room for every position, or (past kSharedListBlocks candidate
   // workgroups) one segment per workgroup, key i in the segment of the
@@ -388,7 +398,7 @@ __global__ __launch_bounds__(1024) void finish_kernel(SelectParams p) {
     }
     return p.cand[key_segment(base, b, lo) + (i - s_pre[lo])];
   };
-  const float* score = p.score + base;
+  const float* score = p.score ? p.score + base : nullptr;  // spill mode only
   bool staged = !overflow && ncand <= static_cast<uint32_t>(kFinishLdsKeys);
   if (staged) {
     constexpr int kBatch = 8;  // loads in flight per thread
@@ -447,7 +457,7 @@ __global__ __launch_bounds__(1024) void finish_kernel(SelectParams p) {
       }
     } else {
       for (int j = t; j < dom; j += blockDim.x) {
-        const float sc = score[j];
+        const float sc = canon_score(score[j]);
         if (BOUND || digit0(sc) == d0) fn(select_key(sc, j));
       }
     }
@@ -557,7 +567,7 @@ __global__ __launch_bounds__(1024) void finish_kernel(SelectParams p) {
     for (uint32_t i = t; i < nwords; i += blockDim.x) bm[i] = 0u;
     __syncthreads();
     const int32_t pos = s_sel[t];
-    atomicOr(&bm[pos >> 5], 1u << (pos & 31));
+    if (pos >= 0 && pos < dom) atomicOr(&bm[pos >> 5], 1u << (pos & 31));
     __syncthreads();
     const uint32_t per = (nwords + 1023) >> 10;
     const uint32_t w0 = t * per, w1 = min(w0 + per, nwords);

@@ -24,7 +24,7 @@ N_STAGES = 4
 STAGE_NAMES = ("full_partial", "full_merge", "score_select", "sparse")
 
 EXPORTED = (
-    "hs2_decode_workspace_bytes", "hs2_decode_block", "hs2_full_decode_score", "hs2_topk_select", "hs2_block_select",
+    "hs2_decode_workspace_bytes", "hs2_decode_score_workspace_bytes", "hs2_decode_block", "hs2_full_decode_score", "hs2_topk_select", "hs2_block_select",
     "hs2_sparse_decode", "hs2_bridge_workspace_bytes", "hs2_bridge_kv", "hs2_bridge_kv_fp8",
     "hs2_bridge_append_workspace_bytes", "hs2_bridge_append", "hs2_full_decode", "hs2_swa_decode",
     "hs2_decode_multi_workspace_bytes", "hs2_decode_multi", "hs2_stage_timing_enable",
@@ -66,6 +66,8 @@ def load(path: str = LIB_PATH):
     dp = ctypes.POINTER(DecodeDesc)
     lib.hs2_decode_workspace_bytes.argtypes = [dp]
     lib.hs2_decode_workspace_bytes.restype = sz
+    lib.hs2_decode_score_workspace_bytes.argtypes = [dp]
+    lib.hs2_decode_score_workspace_bytes.restype = sz
     lib.hs2_decode_block.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hs2_decode_block.restype = ctypes.c_int
     lib.hs2_full_decode_score.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -134,7 +136,10 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def decode_workspace_bytes(desc: DecodeDesc) -> int:
+def decode_workspace_bytes(desc: DecodeDesc, with_score: bool = False) -> int:
+    """Workspace bytes for desc; with_score: for the calls that return per-token scores."""
+    if with_score:
+        return load().hs2_decode_score_workspace_bytes(ctypes.byref(desc))
     return load().hs2_decode_workspace_bytes(ctypes.byref(desc))
 
 
@@ -168,7 +173,7 @@ class DecodeBlock:
         self.sel_idx = torch.empty((batch, 1152), dtype=torch.int32, device=dev)
         self.sel_count = torch.empty((batch,), dtype=torch.int32, device=dev)
         self.score = torch.empty((k.shape[0],), dtype=torch.float32, device=dev) if with_score else None
-        self.workspace = _workspace(decode_workspace_bytes(self.desc), dev)
+        self.workspace = _workspace(decode_workspace_bytes(self.desc, with_score), dev)
 
     def __call__(self):
         check(load().hs2_decode_block(
@@ -228,7 +233,7 @@ def full_decode_score(seq_offsets, k, v, q_full, k_scale=None, v_scale=None, max
     desc = make_desc(batch, k.shape[0], max_context, 0, kv_dtype_of(k))
     o_full = torch.empty((batch, 16, 128), dtype=torch.float32, device=dev)
     score = torch.empty((k.shape[0],), dtype=torch.float32, device=dev)
-    ws = _workspace(decode_workspace_bytes(desc), dev)
+    ws = _workspace(decode_workspace_bytes(desc, with_score=True), dev)
     check(load().hs2_full_decode_score(ctypes.byref(desc), _ptr(seq_offsets), _ptr(k), _ptr(v), _ptr(k_scale),
                                        _ptr(v_scale), _ptr(q_full), _ptr(o_full), _ptr(score), _ptr(ws),
                                        ws.numel(), _stream()))
@@ -277,7 +282,7 @@ class BlockSelectDecode:
         self.sel_idx = torch.empty((batch, 1152), dtype=torch.int32, device=dev)
         self.sel_count = torch.empty((batch,), dtype=torch.int32, device=dev)
         self.score = torch.empty((k.shape[0],), dtype=torch.float32, device=dev)
-        self.workspace = _workspace(decode_workspace_bytes(self.desc), dev)
+        self.workspace = _workspace(decode_workspace_bytes(self.desc, with_score=True), dev)
 
     def __call__(self, marks=None):
         """marks: optional three torch.cuda.Event recorded before the block

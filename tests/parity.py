@@ -48,8 +48,10 @@ def max_abs_rel(got, ref):
     return float(diff / den) if den > 0 else float(diff)
 
 
-def check_selection(sel_gpu, count, length, ref):
-    """Returns the GPU list (ascending positions); raises on a violation."""
+def check_selection(sel_gpu, count, length, ref, band_rel=None):
+    """Returns the GPU list (ascending positions); raises on a violation.
+    band_rel: a wider relative tie band than the oracle's 1e-5 (peaked
+    attention, where fp32 logits cannot resolve 1e-5; see fp32_logit_band)."""
     want = min(length, 1152)
     assert count == want, f"count {count} != {want} (L={length})"
     got = np.asarray(sel_gpu[:count], dtype=np.int64)
@@ -60,17 +62,45 @@ def check_selection(sel_gpu, count, length, ref):
     window = np.arange(max(0, length - 128), length)
     assert np.isin(window, got).all(), "window not fully selected"
     diff = np.setxor1d(got, ref["sel"])
-    outside = np.setdiff1d(diff, ref["band"])
+    band = ref["band"]
+    if band_rel is not None:
+        s_k = ref["s_k"]
+        band = np.nonzero(np.abs(ref["score"][:max(0, length - 128)] - s_k) <= band_rel * s_k)[0]
+    outside = np.setdiff1d(diff, band)
     assert outside.shape[0] == 0, f"selection differs outside the tie band at {outside[:10]} (L={length})"
     return got
 
 
-def check_decode(d, out, seqs=None, tol=None, score_tol=5e-6, oracle_cache=None, selection="token"):
+def fp32_logit_band(max_abs_logit_log2):
+    """Relative precision of an fp32 score when logits reach
+    ``max_abs_logit_log2`` (log2 units) in magnitude.  A logit is accurate to
+    a few units in the last place of its own magnitude, about 2^-22 |l|
+    (log2 units) with the query split into exact parts, and a probability
+    exp2(l - M) / Z carries the errors of l and of the head's maximum M:
+    relative ln2 * 2 * 2^-22 |l| < 2^-21 |l|.  For the workloads' logits
+    (|l| within ~10, up to ~20) that is below the 1e-5 tie band; peaked
+    attention (|l| in the hundreds) goes past it."""
+    return 2.0 ** -21 * float(max_abs_logit_log2)
+
+
+def max_abs_logit_log2(d, b):
+    """max_{h,j} |q_h . k_j| / sqrt(128) * log2(e) of sequence b (oracle's decode of the cache)."""
+    a, e = int(d["seq_offsets"][b]), int(d["seq_offsets"][b + 1])
+    ks = None if d["k_scale"] is None else d["k_scale"][a:e]
+    k = O.decode_kv(d["k"][a:e], d["kv"], ks)
+    return float(np.abs(k @ d["q_full"][b].astype(np.float64).T).max()) / np.sqrt(128.0) * np.log2(np.e)
+
+
+def check_decode(d, out, seqs=None, tol=None, score_tol=5e-6, oracle_cache=None, selection="token",
+                 band_rel=None):
     """Compare GPU outputs (dict of tensors) with the oracle on `seqs`.
 
     Returns a dict of the worst errors seen.  ``oracle_cache`` may hold
     per-sequence oracle results already computed (keyed by sequence).
-    ``selection`` names the oracle's rule ("token", or "block" for gen-1)."""
+    ``selection`` names the oracle's rule ("token", or "block" for gen-1).
+    ``band_rel`` (a dict by sequence, or one float) widens the tie band
+    (see fp32_logit_band); worst["outside_std_band"] counts the sequences
+    whose list differs from the oracle's outside the standard 1e-5 band."""
     kv = d["kv"]
     tol = TOL[kv] if tol is None else tol
     offs = d["seq_offsets"]
@@ -81,7 +111,7 @@ def check_decode(d, out, seqs=None, tol=None, score_tol=5e-6, oracle_cache=None,
     sel_idx = out["sel_idx"].cpu().numpy()
     sel_count = out["sel_count"].cpu().numpy()
     score = out["score"].cpu().numpy() if out.get("score") is not None else None
-    worst = dict(o_full=0.0, o_sparse=0.0, score=0.0, band_diffs=0)
+    worst = dict(o_full=0.0, o_sparse=0.0, score=0.0, band_diffs=0, outside_std_band=0)
     for b in seqs:
         a, e = int(offs[b]), int(offs[b + 1])
         length = e - a
@@ -106,12 +136,16 @@ def check_decode(d, out, seqs=None, tol=None, score_tol=5e-6, oracle_cache=None,
         err = max_abs_rel(o_full[b], ref["o_full"])
         assert err <= tol, f"o_full seq {b}: {err:.3e} > {tol}"
         worst["o_full"] = max(worst["o_full"], err)
-        got = check_selection(sel_idx[b], int(sel_count[b]), length, ref)
+        brel = band_rel.get(b) if isinstance(band_rel, dict) else band_rel
+        got = check_selection(sel_idx[b], int(sel_count[b]), length, ref, brel)
+        if brel is not None and np.setdiff1d(np.setxor1d(got, ref["sel"]), ref["band"]).shape[0]:
+            worst["outside_std_band"] += 1
         if score is not None:
             s_k = O.select_tokens(ref["score"])["s_k"] or ref["score"].max()  # the token-level k-th score
             den = np.maximum(ref["score"], s_k)
             serr = float((np.abs(score[a:e].astype(np.float64) - ref["score"]) / den).max())
-            assert serr <= score_tol, f"score seq {b}: {serr:.3e} (relative, floored at s_k) > {score_tol}"
+            stol = score_tol.get(b) if isinstance(score_tol, dict) else score_tol
+            assert serr <= stol, f"score seq {b}: {serr:.3e} (relative, floored at s_k) > {stol}"
             worst["score"] = max(worst["score"], serr)
         if o_sparse is not None:
             ref_sparse = ref["o_sparse"]
@@ -135,6 +169,18 @@ def bf16_ordinal(bits):
     return np.where(b & 0x8000, -mag, mag)
 
 
+def _accumulation_bound(h_bits, w_bits, rows):
+    """sum_k |h_ik w_kj| and gamma_n = n u / (1 - n u) (u = 2^-24): the
+    textbook bound on fp32 accumulation of n exact products is
+    gamma_n * sum|h w|.  Test-side error bound only; the reference values
+    come from the oracle."""
+    h = np.abs(O.bf16_bits_to_f64(h_bits[rows]))
+    w = np.abs(O.bf16_bits_to_f64(w_bits))
+    n = h.shape[1]
+    u = 2.0 ** -24
+    return h @ w, n * u / (1 - n * u)
+
+
 def check_bridge(h_bits, w_bits, out_bits, rows):
     """Bridge outputs (bf16 bits [T, 128]) for the given rows against the
     oracle.  Element-wise bound from the arithmetic: fp32 accumulation of
@@ -142,18 +188,14 @@ def check_bridge(h_bits, w_bits, out_bits, rows):
     (gamma_n = n u / (1 - n u), u = 2^-24), and the final rounding to bf16
     adds at most one bf16 ulp.  Also: at most 0.1 % of the elements (at least
     one, for small samples) more than one ulp from the correctly rounded value
-    (a statistical guard against a systematic error; elements with a large
-    sum|h w| against a small value may miss by two within the bound above).
+    (elements with a large sum|h w| against a small value may miss by two
+    within the bound above), and at least 99 % of them equal to it (samples of
+    1000 or more): a guard against a systematic error such as truncation.
     No max-abs-relative bar: bf16 output alone is off by up to
     half an ulp, 2^-9 of the largest element, which a 2e-3 bar would not
     reliably admit.  Returns (worst ulps, fraction within 1 ulp)."""
-    h = O.bf16_bits_to_f64(h_bits[rows])
-    w = O.bf16_bits_to_f64(w_bits)
-    ref = h @ w
-    abs_sum = np.abs(h) @ np.abs(w)
-    n = h.shape[1]
-    u = 2.0 ** -24
-    gamma = n * u / (1 - n * u)
+    (ref,), _ = O.bridge_kv(h_bits, [w_bits], [], rows=rows)  # the oracle's float64 product
+    abs_sum, gamma = _accumulation_bound(h_bits, w_bits, rows)
     got_bits = out_bits[rows]
     got = O.bf16_bits_to_f64(got_bits)
     mag = np.abs(ref) + gamma * abs_sum
@@ -173,6 +215,13 @@ def check_bridge(h_bits, w_bits, out_bits, rows):
     frac1 = float((ulps <= 1).mean())
     allowed = max(1, int(0.001 * ulps.size))
     assert int((ulps > 1).sum()) <= allowed, f"only {frac1:.5f} of elements within 1 ulp"
+    # Rounding to nearest: an fp32 accumulation error is far below half a bf16
+    # ulp for nearly every element, so nearly all equal the correctly rounded
+    # value; a directed rounding (truncation) misses about half of them while
+    # staying within one ulp.
+    if ulps.size >= 1000:
+        frac0 = float((ulps == 0).mean())
+        assert frac0 >= 0.99, f"only {frac0:.5f} of elements equal the correctly rounded value"
     return int(ulps.max()), frac1
 
 
@@ -194,14 +243,9 @@ def check_bridge_fp8(h_bits, w_bits, codes, scales, rows):
     Bar: scales within that relative bound, every code within one step, at
     least 99.5 % of the codes equal.  Returns (fraction of equal codes,
     worst relative scale difference)."""
-    h = O.bf16_bits_to_f64(h_bits[rows])
-    w = O.bf16_bits_to_f64(w_bits)
-    ref = h @ w
-    abs_sum = np.abs(h) @ np.abs(w)
-    n = h.shape[1]
-    u = 2.0 ** -24
-    gamma = n * u / (1 - n * u)
-    ref_codes, ref_scale = O.quantize_rows_e4m3(ref)
+    (ref,), _ = O.bridge_kv(h_bits, [w_bits], [], rows=rows)
+    ((ref_codes, ref_scale),), _ = O.bridge_kv_fp8(h_bits, [w_bits], [], rows=rows)  # the oracle's FP8 cache rows
+    abs_sum, gamma = _accumulation_bound(h_bits, w_bits, rows)
     got_codes = np.asarray(codes)[rows]
     got_scale = np.asarray(scales)[rows].astype(np.float64)
     amax = np.abs(ref).max(axis=1)

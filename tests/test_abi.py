@@ -58,10 +58,37 @@ def test_workspace_query():
     lib = hs2.load()
     d = desc()
     n = lib.hs2_decode_workspace_bytes(ctypes.byref(d))
-    # at least the logits spill (64 B per token) and the score buffer
-    assert n >= 5000 * (64 + 4)
-    assert lib.hs2_decode_workspace_bytes(ctypes.byref(desc(head_dim=64))) == 0
-    assert lib.hs2_decode_workspace_bytes(None) == 0
+    n_score = lib.hs2_decode_score_workspace_bytes(ctypes.byref(d))
+    # without a score output: no logit spill; the score calls add exactly the
+    # 64 B a token of every full-layer logit (rounded to the 256-byte layout)
+    assert n_score - n == (5000 * 64 + 255) // 256 * 256
+    for q in (lib.hs2_decode_workspace_bytes, lib.hs2_decode_score_workspace_bytes):
+        assert q(ctypes.byref(desc(head_dim=64))) == 0
+        assert q(None) == 0
+
+
+def test_workspace_sizes_at_the_bench_shape():
+    # 32 x 131072 tokens, bf16, 4 sparse layers: the default path (no score
+    # output) needs no room for the 268 MB of logits
+    lib = hs2.load()
+    d = hs2.make_desc(32, 32 * 131072, 131072, 4)
+    n = lib.hs2_decode_workspace_bytes(ctypes.byref(d))
+    n_score = lib.hs2_decode_score_workspace_bytes(ctypes.byref(d))
+    assert n_score - n >= 32 * 131072 * 64
+    assert n < 96 * 2 ** 20
+
+
+def test_score_output_needs_the_score_workspace():
+    lib = hs2.load()
+    d = desc()
+    n = lib.hs2_decode_workspace_bytes(ctypes.byref(d))
+    n_score = lib.hs2_decode_score_workspace_bytes(ctypes.byref(d))
+    assert call_decode(d, ws_bytes=n, score=FAKE) == SMALL_WS
+    assert "workspace" in lib.hs2_last_error_message().decode()
+    assert call_decode(d, ws_bytes=n_score - 1, score=FAKE) == SMALL_WS
+    v = ctypes.c_void_p
+    assert lib.hs2_full_decode_score(ctypes.byref(d), v(FAKE), v(FAKE), v(FAKE), None, None, v(FAKE), v(FAKE),
+                                     v(FAKE), v(FAKE), n, None) == SMALL_WS
 
 
 @pytest.mark.parametrize("field,value,status", [

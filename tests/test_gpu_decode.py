@@ -295,3 +295,69 @@ def test_fp8_rows_of_zeros():
     out, _, _ = run(d)
     w = parity.check_decode(d, out)
     say(f"worst {w}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_peaked_attention_scores_near_fp32_underflow(kv):
+    """The full-layer query scaled by 50: logits reach hundreds of log2 units,
+    the k-th out-of-window score is ~1e-31 (normal in fp32, whose normal
+    range ends at 2^-126 ~ 1.2e-38) and about half of each context scores
+    below fp32's normal range.  The bound path's bf16 bounds and slack and
+    the exact rescoring then work on tiny, widely spread scores.  Bars: the
+    outputs' (2e-3 bf16, 2e-2 E4M3); the selection exact outside the tie
+    band widened by the fp32 logit precision at these magnitudes
+    (parity.fp32_logit_band), and the score within 5e-6 plus that precision;
+    the run also reports whether any list differs outside the plain 1e-5 band."""
+    lengths = [4096, 9000, 1300]
+    d = inputs.make_decode(lengths=lengths, n_sparse=2, kv=kv, seed=83, needles=0)
+    d["q_full"] = (d["q_full"] * np.float32(50.0)).astype(np.float32)
+    band, stol = {}, {}
+    for b in range(len(lengths)):
+        a, e = int(d["seq_offsets"][b]), int(d["seq_offsets"][b + 1])
+        ks = None if d["k_scale"] is None else d["k_scale"][a:e]
+        ref = O.decode_sequence(d["q_full"][b].astype(np.float64), d["q_sparse"][:, b].astype(np.float64),
+                                O.decode_kv(d["k"][a:e], kv, ks), O.decode_kv(d["v"][a:e], kv,
+                                None if d["v_scale"] is None else d["v_scale"][a:e]))
+        lmax = parity.max_abs_logit_log2(d, b)
+        extra = parity.fp32_logit_band(lmax)
+        band[b], stol[b] = O.BAND_REL + extra, 5e-6 + extra
+        tiny = int((ref["score"] < 2.0 ** -126).sum())
+        say(f"seq {b}: L={lengths[b]} s_k={ref['s_k']:.3e} max|l|={lmax:.0f} (log2) scores below 2^-126: {tiny}; "
+            f"band {band[b]:.2e}")
+        if lengths[b] > 1152:
+            assert 2.0 ** -126 < ref["s_k"] <= 1e-30
+    say(f"case: peaked attention (query x 50) kv={kv} lengths={lengths}")
+    out, _, _ = run(d)
+    w = parity.check_decode(d, out, band_rel=band, score_tol=stol)
+    say(f"worst {w}")
+
+
+def test_topk_select_signed_zero_and_negative_scores():
+    """Given scores that are mostly +0.0 and -0.0 around the k-th rank (plus a
+    few negative values and NaNs, which the call ranks as +0.0): the list
+    equals the oracle's on the scores with those values read as +0.0, bit
+    for bit (ties to the lower position)."""
+    rng = np.random.default_rng(91)
+    lengths = [5000, 1153, 70000, 2000]
+    offs = np.zeros(len(lengths) + 1, np.int64)
+    offs[1:] = np.cumsum(lengths)
+    n = int(offs[-1])
+    score = np.zeros(n, np.float32)
+    score[rng.random(n) < 0.5] = np.float32(-0.0)
+    pos = rng.choice(n, n // 20, replace=False)  # ~5 % positive: fewer than k in the short sequences
+    score[pos] = rng.random(pos.shape[0]).astype(np.float32) + np.float32(0.01)
+    neg = rng.choice(n, 300, replace=False)
+    score[neg] = -rng.random(300).astype(np.float32)
+    score[rng.choice(n, 20, replace=False)] = np.float32("nan")
+    assert np.signbit(score).sum() > n // 4
+    say(f"case: given scores mostly +-0.0 with negatives and NaN, lengths {lengths}")
+    sel_idx, sel_count = hs2.topk_select(torch.from_numpy(offs).cuda(), torch.from_numpy(score).cuda(),
+                                         len(lengths), max(lengths))
+    torch.cuda.synchronize()
+    sel_idx, sel_count = sel_idx.cpu().numpy(), sel_count.cpu().numpy()
+    canon = np.where(np.isnan(score) | (score <= 0), 0.0, score.astype(np.float64))
+    for b, length in enumerate(lengths):
+        ref = O.select_tokens(canon[offs[b]:offs[b + 1]])["sel"]
+        assert sel_count[b] == ref.shape[0]
+        np.testing.assert_array_equal(sel_idx[b][:sel_count[b]], ref)
+        assert np.all(sel_idx[b][sel_count[b]:] == -1)

@@ -132,3 +132,26 @@ def test_full_decode_alone(kv):
         ref, _ = O.full_attention(d["q_full"][b].astype(np.float64), O.decode_kv(d["k"][a:e], kv, ks),
                                   O.decode_kv(d["v"][a:e], kv, vs))
         assert parity.max_abs_rel(got[b], ref) <= parity.TOL[kv]
+
+
+def test_full_decode_writes_only_its_partials():
+    # Full attention alone keeps no score bounds, statistics or selection
+    # state: past the split-K partials (at most B * ceil(max_context / 256)
+    # partials of 2080 floats, chunks being at least 256 tokens) the
+    # workspace is left as it was.
+    lengths = [20000, 3000, 0, 9000]
+    print(f"case: full decode workspace use, lengths {lengths}", flush=True)
+    d = inputs.make_decode(lengths=lengths, n_sparse=1, seed=29, needles=10)
+    t = parity.to_device(d)
+    desc = hs2.make_desc(len(lengths), sum(lengths), t["max_context"], 0)
+    ws = torch.full((hs2.decode_workspace_bytes(desc),), 0xA5, dtype=torch.uint8, device="cuda")
+    o = hs2.full_decode(t["seq_offsets"], t["k"], t["v"], t["q_full"], max_context=t["max_context"], workspace=ws)
+    torch.cuda.synchronize()
+    partial_bytes = len(lengths) * -(-t["max_context"] // 256) * 2080 * 4
+    start = -(-partial_bytes // 256) * 256
+    rest = ws[start:].cpu().numpy()
+    assert rest.size > 0 and np.all(rest == 0xA5), f"{int((rest != 0xA5).sum())} bytes written past the partials"
+    blk = hs2.decode_block(t["seq_offsets"], t["k"], t["v"], t["q_full"], t["q_sparse"],
+                           max_context=t["max_context"], with_score=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o, blk["o_full"])
