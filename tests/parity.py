@@ -73,14 +73,16 @@ def check_selection(sel_gpu, count, length, ref, band_rel=None):
 
 def fp32_logit_band(max_abs_logit_log2):
     """Relative precision of an fp32 score when logits reach
-    ``max_abs_logit_log2`` (log2 units) in magnitude.  A logit is accurate to
-    a few units in the last place of its own magnitude, about 2^-22 |l|
-    (log2 units) with the query split into exact parts, and a probability
-    exp2(l - M) / Z carries the errors of l and of the head's maximum M:
-    relative ln2 * 2 * 2^-22 |l| < 2^-21 |l|.  For the workloads' logits
-    (|l| within ~10, up to ~20) that is below the 1e-5 tie band; peaked
-    attention (|l| in the hundreds) goes past it."""
-    return 2.0 ** -21 * float(max_abs_logit_log2)
+    ``max_abs_logit_log2`` (log2 units) in magnitude: 2^-19 |l|.  A logit is
+    built from exact products (the query split into three exact bf16 parts)
+    by 12 fp32 accumulations (3 parts x 4 MFMA steps), each rounding by at
+    most half an ulp of the running sum, so it is within about 12 * 2^-24 |l|;
+    a probability exp2(l - M) / Z carries the errors of l and of the head's
+    maximum M: relative 2 ln2 * 12 * 2^-24 |l| < 2^-19 |l|.  This worst case
+    stays below the 1e-5 tie band only for |l| under ~5; at the workloads'
+    magnitudes (|l| within ~10) the measured score errors are ~1.5e-6, while
+    peaked attention (|l| in the hundreds) goes well past the band."""
+    return 2.0 ** -19 * float(max_abs_logit_log2)
 
 
 def max_abs_logit_log2(d, b):

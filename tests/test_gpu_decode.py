@@ -299,10 +299,10 @@ def test_fp8_rows_of_zeros():
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
 def test_peaked_attention_scores_near_fp32_underflow(kv):
-    """The full-layer query scaled by 50: logits reach hundreds of log2 units,
-    the k-th out-of-window score is ~1e-31 (normal in fp32, whose normal
-    range ends at 2^-126 ~ 1.2e-38) and about half of each context scores
-    below fp32's normal range.  The bound path's bf16 bounds and slack and
+    """Each sequence's full-layer query scaled (by 50, 55 and 32) so that its
+    k-th out-of-window score lies in 1e-38 .. 1e-30 (normal in fp32, whose
+    normal range ends at 2^-126 ~ 1.2e-38): logits reach hundreds of log2
+    units, and up to ~3/4 of a context scores below fp32's normal range.  The bound path's bf16 bounds and slack and
     the exact rescoring then work on tiny, widely spread scores.  Bars: the
     outputs' (2e-3 bf16, 2e-2 E4M3); the selection exact outside the tie
     band widened by the fp32 logit precision at these magnitudes
@@ -310,7 +310,7 @@ def test_peaked_attention_scores_near_fp32_underflow(kv):
     the run also reports whether any list differs outside the plain 1e-5 band."""
     lengths = [4096, 9000, 1300]
     d = inputs.make_decode(lengths=lengths, n_sparse=2, kv=kv, seed=83, needles=0)
-    d["q_full"] = (d["q_full"] * np.float32(50.0)).astype(np.float32)
+    d["q_full"] = (d["q_full"] * np.array([50.0, 55.0, 32.0], np.float32)[:, None, None]).astype(np.float32)
     band, stol = {}, {}
     for b in range(len(lengths)):
         a, e = int(d["seq_offsets"][b]), int(d["seq_offsets"][b + 1])
@@ -326,7 +326,7 @@ def test_peaked_attention_scores_near_fp32_underflow(kv):
             f"band {band[b]:.2e}")
         if lengths[b] > 1152:
             assert 2.0 ** -126 < ref["s_k"] <= 1e-30
-    say(f"case: peaked attention (query x 50) kv={kv} lengths={lengths}")
+    say(f"case: peaked attention (queries x 50, 55, 32) kv={kv} lengths={lengths}")
     out, _, _ = run(d)
     w = parity.check_decode(d, out, band_rel=band, score_tol=stol)
     say(f"worst {w}")
