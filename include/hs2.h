@@ -121,6 +121,27 @@ hs2_status hs2_decode_block(const hs2_decode_desc* desc, const int64_t* seq_offs
                             int32_t* sel_idx, int32_t* sel_count, float* score_out,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* hs2_decode_block (score_out NULL) for callers that cannot allocate device
+ * memory, such as code under HIP graph capture, tight serving loops or
+ * harnesses that forbid allocation: the workspace is a device array of the
+ * library's own, HS2_NOALLOC_SCRATCH_BYTES long, which each GPU the library
+ * runs on holds until the process ends (looked up on the first call on that
+ * device).  Arguments, outputs, errors and results (bit for bit) as
+ * hs2_decode_block with score_out == NULL.  A shape whose
+ * hs2_decode_workspace_bytes exceeds HS2_NOALLOC_SCRATCH_BYTES is rejected
+ * with HS2_ERR_UNSUPPORTED before any HIP call (64 MiB covers, with 4 sparse
+ * layers, 32 sequences of 131072 tokens (bf16) or 4 of 1048576 (E4M3), and
+ * 8 of 32768).  Every call on one GPU shares that GPU's array: calls
+ * that overlap in time on one GPU (other streams, other threads) race and
+ * must not be made.  The array's contents on entry do not matter.           */
+#define HS2_NOALLOC_SCRATCH_BYTES (64u << 20)
+hs2_status hs2_decode_block_noalloc(const hs2_decode_desc* desc, const int64_t* seq_offsets,
+                                    const void* k_cache, const void* v_cache,
+                                    const float* k_scale, const float* v_scale,
+                                    const float* q_full, const float* q_sparse,
+                                    float* o_full, float* o_sparse,
+                                    int32_t* sel_idx, int32_t* sel_count, void* stream);
+
 /* Multi-token decode (speculative verification): n_query = T query tokens
  * per sequence in one step.  The pages give no multi-token rule for
  * HySparse2; the reading taken: the T tokens are the sequence's last T cache
@@ -305,10 +326,11 @@ hs2_status hs2_bridge_append(int32_t batch, int32_t d_model, int32_t head_dim, i
  * 1 (each marker costs the step about 1.5 us).  Mode 0: off.  Other modes:
  * HS2_ERR_INVALID_ARGUMENT.  The events are timing-only (no system-scope
  * fence).  At most 1024 calls are recorded between reads.
- * This is the library's one piece of process-global state: the mode and the
- * record are shared by every thread and device (guarded by a mutex); with
- * timing on, calls from several threads land in one record in the order they
- * take it.  With timing off (the default) the calls keep no state at all.
+ * Process-global state: the mode and the record are shared by every thread
+ * and device (guarded by a mutex); with timing on, calls from several threads
+ * land in one record in the order they take it.  With timing off (the
+ * default) the calls keep no state (hs2_decode_block_noalloc aside, which
+ * keeps its scratch array's address per device).
  * hs2_stage_timing_read waits for the recorded events and returns, per stage,
  * the mean duration in milliseconds over the calls recorded since the last
  * read (a stage a call did not record counts as 0), and the number of calls

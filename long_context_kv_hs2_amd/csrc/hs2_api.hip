@@ -363,6 +363,26 @@ hs2_status run_sparse(const DecodeArgs& a, const DecodeLayout& L, const int32_t*
 
 hs2_status run_block(const DecodeArgs& a, const DecodeLayout& L);
 
+// The arguments of a decode step other than its workspace.
+hs2_status check_decode_args(const hs2_decode_desc* desc, const int64_t* seq_offsets, const void* k_cache,
+                             const void* v_cache, const float* k_scale, const float* v_scale, const float* q_full,
+                             const float* q_sparse, const float* o_full, const float* o_sparse,
+                             const int32_t* sel_idx, const int32_t* sel_count, const float* score_out) {
+  HS2_TRY(check_desc(desc));
+  const hs2_decode_desc& d = *desc;
+  HS2_TRY(check_kv(d, seq_offsets, k_cache, v_cache, k_scale, v_scale));
+  const bool any = d.batch > 0;
+  const bool sparse = any && d.n_sparse_layers > 0;
+  HS2_TRY(check_ptr(q_full, any, 16, "q_full"));
+  HS2_TRY(check_ptr(o_full, any, 16, "o_full"));
+  HS2_TRY(check_ptr(q_sparse, sparse, 16, "q_sparse"));
+  HS2_TRY(check_ptr(o_sparse, sparse, 16, "o_sparse"));
+  HS2_TRY(check_ptr(sel_idx, any, 4, "sel_idx"));
+  HS2_TRY(check_ptr(sel_count, any, 4, "sel_count"));
+  if (score_out && !aligned(score_out, 4)) return fail(HS2_ERR_INVALID_ARGUMENT, "score_out not 4-byte aligned");
+  return HS2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -382,21 +402,12 @@ hs2_status hs2_decode_block(const hs2_decode_desc* desc, const int64_t* seq_offs
                             const float* q_sparse, float* o_full, float* o_sparse, int32_t* sel_idx,
                             int32_t* sel_count, float* score_out, void* workspace, size_t workspace_bytes,
                             void* stream) {
-  HS2_TRY(check_desc(desc));
+  HS2_TRY(check_decode_args(desc, seq_offsets, k_cache, v_cache, k_scale, v_scale, q_full, q_sparse, o_full,
+                            o_sparse, sel_idx, sel_count, score_out));
   const hs2_decode_desc& d = *desc;
-  HS2_TRY(check_kv(d, seq_offsets, k_cache, v_cache, k_scale, v_scale));
-  const bool any = d.batch > 0;
-  const bool sparse = any && d.n_sparse_layers > 0;
-  HS2_TRY(check_ptr(q_full, any, 16, "q_full"));
-  HS2_TRY(check_ptr(o_full, any, 16, "o_full"));
-  HS2_TRY(check_ptr(q_sparse, sparse, 16, "q_sparse"));
-  HS2_TRY(check_ptr(o_sparse, sparse, 16, "o_sparse"));
-  HS2_TRY(check_ptr(sel_idx, any, 4, "sel_idx"));
-  HS2_TRY(check_ptr(sel_count, any, 4, "sel_count"));
-  if (score_out && !aligned(score_out, 4)) return fail(HS2_ERR_INVALID_ARGUMENT, "score_out not 4-byte aligned");
   DecodeLayout L;
   HS2_TRY(check_workspace(d, workspace, workspace_bytes, L, score_out != nullptr));
-  if (!any) return HS2_OK;
+  if (d.batch == 0) return HS2_OK;
 
   DecodeArgs a{desc, seq_offsets, k_cache, v_cache, k_scale, v_scale, q_full, q_sparse, o_full, o_sparse,
                sel_idx, sel_count, score_out, workspace, static_cast<hipStream_t>(stream)};
@@ -404,6 +415,53 @@ hs2_status hs2_decode_block(const hs2_decode_desc* desc, const int64_t* seq_offs
 }
 
 }  // extern "C"
+
+// ---- the decode step without an allocation ------------------------------------
+// hs2_decode_block_noalloc runs hs2_decode_block (no score output) with its
+// workspace in `scratch`, a device array of the library's own: each GPU the
+// library runs on holds one copy for the life of the process.  The array's
+// device address is looked up once per device (hipGetSymbolAddress, with the
+// device current) and kept; host code uses that address, never the symbol.
+namespace {
+__device__ __align__(256) uint8_t scratch[HS2_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hs2_status scratch_address(void** out) {
+  int dev = -1;
+  HS2_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(HS2_ERR_UNSUPPORTED, "device %d (0..%d supported)", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    HS2_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(HS2_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return HS2_OK;
+}
+}  // namespace
+
+extern "C" hs2_status hs2_decode_block_noalloc(const hs2_decode_desc* desc, const int64_t* seq_offsets,
+                                               const void* k_cache, const void* v_cache, const float* k_scale,
+                                               const float* v_scale, const float* q_full, const float* q_sparse,
+                                               float* o_full, float* o_sparse, int32_t* sel_idx,
+                                               int32_t* sel_count, void* stream) {
+  HS2_TRY(check_decode_args(desc, seq_offsets, k_cache, v_cache, k_scale, v_scale, q_full, q_sparse, o_full,
+                            o_sparse, sel_idx, sel_count, nullptr));
+  const DecodeLayout L = decode_layout(*desc, false);
+  if (L.total > static_cast<size_t>(HS2_NOALLOC_SCRATCH_BYTES))
+    return fail(HS2_ERR_UNSUPPORTED, "this shape needs %zu bytes of workspace; the library's scratch holds %zu",
+                L.total, static_cast<size_t>(HS2_NOALLOC_SCRATCH_BYTES));
+  if (desc->batch == 0) return HS2_OK;
+  void* ws = nullptr;
+  HS2_TRY(scratch_address(&ws));
+  DecodeArgs a{desc, seq_offsets, k_cache, v_cache, k_scale, v_scale, q_full, q_sparse, o_full, o_sparse,
+               sel_idx, sel_count, nullptr, ws, static_cast<hipStream_t>(stream)};
+  return run_block(a, L);
+}
 
 namespace {
 // One hybrid block for the (validated) batch in `a`.

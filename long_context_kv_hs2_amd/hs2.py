@@ -24,7 +24,7 @@ N_STAGES = 4
 STAGE_NAMES = ("full_partial", "full_merge", "score_select", "sparse")
 
 EXPORTED = (
-    "hs2_decode_workspace_bytes", "hs2_decode_score_workspace_bytes", "hs2_decode_block", "hs2_full_decode_score", "hs2_topk_select", "hs2_block_select",
+    "hs2_decode_workspace_bytes", "hs2_decode_score_workspace_bytes", "hs2_decode_block", "hs2_decode_block_noalloc", "hs2_full_decode_score", "hs2_topk_select", "hs2_block_select",
     "hs2_sparse_decode", "hs2_bridge_workspace_bytes", "hs2_bridge_kv", "hs2_bridge_kv_fp8",
     "hs2_bridge_append_workspace_bytes", "hs2_bridge_append", "hs2_full_decode", "hs2_swa_decode",
     "hs2_decode_multi_workspace_bytes", "hs2_decode_multi", "hs2_stage_timing_enable",
@@ -70,6 +70,8 @@ def load(path: str = LIB_PATH):
     lib.hs2_decode_score_workspace_bytes.restype = sz
     lib.hs2_decode_block.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hs2_decode_block.restype = ctypes.c_int
+    lib.hs2_decode_block_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.hs2_decode_block_noalloc.restype = ctypes.c_int
     lib.hs2_full_decode_score.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hs2_full_decode_score.restype = ctypes.c_int
     lib.hs2_topk_select.argtypes = [dp, vp, vp, vp, vp, vp, sz, vp]
@@ -217,6 +219,19 @@ class MultiDecode:
             _ptr(self.o_sparse), _ptr(self.sel_idx), _ptr(self.sel_count), _ptr(self.workspace),
             self.workspace.numel(), _stream()))
         return self
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def decode_block_noalloc(blk: "DecodeBlock"):
+    """hs2_decode_block_noalloc on a DecodeBlock's inputs and outputs (its
+    own workspace is not used: the library's scratch array is)."""
+    check(load().hs2_decode_block_noalloc(
+        ctypes.byref(blk.desc), _ptr(blk.seq_offsets), _ptr(blk.k), _ptr(blk.v), _ptr(blk.k_scale),
+        _ptr(blk.v_scale), _ptr(blk.q_full), _ptr(blk.q_sparse), _ptr(blk.o_full), _ptr(blk.o_sparse),
+        _ptr(blk.sel_idx), _ptr(blk.sel_count), _stream()))
+    return blk
 
 
 def decode_block(seq_offsets, k, v, q_full, q_sparse, k_scale=None, v_scale=None, max_context=None,

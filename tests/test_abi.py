@@ -289,3 +289,24 @@ def test_bridge_fp8_validation():
     assert f(10, 4096, 128, 1, FAKE, one, one, one, arr(None), one, one, FAKE, 1 << 30, None) == INVALID
     assert f(10, 4096, 128, 1, FAKE, one, one, one, arr(FAKE + 2), one, one, FAKE, 1 << 30, None) == INVALID
     assert f(10, 4096, 128, 1, FAKE, one, one, one, one, one, one, FAKE, 100, None) == SMALL_WS
+
+
+def test_noalloc_validation_before_any_hip_call():
+    lib = hs2.load()
+    v = ctypes.c_void_p
+
+    def call(d, qf=FAKE, seq=FAKE):
+        return lib.hs2_decode_block_noalloc(ctypes.byref(d), v(seq), v(FAKE), v(FAKE), None, None, v(qf), v(FAKE),
+                                            v(FAKE), v(FAKE), v(FAKE), v(FAKE), None)
+
+    big = hs2.make_desc(64, 64 * 262144, 262144, 4)
+    assert lib.hs2_decode_workspace_bytes(ctypes.byref(big)) > hs2.NOALLOC_SCRATCH_BYTES
+    assert call(big) == UNSUPPORTED
+    assert "scratch" in lib.hs2_last_error_message().decode()
+    assert call(desc(), qf=None) == INVALID
+    assert call(desc(), seq=FAKE + 4) == INVALID
+    assert call(desc(head_dim=64)) == UNSUPPORTED
+    # the workloads it is sized for fit
+    for b, n, lmax, kv in ((32, 32 * 131072, 131072, 0), (4, 4 * 1048576, 1048576, 1), (8, 262144, 32768, 0)):
+        d = hs2.make_desc(b, n, lmax, 4, kv)
+        assert lib.hs2_decode_workspace_bytes(ctypes.byref(d)) <= hs2.NOALLOC_SCRATCH_BYTES
