@@ -129,12 +129,12 @@ hs2_status hs2_decode_block(const hs2_decode_desc* desc, const int64_t* seq_offs
  * device).  Arguments, outputs, errors and results (bit for bit) as
  * hs2_decode_block with score_out == NULL.  A shape whose
  * hs2_decode_workspace_bytes exceeds HS2_NOALLOC_SCRATCH_BYTES is rejected
- * with HS2_ERR_UNSUPPORTED before any HIP call (64 MiB covers, with 4 sparse
+ * with HS2_ERR_UNSUPPORTED before any HIP call (96 MiB covers, with 4 sparse
  * layers, 32 sequences of 131072 tokens (bf16) or 4 of 1048576 (E4M3), and
  * 8 of 32768).  Every call on one GPU shares that GPU's array: calls
  * that overlap in time on one GPU (other streams, other threads) race and
  * must not be made.  The array's contents on entry do not matter.           */
-#define HS2_NOALLOC_SCRATCH_BYTES (64u << 20)
+#define HS2_NOALLOC_SCRATCH_BYTES (96u << 20)
 hs2_status hs2_decode_block_noalloc(const hs2_decode_desc* desc, const int64_t* seq_offsets,
                                     const void* k_cache, const void* v_cache,
                                     const float* k_scale, const float* v_scale,

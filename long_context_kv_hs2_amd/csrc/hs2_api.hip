@@ -106,7 +106,7 @@ DecodeLayout decode_layout(const hs2_decode_desc& d, bool with_spill) {
   L.tile_stats = take(((N >> 4) + B + 1) * kHeads * sizeof(float));
   L.tile_ub = take(((N >> 4) + B + 1) * 2 * sizeof(float));
   const int n_sparse = d.n_sparse_layers > 0 ? d.n_sparse_layers : 1;
-  const int slices = sparse_slices(d.batch, n_sparse);
+  const int slices = sparse_slices(d.batch);
   L.sparse = take(slices > 1 ? B * n_sparse * static_cast<size_t>(slices) * kPartialFloats * sizeof(float) : 0);
   L.blocks = take(((N >> 6) + B + 1) * sizeof(float));  // gen-1 block selection: per-block score sums
   L.groups = take(((N >> 10) + B + 1) * sizeof(unsigned long long));  // and each 16-block group's largest key

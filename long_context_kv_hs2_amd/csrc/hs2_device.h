@@ -299,20 +299,22 @@ __device__ __forceinline__ void softmax_init(SoftmaxState& st) {
 // into a bf16 head and a bf16 tail, so the product keeps 16 significant bits
 // of each weight (V itself is exact in bf16); MFMA j leaves
 // O[head n][dim 32g + 8i + j] in element i of st.o[j] on lane (n, g).
+// Operands of O^T += V^T P^T for one tile: ph / pl the bf16 head and tail
+// of the lane's four weights (tokens 4g .. 4g + 3), a[j] the lane's V values
+// of dim 8n + j for those tokens (MFMA j's A operand, row n).
 template <bool FP8>
-__device__ __forceinline__ void pv_tile(const u32x4 (&vraw)[4], const float (&p)[4], const float (&vscale)[4],
-                                        SoftmaxState& st) {
+__device__ __forceinline__ void pv_operands(const u32x4 (&vraw)[4], const float (&p)[4], const float (&vscale)[4],
+                                            u32x2 (&a)[8], u32x2& ph, u32x2& pl) {
   float w[4], tail[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     w[r] = FP8 ? p[r] * vscale[r] : p[r];
     tail[r] = w[r] - __uint_as_float(__float_as_uint(w[r]) & 0xFFFF0000u);  // exact
   }
-  const u32x2 ph = {perm(__float_as_uint(w[1]), __float_as_uint(w[0]), kHiHalves),
-                    perm(__float_as_uint(w[3]), __float_as_uint(w[2]), kHiHalves)};
-  const u32x2 pl = {perm(__float_as_uint(tail[1]), __float_as_uint(tail[0]), kHiHalves),
-                    perm(__float_as_uint(tail[3]), __float_as_uint(tail[2]), kHiHalves)};
-  u32x2 a[8];
+  ph = u32x2{perm(__float_as_uint(w[1]), __float_as_uint(w[0]), kHiHalves),
+             perm(__float_as_uint(w[3]), __float_as_uint(w[2]), kHiHalves)};
+  pl = u32x2{perm(__float_as_uint(tail[1]), __float_as_uint(tail[0]), kHiHalves),
+             perm(__float_as_uint(tail[3]), __float_as_uint(tail[2]), kHiHalves)};
   if constexpr (FP8) {
     // codes of dims 4h .. 4h + 3 sit in word h of each token's load
 #pragma unroll
@@ -341,10 +343,39 @@ __device__ __forceinline__ void pv_tile(const u32x4 (&vraw)[4], const float (&p)
       }
     }
   }
+}
+
+template <bool FP8>
+__device__ __forceinline__ void pv_tile(const u32x4 (&vraw)[4], const float (&p)[4], const float (&vscale)[4],
+                                        SoftmaxState& st) {
+  u32x2 a[8], ph, pl;
+  pv_operands<FP8>(vraw, p, vscale, a, ph, pl);
 #pragma unroll
   for (int j = 0; j < 8; ++j) st.o[j] = mfma_bf16_16x16x16(a[j], ph, st.o[j]);
 #pragma unroll
   for (int j = 0; j < 8; ++j) st.o[j] = mfma_bf16_16x16x16(a[j], pl, st.o[j]);
+}
+
+// Two tiles' O^T += V^T P^T on the 16x16x32 MFMA, which reduces over 32
+// tokens at the cost of one 16x16x16: reduction index 8g + r is token
+// 4g + r of the first tile for r < 4 and of the second for r >= 4, so each
+// lane's operands are its own two tiles' values, concatenated.
+template <bool FP8>
+__device__ __forceinline__ void pv_tiles2(const u32x4 (&v0)[4], const float (&p0)[4], const float (&s0)[4],
+                                          const u32x4 (&v1)[4], const float (&p1)[4], const float (&s1)[4],
+                                          SoftmaxState& st) {
+  u32x2 a0[8], a1[8], ph0, pl0, ph1, pl1;
+  pv_operands<FP8>(v0, p0, s0, a0, ph0, pl0);
+  pv_operands<FP8>(v1, p1, s1, a1, ph1, pl1);
+  const bf16x8 ph = as_bf16x8(u32x4{ph0[0], ph0[1], ph1[0], ph1[1]});
+  const bf16x8 pl = as_bf16x8(u32x4{pl0[0], pl0[1], pl1[0], pl1[1]});
+  bf16x8 a[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a[j] = as_bf16x8(u32x4{a0[j][0], a0[j][1], a1[j][0], a1[j][1]});
+#pragma unroll
+  for (int j = 0; j < 8; ++j) st.o[j] = mfma_bf16_16x16x32(a[j], ph, st.o[j]);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) st.o[j] = mfma_bf16_16x16x32(a[j], pl, st.o[j]);
 }
 
 // One tile of 16 context tokens for 16 heads.
@@ -390,6 +421,83 @@ __device__ __forceinline__ void attend_tile(const QSrc& q, const bf16x8 (&kf)[4]
   for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(lg[r] - st.m);
   st.z += (p[0] + p[1]) + (p[2] + p[3]);
   pv_tile<FP8>(vraw, p, vscale, st);
+}
+
+// NT tiles of 16 context tokens at once for 16 heads: attend_tile's
+// arithmetic with the tiles' S^T = K Q^T products computed as NT independent
+// MFMA chains (interleaved, so the matrix core is not left waiting on one
+// chain's latency) and one online-softmax update over the NT * 16 tokens.
+// PARTS of the query's three exact bf16 parts enter the products: 3 gives
+// fp32-accurate logits; 2 keeps 16 significant bits of the query (logits
+// within ~2^-16 relative), enough where no selection depends on them.
+// Operands per tile as attend_tile; vload(t, vraw, vscale) supplies tile t's
+// V rows and scales after the products are formed (their registers then
+// reuse the K operand's).  nvalid[t] <= 0 masks tile t entirely; at least one
+// token of the NT tiles must exist.
+template <bool FP8, int NT, int PARTS, class QSrc, class VLoad>
+__device__ __forceinline__ void attend_tiles(const QSrc& q, const bf16x8 (&kf)[NT][4],
+                                             const float (&kscale)[NT][4], const int (&nvalid)[NT], int g,
+                                             SoftmaxState& st, VLoad vload) {
+  f32x4 s[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int part = 0; part < PARTS; ++part) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) s[t] = mfma_bf16_16x16x32(kf[t][k], q.get(part, k), s[t]);
+    }
+  }
+  float lg[NT][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      lg[t][r] = (4 * g + r < nvalid[t]) ? s[t][r] * kscale[t][r] : -INFINITY;
+      mx = fmaxf(mx, lg[t][r]);
+    }
+  }
+  // As attend_tile, but the head's maximum over the four lane groups is
+  // formed only when some lane's own maximum calls for a rescale: a head's
+  // maximum exceeds the reference by the slack exactly when one of its lanes'
+  // does, so the outcome is the same and the lane exchanges (LDS round trips)
+  // are skipped on the tiles that do not raise the reference.
+  constexpr float kRescaleSlack = 8.f;  // as in attend_tile
+  if (__any(mx > st.m + kRescaleSlack)) {
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool raise = mx > st.m + kRescaleSlack;
+    const float mn = raise ? mx : st.m;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
+    st.z *= alpha;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) st.o[t] *= alpha;
+    st.m = mn;
+  }
+  float p[NT][4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[t][r] = __builtin_amdgcn_exp2f(lg[t][r] - st.m);
+    st.z += (p[t][0] + p[t][1]) + (p[t][2] + p[t][3]);
+  }
+  // P V over pairs of tiles on the 16x16x32 MFMA; an odd last tile alone
+#pragma unroll
+  for (int t = 0; t + 1 < NT; t += 2) {
+    u32x4 v0[4], v1[4];
+    float s0[4], s1[4];
+    vload(t, v0, s0);
+    vload(t + 1, v1, s1);
+    pv_tiles2<FP8>(v0, p[t], s0, v1, p[t + 1], s1, st);
+  }
+  if constexpr (NT % 2) {
+    u32x4 v[4];
+    float sc[4];
+    vload(NT - 1, v, sc);
+    pv_tile<FP8>(v, p[NT - 1], sc, st);
+  }
 }
 
 // DPP lane moves within a row of 16 lanes (plain VALU, no LDS crossbar).

@@ -165,10 +165,11 @@ struct SparseParams {
   float* ring_ks;
   float* ring_vs;
 };
-constexpr int kSparseFillWorkgroups = 128;  // slice the selection while the grid has fewer workgroups
-// Slices of each (layer, sequence) selection the sparse pass uses (1: no partials, no merge).
-int sparse_slices(int batch, int n_layers);
-// Attention over the selected rows: one launch, plus a merge when sliced.
+// Slices of each sequence's selection the sparse pass cuts (1: no partials,
+// no merge); depends on the batch size only.
+int sparse_slices(int batch);
+// Attention of every sparse layer over the selected rows, each row gathered
+// once for all layers: one launch, plus a merge of the slices when sliced.
 hipError_t launch_sparse_attend(const SparseParams& p, bool fp8, hipStream_t s);
 // Window mode: one sliding-window layer over ring caches of p.budget (<= 1152)
 // rows per sequence, in one unsliced launch that also stores the current rows.

@@ -221,7 +221,7 @@ class MultiDecode:
         return self
 
 
-NOALLOC_SCRATCH_BYTES = 64 << 20
+NOALLOC_SCRATCH_BYTES = 96 << 20
 
 
 def decode_block_noalloc(blk: "DecodeBlock"):
