@@ -170,14 +170,19 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_reuse_kernel(SparsePara
   int32_t praw[kRowsPer];
   int32_t sraw = 0;
   if constexpr (kTwoBuffers) {
-    for (int i = t; i < kSliceRows; i += kSparseThreads) s_pos[i] = sel[i];
-  } else {
+    constexpr int kPer = (kSliceRows + kSparseThreads - 1) / kSparseThreads;
+    int32_t v[kPer];
 #pragma unroll
-    for (int i = 0; i < kRowsPer; ++i) {
-      const int row = row0 + kRowStep * i;
-      praw[i] = row < kRoundRows ? sel[row] : 0;
-    }
-    if (FP8 && t < 2 * kRoundRows) sraw = sel[srow];
+    for (int i = 0; i < kPer; ++i) v[i] = sel[min(t + kSparseThreads * i, kSliceRows - 1)];  // all issued first
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (t + kSparseThreads * i < kSliceRows) s_pos[t + kSparseThreads * i] = v[i];
+  } else {
+    // unconditional loads (a row past the round reads the round's last
+    // entry, unused): a load under a branch costs a round trip of its own
+#pragma unroll
+    for (int i = 0; i < kRowsPer; ++i) praw[i] = sel[min(row0 + kRowStep * i, kRoundRows - 1)];
+    if (FP8) sraw = sel[srow];
   }
   if (count == 0) {  // uniform: an empty sequence has zero outputs
     if (SLICES == 1)
@@ -254,10 +259,9 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_reuse_kernel(SparsePara
 #pragma unroll
     for (int i = 0; i < kQVecs; ++i) {
       const int e = 4 * (t + kSparseThreads * i);  // element of [layer][head][dim]
-      const int layer = e / (kHeads * kDim);
-      qv[i] = layer < nlay ? *reinterpret_cast<const float4*>(qsrc + static_cast<size_t>(layer) * p.batch * kHeads * kDim +
-                                                              e % (kHeads * kDim))
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int layer = min(e / (kHeads * kDim), nlay - 1);  // a layer past the group repeats the last (unused)
+      qv[i] = *reinterpret_cast<const float4*>(qsrc + static_cast<size_t>(layer) * p.batch * kHeads * kDim +
+                                               e % (kHeads * kDim));
     }
   }
   Gather gr;

@@ -903,17 +903,28 @@ __global__ __launch_bounds__(256) void collect_rescore_kernel(SelectParams p) {
   const int tile = j + t * nb;
   const bool valid = 16 * tile < dom;
   const int nv = min(16, dom - 16 * tile);
-  float2 ubf = make_float2(0.f, 0.f);  // (tile's largest upper bound, its max_h F_h)
-  if (valid) ubf = *reinterpret_cast<const float2*>(p.tile_ub + tile_slot(base, b, tile) * 2);
+  // Every load of the prologue is issued before any is used, so their
+  // latencies overlap (one round trip, not one per load): the tile's
+  // (largest upper bound, max_h F_h) (a clamped tile when past the end), the
+  // histogram, the rescoring's query and the heads' (M, Z).
+  const float2 ubf_raw =
+      *reinterpret_cast<const float2*>(p.tile_ub + tile_slot(base, b, valid ? tile : (dom - 1) >> 4) * 2);
   const uint32_t* gh = p.hist0 + static_cast<size_t>(b) * kRadixBins;
-  for (int i = t; i < kRadixBins; i += 256) s_hist[i] = gh[i];
+  uint32_t hv[kRadixBins / 256];
+#pragma unroll
+  for (int i = 0; i < kRadixBins / 256; ++i) hv[i] = gh[t + 256 * i];
+  float4 qa, qc;
+  load_q_lds_raw<FP8>(p.q + static_cast<size_t>(b) * kHeads * kDim, qa, qc);
+  const float2 mz = *reinterpret_cast<const float2*>(p.stats + (static_cast<int64_t>(b) * kHeads + (t & 15)) * 2);
+#pragma unroll
+  for (int i = 0; i < kRadixBins / 256; ++i) s_hist[t + 256 * i] = hv[i];
   if (t == 0) s_cnt = 0;
-  // the rescoring's query operand and (M, Z), loaded while the threshold resolves
-  build_q_lds<FP8>(p.q + static_cast<size_t>(b) * kHeads * kDim, p.qscale, s_q);
+  store_q_lds(qa, qc, p.qscale, s_q);
   if (t < kHeads) {
-    s_mx[t] = p.stats[(static_cast<int64_t>(b) * kHeads + t) * 2];
-    s_iz[t] = 1.f / p.stats[(static_cast<int64_t>(b) * kHeads + t) * 2 + 1];
+    s_mx[t] = mz.x;
+    s_iz[t] = 1.f / mz.y;
   }
+  const float2 ubf = valid ? ubf_raw : make_float2(0.f, 0.f);  // (tile's largest upper bound, its max_h F_h)
   __syncthreads();
   const Resolved r0 = block_resolve<256>(s_hist, kRadixBins, static_cast<uint32_t>(p.top_k), s_scan, &s_res);
   const float thr = __uint_as_float(static_cast<uint32_t>(r0.digit) << 20) * kLowSlack;
