@@ -9,12 +9,15 @@
 // The weights (a few MB) are first transposed into the workspace so that both
 // operands are contiguous along the reduction dim, the layout the MFMA
 // fragments read.  GEMM tiles: 256 rows x 256 columns (two output matrices)
-// per workgroup of eight waves, each wave 128 x 64; k-step 64; LDS double
-// buffering, with the next two k-steps' global loads in flight in registers.
-// A tile this large keeps each CU's operand traffic (about 30 bytes per clock
-// at the MFMA peak) within what its load path delivers; 128 x 128 tiles need
-// twice that.  Workgroups are ordered so the column tiles of one row block
-// run back to back on the same XCD and share its L2.
+// per workgroup of eight waves, each wave 128 x 64; k-steps of 64 (one
+// 128-byte line of every operand row).  Operands go from global memory
+// straight into LDS (no register staging), two k-step buffers: one computed
+// while the next is in flight, with the fragments of the next half step read
+// into registers under the MFMAs of the current one.  A tile this
+// large keeps each CU's operand traffic (about 30 bytes per clock at the MFMA
+// peak) within what its load path delivers; 128 x 128 tiles need twice that.
+// Workgroups are ordered so the column tiles of one row block run back to
+// back on the same XCD and share its L2.
 #include "hs2_device.h"
 #include "hs2_internal.h"
 
@@ -23,10 +26,12 @@ namespace hs2 {
 namespace {
 constexpr int kBM = 256;  // workgroup tile: 256 rows x 256 output columns
 constexpr int kBN = 256;
-constexpr int kBK = 64;   // k-step: two 16x16x32 MFMAs deep
+constexpr int kBK = 64;   // k-step: 128 bytes of each row, two 16x16x32 MFMAs deep
 constexpr int kWM = 128;  // wave tile (8 waves, 2 x 4)
 constexpr int kWN = 64;
-constexpr int kPitch = kBK * 2 + 16;  // bytes per LDS row (padded: 8 rows of a fragment read hit all banks)
+constexpr int kRow = kBK * 2;                  // bytes per LDS row of a k-step (one 128-byte line)
+constexpr int kBufBytes = (kBM + kBN) * kRow;  // one k-step's A and B rows: 64 KB
+constexpr int kBuffers = 2;                    // k-steps in LDS: one computed, one in flight
 }  // namespace
 
 struct WeightPtrs {
@@ -65,10 +70,23 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// LDS position of 16-byte chunk c (0..7) of an operand row r is
+// c ^ swizzle(r).  A fragment read has lanes n = 0..15 on rows r0 + n (r0 a
+// multiple of 16), all at one chunk; unswizzled 128-byte rows put those 16
+// lanes on two bank groups.  Rotating the chunk by (r >> 1) & 7 spreads them
+// over all 16 and measures as fast as a linear read on gfx950 (a
+// ds_read_b128 pattern probe timed against the linear pattern).
+__device__ __forceinline__ int swizzle(int r) { return (r >> 1) & 7; }
+
+typedef __attribute__((address_space(1))) void global_void;
+typedef __attribute__((address_space(3))) void lds_void;
+
 template <bool FP8OUT>
 __global__ __launch_bounds__(512) void bridge_gemm_kernel(BridgeParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][kBM * kPitch];
-  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][kBN * kPitch];
+  // Two k-step buffers of 64 KB (A rows then B rows, 128 bytes each, no
+  // padding: the 16-byte chunks of row r sit at position chunk ^ swizzle(r));
+  // the epilogue stages the outputs in the same room.
+  __shared__ __attribute__((aligned(16))) uint8_t s_raw[kBuffers * kBufBytes];
   __shared__ float s_amax[2][2][kBM];  // E4M3 output: [matrix][half of its columns][row] partial row maxima
 
   // XCD-aware order: workgroup id i runs on XCD i % 8; give the column tiles
@@ -84,47 +102,39 @@ __global__ __launch_bounds__(512) void bridge_gemm_kernel(BridgeParams p) {
   const int64_t m0 = static_cast<int64_t>(mt) * kBM;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int n = lane & 15;
   const int g = lane >> 4;
   const int wm = (wave & 1) * kWM;
   const int wn = (wave >> 1) * kWN;
 
-  // Global -> register staging: each thread moves 4 x 16 B of A and of B per
-  // k-step.  Chunk c = tid + 512 * j: row c / 8, 16-byte column c % 8.
+  // Direct global -> LDS loads: a wave instruction moves 8 rows x 128 bytes
+  // (whole cache lines: a k-step of 64 never leaves half a line for the next
+  // one to fetch again), lane L taking row (L >> 3) of the 8 and LDS position
+  // L & 7, which holds the row's chunk (L & 7) ^ swizzle.  Wave w moves A rows
+  // [32 w, 32 w + 32) and B rows [32 w, 32 w + 32) of each k-step (four
+  // instructions each).
   const uint16_t* a_src[4];
   const uint16_t* b_src[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int c = tid + 512 * j;
-    const int row = c >> 3, col = (c & 7) * 8;
+    const int row = 32 * wave + 8 * j + (lane >> 3);
+    const int chunk = (lane & 7) ^ swizzle(row);
     const int64_t arow = min<int64_t>(m0 + row, p.n_tokens - 1);  // clamp the ragged last block
-    a_src[j] = p.hidden + arow * p.d_model + col;
-    b_src[j] = p.w_t + (static_cast<int64_t>(ct) * kBN + row) * p.d_model + col;
+    a_src[j] = p.hidden + arow * p.d_model + chunk * 8;
+    b_src[j] = p.w_t + (static_cast<int64_t>(ct) * kBN + row) * p.d_model + chunk * 8;
   }
-  // Register slots for the k-steps in flight.  (k-steps past the end re-read
-  // the last one: unconditional loads keep the compiler's count of loads in
-  // flight exact.)
-  struct Slot {
-    u32x4 a[4], b[4];
-  };
   const int k_steps = p.d_model / kBK;
-  auto load_tile = [&](int ks, Slot& r) {
+  auto issue = [&](int ks) {  // k-step ks (clamped: steps past the end re-read the last, unused)
     const int k0 = min(ks, k_steps - 1) * kBK;
+    uint8_t* buf = s_raw + (ks % kBuffers) * kBufBytes;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      r.a[j] = *reinterpret_cast<const u32x4*>(a_src[j] + k0);
-      r.b[j] = *reinterpret_cast<const u32x4*>(b_src[j] + k0);
-    }
-  };
-  auto store_tile = [&](int buf, const Slot& r) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = tid + 512 * j;
-      const int row = c >> 3, colb = (c & 7) * 16;
-      *reinterpret_cast<u32x4*>(&s_a[buf][row * kPitch + colb]) = r.a[j];
-      *reinterpret_cast<u32x4*>(&s_b[buf][row * kPitch + colb]) = r.b[j];
+      __builtin_amdgcn_global_load_lds((global_void*)(a_src[j] + k0), (lds_void*)(buf + (32 * wave + 8 * j) * kRow),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_void*)(b_src[j] + k0),
+                                       (lds_void*)(buf + (kBM + 32 * wave + 8 * j) * kRow), 16, 0, 0);
     }
   };
 
@@ -135,47 +145,95 @@ __global__ __launch_bounds__(512) void bridge_gemm_kernel(BridgeParams p) {
 #pragma unroll
     for (int j = 0; j < kFN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // One k-step of 64, as two MFMA steps of 32: lane (n, g) of fragment i holds
-  // row 16i + n, k = 32 kk + 8g .. + 7.
-  auto compute = [&](int buf) {
+  // Half k-step h of step ks (k = 64 ks + 32 h .. + 31) on 16x16x32 MFMAs:
+  // lane (n, g) of fragment i holds row 16 i + n, chunk 4 h + g.
+  struct Frags {
+    bf16x8 a[kFM], b[kFN];
+  };
+  auto read = [&](int ks, int h, Frags& f) {
+    const uint8_t* buf = s_raw + (ks % kBuffers) * kBufBytes;
+    const int c = 4 * h + g;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 af[kFM], bfr[kFN];
+    for (int i = 0; i < kFM; ++i) {
+      const int row = wm + 16 * i + n;
+      f.a[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + row * kRow + 16 * (c ^ swizzle(row))));
+    }
 #pragma unroll
-      for (int i = 0; i < kFM; ++i)
-        af[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&s_a[buf][(wm + 16 * i + n) * kPitch + kk * 64 + 16 * g]));
-#pragma unroll
-      for (int j = 0; j < kFN; ++j)
-        bfr[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(&s_b[buf][(wn + 16 * j + n) * kPitch + kk * 64 + 16 * g]));
-#pragma unroll
-      for (int i = 0; i < kFM; ++i)
-#pragma unroll
-        for (int j = 0; j < kFN; ++j) acc[i][j] = mfma_bf16_16x16x32(af[i], bfr[j], acc[i][j]);
+    for (int j = 0; j < kFN; ++j) {
+      const int row = wn + 16 * j + n;
+      f.b[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + (kBM + row) * kRow + 16 * (c ^ swizzle(row))));
     }
   };
-  // At the top of k-step ks: LDS buffer ks & 1 holds tile ks and the two
-  // register slots hold tiles ks + 1 and ks + 2 in flight.  After computing
-  // tile ks, tile ks + 1 goes to the other buffer (whose readers finished at
-  // the last barrier) and its slot takes tile ks + 3.  Unrolled by two so
-  // each slot keeps its registers.
-  Slot sa, sb;
-  load_tile(0, sa);
-  load_tile(1, sb);
-  store_tile(0, sa);
-  load_tile(2, sa);
-  __syncthreads();
-  for (int ks = 0;; ks += 2) {
-    compute(0);
-    store_tile(1, sb);
-    __syncthreads();
-    if (ks + 1 >= k_steps) break;
-    load_tile(ks + 3, sb);
-    compute(1);
-    store_tile(0, sa);
-    __syncthreads();
-    if (ks + 2 >= k_steps) break;
-    load_tile(ks + 4, sa);
+  auto mma = [&](const Frags& f) {
+#pragma unroll
+    for (int i = 0; i < kFM; ++i)
+#pragma unroll
+      for (int j = 0; j < kFN; ++j) acc[i][j] = mfma_bf16_16x16x32(f.a[i], f.b[j], acc[i][j]);
+  };
+  // The compiler does not see that an asm wait has completed earlier reads
+  // and would hold the first MFMA until the reads issued after it return; an
+  // empty asm that takes the fragments as operands moves its wait there.
+  auto settle = [&](Frags& f) {
+#pragma unroll
+    for (int i = 0; i < kFM; ++i) asm volatile("" : "+v"(f.a[i]));
+#pragma unroll
+    for (int j = 0; j < kFN; ++j) asm volatile("" : "+v"(f.b[j]));
+  };
+  // Pipeline, one barrier per k-step, in its middle.  The first half of step
+  // ks runs the MFMAs of half 0 (fragments already in registers) while the
+  // reads of half 1 fly.  Then: this thread's loads of step ks + 1 have landed
+  // (vmcnt(0): they are the only ones in flight) and its reads of step ks have
+  // returned (lgkmcnt(0)); after the barrier every thread's loads of step
+  // ks + 1 are visible and no wave reads buffer ks any more, so it takes the
+  // loads of step ks + 2 while half 0 of step ks + 1 is read under the MFMAs
+  // of half 1.  The wait and the barrier share one asm block (a fenced
+  // barrier would also wait for the loads just issued), and sched_barrier(0)
+  // keeps the compiler from sinking the reads back next to their MFMAs.
+  // Steps past the end (k_steps and k_steps + 1) re-read the last k-step and
+  // are never used.
+  static_assert(kBuffers == 2, "the waits below count one k-step of loads in flight");
+  issue(0);
+  issue(1);
+  asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");  // step 0 landed (eight loads per step)
+  Frags f0, f1;
+  read(0, 0, f0);
+  // Within each half the loads and reads are threaded between the MFMAs
+  // (sched_group_barrier: one MFMA, then one load or read), so the MFMA pipe
+  // restarts right after the barrier instead of after their issue.
+  constexpr int kMfma = kFM * kFN, kReads = kFM + kFN;
+  for (int ks = 0; ks < k_steps; ++ks) {
+    settle(f0);
+    __builtin_amdgcn_sched_barrier(0);
+    read(ks, 1, f1);
+    mma(f0);
+#pragma unroll
+    for (int i = 0; i < kReads; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    settle(f1);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(ks + 2);
+    read(ks + 1, 0, f0);
+    mma(f1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global -> LDS load
+    }
+#pragma unroll
+    for (int i = 0; i < kReads; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads - 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");  // the unused loads, before the LDS is reused
+  __syncthreads();
 
   // Epilogue.  Fragment (i, j) holds D[row 4g + e][col n] in lane (n, g);
   // tile column c belongs to output matrix c / 128 (two per workgroup).  The
@@ -189,10 +247,11 @@ __global__ __launch_bounds__(512) void bridge_gemm_kernel(BridgeParams p) {
   //   share the matrix, through LDS.
   constexpr int kElemBytes = FP8OUT ? 1 : 2;
   constexpr int kRowBytes = kDim * kElemBytes;  // staged bytes per row and matrix
-  static_assert(kBM * kRowBytes <= 2 * kBM * kPitch, "one matrix of the tile fits in one operand buffer");
+  constexpr int kStageBytes = kBuffers * kBufBytes / 2;
+  static_assert(kBM * kRowBytes <= kStageBytes, "one matrix of the tile fits in half the k-step buffers");
   const int mat = wn >> 7;         // output matrix of this wave (local: 0 or 1)
   const int half = (wn >> 6) & 1;  // which 64 of its 128 columns
-  uint8_t* stage = mat == 0 ? &s_a[0][0] : &s_b[0][0];
+  uint8_t* stage = s_raw + mat * kStageBytes;
   float scale[kFM][4];
   if constexpr (FP8OUT) {
 #pragma unroll
@@ -246,7 +305,7 @@ __global__ __launch_bounds__(512) void bridge_gemm_kernel(BridgeParams p) {
     const int q = idx % kChunks;
     const int64_t row = m0 + r;
     if (row < p.n_tokens) {
-      const uint8_t* src = (mm == 0 ? &s_a[0][0] : &s_b[0][0]) + r * kRowBytes + 16 * q;
+      const uint8_t* src = s_raw + mm * kStageBytes + r * kRowBytes + 16 * q;
       uint8_t* dst = reinterpret_cast<uint8_t*>(p.out[ct * (kBN / kDim) + mm]) + row * kRowBytes + 16 * q;
       *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
     }
