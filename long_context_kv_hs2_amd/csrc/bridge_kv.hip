@@ -29,9 +29,12 @@ constexpr int kBN = 256;
 constexpr int kBK = 64;   // k-step: 128 bytes of each row, two 16x16x32 MFMAs deep
 constexpr int kWM = 128;  // wave tile (8 waves, 2 x 4)
 constexpr int kWN = 64;
-constexpr int kRow = kBK * 2;                  // bytes per LDS row of a k-step (one 128-byte line)
-constexpr int kBufBytes = (kBM + kBN) * kRow;  // one k-step's A and B rows: 64 KB
-constexpr int kBuffers = 2;                    // k-steps in LDS: one computed, one in flight
+constexpr int kRow = kBK * 2;          // bytes per LDS row of a k-step (one 128-byte line)
+constexpr int kBufBytes = kBM * kRow;  // one k-step of A rows (or of B rows): 32 KB
+static_assert(kBM == kBN, "A and B k-step buffers have one size");
+constexpr int kBuffersA = 3;  // A k-steps in LDS: one computed, two in flight
+constexpr int kBuffersB = 2;  // B k-steps in LDS: one computed, one in flight
+constexpr int kLdsBytes = (kBuffersA + kBuffersB) * kBufBytes;  // 160 KB, the whole LDS of a CU
 }  // namespace
 
 struct WeightPtrs {
@@ -83,11 +86,12 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 template <bool FP8OUT>
 __global__ __launch_bounds__(512) void bridge_gemm_kernel(BridgeParams p) {
-  // Two k-step buffers of 64 KB (A rows then B rows, 128 bytes each, no
-  // padding: the 16-byte chunks of row r sit at position chunk ^ swizzle(r));
-  // the epilogue stages the outputs in the same room.
-  __shared__ __attribute__((aligned(16))) uint8_t s_raw[kBuffers * kBufBytes];
-  __shared__ float s_amax[2][2][kBM];  // E4M3 output: [matrix][half of its columns][row] partial row maxima
+  // Three A and two B k-step buffers of 32 KB (rows of 128 bytes, no padding:
+  // the 16-byte chunks of row r sit at position chunk ^ swizzle(r)); the
+  // epilogue stages the outputs and the E4M3 row maxima in the same room.
+  __shared__ __attribute__((aligned(16))) uint8_t s_raw[kLdsBytes];
+  uint8_t* const s_a = s_raw;
+  uint8_t* const s_b = s_raw + kBuffersA * kBufBytes;
 
   // XCD-aware order: workgroup id i runs on XCD i % 8; give the column tiles
   // of one row block consecutive slots on one XCD, so they share its L2.
@@ -126,16 +130,22 @@ __global__ __launch_bounds__(512) void bridge_gemm_kernel(BridgeParams p) {
     b_src[j] = p.w_t + (static_cast<int64_t>(ct) * kBN + row) * p.d_model + chunk * 8;
   }
   const int k_steps = p.d_model / kBK;
-  auto issue = [&](int ks) {  // k-step ks (clamped: steps past the end re-read the last, unused)
+  // Loads of k-step ks (clamped: steps past the end re-read the last, unused).
+  auto issue_a = [&](int ks) {
     const int k0 = min(ks, k_steps - 1) * kBK;
-    uint8_t* buf = s_raw + (ks % kBuffers) * kBufBytes;
+    uint8_t* buf = s_a + (ks % kBuffersA) * kBufBytes;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 4; ++j)
       __builtin_amdgcn_global_load_lds((global_void*)(a_src[j] + k0), (lds_void*)(buf + (32 * wave + 8 * j) * kRow),
                                        16, 0, 0);
-      __builtin_amdgcn_global_load_lds((global_void*)(b_src[j] + k0),
-                                       (lds_void*)(buf + (kBM + 32 * wave + 8 * j) * kRow), 16, 0, 0);
-    }
+  };
+  auto issue_b = [&](int ks) {
+    const int k0 = min(ks, k_steps - 1) * kBK;
+    uint8_t* buf = s_b + (ks % kBuffersB) * kBufBytes;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_global_load_lds((global_void*)(b_src[j] + k0), (lds_void*)(buf + (32 * wave + 8 * j) * kRow),
+                                       16, 0, 0);
   };
 
   constexpr int kFM = kWM / 16, kFN = kWN / 16;  // 16 x 16 fragments per wave
@@ -151,17 +161,18 @@ __global__ __launch_bounds__(512) void bridge_gemm_kernel(BridgeParams p) {
     bf16x8 a[kFM], b[kFN];
   };
   auto read = [&](int ks, int h, Frags& f) {
-    const uint8_t* buf = s_raw + (ks % kBuffers) * kBufBytes;
+    const uint8_t* abuf = s_a + (ks % kBuffersA) * kBufBytes;
+    const uint8_t* bbuf = s_b + (ks % kBuffersB) * kBufBytes;
     const int c = 4 * h + g;
 #pragma unroll
     for (int i = 0; i < kFM; ++i) {
       const int row = wm + 16 * i + n;
-      f.a[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + row * kRow + 16 * (c ^ swizzle(row))));
+      f.a[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(abuf + row * kRow + 16 * (c ^ swizzle(row))));
     }
 #pragma unroll
     for (int j = 0; j < kFN; ++j) {
       const int row = wn + 16 * j + n;
-      f.b[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + (kBM + row) * kRow + 16 * (c ^ swizzle(row))));
+      f.b[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(bbuf + row * kRow + 16 * (c ^ swizzle(row))));
     }
   };
   auto mma = [&](const Frags& f) {
@@ -170,6 +181,30 @@ __global__ __launch_bounds__(512) void bridge_gemm_kernel(BridgeParams p) {
 #pragma unroll
       for (int j = 0; j < kFN; ++j) acc[i][j] = mfma_bf16_16x16x32(f.a[i], f.b[j], acc[i][j]);
   };
+  // Pipeline, one barrier per k-step, in its middle.  The first half of step
+  // ks runs the MFMAs of half 0 (fragments already in registers) while the
+  // reads of half 1 fly.  Then the middle barrier M(ks): this thread's loads
+  // of step ks + 1 have landed and its reads of step ks have returned; after
+  // the barrier every thread's loads of ks + 1 are visible and no wave reads
+  // the buffers of step ks any more, so they take the B loads of step ks + 2
+  // and the A loads of step ks + 3, while half 0 of step ks + 1 is read under
+  // the MFMAs of half 1.  The A rows (the hidden states, mostly from HBM) are
+  // thus asked for two k-steps ahead, the B rows (the weights, L2-resident)
+  // one.  Loads complete in issue order (four per thread per operand and
+  // step) and at M(ks) the last four issued are A(ks + 2), so vmcnt(4) leaves
+  // exactly those in flight.  The wait and the barrier share one asm block (a
+  // fenced barrier would also wait for the loads in flight); sched_barrier(0)
+  // keeps the compiler from sinking the reads back next to their MFMAs.
+  // Steps past the end re-read the last k-step and are never used.
+  static_assert(kBuffersA == 3 && kBuffersB == 2, "the waits below count this pipeline's loads in flight");
+  issue_b(0);
+  issue_a(0);
+  issue_a(1);
+  issue_b(1);
+  issue_a(2);
+  asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");  // B(0) and A(0) landed
+  Frags f0, f1;
+  read(0, 0, f0);
   // The compiler does not see that an asm wait has completed earlier reads
   // and would hold the first MFMA until the reads issued after it return; an
   // empty asm that takes the fragments as operands moves its wait there.
@@ -179,24 +214,6 @@ __global__ __launch_bounds__(512) void bridge_gemm_kernel(BridgeParams p) {
 #pragma unroll
     for (int j = 0; j < kFN; ++j) asm volatile("" : "+v"(f.b[j]));
   };
-  // Pipeline, one barrier per k-step, in its middle.  The first half of step
-  // ks runs the MFMAs of half 0 (fragments already in registers) while the
-  // reads of half 1 fly.  Then: this thread's loads of step ks + 1 have landed
-  // (vmcnt(0): they are the only ones in flight) and its reads of step ks have
-  // returned (lgkmcnt(0)); after the barrier every thread's loads of step
-  // ks + 1 are visible and no wave reads buffer ks any more, so it takes the
-  // loads of step ks + 2 while half 0 of step ks + 1 is read under the MFMAs
-  // of half 1.  The wait and the barrier share one asm block (a fenced
-  // barrier would also wait for the loads just issued), and sched_barrier(0)
-  // keeps the compiler from sinking the reads back next to their MFMAs.
-  // Steps past the end (k_steps and k_steps + 1) re-read the last k-step and
-  // are never used.
-  static_assert(kBuffers == 2, "the waits below count one k-step of loads in flight");
-  issue(0);
-  issue(1);
-  asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");  // step 0 landed (eight loads per step)
-  Frags f0, f1;
-  read(0, 0, f0);
   // Within each half the loads and reads are threaded between the MFMAs
   // (sched_group_barrier: one MFMA, then one load or read), so the MFMA pipe
   // restarts right after the barrier instead of after their issue.
@@ -213,10 +230,11 @@ __global__ __launch_bounds__(512) void bridge_gemm_kernel(BridgeParams p) {
     }
     __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     settle(f1);
     __builtin_amdgcn_sched_barrier(0);
-    issue(ks + 2);
+    issue_b(ks + 2);
+    issue_a(ks + 3);
     read(ks + 1, 0, f0);
     mma(f1);
 #pragma unroll
@@ -238,8 +256,8 @@ __global__ __launch_bounds__(512) void bridge_gemm_kernel(BridgeParams p) {
   // Epilogue.  Fragment (i, j) holds D[row 4g + e][col n] in lane (n, g);
   // tile column c belongs to output matrix c / 128 (two per workgroup).  The
   // rounded values are staged in LDS (the operand buffers are free: the loop
-  // ended on a barrier), matrix 0 in s_a and matrix 1 in s_b, as [row][128]
-  // elements, and then written out row by row with 16-byte stores.
+  // ended on a barrier), matrix 0 then matrix 1, each as [row][128] elements,
+  // and then written out row by row with 16-byte stores.
   //   bf16: round to nearest even.
   //   E4M3: per row and matrix, scale = (largest |value|) / 448 in fp32 (1 for
   //   an all-zero row), code = E4M3(value / scale); the row maxima are reduced
@@ -247,8 +265,9 @@ __global__ __launch_bounds__(512) void bridge_gemm_kernel(BridgeParams p) {
   //   share the matrix, through LDS.
   constexpr int kElemBytes = FP8OUT ? 1 : 2;
   constexpr int kRowBytes = kDim * kElemBytes;  // staged bytes per row and matrix
-  constexpr int kStageBytes = kBuffers * kBufBytes / 2;
-  static_assert(kBM * kRowBytes <= kStageBytes, "one matrix of the tile fits in half the k-step buffers");
+  constexpr int kStageBytes = kBM * kRowBytes;  // one matrix of the tile
+  static_assert(2 * kStageBytes + sizeof(float) * 2 * 2 * kBM <= kLdsBytes, "staging and row maxima fit in the LDS");
+  float (*s_amax)[2][kBM] = reinterpret_cast<float (*)[2][kBM]>(s_raw + 2 * kStageBytes);  // [matrix][half][row]
   const int mat = wn >> 7;         // output matrix of this wave (local: 0 or 1)
   const int half = (wn >> 6) & 1;  // which 64 of its 128 columns
   uint8_t* stage = s_raw + mat * kStageBytes;
