@@ -246,6 +246,36 @@ hs2_status hs2_bridge_kv_fp8(int64_t n_tokens, int32_t d_model, int32_t head_dim
                              void* const* v_out, float* const* v_scale,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* The bridge projection with its weights packed once per weight set, for a
+ * caller that runs it on many hidden-state batches with the same W_k, W_v
+ * (the pages' prefill computes every bridged layer's K and V from one
+ * hidden state: [ko] "HySparse2가 한 일"; [fr] "Le Prefill s'arrête à
+ * mi-chemin").  hs2_bridge_kv and hs2_bridge_kv_fp8 pack the weights into
+ * their workspace on every call; these entry points split that step off.
+ *
+ * hs2_bridge_pack_weights: writes the 2 * n_bridged matrices w_k[0], w_v[0],
+ * w_k[1], ... (host arrays of device pointers, bf16 [d_model][head_dim],
+ * 16-byte aligned) into packed (device, 256-byte aligned, caller-owned,
+ * >= hs2_bridge_packed_weight_bytes(...) bytes) in the layout the GEMM
+ * reads: [2 * n_bridged * head_dim][d_model], the reduction dimension
+ * contiguous.  Asynchronous on stream.  Same support and errors as
+ * hs2_bridge_kv; a short buffer: HS2_ERR_WORKSPACE_TOO_SMALL.
+ *
+ * hs2_bridge_kv_packed: the projection from packed weights, no workspace.
+ * kv_dtype HS2_KV_BF16: the outputs of hs2_bridge_kv (k_scale and v_scale
+ * unused, may be NULL); HS2_KV_FP8_E4M3: those of hs2_bridge_kv_fp8.  The
+ * results are bit-identical to those entry points'.  packed must hold the
+ * packing of the weights for this d_model and n_bridged; nothing checks
+ * that.                                                                       */
+size_t hs2_bridge_packed_weight_bytes(int32_t d_model, int32_t head_dim, int32_t n_bridged);
+hs2_status hs2_bridge_pack_weights(int32_t d_model, int32_t head_dim, int32_t n_bridged,
+                                   const void* const* w_k, const void* const* w_v,
+                                   void* packed, size_t packed_bytes, void* stream);
+hs2_status hs2_bridge_kv_packed(int64_t n_tokens, int32_t d_model, int32_t head_dim, int32_t n_bridged,
+                                int32_t kv_dtype, const void* hidden, const void* packed,
+                                void* const* k_out, float* const* k_scale,
+                                void* const* v_out, float* const* v_scale, void* stream);
+
 /* Self-Decoder layers at decode.  The model's front half (the Self-Decoder)
  * mixes full-attention and sliding-window layers; in the pages' 49-layer
  * model the first 25 layers hold one full-attention layer, whose input hidden

@@ -659,24 +659,29 @@ size_t hs2_bridge_workspace_bytes(int64_t n_tokens, int32_t d_model, int32_t hea
   return align_up(static_cast<size_t>(2 * n_bridged) * kDim * d_model * sizeof(uint16_t));
 }
 
-// The bridge projection, with bf16 or E4M3 (per-token scales) outputs.
-static hs2_status bridge_run(int64_t n_tokens, int32_t d_model, int32_t head_dim, int32_t n_bridged,
-                             const void* hidden, const void* const* w_k, const void* const* w_v,
-                             void* const* k_out, void* const* v_out, float* const* k_scale, float* const* v_scale,
-                             bool fp8, void* workspace, size_t workspace_bytes, void* stream) {
+// Checks shared by every bridge entry point.
+static hs2_status check_bridge_shape(int64_t n_tokens, int32_t d_model, int32_t head_dim, int32_t n_bridged) {
   if (n_tokens < 0) return fail(HS2_ERR_INVALID_ARGUMENT, "n_tokens < 0");
   if (head_dim != kDim) return fail(HS2_ERR_UNSUPPORTED, "head_dim %d (only 128 is supported)", head_dim);
   if (d_model <= 0 || d_model % 64) return fail(HS2_ERR_UNSUPPORTED, "d_model %d must be a positive multiple of 64", d_model);
   if (n_bridged < 1 || n_bridged > 4) return fail(HS2_ERR_UNSUPPORTED, "n_bridged %d (1..4 supported)", n_bridged);
   if (n_tokens > (int64_t(1) << 31)) return fail(HS2_ERR_UNSUPPORTED, "n_tokens above 2^31");
-  if (!w_k || !w_v || !k_out || !v_out) return fail(HS2_ERR_INVALID_ARGUMENT, "weight/output pointer array is NULL");
+  return HS2_OK;
+}
+
+// Interleaves the per-layer weight and output arrays into the GEMM's column
+// blocks (W_k0, W_v0, W_k1, ...) and checks every pointer.
+static hs2_status bridge_columns(int64_t n_tokens, int32_t n_bridged, const void* const* w_k, const void* const* w_v,
+                                 void* const* k_out, void* const* v_out, float* const* k_scale,
+                                 float* const* v_scale, bool fp8, const uint16_t** ws, void** outs, float** scales) {
+  if ((w_k || w_v) && (!w_k || !w_v)) return fail(HS2_ERR_INVALID_ARGUMENT, "weight pointer array is NULL");
+  if (!k_out || !v_out) return fail(HS2_ERR_INVALID_ARGUMENT, "output pointer array is NULL");
   if (fp8 && (!k_scale || !v_scale)) return fail(HS2_ERR_INVALID_ARGUMENT, "scale pointer array is NULL");
-  const uint16_t* ws[8];
-  void* outs[8];
-  float* scales[8] = {};
   for (int l = 0; l < n_bridged; ++l) {
-    ws[2 * l] = static_cast<const uint16_t*>(w_k[l]);
-    ws[2 * l + 1] = static_cast<const uint16_t*>(w_v[l]);
+    if (w_k) {
+      ws[2 * l] = static_cast<const uint16_t*>(w_k[l]);
+      ws[2 * l + 1] = static_cast<const uint16_t*>(w_v[l]);
+    }
     outs[2 * l] = k_out[l];
     outs[2 * l + 1] = v_out[l];
     if (fp8) {
@@ -685,18 +690,15 @@ static hs2_status bridge_run(int64_t n_tokens, int32_t d_model, int32_t head_dim
     }
   }
   for (int i = 0; i < 2 * n_bridged; ++i) {
-    HS2_TRY(check_ptr(ws[i], true, 16, "w_k/w_v entry"));
+    if (w_k) HS2_TRY(check_ptr(ws[i], true, 16, "w_k/w_v entry"));
     HS2_TRY(check_ptr(outs[i], n_tokens > 0, 16, "k_out/v_out entry"));
     if (fp8) HS2_TRY(check_ptr(scales[i], n_tokens > 0, 4, "k_scale/v_scale entry"));
   }
-  HS2_TRY(check_ptr(hidden, n_tokens > 0, 16, "hidden"));
-  const size_t need = hs2_bridge_workspace_bytes(n_tokens, d_model, head_dim, n_bridged);
-  if (workspace_bytes < need) return fail(HS2_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
-  HS2_TRY(check_ptr(workspace, true, 256, "workspace"));
-  if (n_tokens == 0) return HS2_OK;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  uint16_t* w_t = static_cast<uint16_t*>(workspace);
-  HS2_HIP(launch_bridge_transpose_w(ws, 2 * n_bridged, d_model, w_t, s), "bridge weight transpose");
+  return HS2_OK;
+}
+
+static hipError_t bridge_gemm(int64_t n_tokens, int32_t d_model, int32_t n_bridged, const void* hidden,
+                              const uint16_t* w_t, void* const* outs, float* const* scales, bool fp8, hipStream_t s) {
   BridgeParams p;
   p.n_tokens = n_tokens;
   p.d_model = d_model;
@@ -708,7 +710,29 @@ static hs2_status bridge_run(int64_t n_tokens, int32_t d_model, int32_t head_dim
     p.out[i] = i < 2 * n_bridged ? outs[i] : nullptr;
     p.scale[i] = i < 2 * n_bridged ? scales[i] : nullptr;
   }
-  HS2_HIP(launch_bridge_gemm(p, s), "bridge GEMM");
+  return launch_bridge_gemm(p, s);
+}
+
+// The bridge projection, with bf16 or E4M3 (per-token scales) outputs.
+static hs2_status bridge_run(int64_t n_tokens, int32_t d_model, int32_t head_dim, int32_t n_bridged,
+                             const void* hidden, const void* const* w_k, const void* const* w_v,
+                             void* const* k_out, void* const* v_out, float* const* k_scale, float* const* v_scale,
+                             bool fp8, void* workspace, size_t workspace_bytes, void* stream) {
+  HS2_TRY(check_bridge_shape(n_tokens, d_model, head_dim, n_bridged));
+  if (!w_k || !w_v) return fail(HS2_ERR_INVALID_ARGUMENT, "weight pointer array is NULL");
+  const uint16_t* ws[8] = {};
+  void* outs[8] = {};
+  float* scales[8] = {};
+  HS2_TRY(bridge_columns(n_tokens, n_bridged, w_k, w_v, k_out, v_out, k_scale, v_scale, fp8, ws, outs, scales));
+  HS2_TRY(check_ptr(hidden, n_tokens > 0, 16, "hidden"));
+  const size_t need = hs2_bridge_workspace_bytes(n_tokens, d_model, head_dim, n_bridged);
+  if (workspace_bytes < need) return fail(HS2_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  HS2_TRY(check_ptr(workspace, true, 256, "workspace"));
+  if (n_tokens == 0) return HS2_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* w_t = static_cast<uint16_t*>(workspace);
+  HS2_HIP(launch_bridge_transpose_w(ws, 2 * n_bridged, d_model, w_t, s), "bridge weight transpose");
+  HS2_HIP(bridge_gemm(n_tokens, d_model, n_bridged, hidden, w_t, outs, scales, fp8, s), "bridge GEMM");
   return HS2_OK;
 }
 
@@ -725,6 +749,48 @@ hs2_status hs2_bridge_kv_fp8(int64_t n_tokens, int32_t d_model, int32_t head_dim
                              size_t workspace_bytes, void* stream) {
   return bridge_run(n_tokens, d_model, head_dim, n_bridged, hidden, w_k, w_v, k_out, v_out, k_scale, v_scale, true,
                     workspace, workspace_bytes, stream);
+}
+
+size_t hs2_bridge_packed_weight_bytes(int32_t d_model, int32_t head_dim, int32_t n_bridged) {
+  return hs2_bridge_workspace_bytes(0, d_model, head_dim, n_bridged);
+}
+
+hs2_status hs2_bridge_pack_weights(int32_t d_model, int32_t head_dim, int32_t n_bridged, const void* const* w_k,
+                                   const void* const* w_v, void* packed, size_t packed_bytes, void* stream) {
+  HS2_TRY(check_bridge_shape(0, d_model, head_dim, n_bridged));
+  if (!w_k || !w_v) return fail(HS2_ERR_INVALID_ARGUMENT, "weight pointer array is NULL");
+  const uint16_t* ws[8] = {};
+  for (int l = 0; l < n_bridged; ++l) {
+    ws[2 * l] = static_cast<const uint16_t*>(w_k[l]);
+    ws[2 * l + 1] = static_cast<const uint16_t*>(w_v[l]);
+  }
+  for (int i = 0; i < 2 * n_bridged; ++i) HS2_TRY(check_ptr(ws[i], true, 16, "w_k/w_v entry"));
+  const size_t need = hs2_bridge_packed_weight_bytes(d_model, head_dim, n_bridged);
+  if (packed_bytes < need) return fail(HS2_ERR_WORKSPACE_TOO_SMALL, "packed buffer %zu bytes < %zu needed", packed_bytes, need);
+  HS2_TRY(check_ptr(packed, true, 256, "packed"));
+  HS2_HIP(launch_bridge_transpose_w(ws, 2 * n_bridged, d_model, static_cast<uint16_t*>(packed),
+                                    static_cast<hipStream_t>(stream)),
+          "bridge weight packing");
+  return HS2_OK;
+}
+
+hs2_status hs2_bridge_kv_packed(int64_t n_tokens, int32_t d_model, int32_t head_dim, int32_t n_bridged,
+                                int32_t kv_dtype, const void* hidden, const void* packed, void* const* k_out,
+                                float* const* k_scale, void* const* v_out, float* const* v_scale, void* stream) {
+  HS2_TRY(check_bridge_shape(n_tokens, d_model, head_dim, n_bridged));
+  if (kv_dtype != HS2_KV_BF16 && kv_dtype != HS2_KV_FP8_E4M3) return fail(HS2_ERR_UNSUPPORTED, "kv_dtype %d", kv_dtype);
+  const bool fp8 = kv_dtype == HS2_KV_FP8_E4M3;
+  const uint16_t* ws[8] = {};
+  void* outs[8] = {};
+  float* scales[8] = {};
+  HS2_TRY(bridge_columns(n_tokens, n_bridged, nullptr, nullptr, k_out, v_out, k_scale, v_scale, fp8, ws, outs, scales));
+  HS2_TRY(check_ptr(hidden, n_tokens > 0, 16, "hidden"));
+  HS2_TRY(check_ptr(packed, true, 256, "packed"));
+  if (n_tokens == 0) return HS2_OK;
+  HS2_HIP(bridge_gemm(n_tokens, d_model, n_bridged, hidden, static_cast<const uint16_t*>(packed), outs, scales, fp8,
+                      static_cast<hipStream_t>(stream)),
+          "bridge GEMM");
+  return HS2_OK;
 }
 
 size_t hs2_bridge_append_workspace_bytes(int32_t batch, int32_t d_model, int32_t head_dim, int32_t n_bridged) {

@@ -26,6 +26,7 @@ STAGE_NAMES = ("full_partial", "full_merge", "score_select", "sparse")
 EXPORTED = (
     "hs2_decode_workspace_bytes", "hs2_decode_score_workspace_bytes", "hs2_decode_block", "hs2_decode_block_noalloc", "hs2_full_decode_score", "hs2_topk_select", "hs2_block_select",
     "hs2_sparse_decode", "hs2_bridge_workspace_bytes", "hs2_bridge_kv", "hs2_bridge_kv_fp8",
+    "hs2_bridge_packed_weight_bytes", "hs2_bridge_pack_weights", "hs2_bridge_kv_packed",
     "hs2_bridge_append_workspace_bytes", "hs2_bridge_append", "hs2_full_decode", "hs2_swa_decode",
     "hs2_decode_multi_workspace_bytes", "hs2_decode_multi", "hs2_stage_timing_enable",
     "hs2_stage_timing_read", "hs2_stage_timing_read_calls", "hs2_status_string", "hs2_last_error_message",
@@ -89,6 +90,13 @@ def load(path: str = LIB_PATH):
                                       ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
                                       vp, sz, vp]
     lib.hs2_bridge_kv_fp8.restype = ctypes.c_int
+    lib.hs2_bridge_packed_weight_bytes.argtypes = [i32, i32, i32]
+    lib.hs2_bridge_packed_weight_bytes.restype = sz
+    lib.hs2_bridge_pack_weights.argtypes = [i32, i32, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, sz, vp]
+    lib.hs2_bridge_pack_weights.restype = ctypes.c_int
+    lib.hs2_bridge_kv_packed.argtypes = [i64, i32, i32, i32, i32, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                         ctypes.POINTER(vp), ctypes.POINTER(vp), vp]
+    lib.hs2_bridge_kv_packed.restype = ctypes.c_int
     lib.hs2_bridge_append_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.hs2_bridge_append_workspace_bytes.restype = sz
     pp = ctypes.POINTER(vp)
@@ -380,6 +388,40 @@ def bridge_kv_fp8(hidden, w_k, w_v, k_out=None, k_sc=None, v_out=None, v_sc=None
                                    arr(*[o.data_ptr() for o in k_sc]), arr(*[o.data_ptr() for o in v_out]),
                                    arr(*[o.data_ptr() for o in v_sc]), _ptr(ws), ws.numel(), _stream()))
     return k_out, k_sc, v_out, v_sc
+
+
+def bridge_pack_weights(w_k, w_v, packed=None):
+    """Pack the bridge weights once (uint8 device buffer, allocated when not
+    given) for bridge_kv_packed."""
+    dev = w_k[0].device
+    d_model = w_k[0].shape[0]
+    n = len(w_k)
+    need = load().hs2_bridge_packed_weight_bytes(d_model, 128, n)
+    packed = _workspace(need, dev, packed)
+    arr = ctypes.c_void_p * n
+    check(load().hs2_bridge_pack_weights(d_model, 128, n, arr(*[w.data_ptr() for w in w_k]),
+                                         arr(*[w.data_ptr() for w in w_v]), _ptr(packed), packed.numel(), _stream()))
+    return packed
+
+
+def bridge_kv_packed(hidden, packed, n_bridged, k_out=None, v_out=None, k_sc=None, v_sc=None, fp8=False):
+    """The bridge projection from packed weights: (k_out, v_out) as bridge_kv,
+    or (k_codes, k_scales, v_codes, v_scales) as bridge_kv_fp8 when fp8."""
+    dev = hidden.device
+    t, d_model = hidden.shape
+    n = n_bridged
+    new = lambda shape, dt: [torch.empty(shape, dtype=dt, device=dev) for _ in range(n)]
+    code = torch.uint8 if fp8 else torch.bfloat16
+    k_out = new((t, 128), code) if k_out is None else k_out
+    v_out = new((t, 128), code) if v_out is None else v_out
+    if fp8:
+        k_sc = new((t,), torch.float32) if k_sc is None else k_sc
+        v_sc = new((t,), torch.float32) if v_sc is None else v_sc
+    arr = ctypes.c_void_p * n
+    ptrs = lambda ts: arr(*[x.data_ptr() for x in ts]) if ts is not None else None
+    check(load().hs2_bridge_kv_packed(t, d_model, 128, n, KV_FP8_E4M3 if fp8 else KV_BF16, _ptr(hidden), _ptr(packed),
+                                      ptrs(k_out), ptrs(k_sc), ptrs(v_out), ptrs(v_sc), _stream()))
+    return (k_out, k_sc, v_out, v_sc) if fp8 else (k_out, v_out)
 
 
 def bridge_append(seq_offsets, hidden, w_k, w_v, k_cache, v_cache, k_scale=None, v_scale=None, workspace=None):

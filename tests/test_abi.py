@@ -153,6 +153,33 @@ def test_bridge_validation():
     assert lib.hs2_bridge_kv(10, 4096, 128, 1, FAKE, one, one, None, one, FAKE, 1 << 30, None) == INVALID
 
 
+def test_bridge_packed_validation():
+    # Pack-once entry points: shape, pointer and size checks before any HIP call.
+    lib = hs2.load()
+    arr = ctypes.c_void_p * 1
+    one = arr(FAKE)
+    need = lib.hs2_bridge_packed_weight_bytes(4096, 128, 3)
+    assert need == 6 * 128 * 4096 * 2
+    assert lib.hs2_bridge_packed_weight_bytes(100, 128, 3) == 0
+    pack = lib.hs2_bridge_pack_weights
+    assert pack(4096, 64, 1, one, one, FAKE, 1 << 30, None) == UNSUPPORTED
+    assert pack(4000, 128, 1, one, one, FAKE, 1 << 30, None) == UNSUPPORTED
+    assert pack(4096, 128, 5, one, one, FAKE, 1 << 30, None) == UNSUPPORTED
+    assert pack(4096, 128, 1, None, one, FAKE, 1 << 30, None) == INVALID
+    assert pack(4096, 128, 1, one, arr(None), FAKE, 1 << 30, None) == INVALID
+    assert pack(4096, 128, 1, one, one, FAKE, 100, None) == SMALL_WS
+    assert pack(4096, 128, 1, one, one, FAKE + 16, 1 << 30, None) == INVALID  # packed not 256-byte aligned
+    run = lib.hs2_bridge_kv_packed
+    assert run(10, 4096, 128, 1, 7, FAKE, FAKE, one, None, one, None, None) == UNSUPPORTED  # kv_dtype
+    assert run(10, 4096, 64, 1, hs2.KV_BF16, FAKE, FAKE, one, None, one, None, None) == UNSUPPORTED
+    assert run(-1, 4096, 128, 1, hs2.KV_BF16, FAKE, FAKE, one, None, one, None, None) == INVALID
+    assert run(10, 4096, 128, 1, hs2.KV_BF16, None, FAKE, one, None, one, None, None) == INVALID
+    assert run(10, 4096, 128, 1, hs2.KV_BF16, FAKE, None, one, None, one, None, None) == INVALID
+    assert run(10, 4096, 128, 1, hs2.KV_BF16, FAKE, FAKE, None, None, one, None, None) == INVALID
+    assert run(10, 4096, 128, 1, hs2.KV_FP8_E4M3, FAKE, FAKE, one, None, one, one, None) == INVALID  # scales
+    assert run(10, 4096, 128, 1, hs2.KV_FP8_E4M3, FAKE, FAKE, one, arr(FAKE + 2), one, one, None) == INVALID
+
+
 def test_bridge_append_validation():
     lib = hs2.load()
     one = (ctypes.c_void_p * 1)(FAKE)

@@ -49,6 +49,27 @@ def test_bridge_one_hot_weights_copy_columns():
     np.testing.assert_array_equal(got, br["h"][:, cols])
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_bridge_packed_weights_match_per_call_packing(fp8):
+    # Weights packed once, then two hidden-state batches of different sizes
+    # (a ragged last row block): bit-identical to the per-call entry points.
+    d_model, n_bridged = 512, 3
+    br = inputs.make_bridge(tokens=3000, d_model=d_model, n_bridged=n_bridged, seed=77)
+    wk = [to_dev(w) for w in br["w_k"]]
+    wv = [to_dev(w) for w in br["w_v"]]
+    packed = hs2.bridge_pack_weights(wk, wv)
+    for tokens in (3000, 257):
+        print(f"case: bridge packed fp8={fp8} T={tokens}", flush=True)
+        h = to_dev(br["h"][:tokens])
+        got = hs2.bridge_kv_packed(h, packed, n_bridged, fp8=fp8)
+        want = hs2.bridge_kv_fp8(h, wk, wv) if fp8 else hs2.bridge_kv(h, wk, wv)
+        torch.cuda.synchronize()
+        for g_list, w_list in zip(got, want):
+            for g, w in zip(g_list, w_list):
+                assert torch.equal(g.view(torch.uint8) if g.dtype != torch.float32 else g.view(torch.int32),
+                                   w.view(torch.uint8) if w.dtype != torch.float32 else w.view(torch.int32))
+
+
 @pytest.mark.parametrize("tokens,d_model,n_bridged", [(1000, 256, 2), (128, 64, 1), (1, 4096, 3), (5000, 4096, 4)])
 def test_bridge_fp8_small_shapes(tokens, d_model, n_bridged):
     print(f"case: bridge fp8 T={tokens} d_model={d_model} n_bridged={n_bridged}", flush=True)
