@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhs2.so")
-SOURCES = ["hs2_api.hip", "full_decode.hip", "merge.hip", "topk_select.hip", "sparse_decode.hip", "bridge_kv.hip", "block_select.hip", "bridge_append.hip", "multi_decode.hip"]
+SOURCES = ["hs2_api.hip", "full_decode.hip", "merge.hip", "topk_select.hip", "sparse_decode.hip", "bridge_kv.hip", "block_select.hip", "bridge_append.hip", "multi_decode.hip", "full_multi.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -78,11 +78,13 @@ struct DecodeLayout {
 // with_spill: room for the score path's logits ([N][16] fp32, 64 bytes a
 // token), only for calls that return per-token scores.  It comes last, so the
 // layout without it is a prefix of the layout with it.
-DecodeLayout decode_layout(const hs2_decode_desc& d, bool with_spill) {
+// chunk: the full pass's chunk when another batch sets it (multi-token
+// decode: the real batch's), else 0 for this batch's own.
+DecodeLayout decode_layout(const hs2_decode_desc& d, bool with_spill, int chunk = 0) {
   DecodeLayout L;
   const size_t B = static_cast<size_t>(d.batch);
   const size_t N = static_cast<size_t>(d.total_tokens);
-  L.chunk = choose_chunk(d.total_tokens, d.max_context, d.batch, d.kv_dtype == HS2_KV_FP8_E4M3);
+  L.chunk = chunk > 0 ? chunk : choose_chunk(d.total_tokens, d.max_context, d.batch, d.kv_dtype == HS2_KV_FP8_E4M3);
   L.chunks_per_seq = static_cast<int>((d.max_context + L.chunk - 1) / L.chunk);
   if (L.chunks_per_seq < 1) L.chunks_per_seq = 1;
   size_t off = 0;
@@ -240,6 +242,7 @@ struct DecodeArgs {
   void* ws;
   hipStream_t stream;
   const int64_t* kv_start = nullptr;  // multi-token decode: real first K/V row of each virtual sequence
+  const MultiFullParams* multi = nullptr;  // multi-token decode: the shared-stream full pass (real batch)
 };
 
 FullParams full_params(const DecodeArgs& a, const DecodeLayout& L) {
@@ -309,8 +312,27 @@ hs2_status run_full(const DecodeArgs& a, const DecodeLayout& L, int mode, const 
   const bool bound_mode = mode == kFullBound;
   const hs2_decode_desc& d = *a.d;
   const FullParams fp = full_params(a, L);
-  HS2_HIP(launch_full_partial(fp, d.batch, d.kv_dtype == HS2_KV_FP8_E4M3, mode, a.stream),
-          "full-attention partial pass");
+  if (a.multi && bound_mode) {
+    // Multi-token decode: the tokens of a sequence share its K/V stream, in
+    // groups of kMultiQ tokens (one launch per group).
+    MultiFullParams m = *a.multi;
+    const FullParams real = m.f;
+    m.f = fp;
+    m.f.seq_offsets = real.seq_offsets;
+    m.f.batch = real.batch;
+    m.f.total_tokens = real.total_tokens;
+    m.f.max_context = real.max_context;
+    m.f.kv_start = nullptr;
+    m.fp8 = d.kv_dtype == HS2_KV_FP8_E4M3;
+    for (int t = 0; t < m.n_query; t += kMultiQ) {
+      m.t_first = t;
+      m.nq = std::min(kMultiQ, m.n_query - t);
+      HS2_HIP(launch_full_multi(m, a.stream), "multi-token full-attention pass");
+    }
+  } else {
+    HS2_HIP(launch_full_partial(fp, d.batch, d.kv_dtype == HS2_KV_FP8_E4M3, mode, a.stream),
+            "full-attention partial pass");
+  }
   HS2_TRY(mark(rec, 1, a.stream));
   MergeParams mp;
   mp.seq_offsets = a.offs;
@@ -506,12 +528,19 @@ static hs2_decode_desc multi_desc(const hs2_decode_desc& d, int32_t n_query) {
   return v;
 }
 
+// The full pass of multi-token decode runs on the real batch (its tokens
+// share each sequence's K/V stream), with the real batch's chunk.
+static int multi_chunk(const hs2_decode_desc& d) {
+  return choose_chunk(d.total_tokens, d.max_context, d.batch, d.kv_dtype == HS2_KV_FP8_E4M3);
+}
+
 size_t hs2_decode_multi_workspace_bytes(const hs2_decode_desc* desc, int32_t n_query) {
   if (check_desc(desc) != HS2_OK || n_query < 1 || n_query > kMaxQueryTokens) return 0;
   const hs2_decode_desc v = multi_desc(*desc, n_query);
   if (check_desc(&v) != HS2_OK) return 0;
   const size_t n = static_cast<size_t>(v.batch);
-  return align_up(decode_layout(v, false).total) + align_up((n + 1) * sizeof(int64_t)) + align_up(n * sizeof(int64_t));
+  return align_up(decode_layout(v, false, multi_chunk(*desc)).total) + align_up((n + 1) * sizeof(int64_t)) +
+         align_up(n * sizeof(int64_t));
 }
 
 hs2_status hs2_decode_multi(const hs2_decode_desc* desc, int32_t n_query, const int64_t* seq_offsets,
@@ -540,7 +569,7 @@ hs2_status hs2_decode_multi(const hs2_decode_desc* desc, int32_t n_query, const 
   if (workspace_bytes < need) return fail(HS2_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   HS2_TRY(check_ptr(workspace, true, 256, "workspace"));
   if (!any) return HS2_OK;
-  const DecodeLayout L = decode_layout(v, false);
+  const DecodeLayout L = decode_layout(v, false, multi_chunk(d));
   const size_t n = static_cast<size_t>(v.batch);
   MultiParams mp{};
   mp.seq_offsets = seq_offsets;
@@ -551,8 +580,15 @@ hs2_status hs2_decode_multi(const hs2_decode_desc* desc, int32_t n_query, const 
   mp.voffs = reinterpret_cast<int64_t*>(ws_at(workspace, align_up(L.total)));
   mp.kv_start = reinterpret_cast<int64_t*>(ws_at(workspace, align_up(L.total) + align_up((n + 1) * sizeof(int64_t))));
   HS2_HIP(launch_multi_prep(mp, static_cast<hipStream_t>(stream)), "multi-token offsets");
+  MultiFullParams mf{};
+  mf.f.seq_offsets = seq_offsets;
+  mf.f.batch = d.batch;
+  mf.f.total_tokens = d.total_tokens;
+  mf.f.max_context = d.max_context;
+  mf.voffs = mp.voffs;
+  mf.n_query = n_query;
   DecodeArgs a{&v, mp.voffs, k_cache, v_cache, k_scale, v_scale, q_full, q_sparse, o_full, o_sparse,
-               sel_idx, sel_count, nullptr, workspace, static_cast<hipStream_t>(stream), mp.kv_start};
+               sel_idx, sel_count, nullptr, workspace, static_cast<hipStream_t>(stream), mp.kv_start, &mf};
   return run_block(a, L);
 }
 

@@ -302,9 +302,10 @@ __device__ __forceinline__ void softmax_init(SoftmaxState& st) {
 // Operands of O^T += V^T P^T for one tile: ph / pl the bf16 head and tail
 // of the lane's four weights (tokens 4g .. 4g + 3), a[j] the lane's V values
 // of dim 8n + j for those tokens (MFMA j's A operand, row n).
+// The P operand of a tile's P.V (p[r]: weight of token 4g + r, times its V
+// scale for E4M3): bf16 head ph and exact bf16 tail pl.
 template <bool FP8>
-__device__ __forceinline__ void pv_operands(const u32x4 (&vraw)[4], const float (&p)[4], const float (&vscale)[4],
-                                            u32x2 (&a)[8], u32x2& ph, u32x2& pl) {
+__device__ __forceinline__ void pv_p_operand(const float (&p)[4], const float (&vscale)[4], u32x2& ph, u32x2& pl) {
   float w[4], tail[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -315,6 +316,12 @@ __device__ __forceinline__ void pv_operands(const u32x4 (&vraw)[4], const float 
              perm(__float_as_uint(w[3]), __float_as_uint(w[2]), kHiHalves)};
   pl = u32x2{perm(__float_as_uint(tail[1]), __float_as_uint(tail[0]), kHiHalves),
              perm(__float_as_uint(tail[3]), __float_as_uint(tail[2]), kHiHalves)};
+}
+
+// The V operand of a tile's P.V: a[j] holds dims 16 j' .. of the tile's V^T
+// in the 16x16x16 A layout (one query's weights or several queries' share it).
+template <bool FP8>
+__device__ __forceinline__ void pv_v_operand(const u32x4 (&vraw)[4], u32x2 (&a)[8]) {
   if constexpr (FP8) {
     // codes of dims 4h .. 4h + 3 sit in word h of each token's load
 #pragma unroll
@@ -343,6 +350,13 @@ __device__ __forceinline__ void pv_operands(const u32x4 (&vraw)[4], const float 
       }
     }
   }
+}
+
+template <bool FP8>
+__device__ __forceinline__ void pv_operands(const u32x4 (&vraw)[4], const float (&p)[4], const float (&vscale)[4],
+                                            u32x2 (&a)[8], u32x2& ph, u32x2& pl) {
+  pv_p_operand<FP8>(p, vscale, ph, pl);
+  pv_v_operand<FP8>(vraw, a);
 }
 
 template <bool FP8>
@@ -378,25 +392,14 @@ __device__ __forceinline__ void pv_tiles2(const u32x4 (&v0)[4], const float (&p0
   for (int j = 0; j < 8; ++j) st.o[j] = mfma_bf16_16x16x32(a[j], pl, st.o[j]);
 }
 
-// One tile of 16 context tokens for 16 heads.
-//  kf[s]: K operand, lane (n, g): token n, dims kdim0(s, g) + i (bf16)
-//  vraw[r]: V values of token 4g + r, dims 8n .. 8n + 7, lane (n, g): eight
-//           bf16 (16 bytes) or eight E4M3 codes (first 8 bytes)
-//  kscale[r], vscale[r]: per-token scales of token 4g + r (1 for bf16)
-//  nvalid: tokens of the tile that exist (1..16); others are masked out
-// Returns the log2-domain logits of tokens 4g + r for head n in lg[r]
-// (-inf where masked) and p[r] = exp2(lg[r] - st.m), st.m being the head's
-// reference max after this tile (within kRescaleSlack of the true running max).
-template <bool FP8, class QSrc>
-__device__ __forceinline__ void attend_tile(const QSrc& q, const bf16x8 (&kf)[4], const u32x4 (&vraw)[4],
-                                            const float (&kscale)[4], const float (&vscale)[4], int nvalid,
-                                            int g, SoftmaxState& st, float (&lg)[4], float (&p)[4]) {
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int part = 0; part < 3; ++part) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) s = mfma_bf16_16x16x32(kf[k], q.get(part, k), s);
-  }
+// The second half of attend_tile (below): the online-softmax update and P.V
+// from the tile's S^T = K Q^T in s (lane (n, g): head n, tokens 4g + r).  A
+// caller with several queries per tile forms their products as interleaved
+// MFMA chains and then calls this once per query.
+template <bool FP8>
+__device__ __forceinline__ void tile_update(const f32x4& s, const u32x4 (&vraw)[4], const float (&kscale)[4],
+                                            const float (&vscale)[4], int nvalid, int g, SoftmaxState& st,
+                                            float (&lg)[4], float (&p)[4]) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) lg[r] = (4 * g + r < nvalid) ? s[r] * kscale[r] : -INFINITY;
   float mx = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
@@ -421,6 +424,28 @@ __device__ __forceinline__ void attend_tile(const QSrc& q, const bf16x8 (&kf)[4]
   for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(lg[r] - st.m);
   st.z += (p[0] + p[1]) + (p[2] + p[3]);
   pv_tile<FP8>(vraw, p, vscale, st);
+}
+
+// One tile of 16 context tokens for 16 heads.
+//  kf[s]: K operand, lane (n, g): token n, dims kdim0(s, g) + i (bf16)
+//  vraw[r]: V values of token 4g + r, dims 8n .. 8n + 7, lane (n, g): eight
+//           bf16 (16 bytes) or eight E4M3 codes (first 8 bytes)
+//  kscale[r], vscale[r]: per-token scales of token 4g + r (1 for bf16)
+//  nvalid: tokens of the tile that exist (1..16); others are masked out
+// Returns the log2-domain logits of tokens 4g + r for head n in lg[r]
+// (-inf where masked) and p[r] = exp2(lg[r] - st.m), st.m being the head's
+// reference max after this tile (within kRescaleSlack of the true running max).
+template <bool FP8, class QSrc>
+__device__ __forceinline__ void attend_tile(const QSrc& q, const bf16x8 (&kf)[4], const u32x4 (&vraw)[4],
+                                            const float (&kscale)[4], const float (&vscale)[4], int nvalid,
+                                            int g, SoftmaxState& st, float (&lg)[4], float (&p)[4]) {
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int part = 0; part < 3; ++part) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s = mfma_bf16_16x16x32(kf[k], q.get(part, k), s);
+  }
+  tile_update<FP8>(s, vraw, kscale, vscale, nvalid, g, st, lg, p);
 }
 
 // NT tiles of 16 context tokens at once for 16 heads: attend_tile's

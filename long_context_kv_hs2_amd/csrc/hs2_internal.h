@@ -224,5 +224,20 @@ struct MultiParams {
   int64_t* kv_start;           // [B * T] real first row of each virtual sequence
 };
 hipError_t launch_multi_prep(const MultiParams& p, hipStream_t s);
+// The bound-mode full pass for a group of up to kMultiQ of the T tokens of
+// every sequence, reading each K/V row once for the group.  f holds the real
+// batch (seq_offsets, batch, total_tokens, max_context, k, v, scales) and the
+// virtual batch's outputs (q [B T][16][128], partials, pstats, shat,
+// tile_stats, hist0, counters, chunks_per_seq); f.chunk is the real batch's.
+constexpr int kMultiQ = 4;
+struct MultiFullParams {
+  FullParams f;
+  const int64_t* voffs;  // [B T + 1] virtual offsets (multi_prep_kernel)
+  int n_query;           // T
+  int t_first;           // the group's first token
+  int nq;                // tokens in the group, 1..kMultiQ
+  int fp8;
+};
+hipError_t launch_full_multi(const MultiFullParams& p, hipStream_t s);
 
 }  // namespace hs2
