@@ -418,7 +418,7 @@ def bench_multi(args, torch, hs2, inputs, dev):
                    "context_tokens": n_tokens, "kv_cache": kv, "n_sparse_layers": n_s},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "full_partial_kernel over the B x T causal prefixes", "alg_bytes_per_launch": alg_bytes,
+                     "kernel": "full_multi_kernel (the B x T causal prefixes, each K/V row read once per group of 4 tokens)", "alg_bytes_per_launch": alg_bytes,
                      "mean_launch_ms": k1_ms, "launch_ms": pct(k1)},
         "stages_ms_percentiles": stage_pct,
         "device": device_info(torch),
