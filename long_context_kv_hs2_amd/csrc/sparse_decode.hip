@@ -9,7 +9,7 @@
 //
 // Sparse layers (sparse_reuse_kernel): one workgroup of eight waves per
 // (sequence, slice of the selection).  The workgroup gathers its slice's K
-// and V rows from HBM into LDS once, 128 rows a round (all of a round's
+// and V rows from HBM into LDS once, 144 rows a round (all of a round's
 // 16-byte loads in flight together; with several rounds the next round's
 // loads fly while the current round is computed), and every sparse layer
 // attends over them there: each row crosses HBM once for all layers, and
