@@ -16,7 +16,7 @@
 //
 // Work item (b, c): chunk c of real sequence b for the launch's tokens
 // [t_first, t_first + nq).  The chunk geometry is the ordinary pass's (tiles
-// of 16 tokens dealt round-robin over 4 streams per chunk, one per wave) with
+// of 16 tokens dealt round-robin over 4 streams per chunk, one per SIMD) with
 // nblk = ceil(L_lo / chunk) chunks, L_lo the prefix length of the group's
 // shortest token, over the tokens of the group's longest prefix.  A token
 // whose prefix reaches into one more chunk (ceil(L_v / chunk) = nblk + 1: a
@@ -24,8 +24,12 @@
 // partial there, written by chunk 0, so its merge sees exactly its tokens.
 //
 // Per tile, the K operand and the V rows are formed once, then every token of
-// the group runs the ordinary tile step (fp32-accurate logits from the
+// the wave runs the ordinary tile step (fp32-accurate logits from the
 // three-part query, online softmax, P.V) with its own causal mask and state.
+// Groups of four tokens run as two waves per SIMD with two tokens each (both
+// walk the same tiles; the second wave's loads hit the L2), which measured
+// faster than one wave carrying all four (a wave's states then fill the
+// register file and nothing covers its latencies).
 // The per-tile bound outputs wait in LDS and go out every kFlushTiles tiles of
 // a wave: a store shares the load counter (the next wait for loads would
 // include its latency), so they are batched rather than issued per tile.
@@ -36,8 +40,7 @@ namespace hs2 {
 
 namespace {
 
-constexpr int kMultiWaves = 4;     // one wave per SIMD, one tile stream per wave
-constexpr int kMultiStreams = 4;
+constexpr int kMultiStreams = 4;   // tile streams per workgroup, one per SIMD
 constexpr int kFlushTiles = 16;    // staged tiles per wave between flushes
 constexpr int kTileOut = 2 * kHeads;  // per tile and token: shat[16], u[16]
 
@@ -50,11 +53,17 @@ __device__ __forceinline__ int multi_items(const MultiFullParams& mp, int len) {
   return (max(lo, 1) + mp.f.chunk - 1) / mp.f.chunk;
 }
 
-template <bool FP8, int NQ>
-__global__ __launch_bounds__(64 * kMultiWaves) void full_multi_kernel(MultiFullParams mp) {
+// GROUPS token groups of NQ tokens each share the workgroup's streams: wave w
+// takes stream w % 4 and tokens NQ (w / 4) .. NQ (w / 4) + NQ - 1 of the
+// launch's group, so with two groups two waves on a SIMD walk the same tiles
+// (the second's loads hit the L2) and hide each other's latency.
+template <bool FP8, int NQ, int GROUPS>
+__global__ __launch_bounds__(256 * GROUPS) void full_multi_kernel(MultiFullParams mp) {
   const FullParams& p = mp.f;
+  constexpr int kMultiWaves = 4 * GROUPS;
   constexpr int kThreads = 64 * kMultiWaves;
-  __shared__ u32x4 s_q[NQ][kQLdsVecs];
+  constexpr int kTok = NQ * GROUPS;  // tokens of the launch's group
+  __shared__ u32x4 s_q[kTok][kQLdsVecs];
   // staged bound outputs [wave][tile][token][32]; at the end the merge buffer O[wave][16][128]
   constexpr int kStageFloats = kMultiWaves * kFlushTiles * NQ * kTileOut;
   constexpr int kMergeFloats = kMultiWaves * kHeads * kDim;
@@ -72,17 +81,19 @@ __global__ __launch_bounds__(64 * kMultiWaves) void full_multi_kernel(MultiFullP
   int64_t base;
   int len;
   seq_bounds(p.seq_offsets, b, p.total_tokens, p.max_context, base, len);
-  constexpr int nq = NQ;  // the group's tokens (mp.nq)
+  constexpr int nq = NQ;  // this wave's tokens
   const int lo = len - mp.n_query + mp.t_first + 1;  // prefix length of the group's first token
-  const int hi = lo + nq - 1;                        // of its last: the tokens this pass reads
+  const int hi = lo + kTok - 1;                      // of its last: the tokens this pass reads
   const int nblk = multi_items(mp, len);
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;
   const int g = lane >> 4;
+  const int tg = wave >> 2;          // this wave's token group
+  const int lo_w = lo + NQ * tg;     // prefix length of this wave's first token
   const int stream_stride = 16 * kMultiStreams * nblk;
-  const int s0 = 16 * (kMultiStreams * c + wave);  // this wave's first tile
+  const int s0 = 16 * (kMultiStreams * c + (wave & 3));  // this wave's first tile
   const int nt = s0 < hi ? (hi - 1 - s0) / stream_stride + 1 : 0;
   auto tok0 = [&](int i) { return i < nt ? s0 + i * stream_stride : hi; };
 
@@ -92,6 +103,7 @@ __global__ __launch_bounds__(64 * kMultiWaves) void full_multi_kernel(MultiFullP
   const float* __restrict__ ksb = FP8 ? p.k_scale + base : nullptr;
   const float* __restrict__ vsb = FP8 ? p.v_scale + base : nullptr;
   const int v_first = b * mp.n_query + mp.t_first;  // virtual sequence of the group's first token
+  const int v_wave = v_first + NQ * tg;             // and of this wave's first token
 
   SoftmaxState st[NQ];
   float cfac[NQ], lcf[NQ];
@@ -136,9 +148,9 @@ __global__ __launch_bounds__(64 * kMultiWaves) void full_multi_kernel(MultiFullP
     for (int e = lane; e < staged * nq * 8; e += 64) {
       const int ti = e / (8 * nq), t = (e / 8) % nq, part = e % 8;
       const int t0 = s_t0[wave][ti];
-      const int lv = lo + t;  // token t's prefix length
+      const int lv = lo_w + t;  // token t's prefix length
       if (t0 >= lv) continue;
-      const int v = v_first + t;
+      const int v = v_wave + t;
       const int64_t vbase_tok = mp.voffs[v];
       const float* src = stage + (ti * NQ + t) * kTileOut;
       if (part < 4) {
@@ -182,7 +194,8 @@ __global__ __launch_bounds__(64 * kMultiWaves) void full_multi_kernel(MultiFullP
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
 #pragma unroll
-        for (int t = 0; t < NQ; ++t) sc[t] = mfma_bf16_16x16x32(kf[k], QShared{s_q[t], lane}.get(part, k), sc[t]);
+        for (int t = 0; t < NQ; ++t)
+          sc[t] = mfma_bf16_16x16x32(kf[k], QShared{s_q[NQ * tg + t], lane}.get(part, k), sc[t]);
       }
     }
     // The update of attend_tile, phase by phase over the group's tokens so
@@ -196,7 +209,7 @@ __global__ __launch_bounds__(64 * kMultiWaves) void full_multi_kernel(MultiFullP
     float lmx[NQ];
 #pragma unroll
     for (int t = 0; t < NQ; ++t) {
-      const int nv = lo + t - t0;  // > 0: positions of this tile in token t's prefix (capped at 16 by the mask)
+      const int nv = lo_w + t - t0;  // > 0: positions of this tile in token t's prefix (capped at 16 by the mask)
 #pragma unroll
       for (int r = 0; r < 4; ++r) lg[t][r] = (4 * g + r < nv) ? sc[t][r] * cur.ks[r] : -INFINITY;
       lmx[t] = fmaxf(fmaxf(lg[t][0], lg[t][1]), fmaxf(lg[t][2], lg[t][3]));
@@ -263,13 +276,24 @@ __global__ __launch_bounds__(64 * kMultiWaves) void full_multi_kernel(MultiFullP
   };
 
   // The queries' loads, then the first tile's, then the split into LDS.
+  // (each group's four waves split its tokens' queries as load_q_lds_raw
+  // and store_q_lds do with a workgroup of four: wave w % 4 takes k-step w % 4)
   float4 qa[NQ], qc[NQ];
 #pragma unroll
-  for (int t = 0; t < NQ; ++t) load_q_lds_raw<FP8>(p.q + static_cast<size_t>(v_first + t) * kHeads * kDim, qa[t], qc[t]);
+  for (int t = 0; t < NQ; ++t)
+    load_q8<FP8>(p.q + (static_cast<size_t>(v_wave + t) * kHeads + (lane & 15)) * kDim, wave & 3, lane >> 4, qa[t],
+                 qc[t]);
   Raw ra, rb;
   load_tile(tok0(0), ra);
 #pragma unroll
-  for (int t = 0; t < NQ; ++t) store_q_lds(qa[t], qc[t], p.qscale, s_q[t]);
+  for (int t = 0; t < NQ; ++t) {
+    u32x4 ph, pm, pl;
+    split_q8(qa[t], qc[t], p.qscale, ph, pm, pl);
+    u32x4* dst = s_q[NQ * tg + t];
+    dst[(0 * 4 + (wave & 3)) * 64 + lane] = ph;
+    dst[(1 * 4 + (wave & 3)) * 64 + lane] = pm;
+    dst[(2 * 4 + (wave & 3)) * 64 + lane] = pl;
+  }
   __syncthreads();
   // Two-slot ring as in the ordinary pass: the next tile's loads fly while
   // this one is computed; the loop leaves only at its bottom.
@@ -291,12 +315,14 @@ __global__ __launch_bounds__(64 * kMultiWaves) void full_multi_kernel(MultiFullP
 
   // Each token's partial: merge the four waves through LDS, one token at a time.
   float(*s_o)[kHeads][kDim] = reinterpret_cast<float(*)[kHeads][kDim]>(s_raw);
-  constexpr int kDims = kDim * kHeads / kThreads;  // 8
-  const int h = threadIdx.x / (kDim / kDims);
+  // Thread group mg (256 threads) merges the four waves of token group mg.
+  constexpr int kDims = kDim * kHeads / 256;  // 8
+  const int mg = threadIdx.x >> 8;
+  const int h = (threadIdx.x & 255) / (kDim / kDims);
   const int d0 = (threadIdx.x % (kDim / kDims)) * kDims;
 #pragma unroll
   for (int t = 0; t < NQ; ++t) {
-    const int v = v_first + t;
+    const int v = v_first + NQ * mg + t;
     const float z = reduce_z(st[t].z);
     if (g == 0) {
       s_m[wave][n] = st[t].m;
@@ -310,13 +336,13 @@ __global__ __launch_bounds__(64 * kMultiWaves) void full_multi_kernel(MultiFullP
     __syncthreads();
     float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kMultiWaves; ++w) mx = fmaxf(mx, s_m[w][h]);
+    for (int w = 4 * mg; w < 4 * mg + 4; ++w) mx = fmaxf(mx, s_m[w][h]);
     float zz = 0.f;
     float acc[kDims];
 #pragma unroll
     for (int j = 0; j < kDims; ++j) acc[j] = 0.f;
 #pragma unroll
-    for (int w = 0; w < kMultiWaves; ++w) {
+    for (int w = 4 * mg; w < 4 * mg + 4; ++w) {
       const float mw = s_m[w][h];
       if (mw == -INFINITY) continue;  // a wave with no tokens of this prefix
       const float f = exp2f(mw - mx);
@@ -341,7 +367,7 @@ __global__ __launch_bounds__(64 * kMultiWaves) void full_multi_kernel(MultiFullP
   if (c == 0) {
     // Per token: the selection's histogram and counters cleared, and the empty
     // partial of the one chunk its prefix may reach beyond the group's nblk.
-    for (int t = 0; t < nq; ++t) {
+    for (int t = 0; t < kTok; ++t) {
       const int v = v_first + t;
       uint4* hz = reinterpret_cast<uint4*>(p.hist0 + static_cast<size_t>(v) * kRadixBins);
       for (int i = threadIdx.x; i < kRadixBins / 4; i += kThreads) hz[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -368,16 +394,16 @@ hipError_t launch_full_multi(const MultiFullParams& mp, hipStream_t s) {
                                           (p.total_tokens + p.chunk - 1) / p.chunk + p.batch);
   if (items <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(items));
-  const dim3 block(64 * kMultiWaves);
+  const dim3 b4(256), b8(512);
   switch ((mp.nq - 1) * 2 + (mp.fp8 ? 1 : 0)) {
-    case 0: hipLaunchKernelGGL((full_multi_kernel<false, 1>), grid, block, 0, s, mp); break;
-    case 1: hipLaunchKernelGGL((full_multi_kernel<true, 1>), grid, block, 0, s, mp); break;
-    case 2: hipLaunchKernelGGL((full_multi_kernel<false, 2>), grid, block, 0, s, mp); break;
-    case 3: hipLaunchKernelGGL((full_multi_kernel<true, 2>), grid, block, 0, s, mp); break;
-    case 4: hipLaunchKernelGGL((full_multi_kernel<false, 3>), grid, block, 0, s, mp); break;
-    case 5: hipLaunchKernelGGL((full_multi_kernel<true, 3>), grid, block, 0, s, mp); break;
-    case 6: hipLaunchKernelGGL((full_multi_kernel<false, 4>), grid, block, 0, s, mp); break;
-    case 7: hipLaunchKernelGGL((full_multi_kernel<true, 4>), grid, block, 0, s, mp); break;
+    case 0: hipLaunchKernelGGL((full_multi_kernel<false, 1, 1>), grid, b4, 0, s, mp); break;
+    case 1: hipLaunchKernelGGL((full_multi_kernel<true, 1, 1>), grid, b4, 0, s, mp); break;
+    case 2: hipLaunchKernelGGL((full_multi_kernel<false, 2, 1>), grid, b4, 0, s, mp); break;
+    case 3: hipLaunchKernelGGL((full_multi_kernel<true, 2, 1>), grid, b4, 0, s, mp); break;
+    case 4: hipLaunchKernelGGL((full_multi_kernel<false, 3, 1>), grid, b4, 0, s, mp); break;
+    case 5: hipLaunchKernelGGL((full_multi_kernel<true, 3, 1>), grid, b4, 0, s, mp); break;
+    case 6: hipLaunchKernelGGL((full_multi_kernel<false, 2, 2>), grid, b8, 0, s, mp); break;
+    case 7: hipLaunchKernelGGL((full_multi_kernel<true, 2, 2>), grid, b8, 0, s, mp); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
