@@ -78,6 +78,15 @@ def test_multi_token_matches_oracle(kv):
     print(f"worst {check_multi(d, run_multi(d))}", flush=True)
 
 
+@pytest.mark.parametrize("n_query", [2, 3])
+def test_multi_token_two_and_three_tokens(n_query):
+    # The group sizes below four take their own kernel instances.
+    lengths = [2000, 1, 515, 7000]
+    print(f"case: multi-token decode, T={n_query}, lengths {lengths}", flush=True)
+    d = multi_inputs(lengths, n_query, "bf16", seed=94 + n_query)
+    check_multi(d, run_multi(d))
+
+
 def test_multi_token_sixteen_tokens():
     lengths = [5000, 300, 16]
     print(f"case: multi-token decode, T=16, lengths {lengths}", flush=True)
