@@ -23,15 +23,18 @@ rocprofv3 FETCH_SIZE/WRITE_SIZE runs summarised under profiles/ (scaled by a
 The cpu_baseline leg times the fp64 oracle on a bounded sample of the same
 workload (whole sequences, one after another, until about 15 s have passed).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 2|3|4|5] [--selection token|block]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 2|3|4|5] [--selection token|block|block-scores]
 
 ``--tokens T`` (T > 1) times multi-token decode on the same cache: T query
 tokens per sequence, each over its causal prefix with its own selection.
 ``--part self-decoder`` times the model's front half at decode on the same
 batch: its one full-attention layer and 24 sliding-window layers (window 128).
 ``--selection block`` times the same workload through the gen-1 (block-level)
-selection instead, the comparator of the pages' ablation: the full layer with
-every score (hs2_full_decode_score), hs2_block_select, then the sparse layers.
+selection instead, the comparator of the pages' ablation: hs2_decode_block_gen1,
+whose full pass keeps per-tile head sums of its weights and whose merge
+launch forms the block sums from them.  ``--selection block-scores`` times the
+three-call route through every per-token score (hs2_full_decode_score,
+hs2_block_select, then the sparse layers).
 Each line also carries per-launch percentiles, a "cold" full-pass time (after
 1 GiB of writes has evicted the caches), the clock levels sampled during the
 timed steps, and the device.
@@ -482,11 +485,12 @@ def hybrid_block_line(args, torch, hs2, d, dev, workload, selection="token", wit
     q_sparse = torch.from_numpy(d["q_sparse"]).to(dev)
     lens = np.diff(d["seq_offsets"])
     batch, n_tokens = int(lens.shape[0]), int(lens.sum())
-    if selection == "block":
+    if selection == "block-scores":
         blk = hs2.BlockSelectDecode(offs_t, k, v, q_full, q_sparse, ks, vs, int(lens.max()))
         marks = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     else:
-        blk = hs2.DecodeBlock(offs_t, k, v, q_full, q_sparse, ks, vs, int(lens.max()), with_score=False)
+        blk = hs2.DecodeBlock(offs_t, k, v, q_full, q_sparse, ks, vs, int(lens.max()), with_score=False,
+                              selection=selection)
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -518,7 +522,7 @@ def hybrid_block_line(args, torch, hs2, d, dev, workload, selection="token", wit
     hs2.stage_timing(True)
     extra = []
     for _ in range(min(args.steps, 20)):
-        if selection == "block":
+        if selection == "block-scores":
             blk(marks)
             torch.cuda.synchronize()
             extra.append((marks[0].elapsed_time(marks[1]), marks[1].elapsed_time(marks[2])))
@@ -529,7 +533,7 @@ def hybrid_block_line(args, torch, hs2, d, dev, workload, selection="token", wit
     calls = hs2.stage_timing_read_calls()
     stage_pct = {name: pct(calls[:, i]) for i, name in enumerate(hs2.STAGE_NAMES)}
     stages = {name: (stage_pct[name] or {}).get("mean", 0.0) for name in hs2.STAGE_NAMES}
-    if selection == "block":
+    if selection == "block-scores":
         # hs2_full_decode_score records partial pass, merge and score pass; the
         # block selection and the sparse layers are separate calls
         stage_pct = {"full_partial": stage_pct["full_partial"], "full_merge": stage_pct["full_merge"],
@@ -544,9 +548,11 @@ def hybrid_block_line(args, torch, hs2, d, dev, workload, selection="token", wit
     t_both, t_k1 = float(both.mean()), float(k1_calls.mean())
     achieved = alg_bytes / (t_both * 1e-3) / 1e9
     k1_achieved = alg_bytes / (t_k1 * 1e-3) / 1e9
-    name = ("full_partial_kernel + merge_bound_hist_kernel (the full layer and its score bounds, K1 + K1b)"
-            if selection == "token" else
-            "full_partial_kernel + merge_kernel (the full layer keeping every logit; the score pass is apart)")
+    name = {"token": "full_partial_kernel + merge_bound_hist_kernel (the full layer and its score bounds, K1 + K1b)",
+            "block": "full_partial_kernel + merge_block_pool_kernel (the full layer, its per-tile head sums and the "
+                     "block sums)",
+            "block-scores": "full_partial_kernel + merge_kernel (the full layer keeping every logit; the score pass "
+                            "is apart)"}[selection]
     return {
         "value": batch * args.steps / dt,
         "ms_per_step": ms_per_step,
@@ -554,7 +560,8 @@ def hybrid_block_line(args, torch, hs2, d, dev, workload, selection="token", wit
         "config": {"workload": WORKLOADS[workload], "batch": batch, "context_tokens": n_tokens,
                    "max_context": int(lens.max()), "kv_cache": kv, "q_heads": 16, "kv_heads": 1,
                    "head_dim": 128, "window": 128, "top_k": 1024, "n_sparse_layers": int(q_sparse.shape[0]),
-                   "selection": "token" if selection == "token" else "block64 (gen-1 comparator)"},
+                   "selection": {"token": "token", "block": "block64 (gen-1 comparator) from tile sums",
+                                 "block-scores": "block64 (gen-1 comparator) from per-token scores"}[selection]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(workload) if selection == "token" else None,
@@ -583,8 +590,9 @@ def main():
                     help="self-decoder: the front half's attention (1 full + 24 sliding-window layers)")
     ap.add_argument("--tokens", type=int, default=1,
                     help="query tokens per sequence and step (above 1: the multi-token decode line)")
-    ap.add_argument("--selection", choices=("token", "block"), default="token",
-                    help="token: the method's selection; block: the gen-1 64-token-block comparator")
+    ap.add_argument("--selection", choices=("token", "block", "block-scores"), default="token",
+                    help="token: the method's selection; block: the gen-1 64-token-block comparator "
+                         "(block sums from tile sums); block-scores: the same through per-token scores")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-1m", action="store_true",
                     help="workload 2 only: skip the second (1M-token E4M3) roofline object")

@@ -81,7 +81,8 @@ typedef struct {
 
 /* Bytes of workspace for `desc` (0 when desc is invalid):
  *  - hs2_decode_workspace_bytes: hs2_decode_block with score_out == NULL, and
- *    hs2_topk_select, hs2_block_select, hs2_sparse_decode, hs2_full_decode;
+ *    hs2_decode_block_gen1, hs2_topk_select, hs2_block_select,
+ *    hs2_sparse_decode, hs2_full_decode;
  *  - hs2_decode_score_workspace_bytes: the calls that return per-token scores,
  *    hs2_decode_block with score_out != NULL and hs2_full_decode_score; it adds
  *    64 bytes a token (every logit of the full layer) to the first size.
@@ -141,6 +142,34 @@ hs2_status hs2_decode_block_noalloc(const hs2_decode_desc* desc, const int64_t* 
                                     const float* q_full, const float* q_sparse,
                                     float* o_full, float* o_sparse,
                                     int32_t* sel_idx, int32_t* sel_count, void* stream);
+
+/* One decode step of the hybrid block with gen-1 (block-level) selection in
+ * place of the token-level one, without per-token scores: the comparator
+ * the pages' ablation sets against the token-level selection at the same
+ * attention budget ("Luo Fuli Teases Xiaomi MiMo-V3 Architecture",
+ * paragraphs on how the sparse layers select and on the ablation;
+ * readaitime.com news of 2026-09-24, paragraph on block versus token
+ * selection).  Sequence b selects the last `window` positions plus the
+ * top_k / 64 = 16 complete 64-token blocks [64 i, 64 i + 64) that end before
+ * the window, ranked by the sum of their positions' scores (descending; ties
+ * to the lower block), as hs2_full_decode_score, hs2_block_select and
+ * hs2_sparse_decode do in three calls; a context of at most window + top_k
+ * positions selects every position.  Here the full layer keeps, per 16-token
+ * tile and head, the sum of its softmax weights instead of every logit, and
+ * the block sums are formed from those after the merge; they agree with the
+ * per-token route's up to fp32 rounding order (relative ~1e-6), so the two
+ * lists can differ only between blocks whose sums tie that closely.
+ * Arguments, outputs (o_full, o_sparse, sel_idx, sel_count), workspace
+ * (hs2_decode_workspace_bytes(desc)) and errors as hs2_decode_block with
+ * score_out == NULL.  Stage timing records all four stages (2: the block
+ * ranking).                                                                  */
+hs2_status hs2_decode_block_gen1(const hs2_decode_desc* desc, const int64_t* seq_offsets,
+                                 const void* k_cache, const void* v_cache,
+                                 const float* k_scale, const float* v_scale,
+                                 const float* q_full, const float* q_sparse,
+                                 float* o_full, float* o_sparse,
+                                 int32_t* sel_idx, int32_t* sel_count,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* Multi-token decode (speculative verification): n_query = T query tokens
  * per sequence in one step.  The pages give no multi-token rule for

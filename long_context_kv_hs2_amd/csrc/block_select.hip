@@ -14,6 +14,11 @@
 //     block index ascending); a context of at most window + top_k tokens
 //     selects every position, as the token-level rule does.
 //
+// Block sums come from per-token scores (hs2_block_select) or, without
+// per-token scores, from the full pass's per-tile, per-head weight sums
+// (the tile-sum pass): a block is four whole 16-token tiles, and its score is
+// sum over its tiles and the heads of exp2(m_h - M_h) r_h / Z_h.
+//
 // Two launches:
 //   block_pool_kernel    one workgroup per (sequence, 4 groups of 16 candidate
 //                        blocks), over a compact 1-D grid of the non-empty
@@ -21,6 +26,11 @@
 //                        in a fixed order (coalesced loads, then a butterfly
 //                        over the 16 lanes), and each 256-thread quarter also
 //                        writes its group's largest key.
+//   (or merge_block_pool_kernel, from tile sums: one workgroup per head of a
+//                        sequence for the full layer's merge, and one per
+//                        four groups of 16 candidate blocks, each 16-lane
+//                        team taking one block of each group, lane h its
+//                        head)
 //   block_select_kernel  one 1024-thread workgroup per sequence: the exact
 //                        top 16 of the 64-bit keys (block-sum bits above the
 //                        complement of the block index, so keys are distinct,
@@ -36,6 +46,7 @@
 //                        workgroup-wide LDS sort.
 #include "hs2_device.h"
 #include "hs2_internal.h"
+#include "merge.h"
 
 namespace hs2 {
 
@@ -138,6 +149,84 @@ __global__ __launch_bounds__(256 * kPoolGroups) void block_pool_kernel(BlockPara
   const u64* w = s_wave_max + 4 * quarter;
   if ((threadIdx.x & 255) == 0 && g * kPoolBlocks < nb)
     p.group_keys[group_slot(base, b, g)] = max(max(w[0], w[1]), max(w[2], w[3]));
+}
+
+// The full layer's merge and the block sums from the tile-sum pass, one
+// launch: workgroups w < 16 B merge head w % 16 of sequence w / 16 (first,
+// so the merges, the longest items, start first); the others take four
+// groups of 16 candidate blocks each, over a compact grid.  A block's sum:
+// per head (lane h of its team) the four tiles' exp2(m_h - M_h) r_h added in
+// tile order and multiplied by 1 / Z_h, then summed over the 16 heads by a
+// butterfly, which leaves every lane with the same bits.  Every tile of a
+// candidate block holds 16 real tokens, so the pass wrote all four.
+// (M_h, Z_h) are folded from the partials' packed (m, z), the same values in
+// every workgroup of the sequence (the merge's result is not written yet).
+// m_h <= M_h, so the factors are at most 1 and r_h at most 16 * 2^8.
+constexpr int kTilePoolThreads = kMergeThreads;  // 16 teams of 16 lanes
+constexpr int kTilePoolGroups = 4;               // groups of 16 blocks per workgroup: a team takes one block of each
+static_assert(kTilePoolThreads == kPoolBlocks * kHeads, "one team per block of a group, one lane per head");
+
+__global__ __launch_bounds__(kTilePoolThreads) void merge_block_pool_kernel(MergeParams mp, BlockParams p) {
+  __shared__ MergeShared msh;
+  __shared__ float s_mx[kHeads], s_iz[kHeads];
+  __shared__ u64 s_team[kTilePoolGroups][kPoolBlocks];
+  const int merges = kHeads * p.batch;
+  if (static_cast<int>(blockIdx.x) < merges) {
+    merge_one(mp, blockIdx.x % kHeads, blockIdx.x / kHeads, 0, 0, 0, msh);
+    return;
+  }
+  auto items = [](int len) {
+    const int groups = (candidate_blocks(len) + kPoolBlocks - 1) / kPoolBlocks;
+    return (groups + kTilePoolGroups - 1) / kTilePoolGroups;
+  };
+  int b, item;
+  if (!find_item(p.seq_offsets, p.batch, p.total_tokens, p.max_context, blockIdx.x - merges, items, b, item))
+    return;
+  b = __builtin_amdgcn_readfirstlane(b);
+  item = __builtin_amdgcn_readfirstlane(item);
+  int64_t base;
+  int len;
+  seq_bounds(p.seq_offsets, b, p.total_tokens, p.max_context, base, len);
+  const int nb = candidate_blocks(len);
+  const int team = threadIdx.x >> 4, h = threadIdx.x & 15;
+  float m[kTilePoolGroups][4], r[kTilePoolGroups][4];
+#pragma unroll
+  for (int k = 0; k < kTilePoolGroups; ++k) {  // loads first: they fly while (M, Z) are folded
+    const int i = min((item * kTilePoolGroups + k) * kPoolBlocks + team, nb - 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t slot = tile_slot(base, b, 4 * i + q) * kHeads + h;
+      m[k][q] = p.tile_stats[slot];
+      r[k][q] = p.tile_sums[slot];
+    }
+  }
+  head_stats_packed(p.pstats, b, p.chunks_per_seq, (len + p.chunk - 1) / p.chunk, s_mx, s_iz);
+  __syncthreads();
+  const float mh = s_mx[h], izh = s_iz[h];
+#pragma unroll
+  for (int k = 0; k < kTilePoolGroups; ++k) {
+    const int i = (item * kTilePoolGroups + k) * kPoolBlocks + team;
+    float s = ((exp2f(m[k][0] - mh) * r[k][0] + exp2f(m[k][1] - mh) * r[k][1]) + exp2f(m[k][2] - mh) * r[k][2]) +
+              exp2f(m[k][3] - mh) * r[k][3];
+    s *= izh;
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (h == 0) {
+      if (i < nb) p.block_scores[block_slot(base, b, i)] = s;
+      s_team[k][team] = i < nb ? block_key(s, i) : 0ull;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < kTilePoolGroups) {
+    const int k = threadIdx.x;
+    const int g = item * kTilePoolGroups + k;
+    if (g * kPoolBlocks < nb) {
+      u64 best = s_team[k][0];
+#pragma unroll
+      for (int q = 1; q < kPoolBlocks; ++q) best = max(best, s_team[k][q]);
+      p.group_keys[group_slot(base, b, g)] = best;
+    }
+  }
 }
 
 // Sorts s[0, m) descending; m a power of two <= kSortCap; every thread calls it.
@@ -244,6 +333,21 @@ hipError_t launch_block_select(const BlockParams& p, hipStream_t s) {
     hipLaunchKernelGGL(block_pool_kernel, dim3(static_cast<unsigned>(pool_grid)), dim3(256 * kPoolGroups), 0, s, p);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
+  hipLaunchKernelGGL(block_select_kernel, dim3(p.batch), dim3(kSelThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_block_pool(const MergeParams& mp, const BlockParams& p, hipStream_t s) {
+  if (p.batch <= 0) return hipSuccess;
+  // 16 merges per sequence, then sum_b ceil(ceil(nb_b / 16) / 4) <= N / 4096 + B pool items
+  const int64_t grid =
+      static_cast<int64_t>(kHeads + 1) * p.batch + p.total_tokens / (kTilePoolGroups * kPoolBlocks * kSelectBlock);
+  hipLaunchKernelGGL(merge_block_pool_kernel, dim3(static_cast<unsigned>(grid)), dim3(kTilePoolThreads), 0, s, mp, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_rank(const BlockParams& p, hipStream_t s) {
+  if (p.batch <= 0) return hipSuccess;
   hipLaunchKernelGGL(block_select_kernel, dim3(p.batch), dim3(kSelThreads), 0, s, p);
   return hipGetLastError();
 }

@@ -13,11 +13,12 @@
 // three exact bf16 parts (fp32-accurate logits), an online softmax per head in
 // registers, and O^T += V^T P^T on bf16 MFMA with each weight split into a
 // bf16 head and tail (16 significant bits).  The four waves' (m, z, O) are
-// merged through LDS into one partial per workgroup.  Three modes: BOUND keeps
+// merged through LDS into one partial per workgroup.  Four modes: BOUND keeps
 // per-token score bounds for the selection, SPILL keeps every logit for the
-// score pass, PLAIN keeps nothing (full attention alone).  In the first two
-// the first workgroup of each sequence also clears the sequence's selection
-// histogram and counters for the kernels that follow.
+// score pass, PLAIN keeps nothing (full attention alone), TILE_SUMS keeps per
+// tile and head the sum of the weights (gen-1 block selection).  In the first
+// two the first workgroup of each sequence also clears the sequence's
+// selection histogram and counters for the kernels that follow.
 #include <algorithm>
 
 #include "hs2_device.h"
@@ -35,7 +36,13 @@ namespace hs2 {
 // Bound-mode outputs of one wave's tiles wait in LDS until the loop ends: on
 // CDNA loads and stores share one in-order completion counter, so stores in
 // the streaming loop would put their write latency into every load wait.
-constexpr int kTileOut = 2 * kHeads;  // shat[16], u[16]
+constexpr int kTileOut = 2 * kHeads;  // shat[16], u[16] (TILE_SUMS: r[16], m[16])
+// TILE_SUMS: per tile and head, r_h = sum over the tile's tokens of
+// p_hj = exp2(l_hj - m_h), m_h being the wave's reference max the weights are
+// taken against; the score mass of the tile for head h is then
+// exp2(m_h - M_h) r_h / Z_h once the merge knows (M_h, Z_h), and a 64-token
+// block's score (four whole tiles) is the sum of that over its tiles and the
+// heads.  The same LDS staging and end-of-loop flush as BOUND.
 
 // Work item wg of the 1-D grid: the non-empty (sequence, chunk) pairs of the
 // batch, numbered in order.  A 1-D grid of just these deals the workgroups
@@ -79,6 +86,8 @@ template <bool FP8, int MODE>
 __global__ __launch_bounds__(64 * full_waves<FP8>()) void full_partial_kernel(FullParams p) {
   constexpr bool BOUND = MODE == kFullBound;
   constexpr bool SPILL = MODE == kFullSpill;
+  constexpr bool TSUM = MODE == kFullTileSums;
+  constexpr bool STAGED = BOUND || TSUM;  // per-tile outputs staged in LDS
   constexpr int kWaves = full_waves<FP8>();
   constexpr int kStreams = full_streams<FP8>();
   constexpr int kThreads = 64 * kWaves;
@@ -89,7 +98,7 @@ __global__ __launch_bounds__(64 * full_waves<FP8>()) void full_partial_kernel(Fu
   __shared__ float s_m[kWaves][kHeads];
   __shared__ float s_z[kWaves][kHeads];
   // the merge buffer O[kWaves][16][128] and, before it, the bound-mode tile outputs
-  __shared__ __attribute__((aligned(16))) float s_raw[BOUND ? kLocalTiles * kTileOut : kWaves * kHeads * kDim];
+  __shared__ __attribute__((aligned(16))) float s_raw[STAGED ? kLocalTiles * kTileOut : kWaves * kHeads * kDim];
   __shared__ u32x4 s_q[kQLdsVecs];
   float(*s_o)[kHeads][kDim] = reinterpret_cast<float(*)[kHeads][kDim]>(s_raw);
 
@@ -215,6 +224,19 @@ __global__ __launch_bounds__(64 * full_waves<FP8>()) void full_partial_kernel(Fu
       for (int r = 0; r < 4; ++r) {
         if (4 * g + r < nv) spill[static_cast<uint32_t>(t0 + 4 * g + r) * kHeads + n] = lg[r];
       }
+    } else if constexpr (TSUM) {
+      // head n's weights over the tile: four tokens in the lane, then over
+      // the four lane groups (masked tokens weigh 0); every lane of the
+      // head ends with the same sum
+      float x = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      if (nv <= 0) return;  // the masked tile past the end has no slot
+      float* out = s_raw + local(ti) * kTileOut;
+      if (g == 0) {
+        out[n] = x;
+        out[kHeads + n] = st.m;
+      }
     }
   };
 
@@ -252,14 +274,26 @@ __global__ __launch_bounds__(64 * full_waves<FP8>()) void full_partial_kernel(Fu
     }
   }
 
-  if constexpr (BOUND) {
-    // Write this wave's tile outputs: shat of the tokens that exist, and the
-    // per-tile u of every tile.
+  if constexpr (STAGED) {
+    // Write this wave's tile outputs: shat of the tokens that exist (TILE_SUMS:
+    // the sums r of every tile), and the per-tile u (m) of every tile.
     // 16-byte stores, all issued before any completes: the flush is on the
     // critical path of the workgroup's end.
     const int ntiles = nt;
+    if constexpr (TSUM) {
 #pragma unroll
-    for (int it = 0; it < kMaxWaveTiles * 4 / 64; ++it) {
+      for (int it = 0; it < kMaxWaveTiles * 4 / 64; ++it) {
+        const int i = lane + 64 * it;  // float4 i: tile i / 4, heads 4 (i % 4) ..
+        const int ti = i >> 2, e = 4 * (i & 3);
+        if (ti < ntiles) {
+          const int tile = tok0(ti) >> 4;
+          *reinterpret_cast<float4*>(p.tile_sums + tile_slot(base, b, tile) * kHeads + e) =
+              *reinterpret_cast<const float4*>(s_raw + local(ti) * kTileOut + e);
+        }
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < (BOUND ? kMaxWaveTiles * 4 / 64 : 0); ++it) {
       const int i = lane + 64 * it;  // float4 i: tile i / 4, tokens 4 (i % 4) ..
       const int ti = i >> 2, e = 4 * (i & 3);
       if (ti < ntiles) {
@@ -336,7 +370,7 @@ __global__ __launch_bounds__(64 * full_waves<FP8>()) void full_partial_kernel(Fu
   float4* o4 = reinterpret_cast<float4*>(out + 2 * kHeads + h * kDim + d0);
 #pragma unroll
   for (int j = 0; j < kDims / 4; ++j) o4[j] = make_float4(acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]);
-  if (MODE != kFullPlain && c == 0) {
+  if ((BOUND || SPILL) && c == 0) {
     uint4* hz = reinterpret_cast<uint4*>(p.hist0 + static_cast<size_t>(b) * kRadixBins);
     for (int i = threadIdx.x; i < kRadixBins / 4; i += kThreads) hz[i] = make_uint4(0u, 0u, 0u, 0u);
     if (threadIdx.x < 4) p.counters[b * 4 + threadIdx.x] = 0u;
@@ -358,6 +392,9 @@ hipError_t launch_full_partial(const FullParams& p, int batch, bool fp8, int mod
     case kFullBound: fp8 ? launch_mode<true, kFullBound>(p, grid, s) : launch_mode<false, kFullBound>(p, grid, s); break;
     case kFullSpill: fp8 ? launch_mode<true, kFullSpill>(p, grid, s) : launch_mode<false, kFullSpill>(p, grid, s); break;
     case kFullPlain: fp8 ? launch_mode<true, kFullPlain>(p, grid, s) : launch_mode<false, kFullPlain>(p, grid, s); break;
+    case kFullTileSums:
+      fp8 ? launch_mode<true, kFullTileSums>(p, grid, s) : launch_mode<false, kFullTileSums>(p, grid, s);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

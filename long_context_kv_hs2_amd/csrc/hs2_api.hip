@@ -71,7 +71,7 @@ struct DecodeLayout {
   int chunk = 0;
   int chunks_per_seq = 0;
   size_t partials = 0, stats = 0, pstats = 0, spill = 0, hist0 = 0, counters = 0, selbuf = 0, cand = 0, shat = 0,
-         tile_stats = 0, tile_ub = 0, cand_cnt = 0, sparse = 0, blocks = 0, groups = 0, total = 0;
+         tile_stats = 0, tile_ub = 0, cand_cnt = 0, sparse = 0, blocks = 0, groups = 0, tile_sums = 0, total = 0;
   int cand_blocks = 0;
 };
 
@@ -104,6 +104,10 @@ DecodeLayout decode_layout(const hs2_decode_desc& d, bool with_spill, int chunk 
   L.cand = take(std::max(B * kCandCap, N + B * kBoundBlockTokens) * sizeof(unsigned long long));
   L.cand_blocks = static_cast<int>(std::max<int64_t>((d.max_context + kBoundBlockTokens - 1) / kBoundBlockTokens, 1));
   L.cand_cnt = take(B * static_cast<size_t>(L.cand_blocks) * sizeof(uint32_t));
+  // gen-1 selection from the tile-sum pass: the per-tile head sums,
+  // ((N >> 4) + B + 1) x 16 floats (<= 4 N + 64 (B + 1) bytes), live in the
+  // candidate slots (>= 8 N + 8 * 4096 B bytes), which that path leaves unused
+  L.tile_sums = L.cand;
   L.shat = take(N * sizeof(uint16_t));
   L.tile_stats = take(((N >> 4) + B + 1) * kHeads * sizeof(float));
   L.tile_ub = take(((N >> 4) + B + 1) * 2 * sizeof(float));
@@ -265,6 +269,7 @@ FullParams full_params(const DecodeArgs& a, const DecodeLayout& L) {
   p.spill = reinterpret_cast<float*>(ws_at(a.ws, L.spill));
   p.shat = reinterpret_cast<uint16_t*>(ws_at(a.ws, L.shat));
   p.tile_stats = reinterpret_cast<float*>(ws_at(a.ws, L.tile_stats));
+  p.tile_sums = reinterpret_cast<float*>(ws_at(a.ws, L.tile_sums));
   p.hist0 = reinterpret_cast<uint32_t*>(ws_at(a.ws, L.hist0));
   p.counters = reinterpret_cast<uint32_t*>(ws_at(a.ws, L.counters));
   return p;
@@ -305,10 +310,11 @@ SelectParams select_params(const DecodeArgs& a, const DecodeLayout& L, float* sc
 
 // Full-attention pass and merge.  `mode`: kFullBound (the merge launch also
 // runs the selection's first pass, with `bound_sel`), kFullSpill (every logit
-// kept for the score pass) or kFullPlain (full attention alone: partials and
-// o_full only).
+// kept for the score pass), kFullPlain (full attention alone: partials and
+// o_full only) or kFullTileSums (the merge launch also computes the gen-1
+// block sums, with `block_sel`).
 hs2_status run_full(const DecodeArgs& a, const DecodeLayout& L, int mode, const SelectParams* bound_sel,
-                    TimingRecord* rec) {
+                    TimingRecord* rec, const BlockParams* block_sel = nullptr) {
   const bool bound_mode = mode == kFullBound;
   const hs2_decode_desc& d = *a.d;
   const FullParams fp = full_params(a, L);
@@ -351,6 +357,8 @@ hs2_status run_full(const DecodeArgs& a, const DecodeLayout& L, int mode, const 
   mp.stats = mode == kFullPlain ? nullptr : reinterpret_cast<float*>(ws_at(a.ws, L.stats));
   if (bound_mode) {
     HS2_HIP(launch_merge_bound_hist(mp, *bound_sel, d.batch, d.max_context, a.stream), "merge and bound histogram");
+  } else if (mode == kFullTileSums) {
+    HS2_HIP(launch_merge_block_pool(mp, *block_sel, a.stream), "merge and block sums");
   } else {
     HS2_HIP(launch_merge(mp, d.batch, a.stream), "full-attention merge");
   }
@@ -384,6 +392,7 @@ hs2_status run_sparse(const DecodeArgs& a, const DecodeLayout& L, const int32_t*
 }
 
 hs2_status run_block(const DecodeArgs& a, const DecodeLayout& L);
+hs2_status run_block_gen1(const DecodeArgs& a, const DecodeLayout& L);
 
 // The arguments of a decode step other than its workspace.
 hs2_status check_decode_args(const hs2_decode_desc* desc, const int64_t* seq_offsets, const void* k_cache,
@@ -434,6 +443,22 @@ hs2_status hs2_decode_block(const hs2_decode_desc* desc, const int64_t* seq_offs
   DecodeArgs a{desc, seq_offsets, k_cache, v_cache, k_scale, v_scale, q_full, q_sparse, o_full, o_sparse,
                sel_idx, sel_count, score_out, workspace, static_cast<hipStream_t>(stream)};
   return run_block(a, L);
+}
+
+hs2_status hs2_decode_block_gen1(const hs2_decode_desc* desc, const int64_t* seq_offsets, const void* k_cache,
+                                 const void* v_cache, const float* k_scale, const float* v_scale,
+                                 const float* q_full, const float* q_sparse, float* o_full, float* o_sparse,
+                                 int32_t* sel_idx, int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  HS2_TRY(check_decode_args(desc, seq_offsets, k_cache, v_cache, k_scale, v_scale, q_full, q_sparse, o_full,
+                            o_sparse, sel_idx, sel_count, nullptr));
+  const hs2_decode_desc& d = *desc;
+  DecodeLayout L;
+  HS2_TRY(check_workspace(d, workspace, workspace_bytes, L, false));
+  if (d.batch == 0) return HS2_OK;
+  DecodeArgs a{desc, seq_offsets, k_cache, v_cache, k_scale, v_scale, q_full, q_sparse, o_full, o_sparse,
+               sel_idx, sel_count, nullptr, workspace, static_cast<hipStream_t>(stream)};
+  return run_block_gen1(a, L);
 }
 
 }  // extern "C"
@@ -510,6 +535,37 @@ hs2_status run_block(const DecodeArgs& a, const DecodeLayout& L) {
     HS2_HIP(launch_score_hist(sp, d.batch, d.max_context, true, true, a.stream), "score pass");
     HS2_HIP(launch_collect_finish(sp, d.batch, d.max_context, a.stream), "selection");
   }
+  HS2_TRY(mark(rec, 3, a.stream));
+  HS2_TRY(run_sparse(a, L, a.sel_idx, a.sel_count));
+  HS2_TRY(mark(rec, 4, a.stream));
+  return HS2_OK;
+}
+
+// The hybrid block with gen-1 selection and no per-token scores: the full
+// pass keeps per-tile head sums of its weights (8 bytes a token), the merge
+// launch turns them into block sums, then the block ranking and the sparse
+// layers.  Stages as run_block.
+hs2_status run_block_gen1(const DecodeArgs& a, const DecodeLayout& L) {
+  const hs2_decode_desc& d = *a.d;
+  TimingRecord* rec = nullptr;
+  HS2_TRY(timing_begin(&rec));
+  BlockParams bp{};
+  bp.seq_offsets = a.offs;
+  bp.total_tokens = d.total_tokens;
+  bp.max_context = d.max_context;
+  bp.batch = d.batch;
+  bp.block_scores = reinterpret_cast<float*>(ws_at(a.ws, L.blocks));
+  bp.group_keys = reinterpret_cast<unsigned long long*>(ws_at(a.ws, L.groups));
+  bp.sel_idx = a.sel_idx;
+  bp.sel_count = a.sel_count;
+  bp.tile_stats = reinterpret_cast<const float*>(ws_at(a.ws, L.tile_stats));
+  bp.tile_sums = reinterpret_cast<const float*>(ws_at(a.ws, L.tile_sums));
+  bp.pstats = reinterpret_cast<const float*>(ws_at(a.ws, L.pstats));
+  bp.chunk = L.chunk;
+  bp.chunks_per_seq = L.chunks_per_seq;
+  HS2_TRY(mark(rec, 0, a.stream));
+  HS2_TRY(run_full(a, L, kFullTileSums, nullptr, rec, &bp));
+  HS2_HIP(launch_block_rank(bp, a.stream), "block selection");
   HS2_TRY(mark(rec, 3, a.stream));
   HS2_TRY(run_sparse(a, L, a.sel_idx, a.sel_count));
   HS2_TRY(mark(rec, 4, a.stream));

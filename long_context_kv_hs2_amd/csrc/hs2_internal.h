@@ -32,7 +32,9 @@ struct FullParams {
   float* pstats;             // [B][chunks_per_seq][32]: each partial's (m[16], z[16]) again, packed
   float* spill;              // spill mode: [N][16] log2-domain logits
   uint16_t* shat;            // bound mode: [N] per-token sum over heads of the running-normalised weights, bf16 (RNE)
-  float* tile_stats;         // bound mode: [tile_slots][16] per head after each tile: running max - log2(~1/running sum)
+  float* tile_stats;         // bound mode: [tile_slots][16] per head after each tile: running max - log2(~1/running sum);
+                             // tile-sum mode: the running max m_h the tile's weights are taken against
+  float* tile_sums;          // tile-sum mode: [tile_slots][16] per head: sum over the tile's tokens of exp2(l_hj - m_h)
   uint32_t* hist0;           // [B][kRadixBins] selection histogram, cleared here
   uint32_t* counters;        // [B][4] selection counters, cleared here
   const int64_t* kv_start;   // [B] first K/V row of each sequence, or nullptr: the row seq_offsets[b]
@@ -41,8 +43,10 @@ struct FullParams {
 // unique over all sequences, at most N/16 + B.
 __host__ __device__ inline int64_t tile_slot(int64_t base, int b, int t) { return (base >> 4) + b + t; }
 // What the partial pass keeps beside its partials: score bounds (the default
-// selection path), every logit (the score path), or nothing (full attention alone).
-enum FullMode { kFullBound = 0, kFullSpill = 1, kFullPlain = 2 };
+// selection path), every logit (the score path), nothing (full attention
+// alone), or per tile and head the sum of the weights (gen-1 block selection
+// without per-token scores: a 64-token block is four whole tiles).
+enum FullMode { kFullBound = 0, kFullSpill = 1, kFullPlain = 2, kFullTileSums = 3 };
 hipError_t launch_full_partial(const FullParams& p, int batch, bool fp8, int mode, hipStream_t s);
 
 struct MergeParams {
@@ -77,8 +81,20 @@ struct BlockParams {
   unsigned long long* group_keys;  // [N / 1024 + B]: largest key of blocks [16 g, 16 g + 16), slot (base_b >> 10) + b + g
   int32_t* sel_idx;           // [B][window + top_k]
   int32_t* sel_count;         // [B]
+  // Block sums from the full pass's tile sums (no per-token scores): the
+  // pass's pstats give each head's (M, Z); score unused.
+  const float* tile_stats;    // [tile_slots][16] m_h of each tile
+  const float* tile_sums;     // [tile_slots][16] sum of exp2(l - m_h) over the tile
+  const float* pstats;        // [B][chunks_per_seq][32] (m[16], z[16]) per partial
+  int chunk;
+  int chunks_per_seq;
 };
+// From given scores: the pool launch, then the selection launch.
 hipError_t launch_block_select(const BlockParams& p, hipStream_t s);
+// From the tile-sum pass: the full layer's merge and the block sums in one
+// launch (mp: the merge); then launch_block_rank, the selection launch.
+hipError_t launch_merge_block_pool(const MergeParams& mp, const BlockParams& p, hipStream_t s);
+hipError_t launch_block_rank(const BlockParams& p, hipStream_t s);
 
 struct SelectParams {
   const int64_t* seq_offsets;

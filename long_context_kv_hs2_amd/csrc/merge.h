@@ -87,4 +87,50 @@ __device__ __forceinline__ void merge_one(const MergeParams& p, int h, int b, in
   }
 }
 
+// Each head's (M, Z) over a sequence's `count` partials, from the full pass's
+// packed copy of their (m, z) (pstats: [B][chunks_per_seq][m[16], z[16]]):
+// 16 lanes per head fold partials l, l + 16, ... online (eight loads in
+// flight per lane), then across the 16 lanes.  Threads 0 .. 255 call it;
+// s_mx[h] = M_h and s_iz[h] = 1 / Z_h are written (the caller syncs).  The
+// order is fixed, so every workgroup that calls it gets the same values;
+// they differ from merge_one's by rounding order only.
+__device__ __forceinline__ void head_stats_packed(const float* pstats, int b, int chunks_per_seq, int count,
+                                                  float* s_mx, float* s_iz) {
+  const int t = threadIdx.x;
+  const int h = t >> 4, l = t & 15;
+  const float* pb = pstats + static_cast<int64_t>(b) * chunks_per_seq * (2 * kHeads);
+  float m = -INFINITY, z = 0.f;
+  auto fold = [](float& m, float& z, float mc, float zc) {  // (m, z) += (mc, zc)
+    if (mc == -INFINITY) return;
+    if (mc > m) {
+      z = z * exp2f(m - mc) + zc;
+      m = mc;
+    } else {
+      z += zc * exp2f(mc - m);
+    }
+  };
+  constexpr int kBatch = 8;
+  for (int c0 = l; c0 < count; c0 += 16 * kBatch) {
+    float mv[kBatch], zv[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int c = c0 + 16 * u;
+      const float* pc = pb + static_cast<int64_t>(min(c, count - 1)) * (2 * kHeads);
+      mv[u] = c < count ? pc[h] : -INFINITY;
+      zv[u] = pc[kHeads + h];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) fold(m, z, mv[u], zv[u]);
+  }
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) {
+    const float mo = __shfl_xor(m, off), zo = __shfl_xor(z, off);
+    fold(m, z, mo, zo);
+  }
+  if (l == 0) {
+    s_mx[h] = m;
+    s_iz[h] = 1.f / z;
+  }
+}
+
 }  // namespace hs2

@@ -734,45 +734,7 @@ __global__ __launch_bounds__(256) void merge_bound_hist_kernel(MergeParams mp, S
     if (16 * tile < dom) load_tile_bounds(p, base, b, tile, min(16, dom - 16 * tile), v[k], u[k]);
   }
   for (int i = t; i < kRadixBins; i += 256) s_hist[i] = 0;
-  {
-    // (M_h, Z_h): 16 lanes per head, partials c = l, l + 16, ..., eight
-    // loads in flight per lane, merged online; then across the 16 lanes.
-    const int h = t >> 4, l = t & 15;
-    const int count = (len + mp.chunk - 1) / mp.chunk;
-    const float* pb = p.pstats + static_cast<int64_t>(b) * p.chunks_per_seq * (2 * kHeads);
-    float m = -INFINITY, z = 0.f;
-    auto fold = [](float& m, float& z, float mc, float zc) {  // (m, z) += (mc, zc)
-      if (mc == -INFINITY) return;
-      if (mc > m) {
-        z = z * exp2f(m - mc) + zc;
-        m = mc;
-      } else {
-        z += zc * exp2f(mc - m);
-      }
-    };
-    constexpr int kBatch = 8;
-    for (int c0 = l; c0 < count; c0 += 16 * kBatch) {
-      float mv[kBatch], zv[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int c = c0 + 16 * u;
-        const float* pc = pb + static_cast<int64_t>(min(c, count - 1)) * (2 * kHeads);
-        mv[u] = c < count ? pc[h] : -INFINITY;
-        zv[u] = pc[kHeads + h];
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) fold(m, z, mv[u], zv[u]);
-    }
-#pragma unroll
-    for (int off = 8; off > 0; off >>= 1) {
-      const float mo = __shfl_xor(m, off), zo = __shfl_xor(z, off);
-      fold(m, z, mo, zo);
-    }
-    if (l == 0) {
-      s_mx[h] = m;
-      s_iz[h] = 1.f / z;
-    }
-  }
+  head_stats_packed(p.pstats, b, p.chunks_per_seq, (len + mp.chunk - 1) / mp.chunk, s_mx, s_iz);
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < TILES; ++k) {

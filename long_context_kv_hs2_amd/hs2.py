@@ -24,7 +24,7 @@ N_STAGES = 4
 STAGE_NAMES = ("full_partial", "full_merge", "score_select", "sparse")
 
 EXPORTED = (
-    "hs2_decode_workspace_bytes", "hs2_decode_score_workspace_bytes", "hs2_decode_block", "hs2_decode_block_noalloc", "hs2_full_decode_score", "hs2_topk_select", "hs2_block_select",
+    "hs2_decode_workspace_bytes", "hs2_decode_score_workspace_bytes", "hs2_decode_block", "hs2_decode_block_noalloc", "hs2_decode_block_gen1", "hs2_full_decode_score", "hs2_topk_select", "hs2_block_select",
     "hs2_sparse_decode", "hs2_bridge_workspace_bytes", "hs2_bridge_kv", "hs2_bridge_kv_fp8",
     "hs2_bridge_packed_weight_bytes", "hs2_bridge_pack_weights", "hs2_bridge_kv_packed",
     "hs2_bridge_append_workspace_bytes", "hs2_bridge_append", "hs2_full_decode", "hs2_swa_decode",
@@ -73,6 +73,8 @@ def load(path: str = LIB_PATH):
     lib.hs2_decode_block.restype = ctypes.c_int
     lib.hs2_decode_block_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.hs2_decode_block_noalloc.restype = ctypes.c_int
+    lib.hs2_decode_block_gen1.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hs2_decode_block_gen1.restype = ctypes.c_int
     lib.hs2_full_decode_score.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hs2_full_decode_score.restype = ctypes.c_int
     lib.hs2_topk_select.argtypes = [dp, vp, vp, vp, vp, vp, sz, vp]
@@ -165,10 +167,16 @@ def kv_dtype_of(k: torch.Tensor) -> int:
 
 class DecodeBlock:
     """Reusable decode call: holds the descriptor, outputs and workspace so
-    repeated steps (benchmarks) allocate nothing."""
+    repeated steps (benchmarks) allocate nothing.  selection="block" calls
+    hs2_decode_block_gen1 (gen-1 block selection, no per-token scores)."""
 
     def __init__(self, seq_offsets, k, v, q_full, q_sparse, k_scale=None, v_scale=None, max_context=None,
-                 with_score=False, total_tokens=None):
+                 with_score=False, total_tokens=None, selection="token"):
+        if selection not in ("token", "block"):
+            raise ValueError(f"selection {selection!r}: 'token' or 'block'")
+        if selection == "block" and with_score:
+            raise ValueError("the gen-1 call returns no per-token scores")
+        self.selection = selection
         dev = k.device
         self.seq_offsets, self.k, self.v, self.k_scale, self.v_scale = seq_offsets, k, v, k_scale, v_scale
         self.q_full, self.q_sparse = q_full, q_sparse
@@ -186,6 +194,13 @@ class DecodeBlock:
         self.workspace = _workspace(decode_workspace_bytes(self.desc, with_score), dev)
 
     def __call__(self):
+        if self.selection == "block":
+            check(load().hs2_decode_block_gen1(
+                ctypes.byref(self.desc), _ptr(self.seq_offsets), _ptr(self.k), _ptr(self.v), _ptr(self.k_scale),
+                _ptr(self.v_scale), _ptr(self.q_full), _ptr(self.q_sparse), _ptr(self.o_full),
+                _ptr(self.o_sparse), _ptr(self.sel_idx), _ptr(self.sel_count), _ptr(self.workspace),
+                self.workspace.numel(), _stream()))
+            return self
         check(load().hs2_decode_block(
             ctypes.byref(self.desc), _ptr(self.seq_offsets), _ptr(self.k), _ptr(self.v), _ptr(self.k_scale),
             _ptr(self.v_scale), _ptr(self.q_full), _ptr(self.q_sparse), _ptr(self.o_full), _ptr(self.o_sparse),

@@ -274,6 +274,34 @@ def test_stage_calls_validate():
                                  None) == INVALID
 
 
+def test_gen1_block_call_validates():
+    # hs2_decode_block_gen1: hs2_decode_block's checks, on the workspace
+    # without the score spill (it keeps per-tile sums, not every logit)
+    lib = hs2.load()
+    v = ctypes.c_void_p
+    d = desc()
+    n = lib.hs2_decode_workspace_bytes(ctypes.byref(d))
+
+    def call(dd=d, seq=FAKE, qf=FAKE, qs=FAKE, si=FAKE, nbytes=n, ws=FAKE):
+        return lib.hs2_decode_block_gen1(ctypes.byref(dd) if dd is not None else None, v(seq), v(FAKE), v(FAKE),
+                                         None, None, v(qf), v(qs), v(FAKE), v(FAKE), v(si), v(FAKE), v(ws),
+                                         nbytes, None)
+
+    assert call(dd=None) == INVALID
+    assert call(seq=None) == INVALID
+    assert call(seq=FAKE + 4) == INVALID
+    assert call(qf=None) == INVALID
+    assert call(qs=None) == INVALID
+    assert call(si=None) == INVALID
+    assert call(nbytes=n - 1) == SMALL_WS
+    assert call(ws=FAKE + 16) == INVALID
+    assert call(dd=desc(head_dim=64)) == UNSUPPORTED
+    bad = desc()
+    bad.top_k = 512
+    assert call(dd=bad) == UNSUPPORTED
+    assert lib.hs2_decode_score_workspace_bytes(ctypes.byref(d)) > n  # the spill is not needed here
+
+
 def test_status_strings():
     lib = hs2.load()
     assert lib.hs2_status_string(0) == b"HS2_OK"

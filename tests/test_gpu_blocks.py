@@ -76,6 +76,58 @@ def test_hybrid_block_with_block_selection(kv):
     print(f"worst {w}", flush=True)
 
 
+def run_gen1(d):
+    t = parity.to_device(d)
+    g1 = hs2.DecodeBlock(t["seq_offsets"], t["k"], t["v"], t["q_full"], t["q_sparse"], t["k_scale"], t["v_scale"],
+                         t["max_context"], selection="block")
+    g1()
+    torch.cuda.synchronize()
+    return t, g1
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_gen1_call_from_tile_sums(kv):
+    # hs2_decode_block_gen1 (block sums from the full pass's per-tile head
+    # sums, no per-token scores) against the oracle, and against the
+    # three-call route through per-token scores on the same inputs: the full
+    # layer bit for bit (same arithmetic, same merge), the lists equal away
+    # from near-ties, and the sparse outputs bit for bit where the lists are.
+    lengths = [300, 1152, 1153, 1216, 1217, 1280, 1500, 4000, 20000, 0, 70000, 5000]
+    print(f"case: gen-1 call from tile sums, {kv}, lengths {lengths}", flush=True)
+    d = inputs.make_decode(lengths=lengths, n_sparse=3, kv=kv, seed=19, needles=40)
+    t, g1 = run_gen1(d)
+    w = parity.check_decode(d, g1.outputs(), selection="block")
+    print(f"worst {w}", flush=True)
+    blk = hs2.BlockSelectDecode(t["seq_offsets"], t["k"], t["v"], t["q_full"], t["q_sparse"], t["k_scale"],
+                                t["v_scale"], t["max_context"])
+    blk()
+    torch.cuda.synchronize()
+    assert torch.equal(g1.o_full, blk.o_full)
+    assert torch.equal(g1.sel_count, blk.sel_count)
+    same = 0
+    for b in range(len(lengths)):
+        if torch.equal(g1.sel_idx[b], blk.sel_idx[b]):
+            same += 1
+            assert torch.equal(g1.o_sparse[:, b], blk.o_sparse[:, b])
+    assert same >= len(lengths) - 1, f"only {same} of {len(lengths)} lists agree"
+
+
+@pytest.mark.parametrize("workload", [2, 3])
+def test_gen1_call_full_size(workload):
+    # The gen-1 line the benchmark times, at the full workload sizes, every
+    # sequence against the oracle's block rule.
+    print(f"case: gen-1 call, workload {workload}; oracle on every sequence", flush=True)
+    d = inputs.make_decode(workload)
+    _, g1 = run_gen1(d)
+    out = {k: (v.clone() if v is not None else None) for k, v in g1.outputs().items()}
+    g1()  # a second call on the same workspace gives the same results
+    torch.cuda.synchronize()
+    for key in ("o_full", "o_sparse", "sel_idx", "sel_count"):
+        assert torch.equal(out[key], g1.outputs()[key]), f"{key} differs on the second call"
+    w = parity.check_decode(d, out, selection="block")
+    print(f"worst {w}", flush=True)
+
+
 def test_block_selection_differs_from_token_selection():
     # On a needle workload the two rules pick different lists (the ablation's
     # point); both are checked against their own oracle above.
