@@ -91,10 +91,14 @@ __global__ __launch_bounds__(64 * full_waves<FP8>()) void full_partial_kernel(Fu
   constexpr int kWaves = full_waves<FP8>();
   constexpr int kStreams = full_streams<FP8>();
   constexpr int kThreads = 64 * kWaves;
-  // Tiles of one workgroup (bound-mode LDS slots), and of one wave (a bound
-  // for the flush loop): a workgroup holds at most chunk / 16 + kStreams.
-  constexpr int kLocalTiles = max_chunk(FP8) / 16 + kStreams;
+  // Tiles of one wave (a bound for the flush loop) and of one workgroup
+  // (bound-mode LDS slots).  E4M3: a workgroup holds at most chunk / 16 +
+  // kStreams.  bf16: a wave holds at most chunk / 64 + 1, or with the split
+  // below at most (31/32) chunk / 64 + chunk / 1024 + 4 (the even-XCD share).
   constexpr int kMaxWaveTiles = ((FP8 ? 4 : 1) * (max_chunk(FP8) / (16 * kStreams) + 1) + 15) / 16 * 16;
+  static_assert(FP8 || kMaxWaveTiles >= max_chunk(false) / 64 * 31 / 32 + max_chunk(false) / 1024 + 4,
+                "bf16 wave tile bound");
+  constexpr int kLocalTiles = FP8 ? max_chunk(FP8) / 16 + kStreams : kStreams * kMaxWaveTiles;
   __shared__ float s_m[kWaves][kHeads];
   __shared__ float s_z[kWaves][kHeads];
   // the merge buffer O[kWaves][16][128] and, before it, the bound-mode tile outputs
@@ -124,20 +128,53 @@ __global__ __launch_bounds__(64 * full_waves<FP8>()) void full_partial_kernel(Fu
   // the younger three of seven: the two finish together.  A wave visits its
   // streams' k-th tiles in stream order, then the (k + 1)-th.  The split-K
   // merge does not depend on which tokens a partial holds.
+  //
+  // bf16 and an even number of chunks: workgroup w runs on XCD w mod 8 (the
+  // dispatcher deals workgroups round-robin over the XCDs), and with one wave
+  // per SIMD the workgroups on odd XCDs stream about 6.5% slower than those on
+  // even ones (per-workgroup end times, the same on every part measured).  So
+  // the sequence's tiles are dealt in two regions: whole rounds over all its
+  // workgroups up to ~31/32 of its tiles, then the rest over its even-XCD
+  // workgroups only (every other chunk, nblk / 2 of them), which thus take
+  // 33 tiles for every 31 of the others.  The split depends only on the batch,
+  // so every partial holds the same tokens on every call.
   const int nblk = (len + p.chunk - 1) / p.chunk;
   const int simd = FP8 ? (wave & 3) : wave;
   const int per = FP8 ? (wave < 4 ? 4 : 3) : 1;                 // streams of this wave
   const int v0 = FP8 ? 7 * simd + (wave < 4 ? 0 : 4) : wave;    // its first stream
   const int stream_stride = 16 * kStreams * nblk;               // tokens between a stream's tiles
   int nt = 0;                                                   // this wave's tiles
-  for (int j = 0; j < per; ++j) {
-    const int s0 = 16 * (kStreams * c + v0 + j);
-    nt += s0 < len ? (len - 1 - s0) / stream_stride + 1 : 0;
+  int nt_a = 0, s_a = 0, s_b = 0, stride_b = 0;                 // bf16: the two regions
+  if constexpr (FP8) {
+    for (int j = 0; j < per; ++j) {
+      const int s0 = 16 * (kStreams * c + v0 + j);
+      nt += s0 < len ? (len - 1 - s0) / stream_stride + 1 : 0;
+    }
+  } else {
+    const int tiles = (len + 15) >> 4;
+    const bool split = nblk >= 2 && (nblk & 1) == 0;
+    const int round = kStreams * nblk;  // tiles of one round over all the sequence's workgroups
+    const int tiles_a = split ? (tiles - (tiles >> 5)) / round * round : tiles;
+    const int len_a = min(len, 16 * tiles_a);
+    s_a = 16 * (kStreams * c + wave);
+    nt_a = s_a < len_a ? (len_a - 1 - s_a) / stream_stride + 1 : 0;
+    nt = nt_a;
+    if (split && (blockIdx.x & 1) == 0) {
+      // the sequence's even-XCD workgroups are every other chunk, starting
+      // at chunk 0 or 1: this one is the (c / 2)-th of them
+      stride_b = 16 * kStreams * (nblk >> 1);
+      s_b = 16 * (tiles_a + kStreams * (c >> 1) + wave);
+      nt += s_b < len ? (len - 1 - s_b) / stride_b + 1 : 0;
+    }
   }
   // The i-th tile of the wave; a wave's tiles are in increasing token order,
   // so the valid ones are i < nt.  len: past the end.
   auto tok0 = [&](int i) {
-    return i < nt ? 16 * (kStreams * c + v0 + i % per) + (i / per) * stream_stride : len;
+    if constexpr (FP8) {
+      return i < nt ? 16 * (kStreams * c + v0 + i % per) + (i / per) * stream_stride : len;
+    } else {
+      return i < nt_a ? s_a + i * stream_stride : (i < nt ? s_b + (i - nt_a) * stride_b : len);
+    }
   };
   auto local = [&](int i) { return (i / per) * kStreams + v0 + i % per; };  // LDS slot of the i-th tile
 

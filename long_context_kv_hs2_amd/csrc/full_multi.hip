@@ -92,10 +92,29 @@ __global__ __launch_bounds__(256 * GROUPS) void full_multi_kernel(MultiFullParam
   const int g = lane >> 4;
   const int tg = wave >> 2;          // this wave's token group
   const int lo_w = lo + NQ * tg;     // prefix length of this wave's first token
+  // The ordinary pass's bf16 dealing over the group's tokens [0, hi): whole
+  // rounds over all nblk chunks up to ~31/32 of the tiles, the rest over the
+  // even-XCD workgroups only when nblk is even (they stream faster); E4M3 and
+  // odd nblk: whole rounds throughout.  With one token the tiles of every
+  // wave are the ordinary pass's, so the outputs are its bit for bit.
   const int stream_stride = 16 * kMultiStreams * nblk;
-  const int s0 = 16 * (kMultiStreams * c + (wave & 3));  // this wave's first tile
-  const int nt = s0 < hi ? (hi - 1 - s0) / stream_stride + 1 : 0;
-  auto tok0 = [&](int i) { return i < nt ? s0 + i * stream_stride : hi; };
+  const int s_a = 16 * (kMultiStreams * c + (wave & 3));  // this wave's first tile
+  int nt_a, nt, s_b = 0, stride_b = 0;
+  {
+    const int tiles = (hi + 15) >> 4;
+    const bool split = !FP8 && nblk >= 2 && (nblk & 1) == 0;
+    const int round = kMultiStreams * nblk;
+    const int tiles_a = split ? (tiles - (tiles >> 5)) / round * round : tiles;
+    const int len_a = min(hi, 16 * tiles_a);
+    nt_a = s_a < len_a ? (len_a - 1 - s_a) / stream_stride + 1 : 0;
+    nt = nt_a;
+    if (split && (blockIdx.x & 1) == 0) {
+      stride_b = 16 * kMultiStreams * (nblk >> 1);
+      s_b = 16 * (tiles_a + kMultiStreams * (c >> 1) + (wave & 3));
+      nt += s_b < hi ? (hi - 1 - s_b) / stride_b + 1 : 0;
+    }
+  }
+  auto tok0 = [&](int i) { return i < nt_a ? s_a + i * stream_stride : (i < nt ? s_b + (i - nt_a) * stride_b : hi); };
 
   constexpr int kRowBytes = FP8 ? kDim : 2 * kDim;
   const uint8_t* __restrict__ kbase = p.k + base * kRowBytes;
