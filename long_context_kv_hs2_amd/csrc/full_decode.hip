@@ -92,12 +92,12 @@ __global__ __launch_bounds__(64 * full_waves<FP8>()) void full_partial_kernel(Fu
   constexpr int kStreams = full_streams<FP8>();
   constexpr int kThreads = 64 * kWaves;
   // Tiles of one wave (a bound for the flush loop) and of one workgroup
-  // (bound-mode LDS slots).  E4M3: a workgroup holds at most chunk / 16 +
-  // kStreams.  bf16: a wave holds at most chunk / 64 + 1, or with the split
-  // below at most (31/32) chunk / 64 + chunk / 1024 + 4 (the even-XCD share).
-  constexpr int kMaxWaveTiles = ((FP8 ? 4 : 1) * (max_chunk(FP8) / (16 * kStreams) + 1) + 15) / 16 * 16;
-  static_assert(FP8 || kMaxWaveTiles >= max_chunk(false) / 64 * 31 / 32 + max_chunk(false) / 1024 + 4,
-                "bf16 wave tile bound");
+  // (bound-mode LDS slots).  E4M3: a wave holds at most 4 (chunk / 448 + 1)
+  // and a workgroup chunk / 16 + kStreams.  bf16: a wave holds at most
+  // chunk / 64 + 1, or with the even-XCD split below at most
+  // (chunk / 64) (1 + 1 / D) + 4 (D = kEvenXcdDen), and a workgroup four waves'.
+  constexpr int kBf16WaveTiles = (max_chunk(false) / 64 * (kEvenXcdDen + 1) / kEvenXcdDen + 4 + 15) / 16 * 16;
+  constexpr int kMaxWaveTiles = FP8 ? (4 * (max_chunk(true) / (16 * kStreams) + 1) + 15) / 16 * 16 : kBf16WaveTiles;
   constexpr int kLocalTiles = FP8 ? max_chunk(FP8) / 16 + kStreams : kStreams * kMaxWaveTiles;
   __shared__ float s_m[kWaves][kHeads];
   __shared__ float s_z[kWaves][kHeads];
@@ -134,10 +134,11 @@ __global__ __launch_bounds__(64 * full_waves<FP8>()) void full_partial_kernel(Fu
   // per SIMD the workgroups on odd XCDs stream about 6.5% slower than those on
   // even ones (per-workgroup end times, the same on every part measured).  So
   // the sequence's tiles are dealt in two regions: whole rounds over all its
-  // workgroups up to ~31/32 of its tiles, then the rest over its even-XCD
+  // workgroups up to ~(1 - 1/D) of its tiles, then the rest over its even-XCD
   // workgroups only (every other chunk, nblk / 2 of them), which thus take
-  // 33 tiles for every 31 of the others.  The split depends only on the batch,
-  // so every partial holds the same tokens on every call.
+  // D + 1 tiles for every D - 1 of the others (D = kEvenXcdDen).  The split
+  // depends only on the batch, so every partial holds the same tokens on
+  // every call.
   const int nblk = (len + p.chunk - 1) / p.chunk;
   const int simd = FP8 ? (wave & 3) : wave;
   const int per = FP8 ? (wave < 4 ? 4 : 3) : 1;                 // streams of this wave
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(64 * full_waves<FP8>()) void full_partial_kernel(Fu
     const int tiles = (len + 15) >> 4;
     const bool split = nblk >= 2 && (nblk & 1) == 0;
     const int round = kStreams * nblk;  // tiles of one round over all the sequence's workgroups
-    const int tiles_a = split ? (tiles - (tiles >> 5)) / round * round : tiles;
+    const int tiles_a = split ? (tiles - tiles / kEvenXcdDen) / round * round : tiles;
     const int len_a = min(len, 16 * tiles_a);
     s_a = 16 * (kStreams * c + wave);
     nt_a = s_a < len_a ? (len_a - 1 - s_a) / stream_stride + 1 : 0;

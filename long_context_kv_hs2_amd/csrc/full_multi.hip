@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256 * GROUPS) void full_multi_kernel(MultiFullParam
   const int tg = wave >> 2;          // this wave's token group
   const int lo_w = lo + NQ * tg;     // prefix length of this wave's first token
   // The ordinary pass's bf16 dealing over the group's tokens [0, hi): whole
-  // rounds over all nblk chunks up to ~31/32 of the tiles, the rest over the
+  // rounds over all nblk chunks up to ~(1 - 1/kEvenXcdDen) of the tiles, the rest over the
   // even-XCD workgroups only when nblk is even (they stream faster); E4M3 and
   // odd nblk: whole rounds throughout.  With one token the tiles of every
   // wave are the ordinary pass's, so the outputs are its bit for bit.
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256 * GROUPS) void full_multi_kernel(MultiFullParam
     const int tiles = (hi + 15) >> 4;
     const bool split = !FP8 && nblk >= 2 && (nblk & 1) == 0;
     const int round = kMultiStreams * nblk;
-    const int tiles_a = split ? (tiles - (tiles >> 5)) / round * round : tiles;
+    const int tiles_a = split ? (tiles - tiles / kEvenXcdDen) / round * round : tiles;
     const int len_a = min(hi, 16 * tiles_a);
     nt_a = s_a < len_a ? (len_a - 1 - s_a) / stream_stride + 1 : 0;
     nt = nt_a;

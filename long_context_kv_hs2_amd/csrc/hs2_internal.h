@@ -14,6 +14,10 @@ namespace hs2 {
 constexpr int kMaxChunkBf16 = 16384;
 constexpr int kMaxChunkFp8 = 39 * 448;
 constexpr int max_chunk(bool fp8) { return fp8 ? kMaxChunkFp8 : kMaxChunkBf16; }
+// bf16 full pass, even number of chunks: the last 1/kEvenXcdDen of a
+// sequence's tiles go to the workgroups on even XCDs only (they stream
+// faster), which thus take (D + 1) tiles for every (D - 1) of the others.
+constexpr int kEvenXcdDen = 21;
 constexpr int chunk_quantum(bool fp8) { return fp8 ? 448 : 64; }
 struct FullParams {
   const int64_t* seq_offsets;
