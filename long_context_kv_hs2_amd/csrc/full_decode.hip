@@ -129,10 +129,11 @@ __global__ __launch_bounds__(64 * full_waves<FP8>()) void full_partial_kernel(Fu
   // streams' k-th tiles in stream order, then the (k + 1)-th.  The split-K
   // merge does not depend on which tokens a partial holds.
   //
-  // bf16 and an even number of chunks: workgroup w runs on XCD w mod 8 (the
-  // dispatcher deals workgroups round-robin over the XCDs), and with one wave
-  // per SIMD the workgroups on odd XCDs stream about 6.5% slower than those on
-  // even ones (per-workgroup end times, the same on every part measured).  So
+  // bf16, a batch of equal lengths and an even number of chunks: workgroup w
+  // runs on XCD w mod 8 (the dispatcher deals workgroups round-robin over the
+  // XCDs), and with one wave per SIMD the workgroups on odd XCDs stream about
+  // 6.5% slower than those on even ones (per-workgroup end times, the same on
+  // every part measured; a ragged batch is set by its longest sequences).  So
   // the sequence's tiles are dealt in two regions: whole rounds over all its
   // workgroups up to ~(1 - 1/D) of its tiles, then the rest over its even-XCD
   // workgroups only (every other chunk, nblk / 2 of them), which thus take
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(64 * full_waves<FP8>()) void full_partial_kernel(Fu
     }
   } else {
     const int tiles = (len + 15) >> 4;
-    const bool split = nblk >= 2 && (nblk & 1) == 0;
+    const bool split = p.xcd_split && nblk >= 2 && (nblk & 1) == 0;
     const int round = kStreams * nblk;  // tiles of one round over all the sequence's workgroups
     const int tiles_a = split ? (tiles - tiles / kEvenXcdDen) / round * round : tiles;
     const int len_a = min(len, 16 * tiles_a);

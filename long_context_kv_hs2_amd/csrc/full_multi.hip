@@ -92,17 +92,21 @@ __global__ __launch_bounds__(256 * GROUPS) void full_multi_kernel(MultiFullParam
   const int g = lane >> 4;
   const int tg = wave >> 2;          // this wave's token group
   const int lo_w = lo + NQ * tg;     // prefix length of this wave's first token
-  // The ordinary pass's bf16 dealing over the group's tokens [0, hi): whole
-  // rounds over all nblk chunks up to ~(1 - 1/kEvenXcdDen) of the tiles, the rest over the
-  // even-XCD workgroups only when nblk is even (they stream faster); E4M3 and
-  // odd nblk: whole rounds throughout.  With one token the tiles of every
-  // wave are the ordinary pass's, so the outputs are its bit for bit.
+  // The ordinary pass's dealing over the group's tokens [0, hi): whole rounds
+  // over all nblk chunks, and with one token (the ordinary pass's case: one
+  // wave per SIMD, bound by its loads), bf16, a batch of equal lengths and
+  // nblk even, the last ~1/kEvenXcdDen of the tiles over the even-XCD
+  // workgroups only (they stream faster).  With more tokens a wave's
+  // arithmetic hides the XCDs' difference and the split measured slower
+  // (two tokens a wave: 495 -> 531 us at 32 x 128K).  So with one token the
+  // tiles of every wave are the ordinary pass's, and the outputs its bit for
+  // bit.
   const int stream_stride = 16 * kMultiStreams * nblk;
   const int s_a = 16 * (kMultiStreams * c + (wave & 3));  // this wave's first tile
   int nt_a, nt, s_b = 0, stride_b = 0;
   {
     const int tiles = (hi + 15) >> 4;
-    const bool split = !FP8 && nblk >= 2 && (nblk & 1) == 0;
+    const bool split = !FP8 && NQ == 1 && GROUPS == 1 && p.xcd_split && nblk >= 2 && (nblk & 1) == 0;
     const int round = kMultiStreams * nblk;
     const int tiles_a = split ? (tiles - tiles / kEvenXcdDen) / round * round : tiles;
     const int len_a = min(hi, 16 * tiles_a);

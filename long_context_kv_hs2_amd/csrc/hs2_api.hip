@@ -249,6 +249,13 @@ struct DecodeArgs {
   const MultiFullParams* multi = nullptr;  // multi-token decode: the shared-stream full pass (real batch)
 };
 
+// The full pass's even-XCD share (bf16 tiles dealt 22:20 to the workgroups
+// on even XCDs) pays when every workgroup streams the same amount; a ragged
+// batch leaves CUs idle and its longest sequences set the end.
+int even_xcd_split(const hs2_decode_desc& d) {
+  return d.kv_dtype == HS2_KV_BF16 && d.batch > 0 && d.total_tokens == static_cast<int64_t>(d.batch) * d.max_context;
+}
+
 FullParams full_params(const DecodeArgs& a, const DecodeLayout& L) {
   FullParams p{};
   p.kv_start = a.kv_start;
@@ -262,6 +269,7 @@ FullParams full_params(const DecodeArgs& a, const DecodeLayout& L) {
   p.q = a.q_full;
   p.qscale = static_cast<float>(static_cast<double>(a.d->softmax_scale) * kLog2e);
   p.batch = a.d->batch;
+  p.xcd_split = even_xcd_split(*a.d);
   p.chunk = L.chunk;
   p.chunks_per_seq = L.chunks_per_seq;
   p.partials = reinterpret_cast<float*>(ws_at(a.ws, L.partials));
@@ -329,6 +337,7 @@ hs2_status run_full(const DecodeArgs& a, const DecodeLayout& L, int mode, const 
     m.f.total_tokens = real.total_tokens;
     m.f.max_context = real.max_context;
     m.f.kv_start = nullptr;
+    m.f.xcd_split = real.xcd_split;
     m.fp8 = d.kv_dtype == HS2_KV_FP8_E4M3;
     for (int t = 0; t < m.n_query; t += kMultiQ) {
       m.t_first = t;
@@ -641,6 +650,7 @@ hs2_status hs2_decode_multi(const hs2_decode_desc* desc, int32_t n_query, const 
   mf.f.batch = d.batch;
   mf.f.total_tokens = d.total_tokens;
   mf.f.max_context = d.max_context;
+  mf.f.xcd_split = even_xcd_split(d);  // the real batch's, as hs2_decode_block's
   mf.voffs = mp.voffs;
   mf.n_query = n_query;
   DecodeArgs a{&v, mp.voffs, k_cache, v_cache, k_scale, v_scale, q_full, q_sparse, o_full, o_sparse,

@@ -14,9 +14,10 @@ namespace hs2 {
 constexpr int kMaxChunkBf16 = 16384;
 constexpr int kMaxChunkFp8 = 39 * 448;
 constexpr int max_chunk(bool fp8) { return fp8 ? kMaxChunkFp8 : kMaxChunkBf16; }
-// bf16 full pass, even number of chunks: the last 1/kEvenXcdDen of a
-// sequence's tiles go to the workgroups on even XCDs only (they stream
-// faster), which thus take (D + 1) tiles for every (D - 1) of the others.
+// bf16 full pass with one wave per SIMD over a batch of equal lengths, a
+// sequence with an even number of chunks: the last 1/kEvenXcdDen of its
+// tiles go to the workgroups on even XCDs only (they stream faster), which
+// thus take (D + 1) tiles for every (D - 1) of the others.
 constexpr int kEvenXcdDen = 21;
 constexpr int chunk_quantum(bool fp8) { return fp8 ? 448 : 64; }
 struct FullParams {
@@ -42,6 +43,7 @@ struct FullParams {
   uint32_t* hist0;           // [B][kRadixBins] selection histogram, cleared here
   uint32_t* counters;        // [B][4] selection counters, cleared here
   const int64_t* kv_start;   // [B] first K/V row of each sequence, or nullptr: the row seq_offsets[b]
+  int xcd_split;             // 1: bf16 and every sequence of the batch the same length (the even-XCD share)
 };
 // Slot of tile t (tokens [16t, 16t + 16)) of the sequence starting at row `base`:
 // unique over all sequences, at most N/16 + B.
