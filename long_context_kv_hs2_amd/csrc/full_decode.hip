@@ -154,8 +154,10 @@ __global__ __launch_bounds__(64 * full_waves<FP8>()) void full_partial_kernel(Fu
     }
   } else {
     const int tiles = (len + 15) >> 4;
-    const bool split = p.xcd_split && nblk >= 2 && (nblk & 1) == 0;
     const int round = kStreams * nblk;  // tiles of one round over all the sequence's workgroups
+    // (region A ends on a whole round, so the even-XCD share is 1/D to 1/D +
+    // round / tiles: split only with at least 4 D rounds, within a quarter of 1/D)
+    const bool split = p.xcd_split && nblk >= 2 && (nblk & 1) == 0 && tiles >= 4 * kEvenXcdDen * round;
     const int tiles_a = split ? (tiles - tiles / kEvenXcdDen) / round * round : tiles;
     const int len_a = min(len, 16 * tiles_a);
     s_a = 16 * (kStreams * c + wave);

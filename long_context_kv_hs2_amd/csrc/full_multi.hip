@@ -106,8 +106,9 @@ __global__ __launch_bounds__(256 * GROUPS) void full_multi_kernel(MultiFullParam
   int nt_a, nt, s_b = 0, stride_b = 0;
   {
     const int tiles = (hi + 15) >> 4;
-    const bool split = !FP8 && NQ == 1 && GROUPS == 1 && p.xcd_split && nblk >= 2 && (nblk & 1) == 0;
     const int round = kMultiStreams * nblk;
+    const bool split = !FP8 && NQ == 1 && GROUPS == 1 && p.xcd_split && nblk >= 2 && (nblk & 1) == 0 &&
+                       tiles >= 4 * kEvenXcdDen * round;
     const int tiles_a = split ? (tiles - tiles / kEvenXcdDen) / round * round : tiles;
     const int len_a = min(hi, 16 * tiles_a);
     nt_a = s_a < len_a ? (len_a - 1 - s_a) / stream_stride + 1 : 0;
