@@ -169,6 +169,20 @@ def test_zero_queries_uniform_attention():
     parity.check_decode(d, out)
 
 
+def test_equal_lengths_even_xcd_share():
+    # A bf16 batch of equal lengths whose sequences have an even number of
+    # chunks (16 of 6272 tokens) and enough rounds: the full pass deals the
+    # last ~1/21 of each sequence's tiles to its even-XCD workgroups only,
+    # here ending on a partial round and a 3-token last tile.  Every
+    # sequence against the oracle, and the two score paths bitwise equal.
+    lengths = [100003] * 16
+    say(f"case: even-XCD share, {len(lengths)} x {lengths[0]} bf16")
+    d = inputs.make_decode(lengths=lengths, n_sparse=2, seed=37, needles=64)
+    out, _, _ = run(d)
+    w = parity.check_decode(d, out)
+    say(f"worst {w}")
+
+
 def test_deterministic_bitwise():
     say("case: determinism, two runs")
     d = inputs.make_decode(lengths=[7000, 30000], n_sparse=2, seed=31, needles=64)

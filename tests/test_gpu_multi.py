@@ -94,11 +94,13 @@ def test_multi_token_sixteen_tokens():
     check_multi(d, run_multi(d))
 
 
-def test_one_query_token_is_the_hybrid_block():
+@pytest.mark.parametrize("lengths", [[7000, 0, 1500, 40000], [100003] * 16])
+def test_one_query_token_is_the_hybrid_block(lengths):
     # T = 1: the virtual batch is the batch itself, so every output equals
-    # hs2_decode_block's bit for bit.
-    lengths = [7000, 0, 1500, 40000]
-    print(f"case: multi-token decode with T=1 vs the hybrid block, lengths {lengths}", flush=True)
+    # hs2_decode_block's bit for bit.  16 x 100003 is a bf16 batch of equal
+    # lengths with 16 chunks a sequence and ~98 rounds: both passes deal the
+    # last tiles to the even-XCD workgroups only, ending on a partial round.
+    print(f"case: multi-token decode with T=1 vs the hybrid block, lengths {lengths[:4]} x{len(lengths)}", flush=True)
     d = multi_inputs(lengths, 1, "bf16", seed=93)
     m = run_multi(d)
     t = parity.to_device(d)
