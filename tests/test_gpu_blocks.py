@@ -112,7 +112,7 @@ def test_gen1_call_from_tile_sums(kv):
     assert same >= len(lengths) - 1, f"only {same} of {len(lengths)} lists agree"
 
 
-@pytest.mark.parametrize("workload", [2, 3])
+@pytest.mark.parametrize("workload", [2, 3, 4])
 def test_gen1_call_full_size(workload):
     # The gen-1 line the benchmark times, at the full workload sizes, every
     # sequence against the oracle's block rule.
